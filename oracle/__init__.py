@@ -1,0 +1,138 @@
+"""fp64 CPU oracle for the selective-scan forward pass (ctypes wrapper over oracle.c).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the HIP implementation and must never be used as a fallback for it.
+
+What it computes is documented in ``oracle.c``; the pins that tie it to the pages
+live in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+OK = 0
+ERR_NULL = -1
+ERR_EMPTY = -2
+ERR_NONFINITE = -3
+ERR_RETAIN = -4
+ERR_ALLOC = -5
+
+
+class OracleError(RuntimeError):
+    """Raised when the oracle refuses its inputs; ``code`` is the C status."""
+
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: oracle status {code}")
+        self.code = code
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (plain C, -O2, OpenMP over independent rows)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.oracle_softplus.argtypes = [ctypes.c_double]
+        lib.oracle_softplus.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_selective_recurrence.argtypes = [i64, dp, dp, dp, dp, dp]
+        lib.oracle_selective_recurrence.restype = ctypes.c_int
+        lib.oracle_selective_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 9 + [ctypes.c_int]
+        lib.oracle_selective_scan_fwd.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def softplus(x: float) -> float:
+    return _load().oracle_softplus(float(x))
+
+
+def silu(x: float) -> float:
+    return _load().oracle_silu(float(x))
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def selective_recurrence(value, retain, write, read) -> np.ndarray:
+    """Scalar retain/write/read recurrence of the qubittool page's runnable example."""
+    v, r, w, d = (_f64(x).reshape(-1) for x in (value, retain, write, read))
+    n = v.shape[0]
+    if not (r.shape[0] == w.shape[0] == d.shape[0] == n):
+        raise ValueError("all four step fields need the same length")
+    out = np.zeros(max(n, 1), dtype=np.float64)
+    code = _load().oracle_selective_recurrence(n, _ptr(v), _ptr(r), _ptr(w), _ptr(d), _ptr(out))
+    if code != OK:
+        raise OracleError(code, "selective_recurrence")
+    return out[:n]
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, nthreads: int = 0) -> np.ndarray:
+    """fp64 selective-scan forward.
+
+    u, delta, z: (batch, dim, L); B, C: (batch, N, L); A: (dim, N); D, dt_bias: (dim,).
+    Every input is converted to float64 exactly (fp32 and bf16 values are exact in fp64).
+    Returns y as float64 (batch, dim, L).
+    """
+    u, delta, A, B, C = (_f64(x) for x in (u, delta, A, B, C))
+    D, z, dt_bias = _f64(D), _f64(z), _f64(dt_bias)
+    if u.ndim != 3 or B.ndim != 3:
+        raise ValueError("u must be (batch, dim, L) and B (batch, N, L)")
+    batch, dim, L = u.shape
+    N = B.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("delta and z must match u")
+    if B.shape != (batch, N, L) or C.shape != (batch, N, L):
+        raise ValueError("B and C must be (batch, N, L)")
+    if A.shape != (dim, N):
+        raise ValueError("A must be (dim, N)")
+    for v in (D, dt_bias):
+        if v is not None and v.shape != (dim,):
+            raise ValueError("D and dt_bias must be (dim,)")
+    y = np.zeros((batch, dim, L), dtype=np.float64)
+    code = _load().oracle_selective_scan_fwd(
+        batch, L, dim, N, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+        _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y), int(nthreads))
+    if code != OK:
+        raise OracleError(code, "selective_scan_fwd")
+    return y

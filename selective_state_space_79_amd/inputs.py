@@ -1,0 +1,144 @@
+"""Seeded synthetic inputs for the selective-scan forward pass.
+
+This module only draws random numbers and lays them out.  It holds none of the
+scan's arithmetic, so both the HIP path and the fp64 oracle can be fed from it
+without sharing any computation.
+
+Recipe (the same for every workload; see ``make_inputs``):
+
+* generator ``numpy.random.Generator(PCG64(seed))``;
+* draw order: u, delta_raw, z (batch, dim, L), then B, C (batch, N, L), all
+  standard normal in float32, rounded to bfloat16 (round-to-nearest-even) when the
+  I/O type is bf16; then the skip D ~ N(0,1) (float32, dim); then per-channel
+  step targets dt_d, log-uniform on ``dt_range``; then, in scalar-decay mode,
+  one decay a_h = -U(1, 16) per head;
+* A[d, n] = -(n + 1) (float32) in diagonal mode;
+* dt_bias[d] = log(expm1(dt_d)) in float32, the bias whose softplus is dt_d, so
+  that the step size of channel d has median dt_d and spreads by e^{±2} with the
+  unit-normal delta_raw.
+
+Values are returned as float32 numpy arrays holding exactly the values the device
+sees (bf16 values are exact in float32 and float64).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+# The five workloads the scan is tested and measured on.  Shapes follow a
+# Mamba layer's scan: dim = d_inner = 2 * d_model, N = d_state.
+WORKLOADS = {
+    1: dict(name="tiny-fp32", batch=1, L=64, dim=4, N=4, io="f32", nheads=0, dt_range=(1e-3, 1e-1)),
+    2: dict(name="mamba-130m-layer", batch=8, L=2048, dim=1536, N=16, io="bf16", nheads=0, dt_range=(1e-3, 1e-1)),
+    3: dict(name="mamba-1.3b-layer", batch=4, L=4096, dim=4096, N=16, io="bf16", nheads=0, dt_range=(1e-3, 1e-1)),
+    4: dict(name="long-sequence", batch=1, L=131072, dim=2048, N=16, io="bf16", nheads=0, dt_range=(1e-4, 1e-2)),
+    5: dict(name="scalar-decay-large-state", batch=2, L=8192, dim=4096, N=128, io="bf16", nheads=64, dt_range=(1e-3, 1e-1)),
+}
+WORKLOAD_SEEDS = {1: 1, 2: 2, 3: 3, 4: 4, 5: 5}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), returned as float32.
+
+    Works in place on a float32 copy; inputs are finite normals, so NaN handling is
+    not needed.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    bits += np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+    bits &= np.uint32(0xFFFF0000)
+    return x
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of float32 values that are already bf16-exact (as int16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16).view(np.int16)
+
+
+@dataclasses.dataclass
+class ScanInputs:
+    batch: int
+    L: int
+    dim: int
+    N: int
+    nheads: int
+    io: str            # "f32" or "bf16": type of u, delta, z, B, C and y on the device
+    u: np.ndarray      # (batch, dim, L)
+    delta: np.ndarray  # (batch, dim, L)  raw step input, before bias and softplus
+    z: np.ndarray      # (batch, dim, L)
+    B: np.ndarray      # (batch, N, L)
+    C: np.ndarray      # (batch, N, L)
+    A: np.ndarray      # (dim, N) diagonal mode, or (nheads,) scalar-decay mode
+    D: np.ndarray      # (dim,)
+    dt_bias: np.ndarray  # (dim,)
+
+    def A_dense(self) -> np.ndarray:
+        """A as a (dim, N) array; in scalar-decay mode channel d takes its head's a_h.
+
+        Channel d belongs to head d // (dim // nheads) (heads are contiguous
+        channel blocks).
+        """
+        if self.nheads == 0:
+            return self.A
+        hd = self.dim // self.nheads
+        per_channel = np.repeat(self.A, hd)
+        return np.ascontiguousarray(np.broadcast_to(per_channel[:, None], (self.dim, self.N)), dtype=np.float32)
+
+    @property
+    def updates(self) -> int:
+        return self.batch * self.L * self.dim * self.N
+
+
+def make_inputs(batch: int, L: int, dim: int, N: int, *, seed: int, io: str = "bf16", nheads: int = 0,
+                dt_range=(1e-3, 1e-1), a_range=(1.0, 16.0)) -> ScanInputs:
+    """Draw one seeded input set (see the module docstring for the recipe)."""
+    if io not in ("f32", "bf16"):
+        raise ValueError("io must be 'f32' or 'bf16'")
+    if nheads and dim % nheads:
+        raise ValueError("dim must be a multiple of nheads")
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def draw(shape):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        return round_to_bf16(x) if io == "bf16" else x
+
+    u = draw((batch, dim, L))
+    delta = draw((batch, dim, L))
+    z = draw((batch, dim, L))
+    B = draw((batch, N, L))
+    C = draw((batch, N, L))
+    D = rng.standard_normal(dim, dtype=np.float32)
+    lo, hi = dt_range
+    dt = np.exp(rng.uniform(math.log(lo), math.log(hi), size=dim))
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+    if nheads:
+        A = (-rng.uniform(a_range[0], a_range[1], size=nheads)).astype(np.float32)
+    else:
+        A = np.ascontiguousarray(np.broadcast_to(-(np.arange(N, dtype=np.float32) + 1.0), (dim, N)))
+    return ScanInputs(batch, L, dim, N, nheads, io, u, delta, z, B, C, A, D, dt_bias)
+
+
+def make_workload(index: int, seed: int | None = None) -> ScanInputs:
+    """Inputs of one of the five named workloads (seed defaults to its index)."""
+    w = WORKLOADS[index]
+    return make_inputs(w["batch"], w["L"], w["dim"], w["N"], seed=WORKLOAD_SEEDS[index] if seed is None else seed,
+                       io=w["io"], nheads=w["nheads"], dt_range=w["dt_range"])
+
+
+def to_device(x: ScanInputs, device="cuda"):
+    """Upload to torch tensors: u/delta/z/B/C in the I/O type, A/D/dt_bias in float32."""
+    import torch
+
+    def io_tensor(a):
+        if x.io == "bf16":
+            return torch.from_numpy(bf16_bits(a)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    return dict(u=io_tensor(x.u), delta=io_tensor(x.delta), z=io_tensor(x.z), B=io_tensor(x.B), C=io_tensor(x.C),
+                A=f32(x.A), D=f32(x.D), dt_bias=f32(x.dt_bias))
