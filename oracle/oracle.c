@@ -132,8 +132,10 @@ int oracle_selective_scan_fwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
     const int64_t rows = batch * dim;
     int failed = 0;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#else
+    (void)nthreads;
 #endif
     {
         double* h = (double*)malloc((size_t)N * sizeof(double));
