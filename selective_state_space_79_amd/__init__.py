@@ -1,0 +1,199 @@
+"""Python binding of libssm.so, the MI355X selective-scan forward pass.
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``csrc/scan_fwd.hip`` behind the C ABI of ``include/ssm.h``.  There is no CPU or
+PyTorch fallback: if the library is missing, every call raises.
+
+The functions carry the C names (``ssm_selective_scan_fwd``,
+``ssm_selective_scan_workspace_bytes``, ``ssm_selective_scan_plan``,
+``ssm_status_string``); ``selective_scan_fwd`` additionally allocates y and the
+workspace through PyTorch's caching allocator.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libssm.so")
+
+SSM_OK = 0
+SSM_ERR_NULL = -1
+SSM_ERR_EMPTY = -2
+SSM_ERR_DIMS = -3
+SSM_ERR_DTYPE = -4
+SSM_ERR_ALIGN = -5
+SSM_ERR_WORKSPACE = -6
+SSM_ERR_HIP = -7
+SSM_ERR_ALIAS = -8
+SSM_F32 = 0
+SSM_BF16 = 1
+SSM_MAX_DSTATE = 256
+SSM_MAX_CHUNKS = 1024
+
+EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan",
+            "ssm_status_string")
+
+
+class SsmDims(ctypes.Structure):
+    """Mirror of ``ssm_dims`` in include/ssm.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("nheads", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("nchunks", ctypes.c_int32),
+        ("states_per_lane", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class SsmPlan(ctypes.Structure):
+    """Mirror of ``ssm_plan`` in include/ssm.h."""
+    _fields_ = [
+        ("nchunks", ctypes.c_int32),
+        ("states_per_lane", ctypes.c_int32),
+        ("waves_per_group", ctypes.c_int32),
+        ("time_tile", ctypes.c_int32),
+        ("chunk_len", ctypes.c_int64),
+        ("workgroups", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("lds_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {ssm_status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load libssm.so from the package directory (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m selective_state_space_79_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        lib.ssm_selective_scan_fwd.argtypes = [vp] * 9 + [ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_fwd.restype = ctypes.c_int
+        lib.ssm_selective_scan_workspace_bytes.argtypes = [ctypes.POINTER(SsmDims)]
+        lib.ssm_selective_scan_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssm_selective_scan_plan.argtypes = [ctypes.POINTER(SsmDims), ctypes.POINTER(SsmPlan)]
+        lib.ssm_selective_scan_plan.restype = ctypes.c_int
+        lib.ssm_status_string.argtypes = [ctypes.c_int]
+        lib.ssm_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def make_dims(batch, seqlen, dim, dstate, *, nheads=0, io_dtype=SSM_BF16, nchunks=0, states_per_lane=0,
+              workspace=0, workspace_bytes=0, reserved=0) -> SsmDims:
+    return SsmDims(batch, seqlen, dim, dstate, nheads, io_dtype, nchunks, states_per_lane, reserved,
+                   workspace or None, workspace_bytes)
+
+
+def ssm_status_string(status: int) -> str:
+    return load_library().ssm_status_string(int(status)).decode()
+
+
+def ssm_selective_scan_workspace_bytes(dims: SsmDims) -> int:
+    return int(load_library().ssm_selective_scan_workspace_bytes(ctypes.byref(dims)))
+
+
+def ssm_selective_scan_plan(dims: SsmDims) -> SsmPlan:
+    plan = SsmPlan()
+    st = load_library().ssm_selective_scan_plan(ctypes.byref(dims), ctypes.byref(plan))
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_selective_scan_plan")
+    return plan
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def ssm_selective_scan_fwd(u, delta, A, B, C, D, z, dt_bias, y, dims: SsmDims, stream=None) -> int:
+    """Call the C entry point with raw device pointers; returns the status code.
+
+    u, delta, z, y: (batch, dim, L); B, C: (batch, N, L) -- all in the I/O dtype;
+    A: float32 (dim, N) or (nheads,); D, dt_bias: float32 (dim,).  D, z and dt_bias
+    may be None.  ``stream`` is a torch.cuda.Stream (default: the current stream of
+    u's device).
+    """
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device)
+    return int(load_library().ssm_selective_scan_fwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y),
+        ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
+def dims_for(u, B, A, *, nchunks=0, states_per_lane=0) -> SsmDims:
+    """ssm_dims for tensors laid out as include/ssm.h describes."""
+    import torch
+
+    if u.dim() != 3 or B.dim() != 3:
+        raise ValueError("u must be (batch, dim, L) and B (batch, N, L)")
+    if u.dtype == torch.bfloat16:
+        io = SSM_BF16
+    elif u.dtype == torch.float32:
+        io = SSM_F32
+    else:
+        raise TypeError(f"unsupported I/O dtype {u.dtype}")
+    batch, dim, L = u.shape
+    nheads = A.shape[0] if A.dim() == 1 else 0
+    return make_dims(batch, L, dim, B.shape[1], nheads=nheads, io_dtype=io, nchunks=nchunks,
+                     states_per_lane=states_per_lane)
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, out=None, workspace=None, nchunks=0,
+                       states_per_lane=0, stream=None):
+    """Allocate y (and the workspace, if the plan needs one) and run the scan.
+
+    Tensors must be contiguous CUDA tensors with the layouts of include/ssm.h.
+    Raises SsmError on a refused call.  Returns y.
+    """
+    import torch
+
+    tensors = dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias)
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name in ("delta", "B", "C", "z"):
+        t = tensors[name]
+        if t is not None and t.dtype != u.dtype:
+            raise TypeError(f"{name} must have u's dtype {u.dtype}")
+    for name in ("A", "D", "dt_bias"):
+        t = tensors[name]
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    dims = dims_for(u, B, A, nchunks=nchunks, states_per_lane=states_per_lane)
+    if out is None:
+        out = torch.empty_like(u)
+    need = ssm_selective_scan_workspace_bytes(dims)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+        dims.workspace = workspace.data_ptr()
+        dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = ssm_selective_scan_fwd(u, delta, A, B, C, D, z, dt_bias, out, dims, stream)
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_selective_scan_fwd")
+    return out

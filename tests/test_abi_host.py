@@ -1,0 +1,125 @@
+"""Host-side checks of libssm.so that need no GPU.
+
+The library loads and exports every symbol include/ssm.h declares; every refusal
+status is returned before anything reaches the HIP runtime, so these calls are
+made with fake (never dereferenced) device addresses on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_79_amd as ssm
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ssm.h")
+FAKE = 0x10000  # 64 KiB-aligned fake device address, never dereferenced on refusal paths
+
+
+def _declared_symbols():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"SSM_API\s+[\w\s\*]*?\b(ssm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssm.load_library()
+    declared = _declared_symbols()
+    assert set(declared) == set(ssm.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in range(-8, 1):
+        s = ssm.ssm_status_string(st)
+        assert isinstance(s, str) and s and s != "unknown status"
+    assert ssm.ssm_status_string(-99) == "unknown status"
+
+
+def _call(dims, u=FAKE, delta=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000,
+          D=None, z=None, bias=None, y=FAKE + 0x500000):
+    lib = ssm.load_library()
+    args = [u, delta, A, B, C, D, z, bias, y]
+    args = [None if a is None else ctypes.c_void_p(a) for a in args]
+    return lib.ssm_selective_scan_fwd(*args, ctypes.byref(dims) if dims is not None else None, None)
+
+
+def small_dims(**kw):
+    base = dict(batch=1, seqlen=64, dim=4, dstate=4)
+    base.update({k: kw.pop(k) for k in list(kw) if k in base})
+    return ssm.make_dims(base["batch"], base["seqlen"], base["dim"], base["dstate"], **kw)
+
+
+def test_null_and_empty_are_refused():
+    assert _call(None) == ssm.SSM_ERR_NULL
+    assert _call(small_dims(), u=None) == ssm.SSM_ERR_NULL
+    assert _call(small_dims(), y=None) == ssm.SSM_ERR_NULL
+    for field in ("batch", "seqlen", "dim", "dstate"):
+        assert _call(small_dims(**{field: 0})) == ssm.SSM_ERR_EMPTY
+        assert _call(small_dims(**{field: -3})) == ssm.SSM_ERR_EMPTY
+
+
+def test_bad_sizes_dtype_and_options_are_refused():
+    assert _call(small_dims(io_dtype=7)) == ssm.SSM_ERR_DTYPE
+    assert _call(small_dims(dstate=ssm.SSM_MAX_DSTATE + 1)) == ssm.SSM_ERR_DIMS
+    assert _call(small_dims(dim=6, nheads=4)) == ssm.SSM_ERR_DIMS
+    assert _call(small_dims(nheads=-1)) == ssm.SSM_ERR_DIMS
+    assert _call(small_dims(nchunks=-1)) == ssm.SSM_ERR_DIMS
+    assert _call(small_dims(nchunks=ssm.SSM_MAX_CHUNKS + 1)) == ssm.SSM_ERR_DIMS
+    assert _call(small_dims(states_per_lane=3)) == ssm.SSM_ERR_DIMS
+    assert _call(small_dims(reserved=1)) == ssm.SSM_ERR_DIMS
+    assert _call(small_dims(batch=1 << 30, seqlen=1 << 20, dim=1 << 10)) == ssm.SSM_ERR_DIMS
+
+
+def test_misaligned_arrays_are_refused():
+    assert _call(small_dims(io_dtype=ssm.SSM_F32), u=FAKE + 2) == ssm.SSM_ERR_ALIGN
+    assert _call(small_dims(io_dtype=ssm.SSM_BF16), y=FAKE + 0x500001) == ssm.SSM_ERR_ALIGN
+    assert _call(small_dims(), A=FAKE + 0x200002) == ssm.SSM_ERR_ALIGN
+    assert _call(small_dims(), D=FAKE + 0x600002) == ssm.SSM_ERR_ALIGN
+
+
+def test_aliased_output_is_refused():
+    assert _call(small_dims(), y=FAKE) == ssm.SSM_ERR_ALIAS
+    assert _call(small_dims(), y=FAKE + 0x100000 + 64) == ssm.SSM_ERR_ALIAS
+    assert _call(small_dims(), z=FAKE + 0x500000 + 32) == ssm.SSM_ERR_ALIAS
+
+
+def test_workspace_rules():
+    dims = small_dims(seqlen=4096, dstate=16, io_dtype=ssm.SSM_BF16, nchunks=4)
+    need = ssm.ssm_selective_scan_workspace_bytes(dims)
+    assert need > 0 and need % 256 == 0
+    assert _call(dims) == ssm.SSM_ERR_WORKSPACE
+    dims.workspace, dims.workspace_bytes = FAKE + 0x800000, need - 4
+    assert _call(dims) == ssm.SSM_ERR_WORKSPACE
+    dims.workspace, dims.workspace_bytes = FAKE + 0x800000 + 64, need
+    assert _call(dims) == ssm.SSM_ERR_WORKSPACE
+    assert ssm.ssm_selective_scan_workspace_bytes(small_dims(nchunks=1)) == 0
+    assert ssm.ssm_selective_scan_workspace_bytes(small_dims(batch=0)) == 0
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+def test_plans_of_the_five_workloads(index):
+    from selective_state_space_79_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[index]
+    dims = ssm.make_dims(w["batch"], w["L"], w["dim"], w["N"], nheads=w["nheads"],
+                         io_dtype=ssm.SSM_BF16 if w["io"] == "bf16" else ssm.SSM_F32)
+    plan = ssm.ssm_selective_scan_plan(dims).as_dict()
+    assert plan["states_per_lane"] * plan["waves_per_group"] >= w["N"]
+    assert plan["lds_bytes"] <= 160 * 1024
+    assert plan["chunk_len"] * plan["nchunks"] >= w["L"] > plan["chunk_len"] * (plan["nchunks"] - 1)
+    if index == 4:
+        assert plan["nchunks"] > 1 and plan["workspace_bytes"] > 0     # too few channels to fill the GPU
+    if index == 3:
+        assert plan["nchunks"] == 1 and plan["workspace_bytes"] == 0
+
+
+def test_forced_options_show_in_plan():
+    for spl in (1, 2, 4, 8, 16):
+        plan = ssm.ssm_selective_scan_plan(small_dims(dstate=16, states_per_lane=spl))
+        assert plan.states_per_lane == spl and plan.waves_per_group == -(-16 // spl)
+    plan = ssm.ssm_selective_scan_plan(small_dims(seqlen=1000, nchunks=5))
+    assert plan.nchunks == 5
+    plan = ssm.ssm_selective_scan_plan(small_dims(seqlen=10, nchunks=50))
+    assert plan.nchunks == 1      # clamped: one time tile holds the whole sequence
+    assert ssm.ssm_selective_scan_plan(small_dims(dstate=256)).lds_bytes <= 160 * 1024

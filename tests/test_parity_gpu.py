@@ -1,0 +1,111 @@
+"""GPU parity: the HIP scan (through the C ABI) against the fp64 oracle.
+
+Inputs are seeded and synthetic (selective_state_space_79_amd.inputs).  Small and
+ragged shapes are compared element by element over the whole output; the five
+named workloads run at full size in the launch configuration the benchmark uses
+and are compared on whole sampled (batch, channel) rows, which the oracle computes
+one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from scan_cases import TOL, rel_err, run_gpu, run_oracle, run_oracle_rows, sample_rows
+from selective_state_space_79_amd.inputs import ScanInputs, make_inputs, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def test_worked_example_through_abi():
+    """The qubittool scalar example (retain/write/read) as a one-state scan:
+    A = -1, dt = -ln(retain) via its inverse softplus, B = write/dt, u = value, C = 1."""
+    announce("worked example f32 (1,3,1,1)")
+    value = np.array([2.0, 9.0, 1.0])
+    retain = np.array([0.10, 0.95, 0.50])
+    write = np.array([1.0, 0.0, 1.0])
+    dt = -np.log(retain)
+    delta = np.array([math.log(math.expm1(v)) for v in dt])
+    f = lambda a: np.asarray(a, dtype=np.float32).reshape(1, 1, 3)
+    x = ScanInputs(1, 3, 1, 1, 0, "f32", f(value), f(delta), f(np.zeros(3)), f(write / dt), f(np.ones(3)),
+                   np.array([[-1.0]], dtype=np.float32), np.zeros(1, np.float32), np.zeros(1, np.float32))
+    y = run_gpu(x, with_D=False, with_z=False, with_bias=False)
+    np.testing.assert_allclose(y.reshape(-1), [2.0, 1.9, 1.95], rtol=0, atol=2e-6)
+    yref = run_oracle(x, with_D=False, with_z=False, with_bias=False)
+    assert rel_err(y, yref) < 2e-6
+
+
+def test_tiny_fp32_workload():
+    x = make_workload(1)
+    announce(f"workload 1 {x.batch, x.L, x.dim, x.N} f32")
+    y = run_gpu(x)
+    err = rel_err(y, run_oracle(x))
+    print(f"workload 1 err={err:.3e}", flush=True)
+    assert err <= TOL["f32"]
+
+
+# (batch, L, dim, N, io, nheads, with_D, with_z, with_bias, nchunks, states_per_lane)
+RAGGED = [
+    (1, 1, 1, 1, "f32", 0, True, True, True, 0, 0),
+    (1, 7, 3, 2, "f32", 0, True, True, True, 0, 0),
+    (2, 33, 65, 4, "f32", 0, True, True, True, 0, 0),
+    (1, 100, 64, 16, "f32", 0, True, False, True, 0, 0),
+    (3, 257, 130, 16, "bf16", 0, True, True, True, 0, 0),
+    (2, 64, 63, 16, "bf16", 0, False, True, False, 0, 0),
+    (1, 200, 129, 3, "bf16", 0, True, True, True, 0, 0),
+    (1, 96, 64, 5, "f32", 0, True, True, True, 0, 0),
+    (2, 128, 72, 16, "bf16", 4, True, True, True, 0, 0),
+    (1, 160, 128, 128, "bf16", 8, True, True, True, 0, 0),
+    (1, 48, 64, 128, "bf16", 0, True, True, True, 0, 0),
+    (1, 40, 64, 256, "bf16", 0, True, True, True, 0, 0),
+    (1, 40, 70, 256, "f32", 2, True, True, True, 0, 0),
+    # pieces along L: every carry path, ragged last piece
+    (1, 1000, 64, 16, "bf16", 0, True, True, True, 2, 0),
+    (2, 777, 100, 16, "f32", 0, True, True, True, 5, 0),
+    (1, 999, 64, 4, "bf16", 0, True, True, True, 31, 0),
+    (1, 512, 64, 128, "bf16", 4, True, True, True, 3, 0),
+    (1, 300, 65, 16, "f32", 0, True, True, True, 7, 0),
+    # forced states per lane
+    (1, 80, 64, 16, "bf16", 0, True, True, True, 0, 1),
+    (1, 80, 64, 16, "bf16", 0, True, True, True, 0, 2),
+    (1, 80, 64, 16, "f32", 0, True, True, True, 0, 8),
+    (1, 80, 64, 16, "f32", 0, True, True, True, 0, 16),
+    (1, 80, 64, 24, "bf16", 0, True, True, True, 0, 16),
+    (1, 80, 64, 64, "bf16", 0, True, True, True, 3, 4),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "b{}L{}d{}N{}{}h{}D{}z{}bias{}ch{}spl{}".format(*[int(v) if isinstance(v, bool) else v for v in c]))
+def test_ragged_shapes(case):
+    batch, L, dim, N, io, nheads, wD, wz, wb, nch, spl = case
+    seed = 1000 + RAGGED.index(case)
+    announce(f"ragged {case} seed={seed}")
+    x = make_inputs(batch, L, dim, N, seed=seed, io=io, nheads=nheads)
+    y = run_gpu(x, with_D=wD, with_z=wz, with_bias=wb, nchunks=nch, states_per_lane=spl)
+    yref = run_oracle(x, with_D=wD, with_z=wz, with_bias=wb)
+    err = rel_err(y, yref)
+    print(f"err={err:.3e}", flush=True)
+    assert np.all(np.isfinite(y))
+    assert err <= TOL[io]
+
+
+@pytest.mark.parametrize("index", [2, 3, 4, 5])
+def test_full_size_workload_sampled_rows(index):
+    """Full-size run in the benchmark's launch configuration (library-chosen plan),
+    checked on whole sampled rows."""
+    x = make_workload(index)
+    announce(f"workload {index} {(x.batch, x.L, x.dim, x.N, x.nheads)} full size")
+    y = run_gpu(x)
+    assert np.all(np.isfinite(y))
+    rows = sample_rows(x, 24 if index != 4 else 12, seed=index)
+    yref = run_oracle_rows(x, rows)
+    ys = np.stack([y[b, d] for b, d in rows])
+    err = rel_err(ys, yref)
+    print(f"workload {index} rows={len(rows)} err={err:.3e}", flush=True)
+    assert err <= TOL[x.io]
