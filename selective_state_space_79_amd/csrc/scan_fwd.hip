@@ -105,16 +105,22 @@ __device__ inline void store_vec(IO* __restrict__ row, int64_t t, int64_t tend, 
 }
 
 // ------------------------------------------------------------------ elementwise math (fp32)
-// softplus(v) = max(v, 0) + log1p(exp(-|v|)).  log1p(e) for e in (0, 1] is taken as
-// log(w) * e / (w - 1) with w = 1 + e, which cancels the rounding of w (Goldberg's
-// log1p identity); w == 1 means e is below half an ulp of 1 and log1p(e) = e.
-__device__ inline float softplus_f32(float v) {
+// Step sizes are carried in log2 units, dt2 = softplus(v) / ln 2, so that the decay
+// exp(dt * A) is one exp2(dt2 * A) and no ln 2 scaling is needed per state entry
+// (ln 2 is folded into B once per token instead).
+//
+// dt2 = max(v, 0) * log2(e) + log2(1 + e),  e = 2^(-|v| log2 e) in (0, 1].
+// w = fl(1 + e) carries the rounding error c = (w - 1) - e, which is exact in fp32
+// (both subtractions are exact by Sterbenz' lemma), so log2(1 + e) = log2(w - c)
+// = log2(w) - c / (w ln 2) + O(c^2).  Using c / ln 2 instead of c / (w ln 2) changes
+// the result by at most |c| (1 - 1/w) / ln 2 <= 2^-25 / ln 2 absolute, and by at most
+// 2^-24 relative when e is small (w close to 1), i.e. below fp32 rounding.
+__device__ inline float softplus_log2(float v) {
     const float e = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
     const float w = 1.0f + e;
-    const float wm1 = w - 1.0f;
-    const float lw = __builtin_amdgcn_logf(w) * kLn2;
-    const float lp = (wm1 == 0.0f) ? e : lw * (e * __builtin_amdgcn_rcpf(wm1));
-    return fmaxf(v, 0.0f) + lp;
+    const float c = (w - 1.0f) - e;
+    const float l = fmaf(c, -kLog2e, __builtin_amdgcn_logf(w));
+    return fmaf(fmaxf(v, 0.0f), kLog2e, l);
 }
 
 // SiLU(v) = v / (1 + exp(-v)); exp(-v) = inf for very negative v gives -0, the limit.
@@ -140,45 +146,84 @@ struct Params {
     int32_t nblk_d;       // channel blocks per batch row
     int32_t batch;
     int32_t np;           // padded state count = waves * SPL
-    float* ws_H;          // [blocks][nchunks][np][64] piece end states from zero (pass 1)
-    float* ws_S;          // [blocks][nchunks][64]     sum of dt over each piece (pass 1)
-    float* ws_Hin;        // [blocks][nchunks][np][64] true starting state of each piece
+    float* ws_H;          // [groups][nchunks][np][64] piece end states from zero (pass 1)
+    float* ws_S;          // [groups][nchunks][64]     sum of dt2 over each piece (pass 1)
+    float* ws_Hin;        // [groups][nchunks][np][64] true starting state of each piece
 };
 
 enum Mode { kFull = 0, kAggregate = 1 };
 
-// LDS layout (floats): dx[T][64] float2 | sB[T][np] | sC[T][np] | sY[G][T][64]
+// LDS layout (floats); rows of 64 channels are padded to kRow entries so that the
+// staging writes and epilogue reads, whose lanes span 4 time steps of 16 channels,
+// fall in distinct banks:
+//   sDX [T][kRow] float2  per (step, channel): (dt2, dt2*u), or (exp(dt*a_h), dt2*u) in
+//                         scalar-decay full mode
+//   sBC [G][T][2*SPL]     per (wave, step): B*ln2 of the wave's SPL state entries, then C
+//   sY  [G][T][kRowY]     per (wave, step, channel): partial read-out (full mode only)
+constexpr int kRow = kLanes + 1;
+constexpr int kRowY = kLanes + 2;
 inline size_t lds_floats(int T, int G, int np, bool full) {
-    return size_t(T) * kLanes * 2 + 2 * size_t(T) * np + (full ? size_t(G) * T * kLanes : 0);
+    return size_t(T) * kRow * 2 + 2 * size_t(T) * np + (full ? size_t(G) * T * kRowY : 0);
+}
+
+template <int SPL> struct BCVec { float v[2 * SPL]; };
+
+template <int SPL>
+__device__ inline BCVec<SPL> read_bc(const float* __restrict__ q) {
+    BCVec<SPL> r;
+    if constexpr (SPL == 1) {
+        const float2 t = *reinterpret_cast<const float2*>(q);
+        r.v[0] = t.x;
+        r.v[1] = t.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < SPL / 2; ++i) {
+            const float4 t = reinterpret_cast<const float4*>(q)[i];
+            r.v[4 * i + 0] = t.x;
+            r.v[4 * i + 1] = t.y;
+            r.v[4 * i + 2] = t.z;
+            r.v[4 * i + 3] = t.w;
+        }
+    }
+    return r;
 }
 
 // One launch processes, for every (batch, channel block, piece), the piece's time
 // tiles in order.  MODE kFull reads out and stores y (starting from ws_Hin when the
 // piece is not the first); MODE kAggregate only records the piece's end state from
-// zero and its dt sum.
+// zero and its dt2 sum.
 //
-// Threads: NT = 64 * max(G, 4).  Waves 0 .. G-1 walk (SPL state entries per lane);
-// all waves stage and finish tiles.  With T <= 32 this bounds the vectors each
-// thread stages per tile to KMAX (1 for bf16, 2 for f32), checked on the host.
-template <typename IO, int SPL, bool SCALAR, int MODE, bool VEC, int NTMAX>
-__global__ void __launch_bounds__(NTMAX) scan_fwd_kernel(Params p, int T, int G) {
+// G waves (4, 8 or 16; 64*G threads) each carry SPL state entries of every channel;
+// entries n >= N are padding with A = 0 and B = C = 0, which stay zero.  All threads
+// stage and finish tiles.  Staged steps beyond the piece's end are identity steps
+// (dt2 = 0, x = 0), so the walk always runs whole tiles.
+template <typename IO, int SPL, bool SCALAR, int MODE, bool VEC, int G>
+__global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
     constexpr int VW = IOT<IO>::VW;
-    constexpr int KMAX = (VW == 4) ? 2 : 1;
+    constexpr int NT = G * kLanes;
+    constexpr int T = G <= 8 ? 32 : 16;            // time tile
+    constexpr int TV = T / VW;                     // vectors per row per tile
+    constexpr int NVX = kLanes * TV;               // u/delta/z vectors per tile
+    constexpr int KX = (NVX + NT - 1) / NT;        // of them per thread
     constexpr bool kFullMode = (MODE == kFull);
+    constexpr int BCW = 2 * SPL;                   // floats per (wave, step) in sBC
+    constexpr int NBC = G * T * BCW;               // sBC values per tile
+    // B/C staging: one sBC value per thread and pass; a wave's 64 lanes cover 64/BCW
+    // steps x BCW slots, i.e. 64 distinct LDS banks per write.
+    constexpr int KBC = (NBC + NT - 1) / NT;
+    constexpr int QB = SPL <= 4 ? 4 : (SPL == 8 ? 2 : 1);   // steps whose LDS operands are read together
+    constexpr int NP = G * SPL;                    // padded state count
+    constexpr float kLn2f = kLn2;
+    static_assert(T % 8 == 0, "time tile must hold whole vectors and step groups");
 
     extern __shared__ float smem[];
-    const int NT = blockDim.x;
     const int tid = threadIdx.x;
     const int w = tid / kLanes;
     const int lane = tid % kLanes;
-    const int np = p.np;
-    const int TV = T / VW;                         // vectors per row per tile
-    const bool walker = w < G;
 
     float2* sDX = reinterpret_cast<float2*>(smem);
-    float* sB = smem + size_t(T) * kLanes * 2;
-    float* sC = sB + size_t(T) * np;
-    float* sY = sC + size_t(T) * np;
+    float* sBC = smem + size_t(T) * kRow * 2;
+    float* sY = sBC + size_t(NBC);
 
     // blockIdx.x -> (piece, batch, channel block), channel block fastest
     const int64_t bid = blockIdx.x;
@@ -189,6 +234,7 @@ __global__ void __launch_bounds__(NTMAX) scan_fwd_kernel(Params p, int T, int G)
     const int64_t c0 = int64_t(cblk) * kLanes;
     const int64_t tbeg = int64_t(piece) * p.chunk_len;
     const int64_t tend = (tbeg + p.chunk_len < p.L) ? tbeg + p.chunk_len : p.L;
+    const bool has_z = kFullMode && p.z != nullptr;
 
     const IO* __restrict__ gu = static_cast<const IO*>(p.u);
     const IO* __restrict__ gdl = static_cast<const IO*>(p.delta);
@@ -197,131 +243,162 @@ __global__ void __launch_bounds__(NTMAX) scan_fwd_kernel(Params p, int T, int G)
     const IO* __restrict__ gC = static_cast<const IO*>(p.Cm);
     IO* __restrict__ gy = static_cast<IO*>(p.y);
 
-    // ---- per-lane constants: this lane's channel and its SPL decay rates (log2 units)
+    // ---- walk constants: this lane's channel and its SPL decay rates
     const int64_t dch = c0 + lane;
     const bool lane_ok = dch < p.dim;
-    float A2[SPL];
-    float a2_scalar = 0.0f;
+    float Ar[SPL];
+    float a_scalar = 0.0f;
     if constexpr (SCALAR) {
-        a2_scalar = lane_ok ? p.A[dch / p.head_dim] * kLog2e : 0.0f;
+        a_scalar = lane_ok ? p.A[dch / p.head_dim] : 0.0f;
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) A2[j] = a2_scalar;
+        for (int j = 0; j < SPL; ++j) Ar[j] = a_scalar;
     } else {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
             const int64_t n = int64_t(w) * SPL + j;
-            A2[j] = (walker && lane_ok && n < p.N) ? p.A[dch * p.N + n] * kLog2e : 0.0f;
+            Ar[j] = (lane_ok && n < p.N) ? p.A[dch * p.N + n] : 0.0f;
         }
+    }
+
+    // ---- staging/epilogue constants: the channels of this thread's vectors
+    int sv_ch[KX], sv_tv[KX];
+    bool sv_on[KX], sv_ok[KX];
+    float sv_bias[KX], sv_skip[KX], sv_ah[KX];
+    int64_t sv_row[KX];
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+        const int v = tid + k * NT;
+        sv_on[k] = v < NVX;
+        sv_ch[k] = (v / TV) % kLanes;
+        sv_tv[k] = v % TV;
+        const int64_t d = c0 + sv_ch[k];
+        sv_ok[k] = sv_on[k] && d < p.dim;
+        sv_bias[k] = (sv_ok[k] && p.bias) ? p.bias[d] : 0.0f;
+        sv_skip[k] = (sv_ok[k] && p.Dskip) ? p.Dskip[d] : 0.0f;
+        sv_ah[k] = 0.0f;
+        if constexpr (SCALAR) sv_ah[k] = sv_ok[k] ? p.A[d / p.head_dim] : 0.0f;
+        sv_row[k] = (int64_t(b) * p.dim + (sv_ok[k] ? d : 0)) * p.L;
     }
 
     // ---- starting state of this piece
     float h[SPL];
 #pragma unroll
     for (int j = 0; j < SPL; ++j) h[j] = 0.0f;
-    if (kFullMode && piece > 0 && walker) {
-        const float* hin = p.ws_Hin + ((blk * p.nchunks + piece) * np + int64_t(w) * SPL) * kLanes + lane;
+    if (kFullMode && piece > 0) {
+        const float* hin = p.ws_Hin + ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
 #pragma unroll
         for (int j = 0; j < SPL; ++j) h[j] = hin[int64_t(j) * kLanes];
     }
-    float dtsum = 0.0f, dtcomp = 0.0f;   // compensated (Kahan) sum of dt over the piece
+    // Settle these loads now: left pending, they make the compiler wait for every
+    // outstanding load (the next tile's prefetch included) inside the walk.
+    __builtin_amdgcn_s_waitcnt(0);
+    float dtsum = 0.0f, dtcomp = 0.0f;   // compensated (Kahan) sum of dt2 over the piece
 
-    // ---- tile vectors this thread stages: v = tid + k*NT
-    const int nvx = kLanes * TV;                   // u/delta/z vectors per tile
-    const int nvb = np * TV;                       // B/C vectors per tile
-    Vec<IO> nu[KMAX], ndl[KMAX], nz[KMAX], cu[KMAX], cz[KMAX], nB[KMAX], nC[KMAX];
+    Vec<IO> nu[KX], ndl[KX], nz[KX], cu[KX], cz[KX];
+    IO nbcv[KBC];
 
     auto issue_loads = [&](int64_t t0) {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const int v = tid + k * NT;
-            if (v < nvx) {
-                const int ch = v / TV, tv = v % TV;
-                const int64_t d = c0 + ch;
-                const bool ok = d < p.dim;
-                const int64_t row = (int64_t(b) * p.dim + (ok ? d : 0)) * p.L;
-                const int64_t t = t0 + tv * VW;
-                nu[k] = load_vec<IO, VEC>(gu + row, t, tend, ok);
-                ndl[k] = load_vec<IO, VEC>(gdl + row, t, tend, ok);
-                if (kFullMode && gz) nz[k] = load_vec<IO, VEC>(gz + row, t, tend, ok);
+        for (int k = 0; k < KX; ++k) {
+            if (sv_on[k]) {
+                const int64_t t = t0 + sv_tv[k] * VW;
+                nu[k] = load_vec<IO, VEC>(gu + sv_row[k], t, tend, sv_ok[k]);
+                ndl[k] = load_vec<IO, VEC>(gdl + sv_row[k], t, tend, sv_ok[k]);
+                if (has_z) nz[k] = load_vec<IO, VEC>(gz + sv_row[k], t, tend, sv_ok[k]);
             }
-            if (v < nvb) {
-                const int n = v / TV, tv = v % TV;
-                const bool ok = n < p.N;
-                const int64_t row = (int64_t(b) * p.N + (ok ? n : 0)) * p.L;
-                const int64_t t = t0 + tv * VW;
-                nB[k] = load_vec<IO, VEC>(gB + row, t, tend, ok);
-                if (kFullMode) nC[k] = load_vec<IO, VEC>(gC + row, t, tend, ok);
+        }
+#pragma unroll
+        for (int k = 0; k < KBC; ++k) {
+            const int idx = tid + k * NT;
+            if (NBC % NT == 0 || idx < NBC) {
+                const int wn = idx / (T * BCW), rem = idx % (T * BCW);
+                const int t = rem / BCW, slot = rem % BCW;
+                const int64_t n = int64_t(wn) * SPL + (slot % SPL);
+                const bool isC = slot >= SPL;
+                const bool ok = n < p.N && t0 + t < tend && (kFullMode || !isC);
+                const IO* src = isC ? gC : gB;
+                nbcv[k] = ok ? src[(int64_t(b) * p.N + n) * p.L + t0 + t] : IO(0);
             }
         }
     };
 
+    // (dt2, dt2*u) or (exp(dt*a_h), dt2*u) of one element
+    auto stage_elem = [&](int k, int e, bool in) {
+        const float uu = IOT<IO>::to_f32(nu[k].e[e]);
+        const float dt2 = in ? softplus_log2(IOT<IO>::to_f32(ndl[k].e[e]) + sv_bias[k]) : 0.0f;
+        float first = dt2;
+        if constexpr (SCALAR && kFullMode) first = __builtin_amdgcn_exp2f(dt2 * sv_ah[k]);
+        sDX[(sv_tv[k] * VW + e) * kRow + sv_ch[k]] = make_float2(first, dt2 * uu);
+    };
+
     issue_loads(tbeg);
     for (int64_t t0 = tbeg; t0 < tend; t0 += T) {
-        const int tlen = int((tend - t0) < T ? (tend - t0) : T);
-
-        // ---- stage: (dt, dt*u) or (exp(dt*a_h), dt*u) per element; fp32 B and C
+        // ---- stage: per element (dt2, dt2*u) or (exp(dt*a_h), dt2*u); B*ln2 and C
+        const bool full_tile = t0 + T <= tend;
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const int v = tid + k * NT;
-            if (v < nvx) {
-                const int ch = v / TV, tv = v % TV;
-                const int64_t d = c0 + ch;
-                const bool ok = d < p.dim;
-                const float bs = (ok && p.bias) ? p.bias[d] : 0.0f;
-                float a2h = 0.0f;
-                if constexpr (SCALAR) a2h = ok ? p.A[d / p.head_dim] * kLog2e : 0.0f;
+        for (int k = 0; k < KX; ++k) {
+            if (sv_on[k]) {
+                if (full_tile && sv_ok[k]) {
 #pragma unroll
-                for (int e = 0; e < VW; ++e) {
-                    const float uu = IOT<IO>::to_f32(nu[k].e[e]);
-                    const float dt = ok ? softplus_f32(IOT<IO>::to_f32(ndl[k].e[e]) + bs) : 0.0f;
-                    float first = dt;
-                    if constexpr (SCALAR && kFullMode) first = __builtin_amdgcn_exp2f(dt * a2h);
-                    sDX[(tv * VW + e) * kLanes + ch] = make_float2(first, dt * uu);
+                    for (int e = 0; e < VW; ++e) stage_elem(k, e, true);
+                } else {
+                    const int64_t lim = tend - (t0 + sv_tv[k] * VW);
+#pragma unroll
+                    for (int e = 0; e < VW; ++e) stage_elem(k, e, sv_ok[k] && e < lim);
                 }
                 if constexpr (kFullMode) {
                     cu[k] = nu[k];
-                    if (gz) cz[k] = nz[k];
+                    cz[k] = nz[k];
                 }
             }
-            if (v < nvb) {
-                const int n = v / TV, tv = v % TV;
+        }
 #pragma unroll
-                for (int e = 0; e < VW; ++e) {
-                    sB[(tv * VW + e) * np + n] = IOT<IO>::to_f32(nB[k].e[e]);
-                    if constexpr (kFullMode) sC[(tv * VW + e) * np + n] = IOT<IO>::to_f32(nC[k].e[e]);
-                }
-            }
+        for (int k = 0; k < KBC; ++k) {
+            const int idx = tid + k * NT;
+            if (NBC % NT == 0 || idx < NBC)
+                sBC[idx] = IOT<IO>::to_f32(nbcv[k]) * ((idx % BCW) < SPL ? kLn2f : 1.0f);
         }
         // prefetch the next tile while this one is walked
         if (t0 + T < tend) issue_loads(t0 + T);
         __syncthreads();
 
-        // ---- walk: SPL state entries per lane, sequential in t
-        if (walker) {
-            const float* sBw = sB + w * SPL;
-            const float* sCw = sC + w * SPL;
-            for (int t = 0; t < tlen; ++t) {
-                const float2 dx = sDX[t * kLanes + lane];
-                float a_shared = 0.0f;
-                if constexpr (SCALAR) {
-                    if constexpr (kFullMode) a_shared = dx.x;
-                    else a_shared = __builtin_amdgcn_exp2f(dx.x * a2_scalar);
-                }
-                if constexpr (!kFullMode) {
-                    const float yk = dx.x - dtcomp;
-                    const float tk = dtsum + yk;
-                    dtcomp = (tk - dtsum) - yk;
-                    dtsum = tk;
-                }
-                float yp = 0.0f;
+        // ---- walk: SPL state entries per lane, sequential in t; the LDS operands of
+        //      QB steps are read before their arithmetic starts
+        {
+            const float2* dxp = sDX + lane;
+            const float* bcp = sBC + size_t(w) * T * BCW;
+            float* yo = sY + size_t(w) * T * kRowY + lane;
 #pragma unroll
-                for (int j = 0; j < SPL; ++j) {
-                    const float bb = sBw[t * np + j];
-                    const float a = SCALAR ? a_shared : __builtin_amdgcn_exp2f(dx.x * A2[j]);
-                    h[j] = fmaf(a, h[j], dx.y * bb);
-                    if constexpr (kFullMode) yp = fmaf(sCw[t * np + j], h[j], yp);
+            for (int t = 0; t < T; t += QB) {
+                float2 dx[QB];
+                BCVec<SPL> bc[QB];
+#pragma unroll
+                for (int q = 0; q < QB; ++q) {
+                    dx[q] = dxp[(t + q) * kRow];
+                    bc[q] = read_bc<SPL>(bcp + (t + q) * BCW);
                 }
-                if constexpr (kFullMode) sY[(size_t(w) * T + t) * kLanes + lane] = yp;
+#pragma unroll
+                for (int q = 0; q < QB; ++q) {
+                    float a_shared = 0.0f;
+                    if constexpr (SCALAR) {
+                        if constexpr (kFullMode) a_shared = dx[q].x;
+                        else a_shared = __builtin_amdgcn_exp2f(dx[q].x * a_scalar);
+                    }
+                    if constexpr (!kFullMode) {
+                        const float yk = dx[q].x - dtcomp;
+                        const float tk = dtsum + yk;
+                        dtcomp = (tk - dtsum) - yk;
+                        dtsum = tk;
+                    }
+                    float yp = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < SPL; ++j) {
+                        const float a = SCALAR ? a_shared : __builtin_amdgcn_exp2f(dx[q].x * Ar[j]);
+                        h[j] = fmaf(a, h[j], dx[q].y * bc[q].v[j]);
+                        if constexpr (kFullMode) yp = fmaf(bc[q].v[SPL + j], h[j], yp);
+                    }
+                    if constexpr (kFullMode) yo[(t + q) * kRowY] = yp;
+                }
             }
         }
         __syncthreads();
@@ -329,42 +406,40 @@ __global__ void __launch_bounds__(NTMAX) scan_fwd_kernel(Params p, int T, int G)
         // ---- epilogue: sum the G partial read-outs in wave order, skip, gate, store
         if constexpr (kFullMode) {
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                const int v = tid + k * NT;
-                if (v < nvx) {
-                    const int ch = v / TV, tv = v % TV;
-                    const int64_t d = c0 + ch;
-                    const bool ok = d < p.dim;
-                    const float dsk = (ok && p.Dskip) ? p.Dskip[d] : 0.0f;
+            for (int k = 0; k < KX; ++k) {
+                if (sv_on[k]) {
+                    float acc[VW];
+                    const float* yrow = sY + (sv_tv[k] * VW) * kRowY + sv_ch[k];
+#pragma unroll
+                    for (int e = 0; e < VW; ++e) acc[e] = yrow[e * kRowY];
+#pragma unroll
+                    for (int ww = 1; ww < G; ++ww)
+#pragma unroll
+                        for (int e = 0; e < VW; ++e) acc[e] += yrow[(ww * T + e) * kRowY];
                     Vec<IO> out;
 #pragma unroll
                     for (int e = 0; e < VW; ++e) {
-                        const int tl = tv * VW + e;
-                        float acc = 0.0f;
-                        for (int ww = 0; ww < G; ++ww) acc += sY[(size_t(ww) * T + tl) * kLanes + ch];
-                        float o = fmaf(dsk, IOT<IO>::to_f32(cu[k].e[e]), acc);
-                        if (gz) o *= silu_f32(IOT<IO>::to_f32(cz[k].e[e]));
+                        float o = fmaf(sv_skip[k], IOT<IO>::to_f32(cu[k].e[e]), acc[e]);
+                        const float g = silu_f32(IOT<IO>::to_f32(cz[k].e[e]));
+                        o *= has_z ? g : 1.0f;
                         out.e[e] = IOT<IO>::from_f32(o);
                     }
-                    const int64_t row = (int64_t(b) * p.dim + (ok ? d : 0)) * p.L;
-                    store_vec<IO, VEC>(gy + row, t0 + tv * VW, tend, ok, out);
+                    store_vec<IO, VEC>(gy + sv_row[k], t0 + sv_tv[k] * VW, tend, sv_ok[k], out);
                 }
             }
         }
     }
 
     if constexpr (!kFullMode) {
-        if (walker) {
-            float* hout = p.ws_H + ((blk * p.nchunks + piece) * np + int64_t(w) * SPL) * kLanes + lane;
+        float* hout = p.ws_H + ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
 #pragma unroll
-            for (int j = 0; j < SPL; ++j) hout[int64_t(j) * kLanes] = h[j];
-            if (w == 0) p.ws_S[(blk * p.nchunks + piece) * kLanes + lane] = dtsum;
-        }
+        for (int j = 0; j < SPL; ++j) hout[int64_t(j) * kLanes] = h[j];
+        if (w == 0) p.ws_S[(blk * p.nchunks + piece) * kLanes + lane] = dtsum;
     }
 }
 
-// Compose the pieces' affine maps in sequence order: one thread per (block, state, lane).
-//   Hin[0] = 0;  Hin[c+1] = exp(A * S[c]) * Hin[c] + H[c]
+// Compose the pieces' affine maps in sequence order: one thread per (group, state, lane).
+//   Hin[0] = 0;  Hin[c+1] = exp2(A * S2[c]) * Hin[c] + H[c]     (S2 = sum of dt2)
 __global__ void __launch_bounds__(256) scan_carry_kernel(Params p, int64_t total) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= total) return;
@@ -373,15 +448,15 @@ __global__ void __launch_bounds__(256) scan_carry_kernel(Params p, int64_t total
     const int64_t blk = i / (int64_t(kLanes) * p.np);
     const int64_t cblk = blk % p.nblk_d;
     const int64_t d = cblk * kLanes + lane;
-    float a2 = 0.0f;
-    if (d < p.dim && n < p.N) a2 = (p.head_dim ? p.A[d / p.head_dim] : p.A[d * p.N + n]) * kLog2e;
+    float a = 0.0f;
+    if (d < p.dim && n < p.N) a = p.head_dim ? p.A[d / p.head_dim] : p.A[d * p.N + n];
     float hcur = 0.0f;
     for (int c = 0; c < p.nchunks; ++c) {
         const int64_t hidx = ((blk * p.nchunks + c) * p.np + n) * kLanes + lane;
         p.ws_Hin[hidx] = hcur;
         if (c + 1 < p.nchunks) {
             const float s = p.ws_S[(blk * p.nchunks + c) * kLanes + lane];
-            hcur = fmaf(__builtin_amdgcn_exp2f(a2 * s), hcur, p.ws_H[hidx]);
+            hcur = fmaf(__builtin_amdgcn_exp2f(a * s), hcur, p.ws_H[hidx]);
         }
     }
 }
@@ -430,15 +505,18 @@ int make_plan(const ssm_dims* d, Plan* pl) {
     if (spl == 0) {
         // aim for 4 waves per workgroup (scalar decay: 8), at most 16 states per lane
         const int64_t target_waves = pl->scalar ? 8 : 4;
+        // (with fewer state entries than waves, lanes carry one entry each)
         spl = 1;
         while (spl < 16 && cdiv(N, spl) > target_waves) spl *= 2;
     }
     if (cdiv(N, spl) > 16) return SSM_ERR_DIMS;       // more than 1024 threads
     pl->spl = spl;
-    pl->G = int(cdiv(N, spl));
-    // time tile: 32 steps; 16 when the partial read-outs of 16 waves or a wide
-    // B/C tile would not fit the 160 KB of LDS
-    pl->T = (pl->G > 8 || pl->G * spl > 128) ? 16 : 32;
+    // waves per workgroup, rounded up to 4, 8 or 16 (state entries beyond N are padding)
+    const int64_t g = cdiv(N, spl);
+    pl->G = g <= 4 ? 4 : (g <= 8 ? 8 : 16);
+    // time tile: 32 steps; 16 for 16-wave workgroups, whose partial read-outs and
+    // B/C tiles would not fit the 160 KB of LDS
+    pl->T = pl->G > 8 ? 16 : 32;
     pl->nblk_d = cdiv(d->dim, kLanes);
     const int64_t groups = d->batch * pl->nblk_d;
     const int64_t tiles = cdiv(d->seqlen, pl->T);
@@ -474,44 +552,49 @@ int make_plan(const ssm_dims* d, Plan* pl) {
 }
 
 // ------------------------------------------------------------------ host side: launching
-template <typename IO, int SPL, bool SCALAR, bool VEC, int NTMAX>
+template <typename IO, int SPL, bool SCALAR, bool VEC, int G>
 hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
-    const dim3 block(unsigned((pl.G > 4 ? pl.G : 4) * kLanes));
-    if (block.x > unsigned(NTMAX)) return hipErrorInvalidConfiguration;
-    const size_t lds_full = lds_floats(pl.T, pl.G, p.np, true) * sizeof(float);
-    const size_t lds_agg = lds_floats(pl.T, pl.G, p.np, false) * sizeof(float);
+    constexpr int T = G <= 8 ? 32 : 16;
+    if (pl.G != G || pl.T != T || p.np != G * SPL) return hipErrorInvalidConfiguration;
+    const dim3 block(unsigned(G * kLanes));
+    const size_t lds_full = lds_floats(T, G, p.np, true) * sizeof(float);
+    const size_t lds_agg = lds_floats(T, G, p.np, false) * sizeof(float);
     if (pl.nchunks > 1) {
         const int64_t groups = int64_t(p.batch) * p.nblk_d;
         // pass 1 on every piece but the last
         const dim3 grid1(unsigned(groups * (pl.nchunks - 1)));
-        hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kAggregate, VEC, NTMAX>), grid1, block, lds_agg, stream, p, pl.T, pl.G);
+        hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kAggregate, VEC, G>), grid1, block, lds_agg, stream, p);
         const int64_t total = groups * p.np * kLanes;
         hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, p, total);
     }
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, NTMAX>), dim3(unsigned(pl.blocks)), block, lds_full,
-                       stream, p, pl.T, pl.G);
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, G>), dim3(unsigned(pl.blocks)), block, lds_full,
+                       stream, p);
     return hipGetLastError();
 }
 
-// Workgroups of up to 4 waves get the 256-thread launch bound (up to 512 VGPRs per
-// lane); larger ones the 1024-thread bound (128 VGPRs).  Row layouts that cannot use
-// 16-byte vectors only get the latter.
-template <typename IO, bool SCALAR, bool VEC, int NTMAX>
+// One instantiation per (states per lane, waves per workgroup) pair the planner can
+// produce: waves are 4, 8 or 16 and states per lane 1..16.
+template <typename IO, bool SCALAR, bool VEC, int G>
 hipError_t dispatch_spl(const Params& p, const Plan& pl, hipStream_t s) {
     switch (pl.spl) {
-        case 1: return launch_all<IO, 1, SCALAR, VEC, NTMAX>(p, pl, s);
-        case 2: return launch_all<IO, 2, SCALAR, VEC, NTMAX>(p, pl, s);
-        case 4: return launch_all<IO, 4, SCALAR, VEC, NTMAX>(p, pl, s);
-        case 8: return launch_all<IO, 8, SCALAR, VEC, NTMAX>(p, pl, s);
-        default: return launch_all<IO, 16, SCALAR, VEC, NTMAX>(p, pl, s);
+        case 1: return launch_all<IO, 1, SCALAR, VEC, G>(p, pl, s);
+        case 2: return launch_all<IO, 2, SCALAR, VEC, G>(p, pl, s);
+        case 4: return launch_all<IO, 4, SCALAR, VEC, G>(p, pl, s);
+        case 8: return launch_all<IO, 8, SCALAR, VEC, G>(p, pl, s);
+        default: return launch_all<IO, 16, SCALAR, VEC, G>(p, pl, s);
     }
+}
+
+template <typename IO, bool SCALAR, bool VEC>
+hipError_t dispatch_g(const Params& p, const Plan& pl, hipStream_t s) {
+    if (pl.G == 4) return dispatch_spl<IO, SCALAR, VEC, 4>(p, pl, s);
+    if (pl.G == 8) return dispatch_spl<IO, SCALAR, VEC, 8>(p, pl, s);
+    return dispatch_spl<IO, SCALAR, VEC, 16>(p, pl, s);
 }
 
 template <typename IO, bool SCALAR>
 hipError_t dispatch_nt(const Params& p, const Plan& pl, bool vec, hipStream_t s) {
-    if (!vec) return dispatch_spl<IO, SCALAR, false, 1024>(p, pl, s);
-    if (pl.G <= 4) return dispatch_spl<IO, SCALAR, true, 256>(p, pl, s);
-    return dispatch_spl<IO, SCALAR, true, 1024>(p, pl, s);
+    return vec ? dispatch_g<IO, SCALAR, true>(p, pl, s) : dispatch_g<IO, SCALAR, false>(p, pl, s);
 }
 
 template <typename IO>
@@ -631,12 +714,6 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
         p.ws_Hin = base + per * p.np;
         p.ws_S = base + 2 * per * p.np;
     }
-
-    // per-thread staging capacity of the kernel: KMAX vectors (1 for bf16, 2 for f32)
-    const int64_t nthreads = int64_t(pl.G > 4 ? pl.G : 4) * kLanes;
-    const int64_t kmax = esz == 2 ? 1 : 2;
-    const int64_t tv = pl.T / int64_t(vw);
-    if (int64_t(kLanes) * tv > kmax * nthreads || int64_t(p.np) * tv > kmax * nthreads) return SSM_ERR_DIMS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = dims->io_dtype == SSM_BF16 ? dispatch<uint16_t>(p, pl, vec, s) : dispatch<float>(p, pl, vec, s);
