@@ -153,17 +153,19 @@ struct Params {
 
 enum Mode { kFull = 0, kAggregate = 1 };
 
-// LDS layout (floats); rows of 64 channels are padded to kRow entries so that the
-// staging writes and epilogue reads, whose lanes span 4 time steps of 16 channels,
-// fall in distinct banks:
+// LDS layout of one tile buffer (floats); rows of 64 channels are padded to kRow or
+// kRowY entries so that the staging writes and epilogue reads, whose lanes span 4
+// time steps of 16 channels, fall in distinct banks:
 //   sDX [T][kRow] float2  per (step, channel): (dt2, dt2*u), or (exp(dt*a_h), dt2*u) in
 //                         scalar-decay full mode
 //   sBC [G][T][2*SPL]     per (wave, step): B*ln2 of the wave's SPL state entries, then C
-//   sY  [G][T][kRowY]     per (wave, step, channel): partial read-out (full mode only)
+//   sY  [G][T][kRowY]     per (wave, step, channel): partial read-out      } full
+//   sSk [T][kRowY]        per (step, channel): skip term D*u               } mode
+//   sGt [T][kRowY]        per (step, channel): gate SiLU(z), or 1 without z } only
 constexpr int kRow = kLanes + 1;
 constexpr int kRowY = kLanes + 2;
 inline size_t lds_floats(int T, int G, int np, bool full) {
-    return size_t(T) * kRow * 2 + 2 * size_t(T) * np + (full ? size_t(G) * T * kRowY : 0);
+    return size_t(T) * kRow * 2 + 2 * size_t(T) * np + (full ? size_t(G + 2) * T * kRowY : 0);
 }
 
 template <int SPL> struct BCVec { float v[2 * SPL]; };
@@ -188,42 +190,63 @@ __device__ inline BCVec<SPL> read_bc(const float* __restrict__ q) {
     return r;
 }
 
+// Kernel shape, by the number G of waves that walk (4, 8 or 16):
+//   G <= 8: 4 more "helper" waves stage tile k+1 and finish tile k-1 while the G
+//           walkers walk tile k (double-buffered LDS, one barrier per tile), so every
+//           SIMD runs a walker and a helper side by side;
+//   G == 16: all waves stage, walk and finish in turn (single buffer, 2 barriers).
+template <int G, int SPL> struct Shape {
+    static constexpr bool kSpec = G <= 8;
+    static constexpr int NW = kSpec ? G + 4 : G;          // waves per workgroup
+    static constexpr int NS = (kSpec ? 4 : G) * kLanes;    // staging threads
+    static constexpr int T = (G == 4 && SPL <= 8) ? 32 : 16;   // time tile (LDS budget)
+    static constexpr int NBUF = kSpec ? 2 : 1;
+};
+
+inline int tile_len(int G, int spl) { return (G == 4 && spl <= 8) ? 32 : 16; }
+
+inline size_t lds_floats_g(int G, int spl, bool full) {
+    return (G <= 8 ? 2 : 1) * lds_floats(tile_len(G, spl), G, G * spl, full);
+}
+
 // One launch processes, for every (batch, channel block, piece), the piece's time
 // tiles in order.  MODE kFull reads out and stores y (starting from ws_Hin when the
 // piece is not the first); MODE kAggregate only records the piece's end state from
 // zero and its dt2 sum.
 //
-// G waves (4, 8 or 16; 64*G threads) each carry SPL state entries of every channel;
-// entries n >= N are padding with A = 0 and B = C = 0, which stay zero.  All threads
-// stage and finish tiles.  Staged steps beyond the piece's end are identity steps
-// (dt2 = 0, x = 0), so the walk always runs whole tiles.
+// The G walking waves each carry SPL state entries of every channel; entries
+// n >= N are padding with A = 0 and B = C = 0, which stay zero.  Staged steps beyond
+// the piece's end are identity steps (dt2 = 0, x = 0), so the walk always runs
+// whole tiles.
 template <typename IO, int SPL, bool SCALAR, int MODE, bool VEC, int G>
-__global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
+__global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(Params p) {
+    using S = Shape<G, SPL>;
+    constexpr bool kSpec = S::kSpec;
+    constexpr int NS = S::NS;
+    constexpr int T = S::T;
     constexpr int VW = IOT<IO>::VW;
-    constexpr int NT = G * kLanes;
-    constexpr int T = G <= 8 ? 32 : 16;            // time tile
     constexpr int TV = T / VW;                     // vectors per row per tile
     constexpr int NVX = kLanes * TV;               // u/delta/z vectors per tile
-    constexpr int KX = (NVX + NT - 1) / NT;        // of them per thread
+    constexpr int KX = (NVX + NS - 1) / NS;        // of them per staging thread
     constexpr bool kFullMode = (MODE == kFull);
     constexpr int BCW = 2 * SPL;                   // floats per (wave, step) in sBC
     constexpr int NBC = G * T * BCW;               // sBC values per tile
     // B/C staging: one sBC value per thread and pass; a wave's 64 lanes cover 64/BCW
     // steps x BCW slots, i.e. 64 distinct LDS banks per write.
-    constexpr int KBC = (NBC + NT - 1) / NT;
+    constexpr int KBC = (NBC + NS - 1) / NS;
     constexpr int QB = SPL <= 4 ? 4 : (SPL == 8 ? 2 : 1);   // steps whose LDS operands are read together
     constexpr int NP = G * SPL;                    // padded state count
     constexpr float kLn2f = kLn2;
+    constexpr int BUF = T * kRow * 2 + NBC + (kFullMode ? (G + 2) * T * kRowY : 0);   // floats per buffer
     static_assert(T % 8 == 0, "time tile must hold whole vectors and step groups");
 
     extern __shared__ float smem[];
     const int tid = threadIdx.x;
     const int w = tid / kLanes;
     const int lane = tid % kLanes;
-
-    float2* sDX = reinterpret_cast<float2*>(smem);
-    float* sBC = smem + size_t(T) * kRow * 2;
-    float* sY = sBC + size_t(NBC);
+    const bool walker = w < G;
+    const bool stager = kSpec ? !walker : true;
+    const int stid = kSpec ? tid - G * kLanes : tid;     // index among the staging threads
 
     // blockIdx.x -> (piece, batch, channel block), channel block fastest
     const int64_t bid = blockIdx.x;
@@ -234,6 +257,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
     const int64_t c0 = int64_t(cblk) * kLanes;
     const int64_t tbeg = int64_t(piece) * p.chunk_len;
     const int64_t tend = (tbeg + p.chunk_len < p.L) ? tbeg + p.chunk_len : p.L;
+    const int ntiles = int((tend - tbeg + T - 1) / T);
     const bool has_z = kFullMode && p.z != nullptr;
 
     const IO* __restrict__ gu = static_cast<const IO*>(p.u);
@@ -245,7 +269,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
 
     // ---- walk constants: this lane's channel and its SPL decay rates
     const int64_t dch = c0 + lane;
-    const bool lane_ok = dch < p.dim;
+    const bool lane_ok = walker && dch < p.dim;
     float Ar[SPL];
     float a_scalar = 0.0f;
     if constexpr (SCALAR) {
@@ -267,8 +291,8 @@ __global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
     int64_t sv_row[KX];
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
-        const int v = tid + k * NT;
-        sv_on[k] = v < NVX;
+        const int v = stid + k * NS;
+        sv_on[k] = stager && v < NVX;
         sv_ch[k] = (v / TV) % kLanes;
         sv_tv[k] = v % TV;
         const int64_t d = c0 + sv_ch[k];
@@ -284,7 +308,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
     float h[SPL];
 #pragma unroll
     for (int j = 0; j < SPL; ++j) h[j] = 0.0f;
-    if (kFullMode && piece > 0) {
+    if (kFullMode && piece > 0 && walker) {
         const float* hin = p.ws_Hin + ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
 #pragma unroll
         for (int j = 0; j < SPL; ++j) h[j] = hin[int64_t(j) * kLanes];
@@ -294,9 +318,10 @@ __global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
     __builtin_amdgcn_s_waitcnt(0);
     float dtsum = 0.0f, dtcomp = 0.0f;   // compensated (Kahan) sum of dt2 over the piece
 
-    Vec<IO> nu[KX], ndl[KX], nz[KX], cu[KX], cz[KX];
+    Vec<IO> nu[KX], ndl[KX], nz[KX];
     IO nbcv[KBC];
 
+    // ---- global -> registers for the tile starting at t0 (staging threads)
     auto issue_loads = [&](int64_t t0) {
 #pragma unroll
         for (int k = 0; k < KX; ++k) {
@@ -309,8 +334,8 @@ __global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
         }
 #pragma unroll
         for (int k = 0; k < KBC; ++k) {
-            const int idx = tid + k * NT;
-            if (NBC % NT == 0 || idx < NBC) {
+            const int idx = stid + k * NS;
+            if (NBC % NS == 0 || idx < NBC) {
                 const int wn = idx / (T * BCW), rem = idx % (T * BCW);
                 const int t = rem / BCW, slot = rem % BCW;
                 const int64_t n = int64_t(wn) * SPL + (slot % SPL);
@@ -322,119 +347,161 @@ __global__ void __launch_bounds__(G * kLanes) scan_fwd_kernel(Params p) {
         }
     };
 
-    // (dt2, dt2*u) or (exp(dt*a_h), dt2*u) of one element
-    auto stage_elem = [&](int k, int e, bool in) {
-        const float uu = IOT<IO>::to_f32(nu[k].e[e]);
-        const float dt2 = in ? softplus_log2(IOT<IO>::to_f32(ndl[k].e[e]) + sv_bias[k]) : 0.0f;
-        float first = dt2;
-        if constexpr (SCALAR && kFullMode) first = __builtin_amdgcn_exp2f(dt2 * sv_ah[k]);
-        sDX[(sv_tv[k] * VW + e) * kRow + sv_ch[k]] = make_float2(first, dt2 * uu);
-    };
-
-    issue_loads(tbeg);
-    for (int64_t t0 = tbeg; t0 < tend; t0 += T) {
-        // ---- stage: per element (dt2, dt2*u) or (exp(dt*a_h), dt2*u); B*ln2 and C
+    // ---- registers -> LDS buffer `buf` for the tile starting at t0 (staging threads):
+    //      per element (dt2, dt2*u) or (exp(dt*a_h), dt2*u); B*ln2 and C
+    auto stage = [&](float* buf, int64_t t0) {
+        float2* sDX = reinterpret_cast<float2*>(buf);
+        float* sBC = buf + T * kRow * 2;
+        float* sSk = sBC + NBC + G * T * kRowY;
+        float* sGt = sSk + T * kRowY;
         const bool full_tile = t0 + T <= tend;
+        auto elem = [&](int k, int e, bool in) {
+            const float uu = IOT<IO>::to_f32(nu[k].e[e]);
+            const float dt2 = in ? softplus_log2(IOT<IO>::to_f32(ndl[k].e[e]) + sv_bias[k]) : 0.0f;
+            float first = dt2;
+            if constexpr (SCALAR && kFullMode) first = __builtin_amdgcn_exp2f(dt2 * sv_ah[k]);
+            const int tl = sv_tv[k] * VW + e;
+            sDX[tl * kRow + sv_ch[k]] = make_float2(first, dt2 * uu);
+            if constexpr (kFullMode) {
+                sSk[tl * kRowY + sv_ch[k]] = sv_skip[k] * uu;
+                const float g = silu_f32(IOT<IO>::to_f32(nz[k].e[e]));
+                sGt[tl * kRowY + sv_ch[k]] = has_z ? g : 1.0f;
+            }
+        };
 #pragma unroll
         for (int k = 0; k < KX; ++k) {
             if (sv_on[k]) {
                 if (full_tile && sv_ok[k]) {
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) stage_elem(k, e, true);
+                    for (int e = 0; e < VW; ++e) elem(k, e, true);
                 } else {
                     const int64_t lim = tend - (t0 + sv_tv[k] * VW);
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) stage_elem(k, e, sv_ok[k] && e < lim);
-                }
-                if constexpr (kFullMode) {
-                    cu[k] = nu[k];
-                    cz[k] = nz[k];
+                    for (int e = 0; e < VW; ++e) elem(k, e, sv_ok[k] && e < lim);
                 }
             }
         }
 #pragma unroll
         for (int k = 0; k < KBC; ++k) {
-            const int idx = tid + k * NT;
-            if (NBC % NT == 0 || idx < NBC)
+            const int idx = stid + k * NS;
+            if (NBC % NS == 0 || idx < NBC)
                 sBC[idx] = IOT<IO>::to_f32(nbcv[k]) * ((idx % BCW) < SPL ? kLn2f : 1.0f);
         }
-        // prefetch the next tile while this one is walked
-        if (t0 + T < tend) issue_loads(t0 + T);
-        __syncthreads();
+    };
 
-        // ---- walk: SPL state entries per lane, sequential in t; the LDS operands of
-        //      QB steps are read before their arithmetic starts
-        {
-            const float2* dxp = sDX + lane;
-            const float* bcp = sBC + size_t(w) * T * BCW;
-            float* yo = sY + size_t(w) * T * kRowY + lane;
+    // ---- walk one tile from LDS buffer `buf` (walking waves): SPL state entries per
+    //      lane, sequential in t; the LDS operands of QB steps are read up front
+    auto walk = [&](float* buf) {
+        const float2* dxp = reinterpret_cast<const float2*>(buf) + lane;
+        const float* bcp = buf + T * kRow * 2 + w * T * BCW;
+        float* yo = buf + T * kRow * 2 + NBC + w * T * kRowY + lane;
 #pragma unroll
-            for (int t = 0; t < T; t += QB) {
-                float2 dx[QB];
-                BCVec<SPL> bc[QB];
+        for (int t = 0; t < T; t += QB) {
+            float2 dx[QB];
+            BCVec<SPL> bc[QB];
 #pragma unroll
-                for (int q = 0; q < QB; ++q) {
-                    dx[q] = dxp[(t + q) * kRow];
-                    bc[q] = read_bc<SPL>(bcp + (t + q) * BCW);
+            for (int q = 0; q < QB; ++q) {
+                dx[q] = dxp[(t + q) * kRow];
+                bc[q] = read_bc<SPL>(bcp + (t + q) * BCW);
+            }
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                float a_shared = 0.0f;
+                if constexpr (SCALAR) {
+                    if constexpr (kFullMode) a_shared = dx[q].x;
+                    else a_shared = __builtin_amdgcn_exp2f(dx[q].x * a_scalar);
                 }
-#pragma unroll
-                for (int q = 0; q < QB; ++q) {
-                    float a_shared = 0.0f;
-                    if constexpr (SCALAR) {
-                        if constexpr (kFullMode) a_shared = dx[q].x;
-                        else a_shared = __builtin_amdgcn_exp2f(dx[q].x * a_scalar);
-                    }
-                    if constexpr (!kFullMode) {
-                        const float yk = dx[q].x - dtcomp;
-                        const float tk = dtsum + yk;
-                        dtcomp = (tk - dtsum) - yk;
-                        dtsum = tk;
-                    }
-                    float yp = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < SPL; ++j) {
-                        const float a = SCALAR ? a_shared : __builtin_amdgcn_exp2f(dx[q].x * Ar[j]);
-                        h[j] = fmaf(a, h[j], dx[q].y * bc[q].v[j]);
-                        if constexpr (kFullMode) yp = fmaf(bc[q].v[SPL + j], h[j], yp);
-                    }
-                    if constexpr (kFullMode) yo[(t + q) * kRowY] = yp;
+                if constexpr (!kFullMode) {
+                    const float yk = dx[q].x - dtcomp;
+                    const float tk = dtsum + yk;
+                    dtcomp = (tk - dtsum) - yk;
+                    dtsum = tk;
                 }
+                float yp = 0.0f;
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) {
+                    const float a = SCALAR ? a_shared : __builtin_amdgcn_exp2f(dx[q].x * Ar[j]);
+                    h[j] = fmaf(a, h[j], dx[q].y * bc[q].v[j]);
+                    if constexpr (kFullMode) yp = fmaf(bc[q].v[SPL + j], h[j], yp);
+                }
+                if constexpr (kFullMode) yo[(t + q) * kRowY] = yp;
             }
         }
-        __syncthreads();
+    };
 
-        // ---- epilogue: sum the G partial read-outs in wave order, skip, gate, store
+    // ---- finish the tile starting at t0 from LDS buffer `buf` (staging threads): sum
+    //      the G partial read-outs in wave order, skip, gate, round, store
+    auto finish = [&](const float* buf, int64_t t0) {
         if constexpr (kFullMode) {
+            const float* sY = buf + T * kRow * 2 + NBC;
+            const float* sSk = sY + G * T * kRowY;
+            const float* sGt = sSk + T * kRowY;
 #pragma unroll
             for (int k = 0; k < KX; ++k) {
                 if (sv_on[k]) {
+                    const int off = (sv_tv[k] * VW) * kRowY + sv_ch[k];
                     float acc[VW];
-                    const float* yrow = sY + (sv_tv[k] * VW) * kRowY + sv_ch[k];
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) acc[e] = yrow[e * kRowY];
+                    for (int e = 0; e < VW; ++e) acc[e] = sY[off + e * kRowY];
 #pragma unroll
                     for (int ww = 1; ww < G; ++ww)
 #pragma unroll
-                        for (int e = 0; e < VW; ++e) acc[e] += yrow[(ww * T + e) * kRowY];
+                        for (int e = 0; e < VW; ++e) acc[e] += sY[off + (ww * T + e) * kRowY];
                     Vec<IO> out;
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) {
-                        float o = fmaf(sv_skip[k], IOT<IO>::to_f32(cu[k].e[e]), acc[e]);
-                        const float g = silu_f32(IOT<IO>::to_f32(cz[k].e[e]));
-                        o *= has_z ? g : 1.0f;
-                        out.e[e] = IOT<IO>::from_f32(o);
-                    }
+                    for (int e = 0; e < VW; ++e)
+                        out.e[e] = IOT<IO>::from_f32((acc[e] + sSk[off + e * kRowY]) * sGt[off + e * kRowY]);
                     store_vec<IO, VEC>(gy + sv_row[k], t0 + sv_tv[k] * VW, tend, sv_ok[k], out);
                 }
             }
         }
+    };
+
+    if constexpr (kSpec) {
+        // walkers walk tile kt from buffer kt&1 while the helpers finish tile kt-1
+        // (buffer (kt-1)&1) and then stage tile kt+1 into that same buffer
+        if (stager) {
+            issue_loads(tbeg);
+            stage(smem, tbeg);
+            if (ntiles > 1) issue_loads(tbeg + T);
+        }
+        __syncthreads();
+        for (int kt = 0; kt < ntiles; ++kt) {
+            float* cur = smem + (kt & 1) * BUF;
+            float* oth = smem + ((kt + 1) & 1) * BUF;
+            const int64_t t0 = tbeg + int64_t(kt) * T;
+            if (walker) {
+                walk(cur);
+            } else {
+                if (kt >= 1) finish(oth, t0 - T);
+                if (kt + 1 < ntiles) {
+                    stage(oth, t0 + T);
+                    if (kt + 2 < ntiles) issue_loads(t0 + 2 * T);
+                }
+            }
+            __syncthreads();
+        }
+        if (stager) finish(smem + ((ntiles - 1) & 1) * BUF, tbeg + int64_t(ntiles - 1) * T);
+    } else {
+        issue_loads(tbeg);
+        for (int kt = 0; kt < ntiles; ++kt) {
+            const int64_t t0 = tbeg + int64_t(kt) * T;
+            stage(smem, t0);
+            if (kt + 1 < ntiles) issue_loads(t0 + T);   // prefetch the next tile
+            __syncthreads();
+            walk(smem);
+            __syncthreads();
+            finish(smem, t0);
+        }
     }
 
     if constexpr (!kFullMode) {
-        float* hout = p.ws_H + ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
+        if (walker) {
+            float* hout = p.ws_H + ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) hout[int64_t(j) * kLanes] = h[j];
-        if (w == 0) p.ws_S[(blk * p.nchunks + piece) * kLanes + lane] = dtsum;
+            for (int j = 0; j < SPL; ++j) hout[int64_t(j) * kLanes] = h[j];
+            if (w == 0) p.ws_S[(blk * p.nchunks + piece) * kLanes + lane] = dtsum;
+        }
     }
 }
 
@@ -514,9 +581,9 @@ int make_plan(const ssm_dims* d, Plan* pl) {
     // waves per workgroup, rounded up to 4, 8 or 16 (state entries beyond N are padding)
     const int64_t g = cdiv(N, spl);
     pl->G = g <= 4 ? 4 : (g <= 8 ? 8 : 16);
-    // time tile: 32 steps; 16 for 16-wave workgroups, whose partial read-outs and
-    // B/C tiles would not fit the 160 KB of LDS
-    pl->T = pl->G > 8 ? 16 : 32;
+    // time tile: 32 steps for 4 walking waves of up to 8 entries per lane, else 16,
+    // so that the (double-buffered) LDS tiles fit the 160 KB of a CU
+    pl->T = tile_len(pl->G, spl);
     pl->nblk_d = cdiv(d->dim, kLanes);
     const int64_t groups = d->batch * pl->nblk_d;
     const int64_t tiles = cdiv(d->seqlen, pl->T);
@@ -547,18 +614,18 @@ int make_plan(const ssm_dims* d, Plan* pl) {
         size_t bytes = per * np * 2 + per;   // H, Hin, S
         pl->ws_bytes = (bytes + 255) & ~size_t(255);
     }
-    pl->lds_bytes = lds_floats(pl->T, pl->G, np, true) * sizeof(float);
+    pl->lds_bytes = lds_floats_g(pl->G, spl, true) * sizeof(float);
     return SSM_OK;
 }
 
 // ------------------------------------------------------------------ host side: launching
 template <typename IO, int SPL, bool SCALAR, bool VEC, int G>
 hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
-    constexpr int T = G <= 8 ? 32 : 16;
-    if (pl.G != G || pl.T != T || p.np != G * SPL) return hipErrorInvalidConfiguration;
-    const dim3 block(unsigned(G * kLanes));
-    const size_t lds_full = lds_floats(T, G, p.np, true) * sizeof(float);
-    const size_t lds_agg = lds_floats(T, G, p.np, false) * sizeof(float);
+    using S = Shape<G, SPL>;
+    if (pl.G != G || pl.T != S::T || p.np != G * SPL) return hipErrorInvalidConfiguration;
+    const dim3 block(unsigned(S::NW * kLanes));
+    const size_t lds_full = lds_floats_g(G, SPL, true) * sizeof(float);
+    const size_t lds_agg = lds_floats_g(G, SPL, false) * sizeof(float);
     if (pl.nchunks > 1) {
         const int64_t groups = int64_t(p.batch) * p.nblk_d;
         // pass 1 on every piece but the last

@@ -126,3 +126,18 @@ def test_forced_options_show_in_plan():
     plan = ssm.ssm_selective_scan_plan(small_dims(seqlen=10, nchunks=50))
     assert plan.nchunks == 1      # clamped: one time tile holds the whole sequence
     assert ssm.ssm_selective_scan_plan(small_dims(dstate=256)).lds_bytes <= 160 * 1024
+
+
+def test_every_plan_fits_the_lds_of_a_cu():
+    """160 KB of LDS per CU on gfx950: no plan may ask for more."""
+    for N in list(range(1, 33)) + [48, 64, 100, 128, 200, 256]:
+        for spl in (0, 1, 2, 4, 8, 16):
+            for nheads in (0, 1):
+                for io in (ssm.SSM_F32, ssm.SSM_BF16):
+                    dims = ssm.make_dims(1, 100, 64, N, nheads=nheads, io_dtype=io, states_per_lane=spl)
+                    try:
+                        plan = ssm.ssm_selective_scan_plan(dims)
+                    except ssm.SsmError as e:
+                        assert e.status == ssm.SSM_ERR_DIMS and spl and -(-N // spl) > 16
+                        continue
+                    assert plan.lds_bytes <= 160 * 1024, (N, spl, plan.as_dict())
