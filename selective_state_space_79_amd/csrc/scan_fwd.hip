@@ -431,7 +431,13 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
 
     // ---- finish the tile starting at t0 from LDS buffer `buf` (staging threads): sum
     //      the G partial read-outs in wave order, skip, gate, round, store
-    auto finish = [&](const float* buf, int64_t t0) {
+    // With bf16 rows and 32-step tiles a tile covers half of each row's 128-byte
+    // cache line; the even tile's output is held and stored together with the odd
+    // tile's, so both halves of a line reach the L2 back to back and are written to
+    // HBM as one full line.
+    constexpr bool kPairStores = VEC && (T * int(sizeof(IO)) == 64);
+    Vec<IO> held[KX];
+    auto finish = [&](const float* buf, int64_t t0, int kt) {
         if constexpr (kFullMode) {
             const float* sY = buf + T * kRow * 2 + NBC;
             const float* sSk = sY + G * T * kRowY;
@@ -451,6 +457,13 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
 #pragma unroll
                     for (int e = 0; e < VW; ++e)
                         out.e[e] = IOT<IO>::from_f32((acc[e] + sSk[off + e * kRowY]) * sGt[off + e * kRowY]);
+                    if constexpr (kPairStores) {
+                        if ((kt & 1) == 0 && kt + 1 < ntiles) {
+                            held[k] = out;            // stored with the next tile's vector
+                            continue;
+                        }
+                        if (kt & 1) store_vec<IO, VEC>(gy + sv_row[k], t0 - T + sv_tv[k] * VW, tend, sv_ok[k], held[k]);
+                    }
                     store_vec<IO, VEC>(gy + sv_row[k], t0 + sv_tv[k] * VW, tend, sv_ok[k], out);
                 }
             }
@@ -473,7 +486,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
             if (walker) {
                 walk(cur);
             } else {
-                if (kt >= 1) finish(oth, t0 - T);
+                if (kt >= 1) finish(oth, t0 - T, kt - 1);
                 if (kt + 1 < ntiles) {
                     stage(oth, t0 + T);
                     if (kt + 2 < ntiles) issue_loads(t0 + 2 * T);
@@ -481,7 +494,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
             }
             __syncthreads();
         }
-        if (stager) finish(smem + ((ntiles - 1) & 1) * BUF, tbeg + int64_t(ntiles - 1) * T);
+        if (stager) finish(smem + ((ntiles - 1) & 1) * BUF, tbeg + int64_t(ntiles - 1) * T, ntiles - 1);
     } else {
         issue_loads(tbeg);
         for (int kt = 0; kt < ntiles; ++kt) {
@@ -491,7 +504,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
             __syncthreads();
             walk(smem);
             __syncthreads();
-            finish(smem, t0);
+            finish(smem, t0, kt);
         }
     }
 
