@@ -221,6 +221,7 @@ inline size_t lds_floats_g(int G, int spl, bool full) {
 template <typename IO, int SPL, bool SCALAR, int MODE, bool VEC, int G>
 __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(Params p) {
     using S = Shape<G, SPL>;
+    constexpr int NP_ = G * SPL;
     constexpr bool kSpec = S::kSpec;
     constexpr int NS = S::NS;
     constexpr int T = S::T;
@@ -231,11 +232,17 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     constexpr bool kFullMode = (MODE == kFull);
     constexpr int BCW = 2 * SPL;                   // floats per (wave, step) in sBC
     constexpr int NBC = G * T * BCW;               // sBC values per tile
-    // B/C staging: one sBC value per thread and pass; a wave's 64 lanes cover 64/BCW
-    // steps x BCW slots, i.e. 64 distinct LDS banks per write.
-    constexpr int KBC = (NBC + NS - 1) / NS;
+    // B/C staging, two ways.  Small tiles: one sBC value per thread and pass, a
+    // wave's 64 lanes covering 64/BCW steps x BCW slots (64 distinct LDS banks per
+    // write).  Large tiles (more than 8 values per thread): 16-byte row vectors of B
+    // and C, each thread writing its vector's values down one sBC column.
+    constexpr int KBC = (NBC + NS - 1) / NS;       // values per staging thread
+    constexpr bool kVecBC = KBC > 8;
+    constexpr int NBV = 2 * NP_ * TV;              // B and C row vectors per tile
+    constexpr int KBV = kVecBC ? (NBV + NS - 1) / NS : 0;   // of them per staging thread
+    constexpr int KBE = kVecBC ? 0 : KBC;
     constexpr int QB = SPL <= 4 ? 4 : (SPL == 8 ? 2 : 1);   // steps whose LDS operands are read together
-    constexpr int NP = G * SPL;                    // padded state count
+    constexpr int NP = NP_;                        // padded state count
     constexpr float kLn2f = kLn2;
     constexpr int BUF = T * kRow * 2 + NBC + (kFullMode ? (G + 2) * T * kRowY : 0);   // floats per buffer
     static_assert(T % 8 == 0, "time tile must hold whole vectors and step groups");
@@ -304,6 +311,39 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
         sv_row[k] = (int64_t(b) * p.dim + (sv_ok[k] ? d : 0)) * p.L;
     }
 
+    // ---- B/C staging constants: row vectors v = stid + k*NS, B rows first, then C
+    const IO* bc_row[KBV > 0 ? KBV : 1];
+    int bc_dst[KBV > 0 ? KBV : 1], bc_tv[KBV > 0 ? KBV : 1];
+    bool bc_on[KBV > 0 ? KBV : 1], bc_ok[KBV > 0 ? KBV : 1], bc_isC[KBV > 0 ? KBV : 1];
+#pragma unroll
+    for (int k = 0; k < KBV; ++k) {
+        const int v = stid + k * NS;
+        bc_on[k] = stager && v >= 0 && v < NBV;
+        const int isC = v / (NP * TV);
+        const int rem = v % (NP * TV);
+        const int n = rem / TV;
+        bc_tv[k] = rem % TV;
+        bc_isC[k] = isC != 0;
+        bc_ok[k] = bc_on[k] && n < p.N && (kFullMode || !isC);
+        bc_row[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bc_ok[k] ? n : 0)) * p.L;
+        bc_dst[k] = (n / SPL) * T * BCW + (n % SPL) + (isC ? SPL : 0);
+    }
+
+    const IO* bce_ptr[KBE > 0 ? KBE : 1];
+    int bce_t[KBE > 0 ? KBE : 1];
+    bool bce_on[KBE > 0 ? KBE : 1];
+#pragma unroll
+    for (int k = 0; k < KBE; ++k) {
+        const int idx = stid + k * NS;
+        const int wn = idx / (T * BCW), rem = idx % (T * BCW);
+        const int t = rem / BCW, slot = rem % BCW;
+        const int64_t n = int64_t(wn) * SPL + (slot % SPL);
+        const bool isC = slot >= SPL;
+        bce_on[k] = stager && idx >= 0 && idx < NBC && n < p.N && (kFullMode || !isC);
+        bce_t[k] = t;
+        bce_ptr[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bce_on[k] ? n : 0)) * p.L + t;
+    }
+
     // ---- starting state of this piece
     float h[SPL];
 #pragma unroll
@@ -318,8 +358,8 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     float dtsum = 0.0f, dtcomp = 0.0f;   // compensated (Kahan) sum of dt2 over the piece
 
-    Vec<IO> nu[KX], ndl[KX], nz[KX];
-    IO nbcv[KBC];
+    Vec<IO> nu[KX], ndl[KX], nz[KX], nbc[KBV > 0 ? KBV : 1];
+    IO nbce[KBE > 0 ? KBE : 1];
 
     // ---- global -> registers for the tile starting at t0 (staging threads)
     auto issue_loads = [&](int64_t t0) {
@@ -333,18 +373,11 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
             }
         }
 #pragma unroll
-        for (int k = 0; k < KBC; ++k) {
-            const int idx = stid + k * NS;
-            if (NBC % NS == 0 || idx < NBC) {
-                const int wn = idx / (T * BCW), rem = idx % (T * BCW);
-                const int t = rem / BCW, slot = rem % BCW;
-                const int64_t n = int64_t(wn) * SPL + (slot % SPL);
-                const bool isC = slot >= SPL;
-                const bool ok = n < p.N && t0 + t < tend && (kFullMode || !isC);
-                const IO* src = isC ? gC : gB;
-                nbcv[k] = ok ? src[(int64_t(b) * p.N + n) * p.L + t0 + t] : IO(0);
-            }
-        }
+        for (int k = 0; k < KBV; ++k)
+            if (bc_on[k]) nbc[k] = load_vec<IO, VEC>(bc_row[k], t0 + bc_tv[k] * VW, tend, bc_ok[k]);
+#pragma unroll
+        for (int k = 0; k < KBE; ++k)
+            nbce[k] = (bce_on[k] && t0 + bce_t[k] < tend) ? bce_ptr[k][t0] : IO(0);
     };
 
     // ---- registers -> LDS buffer `buf` for the tile starting at t0 (staging threads):
@@ -382,10 +415,19 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
             }
         }
 #pragma unroll
-        for (int k = 0; k < KBC; ++k) {
+        for (int k = 0; k < KBV; ++k) {
+            if (bc_on[k]) {
+                const float sc = bc_isC[k] ? 1.0f : kLn2f;
+                float* dst = sBC + bc_dst[k] + bc_tv[k] * VW * BCW;
+#pragma unroll
+                for (int e = 0; e < VW; ++e) dst[e * BCW] = IOT<IO>::to_f32(nbc[k].e[e]) * sc;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KBE; ++k) {
             const int idx = stid + k * NS;
-            if (NBC % NS == 0 || idx < NBC)
-                sBC[idx] = IOT<IO>::to_f32(nbcv[k]) * ((idx % BCW) < SPL ? kLn2f : 1.0f);
+            if (stager && (NBC % NS == 0 || idx < NBC))
+                sBC[idx] = IOT<IO>::to_f32(nbce[k]) * ((idx % BCW) < SPL ? kLn2f : 1.0f);
         }
     };
 
