@@ -644,17 +644,19 @@ int make_plan(const ssm_dims* d, Plan* pl) {
     const int64_t tiles = cdiv(d->seqlen, pl->T);
     int64_t nch = d->nchunks;
     if (nch == 0) {
-        // one wave per SIMD (256 CUs x 4 SIMDs) is the floor below which the sequence is
-        // cut into pieces; pieces cost a second pass over all but the first, so cut
+        // One wave per SIMD (256 CUs x 4 SIMDs) is the floor below which the sequence is
+        // cut into pieces; pieces cost a second pass over all but the last, so cut
         // only when the machine would otherwise be at most half busy.
+        // Also cut when the workgroups (one CU each: their LDS tiles take most of a
+        // CU's 160 KB) would leave at least half of the 256 CUs idle.
         const int64_t waves = groups * pl->G;
+        const int64_t cus = 256;
         nch = 1;
-        if (waves * 2 <= 1024) {
-            nch = cdiv(2048, waves);
-            const int64_t max_pieces = tiles / 8 > 1 ? tiles / 8 : 1;   // keep >= 8 tiles per piece
-            if (nch > max_pieces) nch = max_pieces;
-            if (nch > SSM_MAX_CHUNKS) nch = SSM_MAX_CHUNKS;
-        }
+        if (waves * 2 <= 1024) nch = cdiv(2048, waves);
+        if (groups * 2 <= cus && cdiv(cus, groups) > nch) nch = cdiv(cus, groups);
+        const int64_t max_pieces = tiles / 8 > 1 ? tiles / 8 : 1;   // keep >= 8 tiles per piece
+        if (nch > max_pieces) nch = max_pieces;
+        if (nch > SSM_MAX_CHUNKS) nch = SSM_MAX_CHUNKS;
     }
     if (nch > tiles) nch = tiles;
     if (nch < 1) nch = 1;

@@ -112,6 +112,8 @@ def test_plans_of_the_five_workloads(index):
         assert plan["nchunks"] > 1 and plan["workspace_bytes"] > 0     # too few channels to fill the GPU
     if index == 3:
         assert plan["nchunks"] == 1 and plan["workspace_bytes"] == 0
+    if index == 5:
+        assert plan["nchunks"] == 2       # 128 channel blocks would leave half of the 256 CUs idle
 
 
 def test_forced_options_show_in_plan():
