@@ -64,6 +64,8 @@ def _load():
         lib.oracle_selective_recurrence.restype = ctypes.c_int
         lib.oracle_selective_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 9 + [ctypes.c_int]
         lib.oracle_selective_scan_fwd.restype = ctypes.c_int
+        lib.oracle_selective_scan_state.argtypes = [i64, i64, i64, i64] + [dp] * 11 + [ctypes.c_int]
+        lib.oracle_selective_scan_state.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -136,3 +138,36 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, nthreads
     if code != OK:
         raise OracleError(code, "selective_scan_fwd")
     return y
+
+
+def selective_scan_state(u, delta, A, B, C, D=None, z=None, dt_bias=None, h0=None, nthreads: int = 0):
+    """fp64 selective scan from state h0 (batch, dim, N; None = zeros).
+
+    Returns (y, h_last): y (batch, dim, L) and the state after the last step.
+    """
+    u, delta, A, B, C = (_f64(x) for x in (u, delta, A, B, C))
+    D, z, dt_bias, h0 = _f64(D), _f64(z), _f64(dt_bias), _f64(h0)
+    batch, dim, L = u.shape
+    N = B.shape[1]
+    if h0 is not None and h0.shape != (batch, dim, N):
+        raise ValueError("h0 must be (batch, dim, N)")
+    if B.shape != (batch, N, L) or C.shape != (batch, N, L) or A.shape != (dim, N):
+        raise ValueError("B, C must be (batch, N, L) and A (dim, N)")
+    y = np.zeros((batch, dim, L), dtype=np.float64)
+    h_last = np.zeros((batch, dim, N), dtype=np.float64)
+    code = _load().oracle_selective_scan_state(
+        batch, L, dim, N, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+        _ptr(h0), _ptr(y), _ptr(h_last), int(nthreads))
+    if code != OK:
+        raise OracleError(code, "selective_scan_state")
+    return y, h_last
+
+
+def selective_scan_step(u, delta, A, B, C, D=None, z=None, dt_bias=None, h=None):
+    """One recurrent decoding step: u, delta, z (batch, dim); B, C (batch, N); state h
+    (batch, dim, N; None = zeros).  Returns (y (batch, dim), new state)."""
+    u = _f64(u)
+    batch, dim = u.shape
+    col = lambda a: None if a is None else _f64(a)[..., None]
+    y, h_new = selective_scan_state(col(u), col(delta), A, col(B), col(C), D, col(z), dt_bias, h0=h)
+    return y[..., 0], h_new

@@ -86,14 +86,18 @@ int oracle_selective_recurrence(int64_t n, const double* value, const double* re
 }
 
 /*
- * Selective-scan forward, one fp64 recurrence per row (b, d).
+ * Selective-scan forward with a carried state, one fp64 recurrence per row (b, d).
  *
  * Layouts (row-major, last index contiguous):
  *   u, delta, z, y : (batch, dim, L)
  *   Bm, Cm         : (batch, N, L)      one B_t, C_t per token, shared by all channels
  *   A              : (dim, N)           fixed diagonal decay per channel
  *   Dskip, dt_bias : (dim,)
- * Dskip, z and dt_bias may be NULL (no skip, no gate, zero bias).
+ *   h0, h_last     : (batch, dim, N)    state before the first and after the last step
+ * Dskip, z and dt_bias may be NULL (no skip, no gate, zero bias); h0 may be NULL (the
+ * state starts at zero, as the scalar model on [QT] does) and h_last may be NULL (the
+ * final state is not returned).  A state carried from one call into the next is the
+ * fixed-size per-token state of recurrent decoding ([QA] Q8 and Q11; [QT] "直接回答").
  *
  * Per row, for t = 0 .. L-1 (all in double):
  *   dt    = softplus(delta[t] + dt_bias[d])                         step size ([QA] Q4/Q5)
@@ -103,7 +107,6 @@ int oracle_selective_recurrence(int64_t n, const double* value, const double* re
  *   y[t]  = (sum_n C[t,n] * h[n] + Dskip[d] * u[t]) * SiLU(z[t])     (readout after the update,
  *           [QT] scalar model; skip term D*u from the continuous output equation, [QA] Q1;
  *           SiLU gate, [GS] §3.1)
- * The state starts at zero, as the scalar model on [QT] does.
  *
  * Refused before anything is computed: a zero or negative size, a NULL required
  * pointer, any non-finite input, or A[d,n] > 0 (which, with dt > 0, would give a
@@ -111,10 +114,11 @@ int oracle_selective_recurrence(int64_t n, const double* value, const double* re
  *
  * nthreads <= 0 lets OpenMP choose.  Returns OR_OK or a negative code.
  */
-int oracle_selective_scan_fwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
-                              const double* u, const double* delta, const double* A,
-                              const double* Bm, const double* Cm, const double* Dskip,
-                              const double* z, const double* dt_bias, double* y, int nthreads)
+int oracle_selective_scan_state(int64_t batch, int64_t L, int64_t dim, int64_t N,
+                                const double* u, const double* delta, const double* A,
+                                const double* Bm, const double* Cm, const double* Dskip,
+                                const double* z, const double* dt_bias, const double* h0,
+                                double* y, double* h_last, int nthreads)
 {
     if (batch <= 0 || L <= 0 || dim <= 0 || N <= 0) return OR_ERR_EMPTY;
     if (!u || !delta || !A || !Bm || !Cm || !y) return OR_ERR_NULL;
@@ -124,7 +128,7 @@ int oracle_selective_scan_fwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
         !all_finite(Bm, nbc) || !all_finite(Cm, nbc))
         return OR_ERR_NONFINITE;
     if ((Dskip && !all_finite(Dskip, dim)) || (z && !all_finite(z, nel)) ||
-        (dt_bias && !all_finite(dt_bias, dim)))
+        (dt_bias && !all_finite(dt_bias, dim)) || (h0 && !all_finite(h0, batch * dim * N)))
         return OR_ERR_NONFINITE;
     for (int64_t i = 0; i < dim * N; ++i)
         if (A[i] > 0.0) return OR_ERR_RETAIN;
@@ -154,7 +158,7 @@ int oracle_selective_scan_fwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
             const int64_t d = r % dim;
             const double bias = dt_bias ? dt_bias[d] : 0.0;
             const double skip = Dskip ? Dskip[d] : 0.0;
-            for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+            for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[r * N + n] : 0.0;
             for (int64_t t = 0; t < L; ++t) {
                 const double dt = oracle_softplus(delta[r * L + t] + bias);
                 const double ut = u[r * L + t];
@@ -170,10 +174,22 @@ int oracle_selective_scan_fwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
                 if (z) out *= oracle_silu(z[r * L + t]);
                 y[r * L + t] = out;
             }
+            if (h_last)
+                for (int64_t n = 0; n < N; ++n) h_last[r * N + n] = h[n];
         }
         free(h);
     }
     return failed ? OR_ERR_ALLOC : OR_OK;
+}
+
+/* The scan from a zero state, without returning the final state. */
+int oracle_selective_scan_fwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
+                              const double* u, const double* delta, const double* A,
+                              const double* Bm, const double* Cm, const double* Dskip,
+                              const double* z, const double* dt_bias, double* y, int nthreads)
+{
+    return oracle_selective_scan_state(batch, L, dim, N, u, delta, A, Bm, Cm, Dskip, z, dt_bias,
+                                       NULL, y, NULL, nthreads);
 }
 
 /* Number of threads an OpenMP parallel region would use (1 without OpenMP). */

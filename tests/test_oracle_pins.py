@@ -325,3 +325,61 @@ def test_thread_count_does_not_change_result():
     y1 = oracle.selective_scan_fwd(u, delta, A, Bm, Cm, D, z, bias, nthreads=1)
     y4 = oracle.selective_scan_fwd(u, delta, A, Bm, Cm, D, z, bias, nthreads=4)
     np.testing.assert_array_equal(y1, y4)
+
+
+# ---------------------------------------------------------------- carried state, decode step
+
+def test_scalar_example_as_decode_steps():
+    """The worked example fed one token at a time, the state carried between calls,
+    gives the printed outputs (recurrent decoding keeps a fixed-size state)."""
+    steps, _, expect = _golden()
+    printed = [float(v) for v in expect["expect_outputs_2dp"]]
+    h = None
+    outs = []
+    for value, retain, write, read in steps:
+        dt = -math.log(retain)
+        dr = math.log(math.expm1(dt))
+        y, h = oracle.selective_scan_step(u=[[value]], delta=[[dr]], A=[[-1.0]], B=[[write / dt]], C=[[read]], h=h)
+        outs.append(y[0, 0])
+    np.testing.assert_allclose(outs, printed, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(h.reshape(-1), [printed[-1]], rtol=0, atol=1e-12)
+
+
+def test_initial_state_closed_form():
+    """With a starting state h0: y_t = [sum_n C_{t,n} (e^{A_n S_t} h0_n + sum_{i<=t}
+    e^{A_n (S_t - S_i)} dt_i B_{i,n} u_i) + D u_t] SiLU(z_t), S_t = sum_{k<=t} dt_k, and
+    the final state is the bracketed state at t = L-1."""
+    rng = np.random.default_rng(23)
+    batch, dim, N, L = 2, 3, 4, 20
+    u, delta, z, Bm, Cm, A, D, bias = _rand_problem(rng, batch, dim, N, L)
+    h0 = rng.standard_normal((batch, dim, N)) * 3.0
+    y, h_last = oracle.selective_scan_state(u, delta, A, Bm, Cm, D, z, bias, h0=h0)
+    for b in range(batch):
+        for d in range(dim):
+            dt = softplus_ref(delta[b, d] + bias[d])
+            S = np.cumsum(dt)
+            for t in range(L):
+                state = np.exp(A[d] * S[t]) * h0[b, d]
+                for i in range(t + 1):
+                    state = state + np.exp(A[d] * (S[t] - S[i])) * dt[i] * Bm[b, :, i] * u[b, d, i]
+                ref = (np.sum(Cm[b, :, t] * state) + D[d] * u[b, d, t]) * silu_ref(z[b, d, t])
+                assert y[b, d, t] == pytest.approx(ref, rel=1e-11, abs=1e-12)
+            np.testing.assert_allclose(h_last[b, d], state, rtol=1e-11, atol=1e-12)
+
+
+def test_zero_initial_state_is_the_plain_scan():
+    rng = np.random.default_rng(24)
+    u, delta, z, Bm, Cm, A, D, bias = _rand_problem(rng, 2, 3, 5, 17)
+    y0 = oracle.selective_scan_fwd(u, delta, A, Bm, Cm, D, z, bias)
+    y1, _ = oracle.selective_scan_state(u, delta, A, Bm, Cm, D, z, bias, h0=np.zeros((2, 3, 5)))
+    np.testing.assert_array_equal(y0, y1)
+
+
+def test_state_refusals():
+    rng = np.random.default_rng(25)
+    u, delta, z, Bm, Cm, A, D, bias = _rand_problem(rng, 1, 2, 3, 5)
+    h0 = np.zeros((1, 2, 3))
+    h0[0, 1, 2] = np.nan
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.selective_scan_state(u, delta, A, Bm, Cm, D, z, bias, h0=h0)
+    assert e.value.code == oracle.ERR_NONFINITE
