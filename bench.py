@@ -172,6 +172,47 @@ def summarize_profiles(d):
     print(json.dumps({"traffic_bytes_per_launch": rd + wr, "ratio_to_algorithmic": (rd + wr) / alg}))
 
 
+def decode_step_bench(batch: int, steps: int = 200, warmup: int = 50):
+    """Time ssm_selective_scan_step on a Mamba-1.3B layer (dim 4096, N 16, bf16 I/O,
+    fp32 state) decoding `batch` sequences at once: one call = one token each."""
+    import numpy as np
+    import torch
+    import selective_state_space_79_amd as ssm
+    from selective_state_space_79_amd.inputs import make_inputs, to_device
+
+    dim, N = 4096, 16
+    x = make_inputs(batch, 1, dim, N, seed=33, io="bf16")
+    dev = to_device(x, "cuda:0")
+    col = {k: dev[k][..., 0].contiguous() for k in ("u", "delta", "z", "B", "C")}
+    rng = np.random.default_rng(34)
+    h = torch.from_numpy(rng.standard_normal((batch, dim, N)).astype(np.float32)).cuda()
+    y = torch.empty_like(col["u"])
+    dims = ssm.make_dims(batch, 1, dim, N, io_dtype=ssm.SSM_BF16)
+    stream = torch.cuda.current_stream()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (p(col["u"]), p(col["delta"]), p(dev["A"]), p(col["B"]), p(col["C"]), p(dev["D"]), p(col["z"]),
+            p(dev["dt_bias"]), p(h), p(y), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream))
+    fn = ssm.load_library().ssm_selective_scan_step
+    for _ in range(warmup):
+        assert fn(*args) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn(*args)
+    e1.record(stream)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    # algorithmic bytes: state read + written, A once, u/delta/z read and y written,
+    # B and C per sequence, D and dt_bias once
+    nbytes = 8 * batch * dim * N + 4 * dim * N + 8 * batch * dim + 4 * batch * N + 8 * dim
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"mamba-1.3b-layer decode step, {batch} sequences (dim {dim}, N {N}, bf16 I/O, fp32 state)",
+            "us_per_step": round(us, 3), "tokens_per_s": round(batch / (us * 1e-6), 1),
+            "updates_per_s": batch * dim * N / (us * 1e-6), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +330,8 @@ def main():
         "timing": {"ms_events": ms_events, "ms_wall": ms_wall, "input_gen_s": round(gen_s, 2),
                    "kernel_source_sha256_16": kernel_hash(), "device": torch.cuda.get_device_name(0)},
     }
+    if args.workload == 3:
+        rec["decode_step"] = [decode_step_bench(64), decode_step_bench(256)]
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_batches)
     print(json.dumps(rec), flush=True)

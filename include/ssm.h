@@ -111,6 +111,28 @@ SSM_API int ssm_selective_scan_fwd(const void* u, const void* delta, const float
                                    const float* D, const void* z, const float* dt_bias, void* y,
                                    const ssm_dims* dims, void* stream);
 
+/* The same pass with a carried state.  h0 (nullable: zeros) is the float32 state
+ * (batch, dim, dstate) before the first step; h_last (nullable: not returned)
+ * receives the state after the last step, in the same layout.  h_last may be h0
+ * itself (the state is then updated in place) but must not overlap any other array.
+ * Carrying the fixed-size state from one call to the next is the recurrent decoding
+ * of yo3nglau.github.io "Mamba 与状态空间模型：面试问题与推荐回答" Q8 and Q11. */
+SSM_API int ssm_selective_scan_fwd_state(const void* u, const void* delta, const float* A, const void* B,
+                                         const void* C, const float* D, const void* z, const float* dt_bias,
+                                         const float* h0, void* y, float* h_last, const ssm_dims* dims,
+                                         void* stream);
+
+/* One decoding step (dims->seqlen must be 1): for every batch row b and channel d,
+ *   h[b,d,n] <- exp(dt*A[d,n]) * h[b,d,n] + dt * B[b,n] * u[b,d],  dt = softplus(delta[b,d] + dt_bias[d])
+ *   y[b,d]    = (sum_n C[b,n] * h[b,d,n] + D[d] * u[b,d]) * SiLU(z[b,d])
+ * u, delta, z, y: (batch, dim) in io_dtype; B, C: (batch, dstate) in io_dtype;
+ * h: float32 (batch, dim, dstate), read and updated in place (required).  The O(1)
+ * per-token update of yo3nglau.github.io Q8/Q11.  Needs no workspace.  Same error
+ * rules as ssm_selective_scan_fwd; seqlen != 1 gives SSM_ERR_DIMS. */
+SSM_API int ssm_selective_scan_step(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                    const float* D, const void* z, const float* dt_bias, float* h, void* y,
+                                    const ssm_dims* dims, void* stream);
+
 /* Static English text for a status value. */
 SSM_API const char* ssm_status_string(int status);
 

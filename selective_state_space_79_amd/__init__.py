@@ -5,9 +5,10 @@ Argument marshalling only: every step of the scan runs in the HIP kernels of
 PyTorch fallback: if the library is missing, every call raises.
 
 The functions carry the C names (``ssm_selective_scan_fwd``,
+``ssm_selective_scan_fwd_state``, ``ssm_selective_scan_step``,
 ``ssm_selective_scan_workspace_bytes``, ``ssm_selective_scan_plan``,
-``ssm_status_string``); ``selective_scan_fwd`` additionally allocates y and the
-workspace through PyTorch's caching allocator.
+``ssm_status_string``); ``selective_scan_fwd`` and ``selective_scan_step``
+additionally allocate outputs and the workspace through PyTorch's caching allocator.
 """
 from __future__ import annotations
 
@@ -31,8 +32,8 @@ SSM_BF16 = 1
 SSM_MAX_DSTATE = 256
 SSM_MAX_CHUNKS = 1024
 
-EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan",
-            "ssm_status_string")
+EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_fwd_state", "ssm_selective_scan_step",
+            "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan", "ssm_status_string")
 
 
 class SsmDims(ctypes.Structure):
@@ -88,6 +89,10 @@ def load_library():
         vp = ctypes.c_void_p
         lib.ssm_selective_scan_fwd.argtypes = [vp] * 9 + [ctypes.POINTER(SsmDims), vp]
         lib.ssm_selective_scan_fwd.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd_state.argtypes = [vp] * 11 + [ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_fwd_state.restype = ctypes.c_int
+        lib.ssm_selective_scan_step.argtypes = [vp] * 10 + [ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_step.restype = ctypes.c_int
         lib.ssm_selective_scan_workspace_bytes.argtypes = [ctypes.POINTER(SsmDims)]
         lib.ssm_selective_scan_workspace_bytes.restype = ctypes.c_size_t
         lib.ssm_selective_scan_plan.argtypes = [ctypes.POINTER(SsmDims), ctypes.POINTER(SsmPlan)]
@@ -141,6 +146,29 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D, z, dt_bias, y, dims: SsmDims, s
         ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
 
 
+def ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, dims: SsmDims,
+                                 stream=None) -> int:
+    """C entry point with a carried state: h0, h_last float32 (batch, dim, N) or None."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device)
+    return int(load_library().ssm_selective_scan_fwd_state(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y),
+        _ptr(h_last), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
+def ssm_selective_scan_step(u, delta, A, B, C, D, z, dt_bias, h, y, dims: SsmDims, stream=None) -> int:
+    """C entry point of one decoding step; h float32 (batch, dim, N) is updated in place."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device)
+    return int(load_library().ssm_selective_scan_step(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h), _ptr(y),
+        ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
 def dims_for(u, B, A, *, nchunks=0, states_per_lane=0) -> SsmDims:
     """ssm_dims for tensors laid out as include/ssm.h describes."""
     import torch
@@ -159,16 +187,9 @@ def dims_for(u, B, A, *, nchunks=0, states_per_lane=0) -> SsmDims:
                      states_per_lane=states_per_lane)
 
 
-def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, out=None, workspace=None, nchunks=0,
-                       states_per_lane=0, stream=None):
-    """Allocate y (and the workspace, if the plan needs one) and run the scan.
-
-    Tensors must be contiguous CUDA tensors with the layouts of include/ssm.h.
-    Raises SsmError on a refused call.  Returns y.
-    """
+def _check_tensors(u, tensors, f32_names=("A", "D", "dt_bias", "h0", "h")):
     import torch
 
-    tensors = dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias)
     for name, t in tensors.items():
         if t is None:
             continue
@@ -176,24 +197,55 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, out=N
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    for name in ("delta", "B", "C", "z"):
-        t = tensors[name]
-        if t is not None and t.dtype != u.dtype:
+        if name in f32_names:
+            if t.dtype != torch.float32:
+                raise TypeError(f"{name} must be float32")
+        elif t.dtype != u.dtype:
             raise TypeError(f"{name} must have u's dtype {u.dtype}")
-    for name in ("A", "D", "dt_bias"):
-        t = tensors[name]
-        if t is not None and t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32")
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, h0=None, return_state=False, out=None,
+                       workspace=None, nchunks=0, states_per_lane=0, stream=None):
+    """Allocate y (and the workspace, if the plan needs one) and run the scan.
+
+    Tensors must be contiguous CUDA tensors with the layouts of include/ssm.h.
+    h0: optional float32 (batch, dim, N) starting state.  With return_state=True the
+    final state is returned too, as (y, h_last).  Raises SsmError on a refused call.
+    """
+    import torch
+
+    _check_tensors(u, dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h0=h0))
     dims = dims_for(u, B, A, nchunks=nchunks, states_per_lane=states_per_lane)
     if out is None:
         out = torch.empty_like(u)
+    h_last = None
+    if return_state:
+        h_last = torch.empty((u.shape[0], u.shape[1], B.shape[1]), dtype=torch.float32, device=u.device)
     need = ssm_selective_scan_workspace_bytes(dims)
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
         dims.workspace = workspace.data_ptr()
         dims.workspace_bytes = workspace.numel() * workspace.element_size()
-    st = ssm_selective_scan_fwd(u, delta, A, B, C, D, z, dt_bias, out, dims, stream)
+    st = ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, h0, out, h_last, dims, stream)
     if st != SSM_OK:
-        raise SsmError(st, "ssm_selective_scan_fwd")
+        raise SsmError(st, "ssm_selective_scan_fwd_state")
+    return (out, h_last) if return_state else out
+
+
+def selective_scan_step(u, delta, A, B, C, D, z, dt_bias, h, *, out=None, stream=None):
+    """One decoding step.  u, delta, z: (batch, dim); B, C: (batch, N); h: float32
+    (batch, dim, N), updated in place.  Returns y (batch, dim)."""
+    import torch
+
+    _check_tensors(u, dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h=h))
+    if u.dim() != 2 or B.dim() != 2 or h.dim() != 3:
+        raise ValueError("u must be (batch, dim), B (batch, N) and h (batch, dim, N)")
+    io = SSM_BF16 if u.dtype == torch.bfloat16 else SSM_F32
+    dims = make_dims(u.shape[0], 1, u.shape[1], B.shape[1], nheads=A.shape[0] if A.dim() == 1 else 0, io_dtype=io)
+    if out is None:
+        out = torch.empty_like(u)
+    st = ssm_selective_scan_step(u, delta, A, B, C, D, z, dt_bias, h, out, dims, stream)
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_selective_scan_step")
     return out

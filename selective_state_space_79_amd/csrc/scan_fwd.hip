@@ -146,6 +146,8 @@ struct Params {
     int32_t nblk_d;       // channel blocks per batch row
     int32_t batch;
     int32_t np;           // padded state count = waves * SPL
+    const float* h0;      // nullable: (batch, dim, N) state before the first step
+    float* h_last;        // nullable: (batch, dim, N) state after the last step
     float* ws_H;          // [groups][nchunks][np][64] piece end states from zero (pass 1)
     float* ws_S;          // [groups][nchunks][64]     sum of dt2 over each piece (pass 1)
     float* ws_Hin;        // [groups][nchunks][np][64] true starting state of each piece
@@ -348,10 +350,20 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     float h[SPL];
 #pragma unroll
     for (int j = 0; j < SPL; ++j) h[j] = 0.0f;
-    if (kFullMode && piece > 0 && walker) {
-        const float* hin = p.ws_Hin + ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
+    if (kFullMode && walker) {
+        if (p.nchunks > 1) {
+            // every piece, the first included, starts from the carried state, so h0 is
+            // read only by the carry kernel and may be the same array as h_last
+            const float* hin = p.ws_Hin + ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) h[j] = hin[int64_t(j) * kLanes];
+            for (int j = 0; j < SPL; ++j) h[j] = hin[int64_t(j) * kLanes];
+        } else if (p.h0 && lane_ok) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t n = int64_t(w) * SPL + j;
+                if (n < p.N) h[j] = p.h0[(int64_t(b) * p.dim + dch) * p.N + n];
+            }
+        }
     }
     // Settle these loads now: left pending, they make the compiler wait for every
     // outstanding load (the next tile's prefetch included) inside the walk.
@@ -550,6 +562,15 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
         }
     }
 
+    if constexpr (kFullMode) {
+        if (walker && lane_ok && p.h_last && piece == p.nchunks - 1) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t n = int64_t(w) * SPL + j;
+                if (n < p.N) p.h_last[(int64_t(b) * p.dim + dch) * p.N + n] = h[j];
+            }
+        }
+    }
     if constexpr (!kFullMode) {
         if (walker) {
             float* hout = p.ws_H + ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
@@ -561,7 +582,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
 }
 
 // Compose the pieces' affine maps in sequence order: one thread per (group, state, lane).
-//   Hin[0] = 0;  Hin[c+1] = exp2(A * S2[c]) * Hin[c] + H[c]     (S2 = sum of dt2)
+//   Hin[0] = h0 (or 0);  Hin[c+1] = exp2(A * S2[c]) * Hin[c] + H[c]     (S2 = sum of dt2)
 __global__ void __launch_bounds__(256) scan_carry_kernel(Params p, int64_t total) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= total) return;
@@ -570,9 +591,12 @@ __global__ void __launch_bounds__(256) scan_carry_kernel(Params p, int64_t total
     const int64_t blk = i / (int64_t(kLanes) * p.np);
     const int64_t cblk = blk % p.nblk_d;
     const int64_t d = cblk * kLanes + lane;
-    float a = 0.0f;
-    if (d < p.dim && n < p.N) a = p.head_dim ? p.A[d / p.head_dim] : p.A[d * p.N + n];
-    float hcur = 0.0f;
+    const int64_t b = blk / p.nblk_d;
+    float a = 0.0f, hcur = 0.0f;
+    if (d < p.dim && n < p.N) {
+        a = p.head_dim ? p.A[d / p.head_dim] : p.A[d * p.N + n];
+        if (p.h0) hcur = p.h0[(b * p.dim + d) * p.N + n];
+    }
     for (int c = 0; c < p.nchunks; ++c) {
         const int64_t hidx = ((blk * p.nchunks + c) * p.np + n) * kLanes + lane;
         p.ws_Hin[hidx] = hcur;
@@ -581,6 +605,75 @@ __global__ void __launch_bounds__(256) scan_carry_kernel(Params p, int64_t total
             hcur = fmaf(__builtin_amdgcn_exp2f(a * s), hcur, p.ws_H[hidx]);
         }
     }
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ decode step
+// One token for every (batch, channel): h <- exp(dt*A) h + dt*B*u in place and
+// y = (C.h + D*u) * SiLU(z).  One thread per (batch, channel) walks its N state
+// entries; a wave's 64 channels read 64 consecutive state rows (whole cache lines),
+// and B, C of the batch row are read by all lanes alike.  The state round trip
+// (8 bytes per entry) dominates: the kernel is bound by HBM.
+struct StepParams {
+    const void* u;
+    const void* delta;
+    const void* z;        // nullable
+    const void* Bm;       // (batch, N)
+    const void* Cm;       // (batch, N)
+    const float* A;
+    const float* Dskip;   // nullable
+    const float* bias;    // nullable
+    float* h;             // (batch, dim, N), updated in place
+    void* y;
+    int64_t batch, dim, N, head_dim;
+};
+
+template <typename IO, bool SCALAR, bool VEC4>
+__global__ void __launch_bounds__(256) scan_step_kernel(StepParams p) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= p.batch * p.dim) return;
+    const int64_t b = i / p.dim, d = i % p.dim;
+    const IO* gB = static_cast<const IO*>(p.Bm) + b * p.N;
+    const IO* gC = static_cast<const IO*>(p.Cm) + b * p.N;
+    const float uu = IOT<IO>::to_f32(static_cast<const IO*>(p.u)[i]);
+    const float dr = IOT<IO>::to_f32(static_cast<const IO*>(p.delta)[i]) + (p.bias ? p.bias[d] : 0.0f);
+    const float dt2 = softplus_log2(dr);
+    const float x = dt2 * uu;
+    const float a_s = SCALAR ? __builtin_amdgcn_exp2f(dt2 * p.A[d / p.head_dim]) : 0.0f;
+    const float* Arow = p.A + d * p.N;
+    float* hrow = p.h + i * p.N;
+    float acc = 0.0f;
+    auto entry = [&](int64_t n, float hv) {
+        const float a = SCALAR ? a_s : __builtin_amdgcn_exp2f(dt2 * Arow[n]);
+        const float hn = fmaf(a, hv, x * (IOT<IO>::to_f32(gB[n]) * kLn2));
+        acc = fmaf(IOT<IO>::to_f32(gC[n]), hn, acc);
+        return hn;
+    };
+    if constexpr (VEC4) {
+        for (int64_t n = 0; n < p.N; n += 4) {
+            float4 hv = *reinterpret_cast<const float4*>(hrow + n);
+            hv.x = entry(n, hv.x);
+            hv.y = entry(n + 1, hv.y);
+            hv.z = entry(n + 2, hv.z);
+            hv.w = entry(n + 3, hv.w);
+            *reinterpret_cast<float4*>(hrow + n) = hv;
+        }
+    } else {
+        for (int64_t n = 0; n < p.N; ++n) hrow[n] = entry(n, hrow[n]);
+    }
+    float o = acc + (p.Dskip ? p.Dskip[d] : 0.0f) * uu;
+    if (p.z) o *= silu_f32(IOT<IO>::to_f32(static_cast<const IO*>(p.z)[i]));
+    static_cast<IO*>(p.y)[i] = IOT<IO>::from_f32(o);
+}
+
+template <typename IO, bool SCALAR>
+hipError_t launch_step(const StepParams& p, bool vec4, hipStream_t s) {
+    const int64_t total = p.batch * p.dim;
+    const dim3 grid(unsigned(cdiv(total, 256))), block(256);
+    if (vec4) hipLaunchKernelGGL((scan_step_kernel<IO, SCALAR, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_step_kernel<IO, SCALAR, false>), grid, block, 0, s, p);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ host side: planning
@@ -598,7 +691,6 @@ struct Plan {
     bool scalar;
 };
 
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int validate_dims(const ssm_dims* d) {
     if (!d) return SSM_ERR_NULL;
@@ -774,9 +866,9 @@ size_t ssm_selective_scan_workspace_bytes(const ssm_dims* dims) {
     return pl.ws_bytes;
 }
 
-int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                           const float* D, const void* z, const float* dt_bias, void* y, const ssm_dims* dims,
-                           void* stream) {
+int ssm_selective_scan_fwd_state(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                 const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
+                                 float* h_last, const ssm_dims* dims, void* stream) {
     if (!dims) return SSM_ERR_NULL;
     Plan pl;
     int st = make_plan(dims, &pl);
@@ -786,23 +878,34 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
     const size_t esz = dims->io_dtype == SSM_BF16 ? 2 : 4;
     auto misaligned = [](const void* q, size_t a) { return q && (reinterpret_cast<uintptr_t>(q) % a) != 0; };
     if (misaligned(u, esz) || misaligned(delta, esz) || misaligned(z, esz) || misaligned(B, esz) ||
-        misaligned(C, esz) || misaligned(y, esz) || misaligned(A, 4) || misaligned(D, 4) || misaligned(dt_bias, 4))
+        misaligned(C, esz) || misaligned(y, esz) || misaligned(A, 4) || misaligned(D, 4) || misaligned(dt_bias, 4) ||
+        misaligned(h0, 4) || misaligned(h_last, 4))
         return SSM_ERR_ALIGN;
 
     const size_t nel = size_t(dims->batch) * dims->dim * dims->seqlen * esz;
     const size_t nbc = size_t(dims->batch) * dims->dstate * dims->seqlen * esz;
     const size_t na = (dims->nheads > 0 ? size_t(dims->nheads) : size_t(dims->dim) * dims->dstate) * 4;
     const size_t nd = size_t(dims->dim) * 4;
+    const size_t nh = size_t(dims->batch) * dims->dim * dims->dstate * 4;
     if (overlaps(y, nel, u, nel) || overlaps(y, nel, delta, nel) || overlaps(y, nel, z, nel) ||
         overlaps(y, nel, B, nbc) || overlaps(y, nel, C, nbc) || overlaps(y, nel, A, na) ||
-        overlaps(y, nel, D, nd) || overlaps(y, nel, dt_bias, nd))
+        overlaps(y, nel, D, nd) || overlaps(y, nel, dt_bias, nd) || overlaps(y, nel, h0, nh) ||
+        overlaps(y, nel, h_last, nh))
+        return SSM_ERR_ALIAS;
+    // h_last may be h0 itself (an in-place state update) but no other input
+    if (h_last && ((h0 != h_last && overlaps(h_last, nh, h0, nh)) || overlaps(h_last, nh, u, nel) ||
+                   overlaps(h_last, nh, delta, nel) || overlaps(h_last, nh, z, nel) || overlaps(h_last, nh, B, nbc) ||
+                   overlaps(h_last, nh, C, nbc) || overlaps(h_last, nh, A, na) || overlaps(h_last, nh, D, nd) ||
+                   overlaps(h_last, nh, dt_bias, nd)))
         return SSM_ERR_ALIAS;
 
     if (pl.ws_bytes > 0) {
         if (!dims->workspace || dims->workspace_bytes < pl.ws_bytes ||
             (reinterpret_cast<uintptr_t>(dims->workspace) % 256) != 0)
             return SSM_ERR_WORKSPACE;
-        if (overlaps(dims->workspace, pl.ws_bytes, y, nel)) return SSM_ERR_ALIAS;
+        if (overlaps(dims->workspace, pl.ws_bytes, y, nel) || overlaps(dims->workspace, pl.ws_bytes, h0, nh) ||
+            overlaps(dims->workspace, pl.ws_bytes, h_last, nh))
+            return SSM_ERR_ALIAS;
     }
 
     // vector (16-byte) loads need 16-byte aligned rows: aligned base pointers and a
@@ -830,6 +933,8 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
     p.nblk_d = int32_t(pl.nblk_d);
     p.batch = int32_t(dims->batch);
     p.np = pl.G * pl.spl;
+    p.h0 = h0;
+    p.h_last = h_last;
     p.ws_H = p.ws_S = p.ws_Hin = nullptr;
     if (pl.ws_bytes > 0) {
         const size_t per = size_t(dims->batch) * pl.nblk_d * pl.nchunks * kLanes;
@@ -841,6 +946,62 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = dims->io_dtype == SSM_BF16 ? dispatch<uint16_t>(p, pl, vec, s) : dispatch<float>(p, pl, vec, s);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* dt_bias, void* y, const ssm_dims* dims,
+                           void* stream) {
+    return ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, nullptr, y, nullptr, dims, stream);
+}
+
+int ssm_selective_scan_step(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const void* z, const float* dt_bias, float* h, void* y,
+                            const ssm_dims* dims, void* stream) {
+    const int st = validate_dims(dims);
+    if (st != SSM_OK) return st;
+    if (dims->seqlen != 1) return SSM_ERR_DIMS;
+    if (!u || !delta || !A || !B || !C || !h || !y) return SSM_ERR_NULL;
+    const size_t esz = dims->io_dtype == SSM_BF16 ? 2 : 4;
+    auto misaligned = [](const void* q, size_t a) { return q && (reinterpret_cast<uintptr_t>(q) % a) != 0; };
+    if (misaligned(u, esz) || misaligned(delta, esz) || misaligned(z, esz) || misaligned(B, esz) ||
+        misaligned(C, esz) || misaligned(y, esz) || misaligned(A, 4) || misaligned(D, 4) || misaligned(dt_bias, 4) ||
+        misaligned(h, 4))
+        return SSM_ERR_ALIGN;
+    const size_t nel = size_t(dims->batch) * dims->dim * esz;
+    const size_t nbc = size_t(dims->batch) * dims->dstate * esz;
+    const size_t na = (dims->nheads > 0 ? size_t(dims->nheads) : size_t(dims->dim) * dims->dstate) * 4;
+    const size_t nd = size_t(dims->dim) * 4;
+    const size_t nh = size_t(dims->batch) * dims->dim * dims->dstate * 4;
+    const void* ins[] = {u, delta, z, B, C, A, D, dt_bias};
+    const size_t sizes[] = {nel, nel, nel, nbc, nbc, na, nd, nd};
+    for (int k = 0; k < 8; ++k)
+        if (overlaps(y, nel, ins[k], sizes[k]) || overlaps(h, nh, ins[k], sizes[k])) return SSM_ERR_ALIAS;
+    if (overlaps(y, nel, h, nh)) return SSM_ERR_ALIAS;
+
+    StepParams p;
+    p.u = u;
+    p.delta = delta;
+    p.z = z;
+    p.Bm = B;
+    p.Cm = C;
+    p.A = A;
+    p.Dskip = D;
+    p.bias = dt_bias;
+    p.h = h;
+    p.y = y;
+    p.batch = dims->batch;
+    p.dim = dims->dim;
+    p.N = dims->dstate;
+    p.head_dim = dims->nheads > 0 ? dims->dim / dims->nheads : 0;
+    const bool vec4 = dims->dstate % 4 == 0 && (reinterpret_cast<uintptr_t>(h) % 16) == 0;
+    const bool scalar = dims->nheads > 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dims->io_dtype == SSM_BF16)
+        e = scalar ? launch_step<uint16_t, true>(p, vec4, s) : launch_step<uint16_t, false>(p, vec4, s);
+    else
+        e = scalar ? launch_step<float, true>(p, vec4, s) : launch_step<float, false>(p, vec4, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -143,3 +143,47 @@ def test_every_plan_fits_the_lds_of_a_cu():
                         assert e.status == ssm.SSM_ERR_DIMS and spl and -(-N // spl) > 16
                         continue
                     assert plan.lds_bytes <= 160 * 1024, (N, spl, plan.as_dict())
+
+
+def _call_state(dims, h0=None, h_last=None, **kw):
+    lib = ssm.load_library()
+    base = dict(u=FAKE, delta=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000,
+                D=None, z=None, bias=None, y=FAKE + 0x500000)
+    base.update(kw)
+    args = [base["u"], base["delta"], base["A"], base["B"], base["C"], base["D"], base["z"], base["bias"], h0,
+            base["y"], h_last]
+    args = [None if a is None else ctypes.c_void_p(a) for a in args]
+    return lib.ssm_selective_scan_fwd_state(*args, ctypes.byref(dims), None)
+
+
+def _call_step(dims, h=FAKE + 0x700000, **kw):
+    lib = ssm.load_library()
+    base = dict(u=FAKE, delta=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000,
+                D=None, z=None, bias=None, y=FAKE + 0x500000)
+    base.update(kw)
+    args = [base["u"], base["delta"], base["A"], base["B"], base["C"], base["D"], base["z"], base["bias"], h,
+            base["y"]]
+    args = [None if a is None else ctypes.c_void_p(a) for a in args]
+    return lib.ssm_selective_scan_step(*args, ctypes.byref(dims), None)
+
+
+def test_state_entry_point_refusals():
+    d = small_dims()
+    assert _call_state(d, h0=FAKE + 0x600002) == ssm.SSM_ERR_ALIGN
+    assert _call_state(d, h_last=FAKE + 0x600002) == ssm.SSM_ERR_ALIGN
+    assert _call_state(d, h_last=FAKE + 0x500000 + 16) == ssm.SSM_ERR_ALIAS          # overlaps y
+    assert _call_state(d, h_last=FAKE + 0x200000) == ssm.SSM_ERR_ALIAS               # overlaps A
+    assert _call_state(d, h0=FAKE + 0x600000, h_last=FAKE + 0x600000 + 8) == ssm.SSM_ERR_ALIAS  # partial overlap
+    assert _call_state(small_dims(batch=0), h0=FAKE + 0x600000) == ssm.SSM_ERR_EMPTY
+    assert _call_state(d, u=None, h0=FAKE + 0x600000) == ssm.SSM_ERR_NULL
+
+
+def test_step_entry_point_refusals():
+    d1 = small_dims(seqlen=1)
+    assert _call_step(small_dims(seqlen=2)) == ssm.SSM_ERR_DIMS
+    assert _call_step(d1, h=None) == ssm.SSM_ERR_NULL
+    assert _call_step(d1, h=FAKE + 0x700002) == ssm.SSM_ERR_ALIGN
+    assert _call_step(d1, h=FAKE) == ssm.SSM_ERR_ALIAS                                # h overlaps u
+    assert _call_step(d1, h=FAKE + 0x500000 - 16) == ssm.SSM_ERR_ALIAS                # h overlaps y
+    assert _call_step(small_dims(seqlen=1, dim=0)) == ssm.SSM_ERR_EMPTY
+    assert _call_step(small_dims(seqlen=1, io_dtype=9)) == ssm.SSM_ERR_DTYPE
