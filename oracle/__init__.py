@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the selective-scan forward pass (ctypes wrapper over oracle.c).
+"""fp64 CPU oracle for the selective scan: forward, carried state, decode step and
+gradients (ctypes wrapper over oracle.c).
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
@@ -66,6 +67,10 @@ def _load():
         lib.oracle_selective_scan_fwd.restype = ctypes.c_int
         lib.oracle_selective_scan_state.argtypes = [i64, i64, i64, i64] + [dp] * 11 + [ctypes.c_int]
         lib.oracle_selective_scan_state.restype = ctypes.c_int
+        lib.oracle_sigmoid.argtypes = [ctypes.c_double]
+        lib.oracle_sigmoid.restype = ctypes.c_double
+        lib.oracle_selective_scan_bwd.argtypes = [i64, i64, i64, i64] + [dp] * 20 + [ctypes.c_int]
+        lib.oracle_selective_scan_bwd.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -90,6 +95,10 @@ def softplus(x: float) -> float:
 
 def silu(x: float) -> float:
     return _load().oracle_silu(float(x))
+
+
+def sigmoid(x: float) -> float:
+    return _load().oracle_sigmoid(float(x))
 
 
 def max_threads() -> int:
@@ -171,3 +180,42 @@ def selective_scan_step(u, delta, A, B, C, D=None, z=None, dt_bias=None, h=None)
     col = lambda a: None if a is None else _f64(a)[..., None]
     y, h_new = selective_scan_state(col(u), col(delta), A, col(B), col(C), D, col(z), dt_bias, h0=h)
     return y[..., 0], h_new
+
+
+def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, dy=None, h0=None, dh_last=None,
+                       nthreads: int = 0) -> dict:
+    """fp64 gradients of the scan for the loss sum(dy * y) + sum(dh_last * h_last).
+
+    Shapes as for selective_scan_state; dy (batch, dim, L); dh_last (batch, dim, N)
+    or None.  Returns a dict with du, ddelta, dA, dB, dC always, dD if D is given,
+    dz if z is given, ddt_bias and dh0 always (ddt_bias is the gradient of the bias
+    even when no bias is passed).
+    """
+    u, delta, A, B, C, dy = (_f64(x) for x in (u, delta, A, B, C, dy))
+    D, z, dt_bias, h0, dh_last = (_f64(x) for x in (D, z, dt_bias, h0, dh_last))
+    batch, dim, L = u.shape
+    N = B.shape[1]
+    if dy is None or dy.shape != u.shape:
+        raise ValueError("dy must be (batch, dim, L)")
+    if B.shape != (batch, N, L) or C.shape != (batch, N, L) or A.shape != (dim, N):
+        raise ValueError("B, C must be (batch, N, L) and A (dim, N)")
+    for name, v in (("h0", h0), ("dh_last", dh_last)):
+        if v is not None and v.shape != (batch, dim, N):
+            raise ValueError(f"{name} must be (batch, dim, N)")
+    out = {
+        "du": np.zeros((batch, dim, L)), "ddelta": np.zeros((batch, dim, L)), "dA": np.zeros((dim, N)),
+        "dB": np.zeros((batch, N, L)), "dC": np.zeros((batch, N, L)), "ddt_bias": np.zeros(dim),
+        "dh0": np.zeros((batch, dim, N)),
+    }
+    if D is not None:
+        out["dD"] = np.zeros(dim)
+    if z is not None:
+        out["dz"] = np.zeros((batch, dim, L))
+    code = _load().oracle_selective_scan_bwd(
+        batch, L, dim, N, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+        _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")), _ptr(out["ddt_bias"]),
+        _ptr(out["dh0"]), int(nthreads))
+    if code != OK:
+        raise OracleError(code, "selective_scan_bwd")
+    return out

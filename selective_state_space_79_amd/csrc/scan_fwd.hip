@@ -611,10 +611,15 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ decode step
 // One token for every (batch, channel): h <- exp(dt*A) h + dt*B*u in place and
-// y = (C.h + D*u) * SiLU(z).  One thread per (batch, channel) walks its N state
-// entries; a wave's 64 channels read 64 consecutive state rows (whole cache lines),
-// and B, C of the batch row are read by all lanes alike.  The state round trip
-// (8 bytes per entry) dominates: the kernel is bound by HBM.
+// y = (C.h + D*u) * SiLU(z).  The state round trip (8 bytes per entry) dominates:
+// the kernel is bound by HBM.
+//
+// Vector form (N a multiple of 4, aligned rows): R lanes share one (batch, channel)
+// row, each lane taking every R-th group of 4 entries, so that one load instruction
+// covers 16*R contiguous bytes of every row it touches; the R partial read-outs are
+// summed with lane shuffles.  Every lane computes the row's step size itself.  A
+// lane may serve several rows (ROWS), issuing their loads together.
+// Scalar form: one lane per row, entry by entry.
 struct StepParams {
     const void* u;
     const void* delta;
@@ -629,50 +634,145 @@ struct StepParams {
     int64_t batch, dim, N, head_dim;
 };
 
-template <typename IO, bool SCALAR, bool VEC4>
-__global__ void __launch_bounds__(256) scan_step_kernel(StepParams p) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= p.batch * p.dim) return;
-    const int64_t b = i / p.dim, d = i % p.dim;
-    const IO* gB = static_cast<const IO*>(p.Bm) + b * p.N;
-    const IO* gC = static_cast<const IO*>(p.Cm) + b * p.N;
-    const float uu = IOT<IO>::to_f32(static_cast<const IO*>(p.u)[i]);
+// 4 consecutive values of an I/O row as fp32 (16-byte or 8-byte aligned)
+__device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ inline float4 load4(const uint16_t* p) {
+    const uint2 r = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+}
+
+template <typename IO, bool SCALAR>
+__device__ inline void step_row_prologue(const StepParams& p, int64_t i, int64_t d, float& uu, float& dt2) {
+    uu = IOT<IO>::to_f32(static_cast<const IO*>(p.u)[i]);
     const float dr = IOT<IO>::to_f32(static_cast<const IO*>(p.delta)[i]) + (p.bias ? p.bias[d] : 0.0f);
-    const float dt2 = softplus_log2(dr);
-    const float x = dt2 * uu;
-    const float a_s = SCALAR ? __builtin_amdgcn_exp2f(dt2 * p.A[d / p.head_dim]) : 0.0f;
-    const float* Arow = p.A + d * p.N;
-    float* hrow = p.h + i * p.N;
-    float acc = 0.0f;
-    auto entry = [&](int64_t n, float hv) {
-        const float a = SCALAR ? a_s : __builtin_amdgcn_exp2f(dt2 * Arow[n]);
-        const float hn = fmaf(a, hv, x * (IOT<IO>::to_f32(gB[n]) * kLn2));
-        acc = fmaf(IOT<IO>::to_f32(gC[n]), hn, acc);
-        return hn;
-    };
-    if constexpr (VEC4) {
-        for (int64_t n = 0; n < p.N; n += 4) {
-            float4 hv = *reinterpret_cast<const float4*>(hrow + n);
-            hv.x = entry(n, hv.x);
-            hv.y = entry(n + 1, hv.y);
-            hv.z = entry(n + 2, hv.z);
-            hv.w = entry(n + 3, hv.w);
-            *reinterpret_cast<float4*>(hrow + n) = hv;
-        }
-    } else {
-        for (int64_t n = 0; n < p.N; ++n) hrow[n] = entry(n, hrow[n]);
-    }
+    dt2 = softplus_log2(dr);
+}
+
+template <typename IO>
+__device__ inline void step_row_epilogue(const StepParams& p, int64_t i, int64_t d, float uu, float acc) {
     float o = acc + (p.Dskip ? p.Dskip[d] : 0.0f) * uu;
     if (p.z) o *= silu_f32(IOT<IO>::to_f32(static_cast<const IO*>(p.z)[i]));
     static_cast<IO*>(p.y)[i] = IOT<IO>::from_f32(o);
 }
 
+template <typename IO, bool SCALAR, int R, int ROWS>
+__global__ void __launch_bounds__(256) scan_step_rows_kernel(StepParams p) {
+    // lane group s takes rows s, s + S, ..., s + (ROWS-1) S (S lane groups in the grid),
+    // so that each load instruction of a wave still covers consecutive rows; all
+    // loads of the first 4-entry group of every row are issued before any arithmetic
+    const int64_t rows = p.batch * p.dim;
+    const int64_t S = int64_t(gridDim.x) * (256 / R);
+    const int64_t s0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) / R;
+    const int q = threadIdx.x % R;
+    const int64_t n0 = 4 * q;   // < N, since 4 R <= N
+    int64_t ri[ROWS];
+    bool live[ROWS];
+    float4 hv[ROWS], bv[ROWS], cv[ROWS], ar[ROWS];
+    float uu[ROWS], dr[ROWS], zz[ROWS];
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) {
+        const int64_t r = s0 + k * S;
+        live[k] = r < rows;
+        ri[k] = live[k] ? r : rows - 1;   // idle lanes read the last row, write nothing
+        const int64_t b = ri[k] / p.dim, d = ri[k] % p.dim;
+        hv[k] = *reinterpret_cast<const float4*>(p.h + ri[k] * p.N + n0);
+        bv[k] = load4(static_cast<const IO*>(p.Bm) + b * p.N + n0);
+        cv[k] = load4(static_cast<const IO*>(p.Cm) + b * p.N + n0);
+        if constexpr (!SCALAR) ar[k] = *reinterpret_cast<const float4*>(p.A + d * p.N + n0);
+        uu[k] = IOT<IO>::to_f32(static_cast<const IO*>(p.u)[ri[k]]);
+        dr[k] = IOT<IO>::to_f32(static_cast<const IO*>(p.delta)[ri[k]]) + (p.bias ? p.bias[d] : 0.0f);
+        zz[k] = p.z ? IOT<IO>::to_f32(static_cast<const IO*>(p.z)[ri[k]]) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) {
+        const int64_t i = ri[k], b = i / p.dim, d = i % p.dim;
+        const float dt2 = softplus_log2(dr[k]);
+        const float x = dt2 * uu[k];
+        const float a_s = SCALAR ? __builtin_amdgcn_exp2f(dt2 * p.A[d / p.head_dim]) : 0.0f;
+        const IO* gB = static_cast<const IO*>(p.Bm) + b * p.N;
+        const IO* gC = static_cast<const IO*>(p.Cm) + b * p.N;
+        const float* Arow = p.A + d * p.N;
+        float* hrow = p.h + i * p.N;
+        float acc = 0.0f;
+        auto group = [&](float4 h4, float4 b4, float4 c4, float4 a4, int64_t n) {
+            float4 av = make_float4(a_s, a_s, a_s, a_s);
+            if constexpr (!SCALAR)
+                av = make_float4(__builtin_amdgcn_exp2f(dt2 * a4.x), __builtin_amdgcn_exp2f(dt2 * a4.y),
+                                 __builtin_amdgcn_exp2f(dt2 * a4.z), __builtin_amdgcn_exp2f(dt2 * a4.w));
+            h4.x = fmaf(av.x, h4.x, x * (b4.x * kLn2));
+            h4.y = fmaf(av.y, h4.y, x * (b4.y * kLn2));
+            h4.z = fmaf(av.z, h4.z, x * (b4.z * kLn2));
+            h4.w = fmaf(av.w, h4.w, x * (b4.w * kLn2));
+            acc = fmaf(c4.x, h4.x, acc);
+            acc = fmaf(c4.y, h4.y, acc);
+            acc = fmaf(c4.z, h4.z, acc);
+            acc = fmaf(c4.w, h4.w, acc);
+            if (live[k]) *reinterpret_cast<float4*>(hrow + n) = h4;
+        };
+        group(hv[k], bv[k], cv[k], ar[k], n0);
+        for (int64_t n = n0 + 4 * R; n < p.N; n += 4 * R) {
+            const float4 a4 = SCALAR ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4*>(Arow + n);
+            group(*reinterpret_cast<const float4*>(hrow + n), load4(gB + n), load4(gC + n), a4, n);
+        }
+#pragma unroll
+        for (int off = R / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, R);
+        if (live[k] && q == 0) {
+            float o = acc + (p.Dskip ? p.Dskip[d] : 0.0f) * uu[k];
+            if (p.z) o *= silu_f32(zz[k]);
+            static_cast<IO*>(p.y)[i] = IOT<IO>::from_f32(o);
+        }
+    }
+}
+
+template <typename IO, bool SCALAR>
+__global__ void __launch_bounds__(256) scan_step_kernel(StepParams p) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= p.batch * p.dim) return;
+    const int64_t b = i / p.dim, d = i % p.dim;
+    float uu, dt2;
+    step_row_prologue<IO, SCALAR>(p, i, d, uu, dt2);
+    const float x = dt2 * uu;
+    const float a_s = SCALAR ? __builtin_amdgcn_exp2f(dt2 * p.A[d / p.head_dim]) : 0.0f;
+    const IO* gB = static_cast<const IO*>(p.Bm) + b * p.N;
+    const IO* gC = static_cast<const IO*>(p.Cm) + b * p.N;
+    const float* Arow = p.A + d * p.N;
+    float* hrow = p.h + i * p.N;
+    float acc = 0.0f;
+    for (int64_t n = 0; n < p.N; ++n) {
+        const float a = SCALAR ? a_s : __builtin_amdgcn_exp2f(dt2 * Arow[n]);
+        const float hn = fmaf(a, hrow[n], x * (IOT<IO>::to_f32(gB[n]) * kLn2));
+        acc = fmaf(IOT<IO>::to_f32(gC[n]), hn, acc);
+        hrow[n] = hn;
+    }
+    step_row_epilogue<IO>(p, i, d, uu, acc);
+}
+
+// lanes per row of the vector form: the largest power of two <= min(N/4, 16)
+inline int step_lanes(int64_t N) {
+    int r = 1;
+    while (r < 16 && 4 * (2 * r) <= N) r *= 2;
+    return r;
+}
+
 template <typename IO, bool SCALAR>
 hipError_t launch_step(const StepParams& p, bool vec4, hipStream_t s) {
-    const int64_t total = p.batch * p.dim;
-    const dim3 grid(unsigned(cdiv(total, 256))), block(256);
-    if (vec4) hipLaunchKernelGGL((scan_step_kernel<IO, SCALAR, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_step_kernel<IO, SCALAR, false>), grid, block, 0, s, p);
+    const int64_t rows = p.batch * p.dim;
+    const dim3 block(256);
+    if (!vec4) {
+        hipLaunchKernelGGL((scan_step_kernel<IO, SCALAR>), dim3(unsigned(cdiv(rows, 256))), block, 0, s, p);
+        return hipGetLastError();
+    }
+    const int R = step_lanes(p.N);
+    constexpr int ROWS = 1;   // measured: 4 rows per lane (a quarter of the waves) was slower
+    const dim3 grid(unsigned(cdiv(rows * R, 256 * ROWS)));
+    switch (R) {
+        case 1: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 1, ROWS>), grid, block, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 2, ROWS>), grid, block, 0, s, p); break;
+        case 4: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 4, ROWS>), grid, block, 0, s, p); break;
+        case 8: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 8, ROWS>), grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 16, ROWS>), grid, block, 0, s, p); break;
+    }
     return hipGetLastError();
 }
 
@@ -994,7 +1094,10 @@ int ssm_selective_scan_step(const void* u, const void* delta, const float* A, co
     p.dim = dims->dim;
     p.N = dims->dstate;
     p.head_dim = dims->nheads > 0 ? dims->dim / dims->nheads : 0;
-    const bool vec4 = dims->dstate % 4 == 0 && (reinterpret_cast<uintptr_t>(h) % 16) == 0;
+    // the vector form reads 4 entries at once: rows of h and A 16-byte aligned, of B and C 4*esz
+    const bool vec4 = dims->dstate % 4 == 0 && !misaligned(h, 16) && !misaligned(B, 4 * esz) &&
+                      !misaligned(C, 4 * esz) && (dims->nheads > 0 || !misaligned(A, 16));
+    if (cdiv(dims->batch * dims->dim * 16, 256) > 0x7fffffff) return SSM_ERR_DIMS;
     const bool scalar = dims->nheads > 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;

@@ -90,7 +90,8 @@ def test_split_sequence_continues_exactly():
 
 
 @pytest.mark.parametrize("case", [(1, 64, 16, "f32", 0), (4, 200, 16, "bf16", 0), (2, 129, 7, "f32", 0),
-                                  (3, 256, 128, "bf16", 4), (2, 96, 64, "bf16", 0)])
+                                  (3, 256, 128, "bf16", 4), (2, 96, 64, "bf16", 0),
+                                  (1, 33, 20, "f32", 0), (2, 50, 12, "bf16", 5)])
 def test_decode_steps_match_oracle_and_scan(case):
     """T decode steps, the state carried in place, against the oracle's decode steps
     and against one GPU scan over the same T tokens."""
