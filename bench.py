@@ -88,9 +88,9 @@ def cpu_baseline(x, rows_batches: int):
 PROFILE_COMMANDS = {
     "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/stats -o scan -- python3 bench.py",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/fetch -o scan -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/write -o scan -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward",
     "copyfetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/copyfetch -o copy -- "
                  "python3 bench.py --calibrate-copy",
     "copywrite": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/copywrite -o copy -- "
@@ -213,6 +213,64 @@ def decode_step_bench(batch: int, steps: int = 200, warmup: int = 50):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
 
 
+# minimal VALU operations per state update of the backward pass: the forward recompute
+# with its read-out (mul, exp2, mul, fma, fma), the reverse step (g = ds*C + e: fma;
+# e = a*g: mul; a*h_prev: mul; g*(a*h_prev): mul; dA, sum A*.., sum g*B: 3 fma;
+# ds*h and g*x for dC, dB: 2 mul) and the sums of dB and dC over channels (2 add)
+BWD_OPS_PER_UPDATE = 16
+
+
+def backward_bench(x, dev, steps: int = 30, warmup: int = 5):
+    """Time ssm_selective_scan_bwd on the same inputs (cotangent dy seeded, no dh_last):
+    one call = every kernel of the backward (state checkpoints, reverse gradient walk,
+    reductions of the partial sums)."""
+    import torch
+    import selective_state_space_79_amd as ssm
+    from selective_state_space_79_amd.inputs import io_to_device, make_cotangents
+
+    dy = io_to_device(x, make_cotangents(x, seed=53)[0], "cuda:0")
+    dims = ssm.dims_for(dev["u"], dev["B"], dev["A"])
+    plan = ssm.ssm_selective_scan_bwd_plan(dims).as_dict()
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
+    dims.workspace, dims.workspace_bytes = ws.data_ptr(), plan["workspace_bytes"]
+    f32 = dict(dtype=torch.float32, device="cuda:0")
+    out = {"du": torch.empty_like(dev["u"]), "ddelta": torch.empty_like(dev["u"]), "dz": torch.empty_like(dev["u"]),
+           "dA": torch.empty(dev["A"].shape, **f32), "dB": torch.empty((x.batch, x.N, x.L), **f32),
+           "dC": torch.empty((x.batch, x.N, x.L), **f32), "dD": torch.empty(x.dim, **f32),
+           "ddt_bias": torch.empty(x.dim, **f32), "dh0": None}
+    grads = ssm.SsmGrads(*[out[k].data_ptr() if out[k] is not None else None for k, _ in ssm.SsmGrads._fields_])
+    stream = torch.cuda.current_stream()
+    p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    args = (p(dev["u"]), p(dev["delta"]), p(dev["A"]), p(dev["B"]), p(dev["C"]), p(dev["D"]), p(dev["z"]),
+            p(dev["dt_bias"]), None, p(dy), None, ctypes.byref(grads), ctypes.byref(dims),
+            ctypes.c_void_p(stream.cuda_stream))
+    fn = ssm.load_library().ssm_selective_scan_bwd
+    for _ in range(warmup):
+        st = fn(*args)
+        if st != 0:
+            raise ssm.SsmError(st, "ssm_selective_scan_bwd")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn(*args)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    esz = 2 if x.io == "bf16" else 4
+    # u, delta, z, dy read and du, ddelta, dz written per element; B, C read and dB, dC
+    # (float32) written per (b, t, n); A, D, dt_bias read and dA, dD, ddt_bias written
+    nbytes = (7 * esz * x.batch * x.L * x.dim + (2 * esz + 8) * x.batch * x.N * x.L
+              + 8 * (x.A.size + 2 * x.dim))
+    tops = BWD_OPS_PER_UPDATE * x.updates / (ms * 1e-3) / 1e12
+    return {"workload": f"{x.batch}x{x.L}x{x.dim}, N {x.N}, {x.io} I/O: gradients of every input",
+            "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3), "plan": plan,
+            "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                         "unit": "TFLOP/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
+                         "note": f"{BWD_OPS_PER_UPDATE} fp32 VALU lane operations per state update"},
+            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +278,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3, help="1..5; the reported line is workload 3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--cpu-batches", type=int, default=2, help="batch rows in the oracle's timing sample")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 2 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs in DIR")
@@ -332,6 +391,8 @@ def main():
     }
     if args.workload == 3:
         rec["decode_step"] = [decode_step_bench(64), decode_step_bench(256)]
+    if not args.no_backward:
+        rec["backward"] = backward_bench(x, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_batches)
     print(json.dumps(rec), flush=True)

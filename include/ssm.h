@@ -1,5 +1,7 @@
 /*
- * ssm.h -- C ABI of libssm.so: the Mamba-1 selective-scan forward pass on MI355X (gfx950).
+ * ssm.h -- C ABI of libssm.so: the Mamba-1 selective scan on MI355X (gfx950): the
+ * forward pass, with a carried state, the single-token decode step, and the
+ * backward pass.
  *
  * What it computes, per batch b, channel d, time t (t = 0 .. L-1), with a state
  * h[b,d,:] of dstate values that starts at zero:
@@ -133,6 +135,68 @@ SSM_API int ssm_selective_scan_step(const void* u, const void* delta, const floa
                                     const float* D, const void* z, const float* dt_bias, float* h, void* y,
                                     const ssm_dims* dims, void* stream);
 
+/* Largest dstate the backward pass accepts. */
+#define SSM_MAX_DSTATE_BWD 128
+
+/* Where ssm_selective_scan_bwd writes the gradients.  All device pointers, owned by
+ * the caller:
+ *   du, ddelta : (batch, dim, seqlen) in io_dtype (rounded to nearest even for bf16)
+ *                -- required; ddelta is the gradient at the raw delta input, i.e.
+ *                through the softplus
+ *   dA         : float32, the shape of A -- required
+ *   dB, dC     : float32 (batch, dstate, seqlen) -- required
+ *   dD         : float32 (dim,) -- nullable (not computed); the gradient at D, or at
+ *                D = 0 when the forward had no skip
+ *   dz         : (batch, dim, seqlen) in io_dtype -- nullable; written only when z is
+ *                given
+ *   ddt_bias   : float32 (dim,) -- nullable; the gradient at dt_bias (or at 0)
+ *   dh0        : float32 (batch, dim, dstate) -- nullable; the gradient at h0 (or at
+ *                the zero starting state) */
+typedef struct ssm_grads {
+    void* du;
+    void* ddelta;
+    float* dA;
+    float* dB;
+    float* dC;
+    float* dD;
+    void* dz;
+    float* ddt_bias;
+    float* dh0;
+} ssm_grads;
+
+/* Bytes of workspace ssm_selective_scan_bwd needs for dims (never 0 for a valid
+ * dims; 0 for a dims pointer the backward would refuse).  The workspace holds the
+ * states recomputed every 16 steps (4*dstate bytes per 16 steps of every channel,
+ * rounded up to whole 64-channel blocks and 4-entry groups), per-block partial sums
+ * of dB and dC (8*dstate bytes per token and 64-channel block) and the carries
+ * between pieces. */
+SSM_API size_t ssm_selective_scan_bwd_workspace_bytes(const ssm_dims* dims);
+
+/* Enqueue the backward pass: the gradients, with respect to every input of
+ * ssm_selective_scan_fwd_state, of the scalar
+ *     sum_{b,d,t} dy[b,d,t] * y[b,d,t]  +  sum_{b,d,n} dh_last[b,d,n] * h_L[b,d,n]
+ * where y and h_L are what the forward computes from the same inputs (dy: the
+ * gradient arriving at y, in io_dtype (batch, dim, seqlen), required; dh_last: the
+ * gradient arriving at the final state, float32 (batch, dim, dstate), nullable = 0).
+ * Training differentiates the scan; as the pages describe for Mamba's kernels, the
+ * states are recomputed from the inputs rather than kept from the forward
+ * (yo3nglau.github.io "Mamba 与状态空间模型：面试问题与推荐回答" Q7; qubittool.com
+ * "Mamba 与状态空间模型：机制、演进与工程选型", section "并行训练不会消除递推关系").
+ * The inputs are those of the forward call, with the same layouts and nullability;
+ * dims is the forward's dims with a workspace of at least
+ * ssm_selective_scan_bwd_workspace_bytes(dims) bytes (256-byte aligned).
+ * dstate must be <= SSM_MAX_DSTATE_BWD; dims->states_per_lane may force 1, 2, 4, 8
+ * or 16 entries per lane as long as that needs at most 8 waves (else SSM_ERR_DIMS).
+ * No output may overlap an input, another output or the workspace (SSM_ERR_ALIAS).
+ * Sums over channels, batch rows and time (dA, dB, dC, dD, ddt_bias) are formed in a
+ * fixed order from per-workgroup partials; the partial read-outs of the state
+ * entries of one step are combined with LDS atomics, so du, ddelta and dz may differ
+ * between runs in the last bits.  Other rules as ssm_selective_scan_fwd. */
+SSM_API int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                   const float* D, const void* z, const float* dt_bias, const float* h0,
+                                   const void* dy, const float* dh_last, const ssm_grads* grads,
+                                   const ssm_dims* dims, void* stream);
+
 /* Static English text for a status value. */
 SSM_API const char* ssm_status_string(int status);
 
@@ -150,6 +214,10 @@ typedef struct ssm_plan {
     size_t lds_bytes;
 } ssm_plan;
 SSM_API int ssm_selective_scan_plan(const ssm_dims* dims, ssm_plan* plan);
+
+/* The same for ssm_selective_scan_bwd (workspace_bytes as
+ * ssm_selective_scan_bwd_workspace_bytes; time_tile is the recompute interval). */
+SSM_API int ssm_selective_scan_bwd_plan(const ssm_dims* dims, ssm_plan* plan);
 
 #ifdef __cplusplus
 }

@@ -1,14 +1,17 @@
-"""Python binding of libssm.so, the MI355X selective-scan forward pass.
+"""Python binding of libssm.so, the MI355X selective scan (forward, decode step,
+backward).
 
 Argument marshalling only: every step of the scan runs in the HIP kernels of
-``csrc/scan_fwd.hip`` behind the C ABI of ``include/ssm.h``.  There is no CPU or
+``csrc/scan_fwd.hip`` and ``csrc/scan_bwd.hip`` behind the C ABI of ``include/ssm.h``.  There is no CPU or
 PyTorch fallback: if the library is missing, every call raises.
 
 The functions carry the C names (``ssm_selective_scan_fwd``,
 ``ssm_selective_scan_fwd_state``, ``ssm_selective_scan_step``,
-``ssm_selective_scan_workspace_bytes``, ``ssm_selective_scan_plan``,
-``ssm_status_string``); ``selective_scan_fwd`` and ``selective_scan_step``
-additionally allocate outputs and the workspace through PyTorch's caching allocator.
+``ssm_selective_scan_bwd``, ``ssm_selective_scan_workspace_bytes``,
+``ssm_selective_scan_bwd_workspace_bytes``, ``ssm_selective_scan_plan``,
+``ssm_selective_scan_bwd_plan``, ``ssm_status_string``); ``selective_scan_fwd``,
+``selective_scan_step`` and ``selective_scan_bwd`` additionally allocate outputs and
+the workspace through PyTorch's caching allocator.
 """
 from __future__ import annotations
 
@@ -33,7 +36,9 @@ SSM_MAX_DSTATE = 256
 SSM_MAX_CHUNKS = 1024
 
 EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_fwd_state", "ssm_selective_scan_step",
-            "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan", "ssm_status_string")
+            "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan", "ssm_status_string",
+            "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd_plan")
+SSM_MAX_DSTATE_BWD = 128
 
 
 class SsmDims(ctypes.Structure):
@@ -70,6 +75,12 @@ class SsmPlan(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class SsmGrads(ctypes.Structure):
+    """Mirror of ``ssm_grads`` in include/ssm.h (device pointers; 0 = NULL)."""
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddt_bias", "dh0")]
+
+
 class SsmError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {ssm_status_string(status)} (status {status})")
@@ -97,6 +108,12 @@ def load_library():
         lib.ssm_selective_scan_workspace_bytes.restype = ctypes.c_size_t
         lib.ssm_selective_scan_plan.argtypes = [ctypes.POINTER(SsmDims), ctypes.POINTER(SsmPlan)]
         lib.ssm_selective_scan_plan.restype = ctypes.c_int
+        lib.ssm_selective_scan_bwd.argtypes = [vp] * 11 + [ctypes.POINTER(SsmGrads), ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_bwd.restype = ctypes.c_int
+        lib.ssm_selective_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(SsmDims)]
+        lib.ssm_selective_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssm_selective_scan_bwd_plan.argtypes = [ctypes.POINTER(SsmDims), ctypes.POINTER(SsmPlan)]
+        lib.ssm_selective_scan_bwd_plan.restype = ctypes.c_int
         lib.ssm_status_string.argtypes = [ctypes.c_int]
         lib.ssm_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -122,6 +139,18 @@ def ssm_selective_scan_plan(dims: SsmDims) -> SsmPlan:
     st = load_library().ssm_selective_scan_plan(ctypes.byref(dims), ctypes.byref(plan))
     if st != SSM_OK:
         raise SsmError(st, "ssm_selective_scan_plan")
+    return plan
+
+
+def ssm_selective_scan_bwd_workspace_bytes(dims: SsmDims) -> int:
+    return int(load_library().ssm_selective_scan_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def ssm_selective_scan_bwd_plan(dims: SsmDims) -> SsmPlan:
+    plan = SsmPlan()
+    st = load_library().ssm_selective_scan_bwd_plan(ctypes.byref(dims), ctypes.byref(plan))
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_selective_scan_bwd_plan")
     return plan
 
 
@@ -248,4 +277,50 @@ def selective_scan_step(u, delta, A, B, C, D, z, dt_bias, h, *, out=None, stream
     st = ssm_selective_scan_step(u, delta, A, B, C, D, z, dt_bias, h, out, dims, stream)
     if st != SSM_OK:
         raise SsmError(st, "ssm_selective_scan_step")
+    return out
+
+
+def ssm_selective_scan_bwd(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, grads: SsmGrads, dims: SsmDims,
+                           stream=None) -> int:
+    """C entry point of the backward pass with raw device pointers; returns the status."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device)
+    return int(load_library().ssm_selective_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(dy),
+        _ptr(dh_last), ctypes.byref(grads), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
+def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, dy, h0=None, dh_last=None,
+                       nchunks=0, states_per_lane=0, workspace=None, stream=None) -> dict:
+    """Gradients of sum(dy * y) + sum(dh_last * h_last) for the forward with the same
+    inputs.  Allocates the outputs (and the workspace) with torch; returns a dict with
+    du, ddelta (u's dtype), dA, dB, dC, dD, ddt_bias, dh0 (float32) and dz (when z is
+    given).  Raises SsmError on a refused call."""
+    import torch
+
+    _check_tensors(u, dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h0=h0, dy=dy,
+                           dh_last=dh_last), f32_names=("A", "D", "dt_bias", "h0", "dh_last"))
+    dims = dims_for(u, B, A, nchunks=nchunks, states_per_lane=states_per_lane)
+    batch, dim, L = u.shape
+    N = B.shape[1]
+    f32 = dict(dtype=torch.float32, device=u.device)
+    out = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u), "dA": torch.empty(A.shape, **f32),
+           "dB": torch.empty((batch, N, L), **f32), "dC": torch.empty((batch, N, L), **f32),
+           "dD": torch.empty(dim, **f32), "ddt_bias": torch.empty(dim, **f32),
+           "dh0": torch.empty((batch, dim, N), **f32)}
+    if z is not None:
+        out["dz"] = torch.empty_like(u)
+    need = ssm_selective_scan_bwd_workspace_bytes(dims)
+    if need == 0:
+        raise SsmError(SSM_ERR_DIMS, "ssm_selective_scan_bwd_workspace_bytes")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+    dims.workspace = workspace.data_ptr()
+    dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    g = SsmGrads(*[out[k].data_ptr() if k in out else None for k, _ in SsmGrads._fields_])
+    st = ssm_selective_scan_bwd(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, g, dims, stream)
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_selective_scan_bwd")
     return out

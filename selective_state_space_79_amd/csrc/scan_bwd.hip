@@ -1,0 +1,986 @@
+// scan_bwd.hip -- backward pass of the selective scan for gfx950 (MI355X) and the C
+// ABI entry points ssm_selective_scan_bwd* declared in include/ssm.h.
+//
+// Gradients of  sum dy*y + sum dh_last*h_L  for the forward of scan_fwd.hip.  With
+// dt2 = softplus(delta + dt_bias) / ln 2 (log2 units, as in the forward), x = dt2*u,
+// a = exp2(dt2*A), B' = B*ln 2 and the per-step total gradient g[n] at h_t[n],
+// walking t backwards with the carried e[n] = a_{t+1}[n] g_{t+1}[n]:
+//   ds = dy * SiLU(z)                   dz = dy * SiLU'(z) * (C.h_t + D*u)
+//   g[n] = ds*C[n] + e[n]               e[n] <- a[n] * g[n]
+//   dC_t[n] += ds * h_t[n]              dB_t[n] += ln2 * g[n] * x        (summed over channels)
+//   dA[n]   += ln2 * dt2 * g[n] * a[n] h_{t-1}[n]                         (summed over b, t)
+//   ddt = sum_n A[n] g[n] a[n] h_{t-1}[n] + u * sum_n g[n] B'[n] / ln2
+//   du  = D*ds + dt2 * sum_n g[n] B'[n]          ddelta = ddt * sigmoid(delta + dt_bias)
+// Training needs these; as the pages say of Mamba's kernels, the states the backward
+// needs are recomputed from the inputs instead of being kept from the forward
+// (yo3nglau.github.io "Mamba 与状态空间模型：面试问题与推荐回答" Q7; qubittool.com
+// "Mamba 与状态空间模型：机制、演进与工程选型", section "并行训练不会消除递推关系").
+//
+// Work decomposition (one workgroup per batch row, 64 channels and piece of the
+// sequence; lane = channel, the dstate entries split over the G waves, SPL per lane,
+// as in the forward):
+//   1. checkpoint pass: walk the piece forward and write the state at the start of
+//      every 16-step tile (4*dstate bytes per 16 steps of a channel);
+//   2. gradient pass: walk the tiles backwards.  Per tile the lanes reload the tile's
+//      start state, recompute its 16 states forward (kept in VGPRs; with more than 4
+//      entries per lane in sub-blocks, re-walked from saved sub-block starts), then
+//      step backwards through them.  The per-step sums over state entries (the
+//      read-out, sum A g a h, sum g B') are combined across waves with LDS atomics;
+//      the sums over channels (dB, dC) are reduced across the 64 lanes through a
+//      per-wave LDS transpose, 16 values at a time, in a fixed order;
+//   3. reduce kernels add the per-workgroup partials of dB, dC, dA, dD and ddt_bias
+//      in a fixed order.
+// Long sequences are cut into pieces exactly as in the forward: the pieces' start
+// states come from a forward aggregate pass and carry, their incoming gradients from
+// a reverse aggregate pass (e from zero at the piece end, and the dt2 sum) and a
+// reverse carry: e_in(c-1) = exp2(A * S_c) * e_in(c) + G_c.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssm.h"
+
+#include "scan_common.h"
+
+namespace {
+
+constexpr int kT = 16;       // time tile = recompute interval
+constexpr int kRound = 8;    // values per cross-lane reduction round
+constexpr int kQB = 2;       // steps per scheduling group in the gradient walk: keeps the
+                             // compiler from hoisting a whole tile's LDS operands at once
+
+struct BwdParams {
+    const void* u;
+    const void* delta;
+    const void* z;         // nullable
+    const void* Bm;
+    const void* Cm;
+    const float* A;
+    const float* Dskip;    // nullable
+    const float* bias;     // nullable
+    const float* h0;       // nullable
+    const void* dy;
+    const float* dh_last;  // nullable
+    void* du;
+    void* ddelta;
+    void* dz;              // nullable
+    float* dh0;            // nullable
+    int64_t L, dim, N, head_dim, chunk_len, ntiles_seq;
+    int32_t nchunks, nblk_d, batch, np;
+    int32_t piece_base;    // first piece index of the launch
+    int32_t vec;           // rows are 16-byte aligned: vector loads and stores
+    float* ck;             // [groups][ntiles_seq][np][64]   tile start states
+    float* pBC;            // [nblk_d][batch][2][N][L]       per-block dB (unscaled), dC
+    float* pA;             // [nchunks][batch][dim][np]      per-piece dA / ln 2
+    float* pD;             // [nchunks][batch][dim]
+    float* pbias;          // [nchunks][batch][dim]
+    float* fH;             // [groups][nchunks][np][64]      piece end states from zero
+    float* fS;             // [groups][nchunks][64]          sum of dt2 over each piece
+    float* fHin;           // [groups][nchunks][np][64]      true start state of each piece
+    float* rG;             // [groups][nchunks][np][64]      e at piece start from zero at its end
+    float* rS;             // [groups][nchunks][64]
+    float* rEin;           // [groups][nchunks][np][64]      true incoming e at each piece end
+};
+
+enum BwdMode { kCkpt = 0, kFwdAgg = 1, kRevAgg = 2, kGrad = 3 };
+
+template <int SPL, int G> struct BShape {
+    static constexpr int T = kT;
+    static constexpr int NP = G * SPL;
+    static constexpr int NT = G * kLanes;
+    static constexpr int TS = (64 / SPL < T) ? 64 / SPL : T;   // states a lane keeps per sub-block
+    static constexpr int NSB = T / TS;
+    static constexpr int JR = SPL < 4 ? SPL : 4;              // entries per reduction round
+    static constexpr int RS = 4 / JR;                         // steps per reduction round
+    static constexpr int NJR = SPL / JR;                      // rounds per step (SPL > 4)
+};
+
+// LDS floats of one workgroup:
+//   sW  [T][64] float4  (dt2, dt2*u, ds, scalar decay)      all modes
+//   sF  [T][64] float4  (u, sigmoid(r), dy*SiLU'(z), D*u)     gradient pass
+//   sBC [T][NP] float2  (B*ln2, C)                           all modes
+//   sYP, sS1, sS2 [T][64]  read-out, sum A g a h, sum g B'  gradient pass (LDS atomics)
+//   sdBC [2][NP][T]     per-block dB, dC of the tile          gradient pass
+//   sRed [G][8][64]     per-wave transpose for lane sums     gradient pass
+inline size_t bwd_lds_floats(int G, int SPL, int mode) {
+    const size_t T = kT, NP = size_t(G) * SPL;
+    size_t f = T * kLanes * 4 + T * NP * 2;
+    if (mode == kGrad) f += T * kLanes * 4 + 3 * T * kLanes + 2 * NP * T + size_t(G) * kRound * kLanes;
+    return f;
+}
+
+template <typename IO>
+__device__ inline Vec<IO> ld_row(const IO* row, int64_t t, int64_t tend, bool ok, bool vec) {
+    return vec ? load_vec<IO, true>(row, t, tend, ok) : load_vec<IO, false>(row, t, tend, ok);
+}
+
+template <typename IO>
+__device__ inline void st_row(IO* row, int64_t t, int64_t tend, bool ok, bool vec, const Vec<IO>& v) {
+    if (vec) store_vec<IO, true>(row, t, tend, ok, v);
+    else store_vec<IO, false>(row, t, tend, ok, v);
+}
+
+template <int CTRL>
+__device__ inline float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <typename IO, int SPL, int G, bool SCALAR, int MODE>
+__global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
+    using S = BShape<SPL, G>;
+    constexpr int T = S::T, NP = S::NP, NT = S::NT, TS = S::TS, NSB = S::NSB;
+    constexpr int JR = S::JR, RS = S::RS, NJR = S::NJR;
+    constexpr int VW = IOT<IO>::VW;
+    constexpr int TV = T / VW;                    // vectors per row per tile
+    constexpr int NVX = kLanes * TV;
+    constexpr int KX = (NVX + NT - 1) / NT;
+    constexpr int NBV = 2 * NP * TV;              // B rows then C rows
+    constexpr int KBV = (NBV + NT - 1) / NT;
+    constexpr bool kG = MODE == kGrad;
+    constexpr bool kRev = MODE == kRevAgg || MODE == kGrad;
+    constexpr bool kUseB = MODE != kRevAgg;
+    constexpr bool kUseC = MODE == kRevAgg || MODE == kGrad;
+    constexpr bool kUseU = MODE != kRevAgg;
+    static_assert(TS % RS == 0 && RS * 2 * JR == kRound, "reduction rounds must tile the sub-block");
+
+    extern __shared__ float smem[];
+    float4* sW = reinterpret_cast<float4*>(smem);
+    float* const after_w = smem + T * kLanes * 4;
+    float4* sF = reinterpret_cast<float4*>(after_w);
+    float* const sBC = after_w + (kG ? T * kLanes * 4 : 0);
+    float* const sYP = sBC + T * NP * 2;
+    float* const sS1 = sYP + T * kLanes;
+    float* const sS2 = sS1 + T * kLanes;
+    float* const sdBC = sS2 + T * kLanes;
+    float* const sRed = sdBC + 2 * NP * T;
+
+    const int tid = threadIdx.x;
+    const int w = tid / kLanes;
+    const int lane = tid % kLanes;
+    const int64_t bid = blockIdx.x;
+    const int cblk = int(bid % p.nblk_d);
+    const int b = int((bid / p.nblk_d) % p.batch);
+    const int piece = int(bid / (int64_t(p.nblk_d) * p.batch)) + p.piece_base;
+    const int64_t blk = int64_t(b) * p.nblk_d + cblk;
+    const int64_t c0 = int64_t(cblk) * kLanes;
+    const int64_t tbeg = int64_t(piece) * p.chunk_len;
+    const int64_t tend = (tbeg + p.chunk_len < p.L) ? tbeg + p.chunk_len : p.L;
+    const int ntiles = int((tend - tbeg + T - 1) / T);
+    const int64_t tile0 = tbeg / T;
+    const bool has_z = kRev && p.z != nullptr;
+    const bool vec = p.vec != 0;
+
+    const IO* __restrict__ gu = static_cast<const IO*>(p.u);
+    const IO* __restrict__ gdl = static_cast<const IO*>(p.delta);
+    const IO* __restrict__ gz = static_cast<const IO*>(p.z);
+    const IO* __restrict__ gdy = static_cast<const IO*>(p.dy);
+    const IO* __restrict__ gB = static_cast<const IO*>(p.Bm);
+    const IO* __restrict__ gC = static_cast<const IO*>(p.Cm);
+
+    // ---- walk constants: this lane's channel and its SPL decay rates
+    const int64_t dch = c0 + lane;
+    const bool lane_ok = dch < p.dim;
+    float Ar[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const int64_t n = int64_t(w) * SPL + j;
+        if constexpr (SCALAR) Ar[j] = lane_ok ? p.A[dch / p.head_dim] : 0.0f;
+        else Ar[j] = (lane_ok && n < p.N) ? p.A[dch * p.N + n] : 0.0f;
+    }
+    const int64_t state_base = ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
+
+    // ---- staging constants: element vectors v = tid + k*NT -> (channel, vector in row)
+    int sv_ch[KX], sv_tv[KX];
+    bool sv_on[KX], sv_ok[KX];
+    float sv_bias[KX], sv_skip[KX], sv_ah[KX];
+    int64_t sv_row[KX];
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+        const int v = tid + k * NT;
+        sv_on[k] = v < NVX;
+        sv_ch[k] = (v / TV) % kLanes;
+        sv_tv[k] = v % TV;
+        const int64_t d = c0 + sv_ch[k];
+        sv_ok[k] = sv_on[k] && d < p.dim;
+        sv_bias[k] = (sv_ok[k] && p.bias) ? p.bias[d] : 0.0f;
+        sv_skip[k] = (sv_ok[k] && p.Dskip) ? p.Dskip[d] : 0.0f;
+        sv_ah[k] = 0.0f;
+        if constexpr (SCALAR) sv_ah[k] = sv_ok[k] ? p.A[d / p.head_dim] : 0.0f;
+        sv_row[k] = (int64_t(b) * p.dim + (sv_ok[k] ? d : 0)) * p.L;
+    }
+    // ---- B/C row vectors v = tid + k*NT -> (B or C, entry n, vector in row)
+    const IO* bc_row[KBV];
+    int bc_slot[KBV], bc_tv[KBV];
+    bool bc_on[KBV], bc_ok[KBV], bc_isC[KBV];
+#pragma unroll
+    for (int k = 0; k < KBV; ++k) {
+        const int v = tid + k * NT;
+        bc_on[k] = v < NBV;
+        const int isC = v / (NP * TV);
+        const int rem = v % (NP * TV);
+        const int n = rem / TV;
+        bc_tv[k] = rem % TV;
+        bc_isC[k] = isC != 0;
+        bc_ok[k] = bc_on[k] && n < p.N && (isC ? kUseC : kUseB);
+        bc_row[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bc_ok[k] ? n : 0)) * p.L;
+        bc_slot[k] = n * 2 + isC;
+    }
+
+    Vec<IO> nu[KX], ndl[KX], nz[KX], ndy[KX], nbc[KBV];
+    auto issue_loads = [&](int64_t t0) {
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+            if (sv_on[k]) {
+                const int64_t t = t0 + sv_tv[k] * VW;
+                if constexpr (kUseU) nu[k] = ld_row<IO>(gu + sv_row[k], t, tend, sv_ok[k], vec);
+                ndl[k] = ld_row<IO>(gdl + sv_row[k], t, tend, sv_ok[k], vec);
+                if constexpr (kRev) {
+                    ndy[k] = ld_row<IO>(gdy + sv_row[k], t, tend, sv_ok[k], vec);
+                    if (has_z) nz[k] = ld_row<IO>(gz + sv_row[k], t, tend, sv_ok[k], vec);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KBV; ++k)
+            if (bc_on[k]) nbc[k] = ld_row<IO>(bc_row[k], t0 + bc_tv[k] * VW, tend, bc_ok[k], vec);
+    };
+
+    // ---- registers -> LDS for the tile starting at t0.  Steps beyond the piece's end
+    //      are identity steps (dt2 = 0, x = 0, ds = 0, decay 1).
+    auto stage = [&](int64_t t0) {
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+            if (!sv_on[k]) continue;
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                const int tl = sv_tv[k] * VW + e;
+                const bool in = sv_ok[k] && t0 + tl < tend;
+                const float uu = kUseU ? IOT<IO>::to_f32(nu[k].e[e]) : 0.0f;
+                const float r = IOT<IO>::to_f32(ndl[k].e[e]) + sv_bias[k];
+                const float dt2 = in ? softplus_log2(r) : 0.0f;
+                const float decay = SCALAR ? __builtin_amdgcn_exp2f(dt2 * sv_ah[k]) : 0.0f;
+                float ds = 0.0f, dyv = 0.0f, zz = 0.0f;
+                if constexpr (kRev) {
+                    dyv = in ? IOT<IO>::to_f32(ndy[k].e[e]) : 0.0f;
+                    zz = has_z ? IOT<IO>::to_f32(nz[k].e[e]) : 0.0f;
+                    ds = has_z ? dyv * silu_f32(zz) : dyv;
+                }
+                const int idx = tl * kLanes + sv_ch[k];
+                sW[idx] = make_float4(dt2, dt2 * uu, ds, decay);
+                if constexpr (kG) {
+                    const float dzf = has_z ? dyv * silu_grad_f32(zz) : 0.0f;
+                    sF[idx] = make_float4(uu, sigmoid_f32(r), dzf, sv_skip[k] * uu);
+                    sYP[idx] = 0.0f;
+                    sS1[idx] = 0.0f;
+                    sS2[idx] = 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KBV; ++k) {
+            if (!bc_on[k]) continue;
+            const float sc = bc_isC[k] ? 1.0f : kLn2;
+#pragma unroll
+            for (int e = 0; e < VW; ++e)
+                sBC[(bc_tv[k] * VW + e) * NP * 2 + bc_slot[k]] = IOT<IO>::to_f32(nbc[k].e[e]) * sc;
+        }
+    };
+
+    // ---- per-lane LDS reads of one step
+    const float4* swl = sW + lane;
+    const float* sbw = sBC + w * SPL * 2;
+    auto read_bc = [&](int t, float (&Bv)[SPL], float (&Cv)[SPL]) {
+        const float* q = sbw + t * NP * 2;
+        if constexpr (SPL == 1) {
+            const float2 v = *reinterpret_cast<const float2*>(q);
+            Bv[0] = v.x;
+            Cv[0] = v.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < SPL / 2; ++i) {
+                const float4 v = reinterpret_cast<const float4*>(q)[i];
+                Bv[2 * i] = v.x;
+                Cv[2 * i] = v.y;
+                Bv[2 * i + 1] = v.z;
+                Cv[2 * i + 1] = v.w;
+            }
+        }
+    };
+
+    float h[SPL], e[SPL], dAacc[SPL], ckn[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) h[j] = e[j] = dAacc[j] = ckn[j] = 0.0f;
+    float dtsum = 0.0f, dtcomp = 0.0f;   // compensated (Kahan) sum of dt2 (aggregate passes)
+    auto kahan = [&](float v) {
+        const float yk = v - dtcomp;
+        const float tk = dtsum + yk;
+        dtcomp = (tk - dtsum) - yk;
+        dtsum = tk;
+    };
+
+    // ---- starting values
+    if constexpr (MODE == kCkpt) {
+        if (p.nchunks > 1) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) h[j] = p.fHin[state_base + int64_t(j) * kLanes];
+        } else if (p.h0 && lane_ok) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t n = int64_t(w) * SPL + j;
+                if (n < p.N) h[j] = p.h0[(int64_t(b) * p.dim + dch) * p.N + n];
+            }
+        }
+    }
+    if constexpr (kG) {
+        if (p.nchunks > 1) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) e[j] = p.rEin[state_base + int64_t(j) * kLanes];
+        } else if (p.dh_last && lane_ok) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t n = int64_t(w) * SPL + j;
+                if (n < p.N) e[j] = p.dh_last[(int64_t(b) * p.dim + dch) * p.N + n];
+            }
+        }
+        const float* ck = p.ck + ((blk * p.ntiles_seq + tile0 + ntiles - 1) * NP + int64_t(w) * SPL) * kLanes + lane;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) ckn[j] = ck[int64_t(j) * kLanes];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- one forward step from LDS (all modes but the reverse aggregate)
+    auto fwd_step = [&](int t, float (&hh)[SPL], float (&Bv)[SPL], float (&Cv)[SPL], float4& W) {
+        W = swl[t * kLanes];
+        read_bc(t, Bv, Cv);
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const float a = SCALAR ? W.w : __builtin_amdgcn_exp2f(W.x * Ar[j]);
+            hh[j] = fmaf(a, hh[j], W.y * Bv[j]);
+        }
+    };
+
+    // ---- reduce 8 per-lane values over the wave's 64 lanes (channels) in a fixed
+    //      order and write the sums to sdBC: value v = (s*2 + isC)*JR + jj belongs to
+    //      step t_base + s and state entry w*SPL + j0 + jj.  The values go to LDS as
+    //      [v][lane]; lane 8o+q then sums lanes 8q..8q+7 of value o, and the 8 lanes of
+    //      an output combine their partials with DPP (quad swaps, then the half-row
+    //      mirror), so every lane of the group holds the same total.
+    float* red = sRed + w * kRound * kLanes;
+    auto flush = [&](const float (&pv)[kRound], int t_base, int j0) {
+#pragma unroll
+        for (int v = 0; v < kRound; ++v) red[v * kLanes + lane] = pv[v];
+        __builtin_amdgcn_wave_barrier();
+        const int o = lane >> 3, q = lane & 7;
+        const float4* rr = reinterpret_cast<const float4*>(red + o * kLanes + q * 8);
+        const float4 a0 = rr[0], a1 = rr[1];
+        float sum = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w));
+        sum += dpp_move<0xB1>(sum);    // quad_perm [1,0,3,2]: lanes 0<->1, 2<->3
+        sum += dpp_move<0x4E>(sum);    // quad_perm [2,3,0,1]: lanes 0<->2, 1<->3
+        sum += dpp_move<0x141>(sum);   // row_half_mirror: lane i <-> 7-i of each 8
+        __builtin_amdgcn_wave_barrier();
+        if (q == 0) {
+            const int s = o / (2 * JR), isC = (o / JR) % 2, jj = o % JR;
+            sdBC[(isC * NP + w * SPL + j0 + jj) * T + t_base + s] = sum;
+        }
+    };
+
+    // ---- the gradient walk of one tile (all waves)
+    auto grad_tile = [&](int kt) {
+        float hst[SPL];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) hst[j] = ckn[j];
+        if (kt > 0) {
+            const float* ck = p.ck + ((blk * p.ntiles_seq + tile0 + kt - 1) * NP + int64_t(w) * SPL) * kLanes + lane;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) ckn[j] = ck[int64_t(j) * kLanes];
+        }
+        float hsb[NSB > 1 ? NSB - 1 : 1][SPL];
+        if constexpr (NSB > 1) {
+            float hh[SPL], Bv[SPL], Cv[SPL];
+            float4 W;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) hh[j] = hst[j];
+#pragma unroll
+            for (int sb = 0; sb < NSB - 1; ++sb) {
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+                    if (ts % kQB == 0) __builtin_amdgcn_sched_barrier(0);
+                    fwd_step(sb * TS + ts, hh, Bv, Cv, W);
+                }
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) hsb[sb][j] = hh[j];
+            }
+        }
+#pragma unroll
+        for (int sb = NSB - 1; sb >= 0; --sb) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            float hb[SPL], H[TS][SPL];
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) hb[j] = (sb == 0) ? hst[j] : hsb[sb > 0 ? sb - 1 : 0][j];
+            {
+                float hh[SPL], Bv[SPL], Cv[SPL];
+                float4 W;
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) hh[j] = hb[j];
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+                    const int t = sb * TS + ts;
+                    if (ts % kQB == 0) __builtin_amdgcn_sched_barrier(0);
+                    fwd_step(t, hh, Bv, Cv, W);
+                    float yp = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < SPL; ++j) {
+                        H[ts][j] = hh[j];
+                        yp = fmaf(Cv[j], hh[j], yp);
+                    }
+                    atomicAdd(&sYP[t * kLanes + lane], yp);
+                }
+            }
+            // re-read the step operands from LDS below rather than keeping the forward
+            // recompute's copies of a whole sub-block live in VGPRs
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            float pv[kRound];
+#pragma unroll
+            for (int ts = TS - 1; ts >= 0; --ts) {
+                const int t = sb * TS + ts;
+                if ((TS - 1 - ts) % kQB == 0) __builtin_amdgcn_sched_barrier(0);
+                const float4 W = swl[t * kLanes];
+                float Bv[SPL], Cv[SPL];
+                read_bc(t, Bv, Cv);
+                float s1 = 0.0f, s2 = 0.0f;
+                const int s = ts % RS;
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) {
+                    const float a = SCALAR ? W.w : __builtin_amdgcn_exp2f(W.x * Ar[j]);
+                    const float hp = ts > 0 ? H[ts > 0 ? ts - 1 : 0][j] : hb[j];
+                    const float g = fmaf(W.z, Cv[j], e[j]);
+                    const float t1 = g * (a * hp);
+                    dAacc[j] = fmaf(W.x, t1, dAacc[j]);
+                    s1 = fmaf(Ar[j], t1, s1);
+                    s2 = fmaf(g, Bv[j], s2);
+                    e[j] = a * g;
+                    const int jj = j % JR;
+                    pv[(s * 2) * JR + jj] = g * W.y;          // dB (unscaled)
+                    pv[(s * 2 + 1) * JR + jj] = W.z * H[ts][j];   // dC
+                    if constexpr (NJR > 1) {
+                        if (jj == JR - 1) flush(pv, t, j - jj);
+                    }
+                }
+                atomicAdd(&sS1[t * kLanes + lane], s1);
+                atomicAdd(&sS2[t * kLanes + lane], s2);
+                if constexpr (NJR == 1) {
+                    if (s == 0) flush(pv, t, 0);
+                }
+            }
+        }
+    };
+
+    // ---- finish the tile starting at t0 (all threads): per-element outputs, the
+    //      per-thread dD / ddt_bias sums, and the tile's dB / dC partials
+    IO* __restrict__ gdu = static_cast<IO*>(p.du);
+    IO* __restrict__ gdd = static_cast<IO*>(p.ddelta);
+    IO* __restrict__ gdz = static_cast<IO*>(p.dz);
+    const bool write_dz = p.dz != nullptr && p.z != nullptr;
+    float accD[KX], accBias[KX];
+#pragma unroll
+    for (int k = 0; k < KX; ++k) accD[k] = accBias[k] = 0.0f;
+    auto finish = [&](int64_t t0) {
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+            if (!sv_on[k]) continue;
+            Vec<IO> odu, odd, odz;
+#pragma unroll
+            for (int e2 = 0; e2 < VW; ++e2) {
+                const int tl = sv_tv[k] * VW + e2;
+                const int idx = tl * kLanes + sv_ch[k];
+                const bool in = sv_ok[k] && t0 + tl < tend;
+                const float4 Wv = sW[idx];
+                const float4 Fv = sF[idx];
+                const float s1 = sS1[idx], s2 = sS2[idx];
+                const float ddt = fmaf(Fv.x * kLog2e, s2, s1);
+                const float dd = ddt * Fv.y;
+                const float dui = fmaf(sv_skip[k], Wv.z, Wv.x * s2);
+                const float dzi = Fv.z * (sYP[idx] + Fv.w);
+                if (in) {
+                    accD[k] = fmaf(Wv.z, Fv.x, accD[k]);
+                    accBias[k] += dd;
+                }
+                odu.e[e2] = IOT<IO>::from_f32(dui);
+                odd.e[e2] = IOT<IO>::from_f32(dd);
+                odz.e[e2] = IOT<IO>::from_f32(dzi);
+            }
+            const int64_t t = t0 + sv_tv[k] * VW;
+            st_row<IO>(gdu + sv_row[k], t, tend, sv_ok[k], vec, odu);
+            st_row<IO>(gdd + sv_row[k], t, tend, sv_ok[k], vec, odd);
+            if (write_dz) st_row<IO>(gdz + sv_row[k], t, tend, sv_ok[k], vec, odz);
+        }
+        for (int i = tid; i < 2 * int(p.N) * T; i += NT) {
+            const int isC = i / (int(p.N) * T);
+            const int rem = i % (int(p.N) * T);
+            const int n = rem / T, t = rem % T;
+            if (t0 + t < tend)
+                p.pBC[(((int64_t(cblk) * p.batch + b) * 2 + isC) * p.N + n) * p.L + t0 + t] = sdBC[(isC * NP + n) * T + t];
+        }
+    };
+
+    // ---- forward walk of one tile (checkpoint pass, forward aggregate)
+    auto fwd_tile = [&](int kt) {
+        if constexpr (MODE == kCkpt) {
+            float* ck = p.ck + ((blk * p.ntiles_seq + tile0 + kt) * NP + int64_t(w) * SPL) * kLanes + lane;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) ck[int64_t(j) * kLanes] = h[j];
+        }
+        float Bv[SPL], Cv[SPL];
+        float4 W;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            fwd_step(t, h, Bv, Cv, W);
+            if constexpr (MODE == kFwdAgg) kahan(W.x);
+        }
+    };
+
+    // ---- reverse walk of one tile without gradients (reverse aggregate)
+    auto rev_tile = [&]() {
+#pragma unroll
+        for (int t = T - 1; t >= 0; --t) {
+            const float4 W = swl[t * kLanes];
+            float Bv[SPL], Cv[SPL];
+            read_bc(t, Bv, Cv);
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const float a = SCALAR ? W.w : __builtin_amdgcn_exp2f(W.x * Ar[j]);
+                e[j] = a * fmaf(W.z, Cv[j], e[j]);
+            }
+            kahan(W.x);
+        }
+    };
+
+    // ---- tile loop: stage, (settle the state loads), prefetch, walk, finish
+    const int first = kRev ? ntiles - 1 : 0;
+    issue_loads(tbeg + int64_t(first) * T);
+    for (int i = 0; i < ntiles; ++i) {
+        const int kt = kRev ? ntiles - 1 - i : i;
+        const int64_t t0 = tbeg + int64_t(kt) * T;
+        stage(t0);
+        // the previous walk's checkpoint prefetch and finish stores are old by now;
+        // settling them here keeps the walk from waiting on the next tile's prefetch
+        __builtin_amdgcn_s_waitcnt(0);
+        if (i + 1 < ntiles) issue_loads(tbeg + int64_t(kRev ? kt - 1 : kt + 1) * T);
+        __syncthreads();
+        if constexpr (kG) grad_tile(kt);
+        else if constexpr (MODE == kRevAgg) rev_tile();
+        else fwd_tile(kt);
+        __syncthreads();
+        if constexpr (kG) {
+            finish(t0);
+            __syncthreads();
+        }
+    }
+
+    // ---- results of the pass
+    if constexpr (MODE == kFwdAgg || MODE == kRevAgg) {
+        float* dst = (MODE == kFwdAgg ? p.fH : p.rG) + state_base;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) dst[int64_t(j) * kLanes] = MODE == kFwdAgg ? h[j] : e[j];
+        if (w == 0) (MODE == kFwdAgg ? p.fS : p.rS)[(blk * p.nchunks + piece) * kLanes + lane] = dtsum;
+    }
+    if constexpr (kG) {
+        if (lane_ok) {
+            float* pa = p.pA + ((int64_t(piece) * p.batch + b) * p.dim + dch) * NP + int64_t(w) * SPL;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) pa[j] = dAacc[j];
+            if (piece == 0 && p.dh0) {
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) {
+                    const int64_t n = int64_t(w) * SPL + j;
+                    if (n < p.N) p.dh0[(int64_t(b) * p.dim + dch) * p.N + n] = e[j];
+                }
+            }
+        }
+        // per-channel sums of the TV threads of a channel, in vector order
+        float* fin = smem;   // [2][TV][64]
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+            if (sv_on[k]) {
+                fin[sv_tv[k] * kLanes + sv_ch[k]] = accD[k];
+                fin[(TV + sv_tv[k]) * kLanes + sv_ch[k]] = accBias[k];
+            }
+        }
+        __syncthreads();
+        if (tid < kLanes && c0 + tid < p.dim) {
+            float sd = 0.0f, sb = 0.0f;
+#pragma unroll
+            for (int tv = 0; tv < TV; ++tv) {
+                sd += fin[tv * kLanes + tid];
+                sb += fin[(TV + tv) * kLanes + tid];
+            }
+            const int64_t o = (int64_t(piece) * p.batch + b) * p.dim + c0 + tid;
+            p.pD[o] = sd;
+            p.pbias[o] = sb;
+        }
+    }
+}
+
+// Piece carries, one thread per (group, state entry, lane), in sequence order:
+//   forward:  Hin[0] = h0 (or 0),     Hin[c+1] = exp2(A*S[c]) Hin[c] + H[c]
+//   reverse:  Ein[P-1] = dh_last (or 0), Ein[c-1] = exp2(A*S[c]) Ein[c] + G[c]
+__global__ void __launch_bounds__(256) bwd_carry_kernel(BwdParams p, int64_t total, int reverse) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int lane = int(i % kLanes);
+    const int64_t n = (i / kLanes) % p.np;
+    const int64_t blk = i / (int64_t(kLanes) * p.np);
+    const int64_t d = (blk % p.nblk_d) * kLanes + lane;
+    const int64_t b = blk / p.nblk_d;
+    const bool ok = d < p.dim && n < p.N;
+    const float a = ok ? (p.head_dim ? p.A[d / p.head_dim] : p.A[d * p.N + n]) : 0.0f;
+    const int P = p.nchunks;
+    auto at = [&](int c) { return ((blk * P + c) * p.np + n) * kLanes + lane; };
+    float cur = 0.0f;
+    if (!reverse) {
+        if (ok && p.h0) cur = p.h0[(b * p.dim + d) * p.N + n];
+        for (int c = 0; c < P; ++c) {
+            p.fHin[at(c)] = cur;
+            if (c + 1 < P) cur = fmaf(__builtin_amdgcn_exp2f(a * p.fS[(blk * P + c) * kLanes + lane]), cur, p.fH[at(c)]);
+        }
+    } else {
+        if (ok && p.dh_last) cur = p.dh_last[(b * p.dim + d) * p.N + n];
+        for (int c = P - 1; c >= 0; --c) {
+            p.rEin[at(c)] = cur;
+            if (c > 0) cur = fmaf(__builtin_amdgcn_exp2f(a * p.rS[(blk * P + c) * kLanes + lane]), cur, p.rG[at(c)]);
+        }
+    }
+}
+
+// dB[b,n,t] = ln2 * sum over channel blocks, dC likewise unscaled; one thread per output.
+__global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(BwdParams p, float* dB, float* dC, int64_t total) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int64_t t = i % p.L;
+    int64_t r = i / p.L;
+    const int64_t n = r % p.N;
+    r /= p.N;
+    const int isC = int(r % 2);
+    const int64_t b = r / 2;
+    const int64_t stride = int64_t(p.batch) * 2 * p.N * p.L;
+    const float* src = p.pBC + ((b * 2 + isC) * p.N + n) * p.L + t;
+    float sum = 0.0f;
+    for (int cb = 0; cb < p.nblk_d; ++cb) sum += src[cb * stride];
+    (isC ? dC : dB)[(b * p.N + n) * p.L + t] = isC ? sum : sum * kLn2;
+}
+
+// Diagonal A: dA[d,n] = ln2 * sum over pieces and batch rows.  Also dD and ddt_bias
+// (threads with d < dim, n == 0).
+__global__ void __launch_bounds__(256) bwd_reduce_param_kernel(BwdParams p, float* dA, float* dD, float* dbias,
+                                                               int64_t total) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int64_t d = i / p.N, n = i % p.N;
+    const int64_t rows = int64_t(p.nchunks) * p.batch;
+    if (dA) {
+        float s = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) s += p.pA[(r * p.dim + d) * p.np + n];
+        dA[d * p.N + n] = s * kLn2;
+    }
+    if (n == 0) {
+        float sd = 0.0f, sb = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) {
+            sd += p.pD[r * p.dim + d];
+            sb += p.pbias[r * p.dim + d];
+        }
+        if (dD) dD[d] = sd;
+        if (dbias) dbias[d] = sb;
+    }
+}
+
+// Scalar decay: dA[h] = ln2 * sum over pieces, batch rows, the head's channels and
+// the state entries; one workgroup per head, fixed-order tree.
+__global__ void __launch_bounds__(256) bwd_reduce_heads_kernel(BwdParams p, float* dA) {
+    __shared__ float part[256];
+    const int64_t hd = blockIdx.x;
+    const int64_t per_row = p.head_dim * p.N;
+    const int64_t total = int64_t(p.nchunks) * p.batch * per_row;
+    float s = 0.0f;
+    for (int64_t k = threadIdx.x; k < total; k += 256) {
+        const int64_t r = k / per_row, q = k % per_row;
+        const int64_t d = hd * p.head_dim + q / p.N, n = q % p.N;
+        s += p.pA[(r * p.dim + d) * p.np + n];
+    }
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (int(threadIdx.x) < off) part[threadIdx.x] += part[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) dA[hd] = part[0] * kLn2;
+}
+
+// ------------------------------------------------------------------ host side
+struct BwdPlan {
+    int spl, G, nch;
+    int64_t chunk_len, nblk_d, groups, ntiles_seq;
+    size_t off_ck, off_bc, off_a, off_d, off_bias, off_fh, off_fs, off_fhin, off_rg, off_rs, off_rein, ws_bytes;
+    size_t lds_grad, lds_fwd;
+};
+
+inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
+    int st = validate_dims(d);
+    if (st != SSM_OK) return st;
+    const int64_t N = d->dstate;
+    if (N > SSM_MAX_DSTATE_BWD) return SSM_ERR_DIMS;
+    int spl = d->states_per_lane;
+    if (spl == 0) {
+        // The gradient walk keeps a tile's recomputed states in VGPRs (16 steps x SPL
+        // per lane) next to the staging and finishing registers, so few entries per
+        // lane keep the kernel at two waves per SIMD without spills: up to 8 waves
+        // of 2 entries for N <= 16, then more entries per lane at 8 waves.
+        if (N <= 4) spl = 1;
+        else if (N <= 16) spl = 2;
+        else if (N <= 32) spl = 4;
+        else if (N <= 64) spl = 8;
+        else spl = 16;
+    }
+    const int64_t g = cdiv(N, spl);
+    if (g > 8) return SSM_ERR_DIMS;
+    pl->spl = spl;
+    pl->G = g <= 4 ? 4 : 8;
+    const int np = pl->G * spl;
+    pl->nblk_d = cdiv(d->dim, kLanes);
+    pl->groups = d->batch * pl->nblk_d;
+    pl->ntiles_seq = cdiv(d->seqlen, kT);
+    int64_t nch = d->nchunks;
+    if (nch == 0) {
+        // below two waves per SIMD the sequence is cut into pieces (each piece costs a
+        // forward and a reverse aggregate walk), keeping >= 8 tiles per piece
+        const int64_t waves = pl->groups * pl->G;
+        nch = waves < 2048 ? cdiv(2048, waves) : 1;
+        const int64_t max_pieces = pl->ntiles_seq / 8 > 1 ? pl->ntiles_seq / 8 : 1;
+        if (nch > max_pieces) nch = max_pieces;
+        if (nch > SSM_MAX_CHUNKS) nch = SSM_MAX_CHUNKS;
+    }
+    if (nch > pl->ntiles_seq) nch = pl->ntiles_seq;
+    if (nch < 1) nch = 1;
+    pl->chunk_len = cdiv(pl->ntiles_seq, nch) * kT;
+    pl->nch = int(cdiv(d->seqlen, pl->chunk_len));
+    if (pl->groups * pl->nch > 0x7fffffffLL) return SSM_ERR_DIMS;
+    const size_t f = sizeof(float);
+    size_t off = 0;
+    pl->off_ck = off;
+    off += round256(size_t(pl->groups) * pl->ntiles_seq * np * kLanes * f);
+    pl->off_bc = off;
+    off += round256(size_t(pl->nblk_d) * d->batch * 2 * N * d->seqlen * f);
+    pl->off_a = off;
+    off += round256(size_t(pl->nch) * d->batch * d->dim * np * f);
+    pl->off_d = off;
+    off += round256(size_t(pl->nch) * d->batch * d->dim * f);
+    pl->off_bias = off;
+    off += round256(size_t(pl->nch) * d->batch * d->dim * f);
+    const size_t st_bytes = round256(size_t(pl->groups) * pl->nch * np * kLanes * f);
+    const size_t s_bytes = round256(size_t(pl->groups) * pl->nch * kLanes * f);
+    pl->off_fh = pl->off_fs = pl->off_fhin = pl->off_rg = pl->off_rs = pl->off_rein = 0;
+    if (pl->nch > 1) {
+        pl->off_fh = off;
+        off += st_bytes;
+        pl->off_fs = off;
+        off += s_bytes;
+        pl->off_fhin = off;
+        off += st_bytes;
+        pl->off_rg = off;
+        off += st_bytes;
+        pl->off_rs = off;
+        off += s_bytes;
+        pl->off_rein = off;
+        off += st_bytes;
+    }
+    pl->ws_bytes = off;
+    pl->lds_grad = bwd_lds_floats(pl->G, spl, kGrad) * f;
+    pl->lds_fwd = bwd_lds_floats(pl->G, spl, kCkpt) * f;
+    return SSM_OK;
+}
+
+template <typename IO, int SPL, int G, bool SCALAR>
+hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, float* dA, float* dB, float* dC, float* dD, float* dbias,
+                      hipStream_t s) {
+    const dim3 block(unsigned(G * kLanes));
+    const int64_t groups = pl.groups;
+    if (pl.nch > 1) {
+        const dim3 grid1(unsigned(groups * (pl.nch - 1)));
+        p.piece_base = 0;
+        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kFwdAgg>), grid1, block, pl.lds_fwd, s, p);
+        p.piece_base = 1;
+        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kRevAgg>), grid1, block, pl.lds_fwd, s, p);
+        p.piece_base = 0;
+        const int64_t total = groups * p.np * kLanes;
+        const dim3 gridc(unsigned(cdiv(total, 256)));
+        hipLaunchKernelGGL(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 0);
+        hipLaunchKernelGGL(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 1);
+    }
+    p.piece_base = 0;
+    const dim3 grid(unsigned(groups * pl.nch));
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt>), grid, block, pl.lds_fwd, s, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kGrad>), grid, block, pl.lds_grad, s, p);
+    const int64_t nbc = int64_t(p.batch) * 2 * p.N * p.L;
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned(cdiv(nbc, 256))), dim3(256), 0, s, p, dB, dC, nbc);
+    const int64_t npar = p.dim * p.N;
+    hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3(unsigned(cdiv(npar, 256))), dim3(256), 0, s, p,
+                       SCALAR ? nullptr : dA, dD, dbias, npar);
+    if (SCALAR) {
+        const int64_t nheads = p.dim / p.head_dim;
+        hipLaunchKernelGGL(bwd_reduce_heads_kernel, dim3(unsigned(nheads)), dim3(256), 0, s, p, dA);
+    }
+    return hipGetLastError();
+}
+
+template <typename IO, bool SCALAR>
+hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, float* dA, float* dB, float* dC, float* dD,
+                        float* dbias, hipStream_t s) {
+#define SSM_BWD_CASE(S_, G_)                                                              \
+    if (pl.spl == S_ && pl.G == G_) return bwd_launch<IO, S_, G_, SCALAR>(p, pl, dA, dB, dC, dD, dbias, s);
+    SSM_BWD_CASE(1, 4)
+    SSM_BWD_CASE(2, 4)
+    SSM_BWD_CASE(4, 4)
+    SSM_BWD_CASE(8, 4)
+    SSM_BWD_CASE(16, 4)
+    SSM_BWD_CASE(1, 8)
+    SSM_BWD_CASE(2, 8)
+    SSM_BWD_CASE(4, 8)
+    SSM_BWD_CASE(8, 8)
+    SSM_BWD_CASE(16, 8)
+#undef SSM_BWD_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+extern "C" {
+
+size_t ssm_selective_scan_bwd_workspace_bytes(const ssm_dims* dims) {
+    BwdPlan pl;
+    if (make_bwd_plan(dims, &pl) != SSM_OK) return 0;
+    return pl.ws_bytes;
+}
+
+int ssm_selective_scan_bwd_plan(const ssm_dims* dims, ssm_plan* plan) {
+    if (!plan) return SSM_ERR_NULL;
+    BwdPlan pl;
+    const int st = make_bwd_plan(dims, &pl);
+    if (st != SSM_OK) return st;
+    plan->nchunks = pl.nch;
+    plan->states_per_lane = pl.spl;
+    plan->waves_per_group = pl.G;
+    plan->time_tile = kT;
+    plan->chunk_len = pl.chunk_len;
+    plan->workgroups = pl.groups * pl.nch;
+    plan->workspace_bytes = pl.ws_bytes;
+    plan->lds_bytes = pl.lds_grad;
+    return SSM_OK;
+}
+
+int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* dt_bias, const float* h0, const void* dy,
+                           const float* dh_last, const ssm_grads* grads, const ssm_dims* dims, void* stream) {
+    if (!dims || !grads) return SSM_ERR_NULL;
+    BwdPlan pl;
+    int st = make_bwd_plan(dims, &pl);
+    if (st != SSM_OK) return st;
+    if (!u || !delta || !A || !B || !C || !dy || !grads->du || !grads->ddelta || !grads->dA || !grads->dB ||
+        !grads->dC)
+        return SSM_ERR_NULL;
+    void* dz = z ? grads->dz : nullptr;
+    const size_t esz = dims->io_dtype == SSM_BF16 ? 2 : 4;
+    if (misaligned(u, esz) || misaligned(delta, esz) || misaligned(z, esz) || misaligned(B, esz) ||
+        misaligned(C, esz) || misaligned(dy, esz) || misaligned(grads->du, esz) || misaligned(grads->ddelta, esz) ||
+        misaligned(dz, esz) || misaligned(A, 4) || misaligned(D, 4) || misaligned(dt_bias, 4) ||
+        misaligned(h0, 4) || misaligned(dh_last, 4) || misaligned(grads->dA, 4) || misaligned(grads->dB, 4) ||
+        misaligned(grads->dC, 4) || misaligned(grads->dD, 4) || misaligned(grads->ddt_bias, 4) ||
+        misaligned(grads->dh0, 4))
+        return SSM_ERR_ALIGN;
+
+    const size_t nel = size_t(dims->batch) * dims->dim * dims->seqlen * esz;
+    const size_t nbc = size_t(dims->batch) * dims->dstate * dims->seqlen * esz;
+    const size_t nbc4 = size_t(dims->batch) * dims->dstate * dims->seqlen * 4;
+    const size_t na = (dims->nheads > 0 ? size_t(dims->nheads) : size_t(dims->dim) * dims->dstate) * 4;
+    const size_t nd = size_t(dims->dim) * 4;
+    const size_t nh = size_t(dims->batch) * dims->dim * dims->dstate * 4;
+    const void* ins[] = {u, delta, z, B, C, A, D, dt_bias, h0, dy, dh_last};
+    const size_t in_sz[] = {nel, nel, nel, nbc, nbc, na, nd, nd, nh, nel, nh};
+    const void* outs[] = {grads->du, grads->ddelta, dz, grads->dA, grads->dB, grads->dC, grads->dD,
+                          grads->ddt_bias, grads->dh0, dims->workspace};
+    const size_t out_sz[] = {nel, nel, nel, na, nbc4, nbc4, nd, nd, nh, pl.ws_bytes};
+    constexpr int kIn = 11, kOut = 10;
+    for (int i = 0; i < kOut; ++i) {
+        for (int k = 0; k < kIn; ++k)
+            if (overlaps(outs[i], out_sz[i], ins[k], in_sz[k])) return SSM_ERR_ALIAS;
+        for (int k = i + 1; k < kOut; ++k)
+            if (overlaps(outs[i], out_sz[i], outs[k], out_sz[k])) return SSM_ERR_ALIAS;
+    }
+    if (!dims->workspace || dims->workspace_bytes < pl.ws_bytes ||
+        (reinterpret_cast<uintptr_t>(dims->workspace) % 256) != 0)
+        return SSM_ERR_WORKSPACE;
+
+    const size_t vw = 16 / esz;
+    auto a16 = [](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) % 16) == 0; };
+    const bool vec = (dims->seqlen % int64_t(vw)) == 0 && a16(u) && a16(delta) && a16(z) && a16(B) && a16(C) &&
+                     a16(dy) && a16(grads->du) && a16(grads->ddelta) && a16(dz);
+
+    BwdParams p;
+    p.u = u;
+    p.delta = delta;
+    p.z = z;
+    p.Bm = B;
+    p.Cm = C;
+    p.A = A;
+    p.Dskip = D;
+    p.bias = dt_bias;
+    p.h0 = h0;
+    p.dy = dy;
+    p.dh_last = dh_last;
+    p.du = grads->du;
+    p.ddelta = grads->ddelta;
+    p.dz = dz;
+    p.dh0 = grads->dh0;
+    p.L = dims->seqlen;
+    p.dim = dims->dim;
+    p.N = dims->dstate;
+    p.head_dim = dims->nheads > 0 ? dims->dim / dims->nheads : 0;
+    p.chunk_len = pl.chunk_len;
+    p.ntiles_seq = pl.ntiles_seq;
+    p.nchunks = pl.nch;
+    p.nblk_d = int32_t(pl.nblk_d);
+    p.batch = int32_t(dims->batch);
+    p.np = pl.G * pl.spl;
+    p.piece_base = 0;
+    p.vec = vec ? 1 : 0;
+    char* ws = static_cast<char*>(dims->workspace);
+    auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    p.ck = at(pl.off_ck);
+    p.pBC = at(pl.off_bc);
+    p.pA = at(pl.off_a);
+    p.pD = at(pl.off_d);
+    p.pbias = at(pl.off_bias);
+    p.fH = p.fS = p.fHin = p.rG = p.rS = p.rEin = nullptr;
+    if (pl.nch > 1) {
+        p.fH = at(pl.off_fh);
+        p.fS = at(pl.off_fs);
+        p.fHin = at(pl.off_fhin);
+        p.rG = at(pl.off_rg);
+        p.rS = at(pl.off_rs);
+        p.rEin = at(pl.off_rein);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool scalar = dims->nheads > 0;
+    hipError_t e;
+    if (dims->io_dtype == SSM_BF16)
+        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<uint16_t, false>(p, pl, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+    else
+        e = scalar ? bwd_dispatch<float, true>(p, pl, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<float, false>(p, pl, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

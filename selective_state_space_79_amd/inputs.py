@@ -142,3 +142,25 @@ def to_device(x: ScanInputs, device="cuda"):
 
     return dict(u=io_tensor(x.u), delta=io_tensor(x.delta), z=io_tensor(x.z), B=io_tensor(x.B), C=io_tensor(x.C),
                 A=f32(x.A), D=f32(x.D), dt_bias=f32(x.dt_bias))
+
+
+def make_cotangents(x: ScanInputs, *, seed: int, with_dh_last: bool = False):
+    """Seeded gradients arriving at the scan's outputs, for the backward pass: dy
+    (batch, dim, L) standard normal in the I/O type (bf16-rounded like the inputs) and,
+    optionally, dh_last (batch, dim, N) standard normal float32.  Returns (dy, dh_last
+    or None) as float32 numpy arrays."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dy = rng.standard_normal((x.batch, x.dim, x.L), dtype=np.float32)
+    if x.io == "bf16":
+        dy = round_to_bf16(dy)
+    dhl = rng.standard_normal((x.batch, x.dim, x.N), dtype=np.float32) if with_dh_last else None
+    return dy, dhl
+
+
+def io_to_device(x: ScanInputs, a: np.ndarray, device="cuda"):
+    """Upload one (batch, dim, L) array in the I/O type of x."""
+    import torch
+
+    if x.io == "bf16":
+        return torch.from_numpy(bf16_bits(a)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)

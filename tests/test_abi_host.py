@@ -187,3 +187,76 @@ def test_step_entry_point_refusals():
     assert _call_step(d1, h=FAKE + 0x500000 - 16) == ssm.SSM_ERR_ALIAS                # h overlaps y
     assert _call_step(small_dims(seqlen=1, dim=0)) == ssm.SSM_ERR_EMPTY
     assert _call_step(small_dims(seqlen=1, io_dtype=9)) == ssm.SSM_ERR_DTYPE
+
+
+# ---------------------------------------------------------------- backward pass
+
+def _bwd(dims, grads=None, *, u=FAKE, delta=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
+         C=FAKE + 0x400000, D=None, z=None, bias=None, h0=None, dy=FAKE + 0x500000, dh_last=None):
+    if grads is None:
+        base = 0x40000000
+        grads = ssm.SsmGrads(base, base + 0x1000000, base + 0x2000000, base + 0x3000000, base + 0x4000000,
+                             None, None, None, None)
+    p = lambda a: ctypes.c_void_p(a) if a else None
+    return ssm.load_library().ssm_selective_scan_bwd(
+        p(u), p(delta), p(A), p(B), p(C), p(D), p(z), p(bias), p(h0), p(dy), p(dh_last), ctypes.byref(grads),
+        ctypes.byref(dims), None)
+
+
+def _bwd_dims(*args, **kw):
+    d = ssm.make_dims(*args, **kw)
+    need = ssm.ssm_selective_scan_bwd_workspace_bytes(d)
+    d.workspace, d.workspace_bytes = 0x80000000, need
+    return d
+
+
+def test_backward_plans():
+    """Backward plans: 8 waves of 2 entries for N = 16, 16 per lane for N = 128, pieces
+    where the channel blocks give fewer than two waves per SIMD, and a workspace that
+    holds the 16-step states, the dB/dC partials and the carries."""
+    d3 = ssm.make_dims(4, 4096, 4096, 16)
+    p = ssm.ssm_selective_scan_bwd_plan(d3)
+    assert (p.states_per_lane, p.waves_per_group, p.time_tile, p.nchunks) == (2, 8, 16, 1)
+    ck = 4 * 64 * 256 * 16 * 64 * 4          # groups x tiles x entries x lanes x 4 B
+    bc = 64 * 4 * 2 * 16 * 4096 * 4          # blocks x batch x {B,C} x N x L x 4 B
+    assert p.workspace_bytes >= ck + bc
+    assert ssm.ssm_selective_scan_bwd_workspace_bytes(d3) == p.workspace_bytes
+    p4 = ssm.ssm_selective_scan_bwd_plan(ssm.make_dims(1, 131072, 2048, 16))
+    assert p4.nchunks > 1 and p4.chunk_len % 16 == 0
+    p5 = ssm.ssm_selective_scan_bwd_plan(ssm.make_dims(2, 8192, 4096, 128, nheads=64))
+    assert (p5.states_per_lane, p5.waves_per_group) == (16, 8)
+    for args in [(1, 1, 1, 1), (1, 64, 4, 4), (3, 257, 130, 5), (1, 100, 64, 128)]:
+        pl = ssm.ssm_selective_scan_bwd_plan(ssm.make_dims(*args))
+        assert pl.lds_bytes <= 160 * 1024 // 2 or pl.waves_per_group == 8
+        assert pl.lds_bytes <= 160 * 1024
+
+
+def test_backward_refusals():
+    d = _bwd_dims(2, 100, 70, 16)
+    # a valid call would be enqueued; every refusal below must come first
+    assert _bwd(d, u=None) == ssm.SSM_ERR_NULL
+    assert _bwd(d, dy=None) == ssm.SSM_ERR_NULL
+    g = ssm.SsmGrads(0x40000000, None, 0x42000000, 0x43000000, 0x44000000, None, None, None, None)
+    assert _bwd(d, g) == ssm.SSM_ERR_NULL
+    # dstate above the backward's limit, too many waves for a forced split
+    big = _bwd_dims(1, 100, 64, 129)
+    assert _bwd(big) == ssm.SSM_ERR_DIMS
+    assert ssm.ssm_selective_scan_bwd_workspace_bytes(ssm.make_dims(1, 100, 64, 129)) == 0
+    assert _bwd(_bwd_dims(1, 100, 64, 64, states_per_lane=4)) == ssm.SSM_ERR_DIMS
+    # workspace missing or short
+    short = _bwd_dims(2, 100, 70, 16)
+    short.workspace_bytes -= 4
+    assert _bwd(short) == ssm.SSM_ERR_WORKSPACE
+    none = ssm.make_dims(2, 100, 70, 16)
+    assert _bwd(none) == ssm.SSM_ERR_WORKSPACE
+    # misaligned gradient output
+    g = ssm.SsmGrads(0x40000000, 0x41000000, 0x42000002, 0x43000000, 0x44000000, None, None, None, None)
+    assert _bwd(d, g) == ssm.SSM_ERR_ALIGN
+    # an output overlapping an input, another output or the workspace
+    g = ssm.SsmGrads(FAKE, 0x41000000, 0x42000000, 0x43000000, 0x44000000, None, None, None, None)
+    assert _bwd(d, g) == ssm.SSM_ERR_ALIAS
+    g = ssm.SsmGrads(0x40000000, 0x40000000, 0x42000000, 0x43000000, 0x44000000, None, None, None, None)
+    assert _bwd(d, g) == ssm.SSM_ERR_ALIAS
+    g = ssm.SsmGrads(0x40000000, 0x41000000, 0x42000000, 0x43000000, 0x80000000, None, None, None, None)
+    assert _bwd(d, g) == ssm.SSM_ERR_ALIAS
+    assert _bwd(ssm.make_dims(0, 100, 70, 16)) == ssm.SSM_ERR_EMPTY
