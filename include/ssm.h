@@ -166,10 +166,10 @@ typedef struct ssm_grads {
 
 /* Bytes of workspace ssm_selective_scan_bwd needs for dims (never 0 for a valid
  * dims; 0 for a dims pointer the backward would refuse).  The workspace holds the
- * states recomputed every 16 steps (4*dstate bytes per 16 steps of every channel,
- * rounded up to whole 64-channel blocks and 4-entry groups), per-block partial sums
- * of dB and dC (8*dstate bytes per token and 64-channel block) and the carries
- * between pieces. */
+ * states recomputed every 16 steps (every 8 steps when dstate > 64): 4 bytes per
+ * state entry and interval of every channel, rounded up to whole 64-channel blocks
+ * and to the padded entry count; per-block partial sums of dB and dC (8*dstate bytes
+ * per token and 64-channel block); and the carries between pieces. */
 SSM_API size_t ssm_selective_scan_bwd_workspace_bytes(const ssm_dims* dims);
 
 /* Enqueue the backward pass: the gradients, with respect to every input of
@@ -188,10 +188,9 @@ SSM_API size_t ssm_selective_scan_bwd_workspace_bytes(const ssm_dims* dims);
  * dstate must be <= SSM_MAX_DSTATE_BWD; dims->states_per_lane may force 1, 2, 4, 8
  * or 16 entries per lane as long as that needs at most 8 waves (else SSM_ERR_DIMS).
  * No output may overlap an input, another output or the workspace (SSM_ERR_ALIAS).
- * Sums over channels, batch rows and time (dA, dB, dC, dD, ddt_bias) are formed in a
- * fixed order from per-workgroup partials; the partial read-outs of the state
- * entries of one step are combined with LDS atomics, so du, ddelta and dz may differ
- * between runs in the last bits.  Other rules as ssm_selective_scan_fwd. */
+ * Every sum (over state entries, channels, batch rows and time) is formed in a fixed
+ * order, so repeated calls give bitwise identical gradients.  The workspace holds
+ * no state between calls.  Other rules as ssm_selective_scan_fwd. */
 SSM_API int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                                    const float* D, const void* z, const float* dt_bias, const float* h0,
                                    const void* dy, const float* dh_last, const ssm_grads* grads,

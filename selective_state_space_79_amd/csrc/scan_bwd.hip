@@ -25,7 +25,8 @@
 //      start state, recompute its 16 states forward (kept in VGPRs; with more than 4
 //      entries per lane in sub-blocks, re-walked from saved sub-block starts), then
 //      step backwards through them.  The per-step sums over state entries (the
-//      read-out, sum A g a h, sum g B') are combined across waves with LDS atomics;
+//      read-out, sum A g a h, sum g B') are left per wave in LDS and summed over the
+//      waves in a fixed order;
 //      the sums over channels (dB, dC) are reduced across the 64 lanes through a
 //      per-wave LDS transpose, 16 values at a time, in a fixed order;
 //   3. reduce kernels add the per-workgroup partials of dB, dC, dA, dD and ddt_bias
@@ -45,7 +46,9 @@
 
 namespace {
 
-constexpr int kT = 16;       // time tile = recompute interval
+// time tile = recompute interval: 16 steps, 8 when a workgroup carries more than 64
+// state entries per channel (the per-wave partial slabs must fit the LDS)
+inline constexpr int bwd_tile(int np) { return np <= 64 ? 16 : 8; }
 constexpr int kRound = 8;    // values per cross-lane reduction round
 constexpr int kQB = 2;       // steps per scheduling group in the gradient walk: keeps the
                              // compiler from hoisting a whole tile's LDS operands at once
@@ -86,7 +89,7 @@ struct BwdParams {
 enum BwdMode { kCkpt = 0, kFwdAgg = 1, kRevAgg = 2, kGrad = 3 };
 
 template <int SPL, int G> struct BShape {
-    static constexpr int T = kT;
+    static constexpr int T = bwd_tile(G * SPL);
     static constexpr int NP = G * SPL;
     static constexpr int NT = G * kLanes;
     static constexpr int TS = (64 / SPL < T) ? 64 / SPL : T;   // states a lane keeps per sub-block
@@ -97,28 +100,64 @@ template <int SPL, int G> struct BShape {
 };
 
 // LDS floats of one workgroup:
-//   sW  [T][64] float4  (dt2, dt2*u, ds, scalar decay)      all modes
-//   sF  [T][64] float4  (u, sigmoid(r), dy*SiLU'(z), D*u)     gradient pass
-//   sBC [T][NP] float2  (B*ln2, C)                           all modes
-//   sYP, sS1, sS2 [T][64]  read-out, sum A g a h, sum g B'  gradient pass (LDS atomics)
-//   sdBC [2][NP][T]     per-block dB, dC of the tile          gradient pass
-//   sRed [G][8][64]     per-wave transpose for lane sums     gradient pass
+//   sW  [T][64] float4     (dt2, dt2*u, ds, scalar decay)         all modes
+//   sF  [T][64] float4     (u, sigmoid(r), dy*SiLU'(z), D*u)      gradient pass
+//   sBC [T][NP] float2     (B*ln2, C)                             all modes
+//   sP  [3][G][T][64]      per-wave partial read-out, sum A g a h, sum g B' of each
+//                          step and channel, summed over the waves in a fixed order
+//   sdBC [2][NP][T]        per-block dB, dC of the tile            gradient pass
+//   sRed [G][8][64]        per-wave transpose for lane sums        gradient pass
 inline size_t bwd_lds_floats(int G, int SPL, int mode) {
-    const size_t T = kT, NP = size_t(G) * SPL;
+    const size_t NP = size_t(G) * SPL, T = bwd_tile(G * SPL);
     size_t f = T * kLanes * 4 + T * NP * 2;
-    if (mode == kGrad) f += T * kLanes * 4 + 3 * T * kLanes + 2 * NP * T + size_t(G) * kRound * kLanes;
+    if (mode == kGrad) f += T * kLanes * 4 + 3 * size_t(G) * T * kLanes + 2 * NP * T + size_t(G) * kRound * kLanes;
     return f;
 }
 
-template <typename IO>
-__device__ inline Vec<IO> ld_row(const IO* row, int64_t t, int64_t tend, bool ok, bool vec) {
-    return vec ? load_vec<IO, true>(row, t, tend, ok) : load_vec<IO, false>(row, t, tend, ok);
+// EPT consecutive elements of one row: one load or store of EPT*sizeof(IO) bytes when
+// the row is aligned for it (vec), else element by element.  Elements at or beyond
+// tend (or of a row that does not exist, ok == false) read as 0 and are not written.
+template <typename IO, int EPT> struct Seg {
+    IO e[EPT];
+};
+
+template <int BYTES> struct RawOf;
+template <> struct RawOf<2> { using T = uint16_t; };
+template <> struct RawOf<4> { using T = uint32_t; };
+template <> struct RawOf<8> { using T = uint2; };
+template <> struct RawOf<16> { using T = uint4; };
+
+template <typename IO, int EPT>
+__device__ inline Seg<IO, EPT> load_seg(const IO* __restrict__ row, int64_t t, int64_t tend, bool ok, bool vec) {
+    using R = typename RawOf<EPT * int(sizeof(IO))>::T;
+    Seg<IO, EPT> v;
+    if (vec) {
+        R raw;
+        __builtin_memset(&raw, 0, sizeof(R));
+        if (ok && t < tend) raw = *reinterpret_cast<const R*>(row + t);
+        __builtin_memcpy(&v, &raw, sizeof(R));
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) v.e[e] = (ok && t + e < tend) ? row[t + e] : IO(0);
+    }
+    return v;
 }
 
-template <typename IO>
-__device__ inline void st_row(IO* row, int64_t t, int64_t tend, bool ok, bool vec, const Vec<IO>& v) {
-    if (vec) store_vec<IO, true>(row, t, tend, ok, v);
-    else store_vec<IO, false>(row, t, tend, ok, v);
+template <typename IO, int EPT>
+__device__ inline void store_seg(IO* __restrict__ row, int64_t t, int64_t tend, bool ok, bool vec,
+                                 const Seg<IO, EPT>& v) {
+    using R = typename RawOf<EPT * int(sizeof(IO))>::T;
+    if (vec) {
+        if (ok && t < tend) {
+            R raw;
+            __builtin_memcpy(&raw, &v, sizeof(R));
+            *reinterpret_cast<R*>(row + t) = raw;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            if (ok && t + e < tend) row[t + e] = v.e[e];
+    }
 }
 
 template <int CTRL>
@@ -131,17 +170,16 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     using S = BShape<SPL, G>;
     constexpr int T = S::T, NP = S::NP, NT = S::NT, TS = S::TS, NSB = S::NSB;
     constexpr int JR = S::JR, RS = S::RS, NJR = S::NJR;
-    constexpr int VW = IOT<IO>::VW;
-    constexpr int TV = T / VW;                    // vectors per row per tile
-    constexpr int NVX = kLanes * TV;
-    constexpr int KX = (NVX + NT - 1) / NT;
-    constexpr int NBV = 2 * NP * TV;              // B rows then C rows
-    constexpr int KBV = (NBV + NT - 1) / NT;
+    constexpr int EPT = T / G;                    // elements per thread and tile (each thread
+                                                  // takes EPT consecutive steps of one channel)
+    constexpr int NBCV = 2 * NP * T;              // B and C values per tile
+    constexpr int KB = (NBCV + NT - 1) / NT;      // of them per thread
     constexpr bool kG = MODE == kGrad;
     constexpr bool kRev = MODE == kRevAgg || MODE == kGrad;
     constexpr bool kUseB = MODE != kRevAgg;
     constexpr bool kUseC = MODE == kRevAgg || MODE == kGrad;
     constexpr bool kUseU = MODE != kRevAgg;
+    static_assert(T % G == 0 && EPT * G == T, "a tile's steps must split evenly over the waves");
     static_assert(TS % RS == 0 && RS * 2 * JR == kRound, "reduction rounds must tile the sub-block");
 
     extern __shared__ float smem[];
@@ -149,10 +187,9 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     float* const after_w = smem + T * kLanes * 4;
     float4* sF = reinterpret_cast<float4*>(after_w);
     float* const sBC = after_w + (kG ? T * kLanes * 4 : 0);
-    float* const sYP = sBC + T * NP * 2;
-    float* const sS1 = sYP + T * kLanes;
-    float* const sS2 = sS1 + T * kLanes;
-    float* const sdBC = sS2 + T * kLanes;
+    float* const sP = sBC + T * NP * 2;                 // [3][G][T][64]
+    constexpr int kSlab = G * T * kLanes;
+    float* const sdBC = sP + 3 * kSlab;
     float* const sRed = sdBC + 2 * NP * T;
 
     const int tid = threadIdx.x;
@@ -190,101 +227,84 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     }
     const int64_t state_base = ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
 
-    // ---- staging constants: element vectors v = tid + k*NT -> (channel, vector in row)
-    int sv_ch[KX], sv_tv[KX];
-    bool sv_on[KX], sv_ok[KX];
-    float sv_bias[KX], sv_skip[KX], sv_ah[KX];
-    int64_t sv_row[KX];
+    // ---- element constants: thread tid takes steps e_seg*EPT .. +EPT-1 of channel e_ch
+    const int e_ch = tid / G;
+    const int e_seg = tid % G;
+    const int64_t e_d = c0 + e_ch;
+    const bool e_ok = e_d < p.dim;
+    const float e_bias = (e_ok && p.bias) ? p.bias[e_d] : 0.0f;
+    const float e_skip = (e_ok && p.Dskip) ? p.Dskip[e_d] : 0.0f;
+    const float e_ah = (SCALAR && e_ok) ? p.A[e_d / p.head_dim] : 0.0f;
+    const int64_t e_row = (int64_t(b) * p.dim + (e_ok ? e_d : 0)) * p.L;
+
+    // ---- B/C constants: value v = tid + k*NT -> (B or C, entry n, step t of the tile)
+    const IO* bc_ptr[KB];
+    int bc_slot[KB], bc_t[KB];
+    bool bc_on[KB], bc_ok[KB];
 #pragma unroll
-    for (int k = 0; k < KX; ++k) {
+    for (int k = 0; k < KB; ++k) {
         const int v = tid + k * NT;
-        sv_on[k] = v < NVX;
-        sv_ch[k] = (v / TV) % kLanes;
-        sv_tv[k] = v % TV;
-        const int64_t d = c0 + sv_ch[k];
-        sv_ok[k] = sv_on[k] && d < p.dim;
-        sv_bias[k] = (sv_ok[k] && p.bias) ? p.bias[d] : 0.0f;
-        sv_skip[k] = (sv_ok[k] && p.Dskip) ? p.Dskip[d] : 0.0f;
-        sv_ah[k] = 0.0f;
-        if constexpr (SCALAR) sv_ah[k] = sv_ok[k] ? p.A[d / p.head_dim] : 0.0f;
-        sv_row[k] = (int64_t(b) * p.dim + (sv_ok[k] ? d : 0)) * p.L;
-    }
-    // ---- B/C row vectors v = tid + k*NT -> (B or C, entry n, vector in row)
-    const IO* bc_row[KBV];
-    int bc_slot[KBV], bc_tv[KBV];
-    bool bc_on[KBV], bc_ok[KBV], bc_isC[KBV];
-#pragma unroll
-    for (int k = 0; k < KBV; ++k) {
-        const int v = tid + k * NT;
-        bc_on[k] = v < NBV;
-        const int isC = v / (NP * TV);
-        const int rem = v % (NP * TV);
-        const int n = rem / TV;
-        bc_tv[k] = rem % TV;
-        bc_isC[k] = isC != 0;
+        bc_on[k] = v < NBCV;
+        const int isC = v / (NP * T);
+        const int n = (v / T) % NP;
+        bc_t[k] = v % T;
         bc_ok[k] = bc_on[k] && n < p.N && (isC ? kUseC : kUseB);
-        bc_row[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bc_ok[k] ? n : 0)) * p.L;
-        bc_slot[k] = n * 2 + isC;
+        bc_ptr[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bc_ok[k] ? n : 0)) * p.L + bc_t[k];
+        bc_slot[k] = (bc_t[k] * NP + n) * 2 + isC;
     }
 
-    Vec<IO> nu[KX], ndl[KX], nz[KX], ndy[KX], nbc[KBV];
-    auto issue_loads = [&](int64_t t0) {
+    // ---- prefetch registers (one tile ahead): checkpoint entries first, so that the
+    //      wait for a tile's staging data also covers them
+    Seg<IO, EPT> nu, ndl, nz, ndy;
+    IO nbc[KB];
+    float ckn[SPL];
 #pragma unroll
-        for (int k = 0; k < KX; ++k) {
-            if (sv_on[k]) {
-                const int64_t t = t0 + sv_tv[k] * VW;
-                if constexpr (kUseU) nu[k] = ld_row<IO>(gu + sv_row[k], t, tend, sv_ok[k], vec);
-                ndl[k] = ld_row<IO>(gdl + sv_row[k], t, tend, sv_ok[k], vec);
-                if constexpr (kRev) {
-                    ndy[k] = ld_row<IO>(gdy + sv_row[k], t, tend, sv_ok[k], vec);
-                    if (has_z) nz[k] = ld_row<IO>(gz + sv_row[k], t, tend, sv_ok[k], vec);
-                }
-            }
+    for (int j = 0; j < SPL; ++j) ckn[j] = 0.0f;
+    auto issue_loads = [&](int kt) {
+        const int64_t t0 = tbeg + int64_t(kt) * T;
+        if constexpr (kG) {
+            const float* ck = p.ck + ((blk * p.ntiles_seq + tile0 + kt) * NP + int64_t(w) * SPL) * kLanes + lane;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) ckn[j] = ck[int64_t(j) * kLanes];
+        }
+        const int64_t t = t0 + e_seg * EPT;
+        if constexpr (kUseU) nu = load_seg<IO, EPT>(gu + e_row, t, tend, e_ok, vec);
+        ndl = load_seg<IO, EPT>(gdl + e_row, t, tend, e_ok, vec);
+        if constexpr (kRev) {
+            ndy = load_seg<IO, EPT>(gdy + e_row, t, tend, e_ok, vec);
+            if (has_z) nz = load_seg<IO, EPT>(gz + e_row, t, tend, e_ok, vec);
         }
 #pragma unroll
-        for (int k = 0; k < KBV; ++k)
-            if (bc_on[k]) nbc[k] = ld_row<IO>(bc_row[k], t0 + bc_tv[k] * VW, tend, bc_ok[k], vec);
+        for (int k = 0; k < KB; ++k) nbc[k] = (bc_ok[k] && t0 + bc_t[k] < tend) ? bc_ptr[k][t0] : IO(0);
     };
 
     // ---- registers -> LDS for the tile starting at t0.  Steps beyond the piece's end
     //      are identity steps (dt2 = 0, x = 0, ds = 0, decay 1).
     auto stage = [&](int64_t t0) {
 #pragma unroll
-        for (int k = 0; k < KX; ++k) {
-            if (!sv_on[k]) continue;
-#pragma unroll
-            for (int e = 0; e < VW; ++e) {
-                const int tl = sv_tv[k] * VW + e;
-                const bool in = sv_ok[k] && t0 + tl < tend;
-                const float uu = kUseU ? IOT<IO>::to_f32(nu[k].e[e]) : 0.0f;
-                const float r = IOT<IO>::to_f32(ndl[k].e[e]) + sv_bias[k];
-                const float dt2 = in ? softplus_log2(r) : 0.0f;
-                const float decay = SCALAR ? __builtin_amdgcn_exp2f(dt2 * sv_ah[k]) : 0.0f;
-                float ds = 0.0f, dyv = 0.0f, zz = 0.0f;
-                if constexpr (kRev) {
-                    dyv = in ? IOT<IO>::to_f32(ndy[k].e[e]) : 0.0f;
-                    zz = has_z ? IOT<IO>::to_f32(nz[k].e[e]) : 0.0f;
-                    ds = has_z ? dyv * silu_f32(zz) : dyv;
-                }
-                const int idx = tl * kLanes + sv_ch[k];
-                sW[idx] = make_float4(dt2, dt2 * uu, ds, decay);
-                if constexpr (kG) {
-                    const float dzf = has_z ? dyv * silu_grad_f32(zz) : 0.0f;
-                    sF[idx] = make_float4(uu, sigmoid_f32(r), dzf, sv_skip[k] * uu);
-                    sYP[idx] = 0.0f;
-                    sS1[idx] = 0.0f;
-                    sS2[idx] = 0.0f;
-                }
+        for (int e = 0; e < EPT; ++e) {
+            const int tl = e_seg * EPT + e;
+            const bool in = e_ok && t0 + tl < tend;
+            const float uu = kUseU ? IOT<IO>::to_f32(nu.e[e]) : 0.0f;
+            const float r = IOT<IO>::to_f32(ndl.e[e]) + e_bias;
+            const float dt2 = in ? softplus_log2(r) : 0.0f;
+            const float decay = SCALAR ? __builtin_amdgcn_exp2f(dt2 * e_ah) : 0.0f;
+            float ds = 0.0f, dyv = 0.0f, zz = 0.0f;
+            if constexpr (kRev) {
+                dyv = in ? IOT<IO>::to_f32(ndy.e[e]) : 0.0f;
+                zz = has_z ? IOT<IO>::to_f32(nz.e[e]) : 0.0f;
+                ds = has_z ? dyv * silu_f32(zz) : dyv;
+            }
+            const int idx = tl * kLanes + e_ch;
+            sW[idx] = make_float4(dt2, dt2 * uu, ds, decay);
+            if constexpr (kG) {
+                const float dzf = has_z ? dyv * silu_grad_f32(zz) : 0.0f;
+                sF[idx] = make_float4(uu, sigmoid_f32(r), dzf, e_skip * uu);
             }
         }
 #pragma unroll
-        for (int k = 0; k < KBV; ++k) {
-            if (!bc_on[k]) continue;
-            const float sc = bc_isC[k] ? 1.0f : kLn2;
-#pragma unroll
-            for (int e = 0; e < VW; ++e)
-                sBC[(bc_tv[k] * VW + e) * NP * 2 + bc_slot[k]] = IOT<IO>::to_f32(nbc[k].e[e]) * sc;
-        }
+        for (int k = 0; k < KB; ++k)
+            if (bc_on[k]) sBC[bc_slot[k]] = IOT<IO>::to_f32(nbc[k]) * ((bc_slot[k] & 1) ? 1.0f : kLn2);
     };
 
     // ---- per-lane LDS reads of one step
@@ -308,9 +328,9 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
         }
     };
 
-    float h[SPL], e[SPL], dAacc[SPL], ckn[SPL];
+    float h[SPL], e[SPL], dAacc[SPL], hst[SPL];
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) h[j] = e[j] = dAacc[j] = ckn[j] = 0.0f;
+    for (int j = 0; j < SPL; ++j) h[j] = e[j] = dAacc[j] = hst[j] = 0.0f;
     float dtsum = 0.0f, dtcomp = 0.0f;   // compensated (Kahan) sum of dt2 (aggregate passes)
     auto kahan = [&](float v) {
         const float yk = v - dtcomp;
@@ -343,11 +363,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 if (n < p.N) e[j] = p.dh_last[(int64_t(b) * p.dim + dch) * p.N + n];
             }
         }
-        const float* ck = p.ck + ((blk * p.ntiles_seq + tile0 + ntiles - 1) * NP + int64_t(w) * SPL) * kLanes + lane;
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) ckn[j] = ck[int64_t(j) * kLanes];
     }
-    __builtin_amdgcn_s_waitcnt(0);
 
     // ---- one forward step from LDS (all modes but the reverse aggregate)
     auto fwd_step = [&](int t, float (&hh)[SPL], float (&Bv)[SPL], float (&Cv)[SPL], float4& W) {
@@ -385,16 +401,8 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
         }
     };
 
-    // ---- the gradient walk of one tile (all waves)
-    auto grad_tile = [&](int kt) {
-        float hst[SPL];
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) hst[j] = ckn[j];
-        if (kt > 0) {
-            const float* ck = p.ck + ((blk * p.ntiles_seq + tile0 + kt - 1) * NP + int64_t(w) * SPL) * kLanes + lane;
-#pragma unroll
-            for (int j = 0; j < SPL; ++j) ckn[j] = ck[int64_t(j) * kLanes];
-        }
+    // ---- the gradient walk of one tile (all waves); hst holds the tile's start state
+    auto grad_tile = [&]() {
         float hsb[NSB > 1 ? NSB - 1 : 1][SPL];
         if constexpr (NSB > 1) {
             float hh[SPL], Bv[SPL], Cv[SPL];
@@ -404,10 +412,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int sb = 0; sb < NSB - 1; ++sb) {
 #pragma unroll
-                for (int ts = 0; ts < TS; ++ts) {
-                    if (ts % kQB == 0) __builtin_amdgcn_sched_barrier(0);
-                    fwd_step(sb * TS + ts, hh, Bv, Cv, W);
-                }
+                for (int ts = 0; ts < TS; ++ts) fwd_step(sb * TS + ts, hh, Bv, Cv, W);
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) hsb[sb][j] = hh[j];
             }
@@ -426,7 +431,6 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
                 for (int ts = 0; ts < TS; ++ts) {
                     const int t = sb * TS + ts;
-                    if (ts % kQB == 0) __builtin_amdgcn_sched_barrier(0);
                     fwd_step(t, hh, Bv, Cv, W);
                     float yp = 0.0f;
 #pragma unroll
@@ -434,7 +438,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                         H[ts][j] = hh[j];
                         yp = fmaf(Cv[j], hh[j], yp);
                     }
-                    atomicAdd(&sYP[t * kLanes + lane], yp);
+                    sP[(w * T + t) * kLanes + lane] = yp;
                 }
             }
             // re-read the step operands from LDS below rather than keeping the forward
@@ -444,7 +448,6 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int ts = TS - 1; ts >= 0; --ts) {
                 const int t = sb * TS + ts;
-                if ((TS - 1 - ts) % kQB == 0) __builtin_amdgcn_sched_barrier(0);
                 const float4 W = swl[t * kLanes];
                 float Bv[SPL], Cv[SPL];
                 read_bc(t, Bv, Cv);
@@ -461,14 +464,14 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                     s2 = fmaf(g, Bv[j], s2);
                     e[j] = a * g;
                     const int jj = j % JR;
-                    pv[(s * 2) * JR + jj] = g * W.y;          // dB (unscaled)
+                    pv[(s * 2) * JR + jj] = g * W.y;              // dB (unscaled)
                     pv[(s * 2 + 1) * JR + jj] = W.z * H[ts][j];   // dC
                     if constexpr (NJR > 1) {
                         if (jj == JR - 1) flush(pv, t, j - jj);
                     }
                 }
-                atomicAdd(&sS1[t * kLanes + lane], s1);
-                atomicAdd(&sS2[t * kLanes + lane], s2);
+                sP[kSlab + (w * T + t) * kLanes + lane] = s1;
+                sP[2 * kSlab + (w * T + t) * kLanes + lane] = s2;
                 if constexpr (NJR == 1) {
                     if (s == 0) flush(pv, t, 0);
                 }
@@ -482,45 +485,46 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     IO* __restrict__ gdd = static_cast<IO*>(p.ddelta);
     IO* __restrict__ gdz = static_cast<IO*>(p.dz);
     const bool write_dz = p.dz != nullptr && p.z != nullptr;
-    float accD[KX], accBias[KX];
-#pragma unroll
-    for (int k = 0; k < KX; ++k) accD[k] = accBias[k] = 0.0f;
+    float accD = 0.0f, accBias = 0.0f;
     auto finish = [&](int64_t t0) {
+        Seg<IO, EPT> odu, odd, odz;
 #pragma unroll
-        for (int k = 0; k < KX; ++k) {
-            if (!sv_on[k]) continue;
-            Vec<IO> odu, odd, odz;
+        for (int e2 = 0; e2 < EPT; ++e2) {
+            const int tl = e_seg * EPT + e2;
+            const int idx = tl * kLanes + e_ch;
+            const bool in = e_ok && t0 + tl < tend;
+            const float4 Wv = sW[idx];
+            const float4 Fv = sF[idx];
+            float yp = sP[idx], s1 = sP[kSlab + idx], s2 = sP[2 * kSlab + idx];
 #pragma unroll
-            for (int e2 = 0; e2 < VW; ++e2) {
-                const int tl = sv_tv[k] * VW + e2;
-                const int idx = tl * kLanes + sv_ch[k];
-                const bool in = sv_ok[k] && t0 + tl < tend;
-                const float4 Wv = sW[idx];
-                const float4 Fv = sF[idx];
-                const float s1 = sS1[idx], s2 = sS2[idx];
-                const float ddt = fmaf(Fv.x * kLog2e, s2, s1);
-                const float dd = ddt * Fv.y;
-                const float dui = fmaf(sv_skip[k], Wv.z, Wv.x * s2);
-                const float dzi = Fv.z * (sYP[idx] + Fv.w);
-                if (in) {
-                    accD[k] = fmaf(Wv.z, Fv.x, accD[k]);
-                    accBias[k] += dd;
-                }
-                odu.e[e2] = IOT<IO>::from_f32(dui);
-                odd.e[e2] = IOT<IO>::from_f32(dd);
-                odz.e[e2] = IOT<IO>::from_f32(dzi);
+            for (int ww = 1; ww < G; ++ww) {
+                const int o = ww * T * kLanes + idx;
+                yp += sP[o];
+                s1 += sP[kSlab + o];
+                s2 += sP[2 * kSlab + o];
             }
-            const int64_t t = t0 + sv_tv[k] * VW;
-            st_row<IO>(gdu + sv_row[k], t, tend, sv_ok[k], vec, odu);
-            st_row<IO>(gdd + sv_row[k], t, tend, sv_ok[k], vec, odd);
-            if (write_dz) st_row<IO>(gdz + sv_row[k], t, tend, sv_ok[k], vec, odz);
+            const float ddt = fmaf(Fv.x * kLog2e, s2, s1);
+            const float dd = ddt * Fv.y;
+            const float dui = fmaf(e_skip, Wv.z, Wv.x * s2);
+            const float dzi = Fv.z * (yp + Fv.w);
+            if (in) {
+                accD = fmaf(Wv.z, Fv.x, accD);
+                accBias += dd;
+            }
+            odu.e[e2] = IOT<IO>::from_f32(dui);
+            odd.e[e2] = IOT<IO>::from_f32(dd);
+            odz.e[e2] = IOT<IO>::from_f32(dzi);
         }
+        const int64_t t = t0 + e_seg * EPT;
+        store_seg<IO, EPT>(gdu + e_row, t, tend, e_ok, vec, odu);
+        store_seg<IO, EPT>(gdd + e_row, t, tend, e_ok, vec, odd);
+        if (write_dz) store_seg<IO, EPT>(gdz + e_row, t, tend, e_ok, vec, odz);
         for (int i = tid; i < 2 * int(p.N) * T; i += NT) {
             const int isC = i / (int(p.N) * T);
             const int rem = i % (int(p.N) * T);
-            const int n = rem / T, t = rem % T;
-            if (t0 + t < tend)
-                p.pBC[(((int64_t(cblk) * p.batch + b) * 2 + isC) * p.N + n) * p.L + t0 + t] = sdBC[(isC * NP + n) * T + t];
+            const int n = rem / T, tt = rem % T;
+            if (t0 + tt < tend)
+                p.pBC[(((int64_t(cblk) * p.batch + b) * 2 + isC) * p.N + n) * p.L + t0 + tt] = sdBC[(isC * NP + n) * T + tt];
         }
     };
 
@@ -556,19 +560,20 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
         }
     };
 
-    // ---- tile loop: stage, (settle the state loads), prefetch, walk, finish
+    // ---- tile loop: stage (from the prefetch), prefetch the next tile, walk, finish
     const int first = kRev ? ntiles - 1 : 0;
-    issue_loads(tbeg + int64_t(first) * T);
+    issue_loads(first);
     for (int i = 0; i < ntiles; ++i) {
         const int kt = kRev ? ntiles - 1 - i : i;
         const int64_t t0 = tbeg + int64_t(kt) * T;
         stage(t0);
-        // the previous walk's checkpoint prefetch and finish stores are old by now;
-        // settling them here keeps the walk from waiting on the next tile's prefetch
-        __builtin_amdgcn_s_waitcnt(0);
-        if (i + 1 < ntiles) issue_loads(tbeg + int64_t(kRev ? kt - 1 : kt + 1) * T);
+        if constexpr (kG) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) hst[j] = ckn[j];
+        }
+        if (i + 1 < ntiles) issue_loads(kRev ? kt - 1 : kt + 1);
         __syncthreads();
-        if constexpr (kG) grad_tile(kt);
+        if constexpr (kG) grad_tile();
         else if constexpr (MODE == kRevAgg) rev_tile();
         else fwd_tile(kt);
         __syncthreads();
@@ -598,22 +603,17 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 }
             }
         }
-        // per-channel sums of the TV threads of a channel, in vector order
-        float* fin = smem;   // [2][TV][64]
-#pragma unroll
-        for (int k = 0; k < KX; ++k) {
-            if (sv_on[k]) {
-                fin[sv_tv[k] * kLanes + sv_ch[k]] = accD[k];
-                fin[(TV + sv_tv[k]) * kLanes + sv_ch[k]] = accBias[k];
-            }
-        }
+        // per-channel sums of the G threads of a channel, in segment order
+        float* fin = smem;   // [2][G][64]
+        fin[e_seg * kLanes + e_ch] = accD;
+        fin[(G + e_seg) * kLanes + e_ch] = accBias;
         __syncthreads();
         if (tid < kLanes && c0 + tid < p.dim) {
             float sd = 0.0f, sb = 0.0f;
 #pragma unroll
-            for (int tv = 0; tv < TV; ++tv) {
-                sd += fin[tv * kLanes + tid];
-                sb += fin[(TV + tv) * kLanes + tid];
+            for (int sg = 0; sg < G; ++sg) {
+                sd += fin[sg * kLanes + tid];
+                sb += fin[(G + sg) * kLanes + tid];
             }
             const int64_t o = (int64_t(piece) * p.batch + b) * p.dim + c0 + tid;
             p.pD[o] = sd;
@@ -718,7 +718,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_heads_kernel(BwdParams p, floa
 
 // ------------------------------------------------------------------ host side
 struct BwdPlan {
-    int spl, G, nch;
+    int spl, G, nch, T;
     int64_t chunk_len, nblk_d, groups, ntiles_seq;
     size_t off_ck, off_bc, off_a, off_d, off_bias, off_fh, off_fs, off_fhin, off_rg, off_rs, off_rein, ws_bytes;
     size_t lds_grad, lds_fwd;
@@ -750,7 +750,9 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
     const int np = pl->G * spl;
     pl->nblk_d = cdiv(d->dim, kLanes);
     pl->groups = d->batch * pl->nblk_d;
-    pl->ntiles_seq = cdiv(d->seqlen, kT);
+    const int T = bwd_tile(np);
+    pl->T = T;
+    pl->ntiles_seq = cdiv(d->seqlen, T);
     int64_t nch = d->nchunks;
     if (nch == 0) {
         // below two waves per SIMD the sequence is cut into pieces (each piece costs a
@@ -763,7 +765,7 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
     }
     if (nch > pl->ntiles_seq) nch = pl->ntiles_seq;
     if (nch < 1) nch = 1;
-    pl->chunk_len = cdiv(pl->ntiles_seq, nch) * kT;
+    pl->chunk_len = cdiv(pl->ntiles_seq, nch) * T;
     pl->nch = int(cdiv(d->seqlen, pl->chunk_len));
     if (pl->groups * pl->nch > 0x7fffffffLL) return SSM_ERR_DIMS;
     const size_t f = sizeof(float);
@@ -872,7 +874,7 @@ int ssm_selective_scan_bwd_plan(const ssm_dims* dims, ssm_plan* plan) {
     plan->nchunks = pl.nch;
     plan->states_per_lane = pl.spl;
     plan->waves_per_group = pl.G;
-    plan->time_tile = kT;
+    plan->time_tile = pl.T;
     plan->chunk_len = pl.chunk_len;
     plan->workgroups = pl.groups * pl.nch;
     plan->workspace_bytes = pl.ws_bytes;
@@ -922,10 +924,12 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
         (reinterpret_cast<uintptr_t>(dims->workspace) % 256) != 0)
         return SSM_ERR_WORKSPACE;
 
-    const size_t vw = 16 / esz;
-    auto a16 = [](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) % 16) == 0; };
-    const bool vec = (dims->seqlen % int64_t(vw)) == 0 && a16(u) && a16(delta) && a16(z) && a16(B) && a16(C) &&
-                     a16(dy) && a16(grads->du) && a16(grads->ddelta) && a16(dz);
+    // each thread moves T/G consecutive elements of a row at once when the rows allow it
+    const int64_t ept = pl.T / pl.G;
+    const size_t seg = size_t(ept) * esz;
+    auto aligned = [seg](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) % seg) == 0; };
+    const bool vec = (dims->seqlen % ept) == 0 && aligned(u) && aligned(delta) && aligned(z) && aligned(dy) &&
+                     aligned(grads->du) && aligned(grads->ddelta) && aligned(dz);
 
     BwdParams p;
     p.u = u;
