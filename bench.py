@@ -65,9 +65,11 @@ def measured_traffic(launch_units: float):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, rows_batches: int):
+def cpu_baseline(x, rows_batches: int, repeats: int = 3):
     """Time the fp64 oracle on the first ``rows_batches`` batch rows (all channels,
-    the full sequence) of the same inputs, with all host threads OpenMP offers."""
+    the full sequence) of the same inputs, with all host threads OpenMP offers;
+    ``repeats`` runs, the median is reported."""
+    import statistics
     import numpy as np
     import oracle
 
@@ -76,13 +78,17 @@ def cpu_baseline(x, rows_batches: int):
     args = [np.ascontiguousarray(a[sl], dtype=np.float64) for a in (x.u, x.delta, x.B, x.C, x.z)]
     A = x.A_dense().astype(np.float64)
     threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    oracle.selective_scan_fwd(args[0], args[1], A, args[2], args[3], x.D, args[4], x.dt_bias, nthreads=threads)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.selective_scan_fwd(args[0], args[1], A, args[2], args[3], x.D, args[4], x.dt_bias, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
     updates = nb * x.L * x.dim * x.N
     return {"value": updates / dt, "unit": "state updates/s", "cores": threads, "kind": "oracle",
             "sample": f"batch rows 0..{nb - 1} of {x.batch} (all {x.dim} channels, full L={x.L}, N={x.N}); "
-                      f"{updates:.3e} updates in {dt:.2f} s wall on {threads} OpenMP threads, fp64"}
+                      f"{updates:.3e} updates, median of {repeats} runs {dt:.2f} s wall on {threads} OpenMP "
+                      f"threads (about {dt * threads * repeats:.0f} s of CPU time in all), fp64"}
 
 
 PROFILE_COMMANDS = {
@@ -279,7 +285,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="1..5; the reported line is workload 3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
-    ap.add_argument("--cpu-batches", type=int, default=2, help="batch rows in the oracle's timing sample")
+    ap.add_argument("--cpu-batches", type=int, default=4, help="batch rows in the oracle's timing sample")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 2 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs in DIR")
     args = ap.parse_args()
