@@ -72,7 +72,6 @@ struct BwdParams {
     int64_t L, dim, N, head_dim, chunk_len, ntiles_seq;
     int32_t nchunks, nblk_d, batch, np;
     int32_t piece_base;    // first piece index of the launch
-    int32_t vec;           // rows are 16-byte aligned: vector loads and stores
     float* ck;             // [groups][ntiles_seq][np][64]   tile start states
     float* pBC;            // [nblk_d][batch][2][N][L]       per-block dB (unscaled), dC
     float* pA;             // [nchunks][batch][dim][np]      per-piece dA / ln 2
@@ -117,37 +116,57 @@ inline size_t bwd_lds_floats(int G, int SPL, int mode) {
 // EPT consecutive elements of one row: one load or store of EPT*sizeof(IO) bytes when
 // the row is aligned for it (vec), else element by element.  Elements at or beyond
 // tend (or of a row that does not exist, ok == false) read as 0 and are not written.
-template <typename IO, int EPT> struct Seg {
-    IO e[EPT];
-};
-
 template <int BYTES> struct RawOf;
 template <> struct RawOf<2> { using T = uint16_t; };
 template <> struct RawOf<4> { using T = uint32_t; };
 template <> struct RawOf<8> { using T = uint2; };
 template <> struct RawOf<16> { using T = uint4; };
 
-template <typename IO, int EPT>
-__device__ inline Seg<IO, EPT> load_seg(const IO* __restrict__ row, int64_t t, int64_t tend, bool ok, bool vec) {
+// Output elements of one thread's segment.
+template <typename IO, int EPT> struct Seg {
+    IO e[EPT];
+};
+
+// Prefetched input elements of one thread's segment, kept as loaded (one raw word
+// when VEC) until the consumer unpacks them: unpacking right after the load would
+// make the compiler wait for it there.
+template <typename IO, int EPT, bool VEC> struct InSeg {
     using R = typename RawOf<EPT * int(sizeof(IO))>::T;
-    Seg<IO, EPT> v;
-    if (vec) {
-        R raw;
-        __builtin_memset(&raw, 0, sizeof(R));
-        if (ok && t < tend) raw = *reinterpret_cast<const R*>(row + t);
-        __builtin_memcpy(&v, &raw, sizeof(R));
+    R raw;
+    IO e[VEC ? 1 : EPT];
+    __device__ inline float get(int k) const {
+        if constexpr (VEC) {
+            IO t[EPT];
+            __builtin_memcpy(t, &raw, sizeof(R));
+            return IOT<IO>::to_f32(t[k]);
+        } else {
+            return IOT<IO>::to_f32(e[k]);
+        }
+    }
+};
+
+// Prefetch loads never branch and never inspect what they load: an element outside
+// the row's valid range is read from the row's start (always valid memory) and the
+// consumer masks it (stage tests the same range).  A load inside a branch, or a select
+// on its value right after it, makes the compiler wait for the load on the spot,
+// which would serialise the prefetch.
+template <typename IO, int EPT, bool VEC>
+__device__ inline InSeg<IO, EPT, VEC> load_seg(const IO* __restrict__ row, int64_t t, int64_t tend, bool ok) {
+    using R = typename RawOf<EPT * int(sizeof(IO))>::T;
+    InSeg<IO, EPT, VEC> v;
+    if constexpr (VEC) {
+        v.raw = *reinterpret_cast<const R*>(row + ((ok && t < tend) ? t : 0));
     } else {
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) v.e[e] = (ok && t + e < tend) ? row[t + e] : IO(0);
+        for (int e = 0; e < EPT; ++e) v.e[e] = row[(ok && t + e < tend) ? t + e : 0];
     }
     return v;
 }
 
-template <typename IO, int EPT>
-__device__ inline void store_seg(IO* __restrict__ row, int64_t t, int64_t tend, bool ok, bool vec,
-                                 const Seg<IO, EPT>& v) {
+template <typename IO, int EPT, bool VEC>
+__device__ inline void store_seg(IO* __restrict__ row, int64_t t, int64_t tend, bool ok, const Seg<IO, EPT>& v) {
     using R = typename RawOf<EPT * int(sizeof(IO))>::T;
-    if (vec) {
+    if constexpr (VEC) {
         if (ok && t < tend) {
             R raw;
             __builtin_memcpy(&raw, &v, sizeof(R));
@@ -165,13 +184,13 @@ __device__ inline float dpp_move(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-template <typename IO, int SPL, int G, bool SCALAR, int MODE>
+template <typename IO, int SPL, int G, bool SCALAR, int MODE, bool VEC>
 __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     using S = BShape<SPL, G>;
     constexpr int T = S::T, NP = S::NP, NT = S::NT, TS = S::TS, NSB = S::NSB;
     constexpr int JR = S::JR, RS = S::RS, NJR = S::NJR;
-    constexpr int EPT = T / G;                    // elements per thread and tile (each thread
-                                                  // takes EPT consecutive steps of one channel)
+    constexpr int EPT = T / G;                    // elements per thread and tile: wave w takes
+                                                  // steps w*EPT .. w*EPT+EPT-1 of all 64 channels
     constexpr int NBCV = 2 * NP * T;              // B and C values per tile
     constexpr int KB = (NBCV + NT - 1) / NT;      // of them per thread
     constexpr bool kG = MODE == kGrad;
@@ -206,7 +225,6 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     const int ntiles = int((tend - tbeg + T - 1) / T);
     const int64_t tile0 = tbeg / T;
     const bool has_z = kRev && p.z != nullptr;
-    const bool vec = p.vec != 0;
 
     const IO* __restrict__ gu = static_cast<const IO*>(p.u);
     const IO* __restrict__ gdl = static_cast<const IO*>(p.delta);
@@ -227,9 +245,11 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     }
     const int64_t state_base = ((blk * p.nchunks + piece) * NP + int64_t(w) * SPL) * kLanes + lane;
 
-    // ---- element constants: thread tid takes steps e_seg*EPT .. +EPT-1 of channel e_ch
-    const int e_ch = tid / G;
-    const int e_seg = tid % G;
+    // ---- element constants: thread tid takes steps e_seg*EPT .. +EPT-1 of channel e_ch.
+    //      Lane = channel keeps every LDS access of staging and finishing free of bank
+    //      conflicts; each global access then moves EPT elements of 64 different rows.
+    const int e_ch = lane;
+    const int e_seg = w;
     const int64_t e_d = c0 + e_ch;
     const bool e_ok = e_d < p.dim;
     const float e_bias = (e_ok && p.bias) ? p.bias[e_d] : 0.0f;
@@ -255,7 +275,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
 
     // ---- prefetch registers (one tile ahead): checkpoint entries first, so that the
     //      wait for a tile's staging data also covers them
-    Seg<IO, EPT> nu, ndl, nz, ndy;
+    InSeg<IO, EPT, VEC> nu, ndl, nz, ndy;
     IO nbc[KB];
     float ckn[SPL];
 #pragma unroll
@@ -268,14 +288,14 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
             for (int j = 0; j < SPL; ++j) ckn[j] = ck[int64_t(j) * kLanes];
         }
         const int64_t t = t0 + e_seg * EPT;
-        if constexpr (kUseU) nu = load_seg<IO, EPT>(gu + e_row, t, tend, e_ok, vec);
-        ndl = load_seg<IO, EPT>(gdl + e_row, t, tend, e_ok, vec);
+        if constexpr (kUseU) nu = load_seg<IO, EPT, VEC>(gu + e_row, t, tend, e_ok);
+        ndl = load_seg<IO, EPT, VEC>(gdl + e_row, t, tend, e_ok);
         if constexpr (kRev) {
-            ndy = load_seg<IO, EPT>(gdy + e_row, t, tend, e_ok, vec);
-            if (has_z) nz = load_seg<IO, EPT>(gz + e_row, t, tend, e_ok, vec);
+            ndy = load_seg<IO, EPT, VEC>(gdy + e_row, t, tend, e_ok);
+            nz = load_seg<IO, EPT, VEC>((has_z ? gz : gdy) + e_row, t, tend, e_ok && has_z);
         }
 #pragma unroll
-        for (int k = 0; k < KB; ++k) nbc[k] = (bc_ok[k] && t0 + bc_t[k] < tend) ? bc_ptr[k][t0] : IO(0);
+        for (int k = 0; k < KB; ++k) nbc[k] = *((bc_ok[k] && t0 + bc_t[k] < tend) ? bc_ptr[k] + t0 : gB);
     };
 
     // ---- registers -> LDS for the tile starting at t0.  Steps beyond the piece's end
@@ -284,15 +304,15 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const int tl = e_seg * EPT + e;
-            const bool in = e_ok && t0 + tl < tend;
-            const float uu = kUseU ? IOT<IO>::to_f32(nu.e[e]) : 0.0f;
-            const float r = IOT<IO>::to_f32(ndl.e[e]) + e_bias;
+            const bool in = e_ok && t0 + tl < tend;   // else the prefetched value is not this element's
+            const float uu = (kUseU && in) ? nu.get(e) : 0.0f;
+            const float r = in ? ndl.get(e) + e_bias : 0.0f;
             const float dt2 = in ? softplus_log2(r) : 0.0f;
             const float decay = SCALAR ? __builtin_amdgcn_exp2f(dt2 * e_ah) : 0.0f;
             float ds = 0.0f, dyv = 0.0f, zz = 0.0f;
             if constexpr (kRev) {
-                dyv = in ? IOT<IO>::to_f32(ndy.e[e]) : 0.0f;
-                zz = has_z ? IOT<IO>::to_f32(nz.e[e]) : 0.0f;
+                dyv = in ? ndy.get(e) : 0.0f;
+                zz = (has_z && in) ? nz.get(e) : 0.0f;
                 ds = has_z ? dyv * silu_f32(zz) : dyv;
             }
             const int idx = tl * kLanes + e_ch;
@@ -303,8 +323,10 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
             }
         }
 #pragma unroll
-        for (int k = 0; k < KB; ++k)
-            if (bc_on[k]) sBC[bc_slot[k]] = IOT<IO>::to_f32(nbc[k]) * ((bc_slot[k] & 1) ? 1.0f : kLn2);
+        for (int k = 0; k < KB; ++k) {
+            const bool in = bc_ok[k] && t0 + bc_t[k] < tend;
+            if (bc_on[k]) sBC[bc_slot[k]] = in ? IOT<IO>::to_f32(nbc[k]) * ((bc_slot[k] & 1) ? 1.0f : kLn2) : 0.0f;
+        }
     };
 
     // ---- per-lane LDS reads of one step
@@ -381,12 +403,13 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     //      step t_base + s and state entry w*SPL + j0 + jj.  The values go to LDS as
     //      [v][lane]; lane 8o+q then sums lanes 8q..8q+7 of value o, and the 8 lanes of
     //      an output combine their partials with DPP (quad swaps, then the half-row
-    //      mirror), so every lane of the group holds the same total.
+    //      mirror), so every lane of the group holds the same total.  A wave's LDS
+    //      operations complete in issue order, so the reads see this round's writes and
+    //      the next round's writes cannot overtake these reads.
     float* red = sRed + w * kRound * kLanes;
     auto flush = [&](const float (&pv)[kRound], int t_base, int j0) {
 #pragma unroll
         for (int v = 0; v < kRound; ++v) red[v * kLanes + lane] = pv[v];
-        __builtin_amdgcn_wave_barrier();
         const int o = lane >> 3, q = lane & 7;
         const float4* rr = reinterpret_cast<const float4*>(red + o * kLanes + q * 8);
         const float4 a0 = rr[0], a1 = rr[1];
@@ -394,27 +417,44 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
         sum += dpp_move<0xB1>(sum);    // quad_perm [1,0,3,2]: lanes 0<->1, 2<->3
         sum += dpp_move<0x4E>(sum);    // quad_perm [2,3,0,1]: lanes 0<->2, 1<->3
         sum += dpp_move<0x141>(sum);   // row_half_mirror: lane i <-> 7-i of each 8
-        __builtin_amdgcn_wave_barrier();
         if (q == 0) {
             const int s = o / (2 * JR), isC = (o / JR) % 2, jj = o % JR;
             sdBC[(isC * NP + w * SPL + j0 + jj) * T + t_base + s] = sum;
         }
     };
 
-    // ---- the gradient walk of one tile (all waves); hst holds the tile's start state
+    // ---- the gradient walk of one tile (all waves); hst holds the tile's start state.
+    //      Both walks read the LDS operands of the next step before the arithmetic of
+    //      the current one, so that the LDS latency overlaps the work.
+    struct StepOps {
+        float4 W;
+        float Bv[SPL], Cv[SPL];
+    };
+    auto read_step = [&](int t, StepOps& o) {
+        o.W = swl[t * kLanes];
+        read_bc(t, o.Bv, o.Cv);
+    };
     auto grad_tile = [&]() {
         float hsb[NSB > 1 ? NSB - 1 : 1][SPL];
         if constexpr (NSB > 1) {
-            float hh[SPL], Bv[SPL], Cv[SPL];
-            float4 W;
+            float hh[SPL];
 #pragma unroll
             for (int j = 0; j < SPL; ++j) hh[j] = hst[j];
+            StepOps cur, nxt;
+            read_step(0, cur);
 #pragma unroll
-            for (int sb = 0; sb < NSB - 1; ++sb) {
+            for (int t = 0; t < (NSB - 1) * TS; ++t) {
+                if (t + 1 < (NSB - 1) * TS) read_step(t + 1, nxt);
 #pragma unroll
-                for (int ts = 0; ts < TS; ++ts) fwd_step(sb * TS + ts, hh, Bv, Cv, W);
+                for (int j = 0; j < SPL; ++j) {
+                    const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[j]);
+                    hh[j] = fmaf(a, hh[j], cur.W.y * cur.Bv[j]);
+                }
+                if ((t + 1) % TS == 0) {
 #pragma unroll
-                for (int j = 0; j < SPL; ++j) hsb[sb][j] = hh[j];
+                    for (int j = 0; j < SPL; ++j) hsb[t / TS][j] = hh[j];
+                }
+                cur = nxt;
             }
         }
 #pragma unroll
@@ -424,48 +464,52 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int j = 0; j < SPL; ++j) hb[j] = (sb == 0) ? hst[j] : hsb[sb > 0 ? sb - 1 : 0][j];
             {
-                float hh[SPL], Bv[SPL], Cv[SPL];
-                float4 W;
+                float hh[SPL];
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) hh[j] = hb[j];
+                StepOps cur, nxt;
+                read_step(sb * TS, cur);
 #pragma unroll
                 for (int ts = 0; ts < TS; ++ts) {
                     const int t = sb * TS + ts;
-                    fwd_step(t, hh, Bv, Cv, W);
+                    if (ts + 1 < TS) read_step(t + 1, nxt);
                     float yp = 0.0f;
 #pragma unroll
                     for (int j = 0; j < SPL; ++j) {
+                        const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[j]);
+                        hh[j] = fmaf(a, hh[j], cur.W.y * cur.Bv[j]);
                         H[ts][j] = hh[j];
-                        yp = fmaf(Cv[j], hh[j], yp);
+                        yp = fmaf(cur.Cv[j], hh[j], yp);
                     }
                     sP[(w * T + t) * kLanes + lane] = yp;
+                    cur = nxt;
                 }
             }
             // re-read the step operands from LDS below rather than keeping the forward
             // recompute's copies of a whole sub-block live in VGPRs
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             float pv[kRound];
+            StepOps cur, nxt;
+            read_step(sb * TS + TS - 1, cur);
 #pragma unroll
             for (int ts = TS - 1; ts >= 0; --ts) {
                 const int t = sb * TS + ts;
-                const float4 W = swl[t * kLanes];
-                float Bv[SPL], Cv[SPL];
-                read_bc(t, Bv, Cv);
+                if (ts > 0) read_step(t - 1, nxt);
                 float s1 = 0.0f, s2 = 0.0f;
                 const int s = ts % RS;
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) {
-                    const float a = SCALAR ? W.w : __builtin_amdgcn_exp2f(W.x * Ar[j]);
+                    const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[j]);
                     const float hp = ts > 0 ? H[ts > 0 ? ts - 1 : 0][j] : hb[j];
-                    const float g = fmaf(W.z, Cv[j], e[j]);
+                    const float g = fmaf(cur.W.z, cur.Cv[j], e[j]);
                     const float t1 = g * (a * hp);
-                    dAacc[j] = fmaf(W.x, t1, dAacc[j]);
+                    dAacc[j] = fmaf(cur.W.x, t1, dAacc[j]);
                     s1 = fmaf(Ar[j], t1, s1);
-                    s2 = fmaf(g, Bv[j], s2);
+                    s2 = fmaf(g, cur.Bv[j], s2);
                     e[j] = a * g;
                     const int jj = j % JR;
-                    pv[(s * 2) * JR + jj] = g * W.y;              // dB (unscaled)
-                    pv[(s * 2 + 1) * JR + jj] = W.z * H[ts][j];   // dC
+                    pv[(s * 2) * JR + jj] = g * cur.W.y;              // dB (unscaled)
+                    pv[(s * 2 + 1) * JR + jj] = cur.W.z * H[ts][j];   // dC
                     if constexpr (NJR > 1) {
                         if (jj == JR - 1) flush(pv, t, j - jj);
                     }
@@ -475,6 +519,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 if constexpr (NJR == 1) {
                     if (s == 0) flush(pv, t, 0);
                 }
+                cur = nxt;
             }
         }
     };
@@ -516,9 +561,9 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
             odz.e[e2] = IOT<IO>::from_f32(dzi);
         }
         const int64_t t = t0 + e_seg * EPT;
-        store_seg<IO, EPT>(gdu + e_row, t, tend, e_ok, vec, odu);
-        store_seg<IO, EPT>(gdd + e_row, t, tend, e_ok, vec, odd);
-        if (write_dz) store_seg<IO, EPT>(gdz + e_row, t, tend, e_ok, vec, odz);
+        store_seg<IO, EPT, VEC>(gdu + e_row, t, tend, e_ok, odu);
+        store_seg<IO, EPT, VEC>(gdd + e_row, t, tend, e_ok, odd);
+        if (write_dz) store_seg<IO, EPT, VEC>(gdz + e_row, t, tend, e_ok, odz);
         for (int i = tid; i < 2 * int(p.N) * T; i += NT) {
             const int isC = i / (int(p.N) * T);
             const int rem = i % (int(p.N) * T);
@@ -604,7 +649,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
             }
         }
         // per-channel sums of the G threads of a channel, in segment order
-        float* fin = smem;   // [2][G][64]
+        float* fin = smem;   // [2][G][64], the segment index is the wave index
         fin[e_seg * kLanes + e_ch] = accD;
         fin[(G + e_seg) * kLanes + e_ch] = accBias;
         __syncthreads();
@@ -747,6 +792,7 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
     if (g > 8) return SSM_ERR_DIMS;
     pl->spl = spl;
     pl->G = g <= 4 ? 4 : 8;
+    if ((pl->G == 4 && spl > 4) || (pl->G == 8 && spl < 2)) return SSM_ERR_DIMS;   // no such kernel
     const int np = pl->G * spl;
     pl->nblk_d = cdiv(d->dim, kLanes);
     pl->groups = d->batch * pl->nblk_d;
@@ -803,7 +849,7 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
     return SSM_OK;
 }
 
-template <typename IO, int SPL, int G, bool SCALAR>
+template <typename IO, int SPL, int G, bool SCALAR, bool VEC>
 hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, float* dA, float* dB, float* dC, float* dD, float* dbias,
                       hipStream_t s) {
     const dim3 block(unsigned(G * kLanes));
@@ -811,9 +857,9 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, float* dA, float* dB, floa
     if (pl.nch > 1) {
         const dim3 grid1(unsigned(groups * (pl.nch - 1)));
         p.piece_base = 0;
-        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kFwdAgg>), grid1, block, pl.lds_fwd, s, p);
+        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kFwdAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
         p.piece_base = 1;
-        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kRevAgg>), grid1, block, pl.lds_fwd, s, p);
+        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kRevAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
         p.piece_base = 0;
         const int64_t total = groups * p.np * kLanes;
         const dim3 gridc(unsigned(cdiv(total, 256)));
@@ -822,8 +868,8 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, float* dA, float* dB, floa
     }
     p.piece_base = 0;
     const dim3 grid(unsigned(groups * pl.nch));
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt>), grid, block, pl.lds_fwd, s, p);
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kGrad>), grid, block, pl.lds_grad, s, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt, VEC>), grid, block, pl.lds_fwd, s, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kGrad, VEC>), grid, block, pl.lds_grad, s, p);
     const int64_t nbc = int64_t(p.batch) * 2 * p.N * p.L;
     hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned(cdiv(nbc, 256))), dim3(256), 0, s, p, dB, dC, nbc);
     const int64_t npar = p.dim * p.N;
@@ -836,23 +882,29 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, float* dA, float* dB, floa
     return hipGetLastError();
 }
 
-template <typename IO, bool SCALAR>
-hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, float* dA, float* dB, float* dC, float* dD,
-                        float* dbias, hipStream_t s) {
+// The (entries per lane, waves) pairs the planner produces: 1..4 entries with 4 waves
+// (dstate <= 16, or forced), and 2..16 entries with 8 waves.
+template <typename IO, bool SCALAR, bool VEC>
+hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, float* dA, float* dB, float* dC, float* dD,
+                            float* dbias, hipStream_t s) {
 #define SSM_BWD_CASE(S_, G_)                                                              \
-    if (pl.spl == S_ && pl.G == G_) return bwd_launch<IO, S_, G_, SCALAR>(p, pl, dA, dB, dC, dD, dbias, s);
+    if (pl.spl == S_ && pl.G == G_) return bwd_launch<IO, S_, G_, SCALAR, VEC>(p, pl, dA, dB, dC, dD, dbias, s);
     SSM_BWD_CASE(1, 4)
     SSM_BWD_CASE(2, 4)
     SSM_BWD_CASE(4, 4)
-    SSM_BWD_CASE(8, 4)
-    SSM_BWD_CASE(16, 4)
-    SSM_BWD_CASE(1, 8)
     SSM_BWD_CASE(2, 8)
     SSM_BWD_CASE(4, 8)
     SSM_BWD_CASE(8, 8)
     SSM_BWD_CASE(16, 8)
 #undef SSM_BWD_CASE
     return hipErrorInvalidConfiguration;
+}
+
+template <typename IO, bool SCALAR>
+hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, bool vec, float* dA, float* dB, float* dC,
+                        float* dD, float* dbias, hipStream_t s) {
+    return vec ? bwd_dispatch_vec<IO, SCALAR, true>(p, pl, dA, dB, dC, dD, dbias, s)
+               : bwd_dispatch_vec<IO, SCALAR, false>(p, pl, dA, dB, dC, dD, dbias, s);
 }
 
 }  // namespace
@@ -958,7 +1010,6 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     p.batch = int32_t(dims->batch);
     p.np = pl.G * pl.spl;
     p.piece_base = 0;
-    p.vec = vec ? 1 : 0;
     char* ws = static_cast<char*>(dims->workspace);
     auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
     p.ck = at(pl.off_ck);
@@ -979,11 +1030,11 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     const bool scalar = dims->nheads > 0;
     hipError_t e;
     if (dims->io_dtype == SSM_BF16)
-        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
-                   : bwd_dispatch<uint16_t, false>(p, pl, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, vec, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<uint16_t, false>(p, pl, vec, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
     else
-        e = scalar ? bwd_dispatch<float, true>(p, pl, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
-                   : bwd_dispatch<float, false>(p, pl, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+        e = scalar ? bwd_dispatch<float, true>(p, pl, vec, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<float, false>(p, pl, vec, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -241,7 +241,9 @@ def test_backward_refusals():
     big = _bwd_dims(1, 100, 64, 129)
     assert _bwd(big) == ssm.SSM_ERR_DIMS
     assert ssm.ssm_selective_scan_bwd_workspace_bytes(ssm.make_dims(1, 100, 64, 129)) == 0
-    assert _bwd(_bwd_dims(1, 100, 64, 64, states_per_lane=4)) == ssm.SSM_ERR_DIMS
+    assert _bwd(_bwd_dims(1, 100, 64, 64, states_per_lane=4)) == ssm.SSM_ERR_DIMS   # 16 waves
+    assert _bwd(_bwd_dims(1, 100, 64, 16, states_per_lane=8)) == ssm.SSM_ERR_DIMS   # 8 per lane on 4 waves
+    assert _bwd(_bwd_dims(1, 100, 64, 8, states_per_lane=1)) == ssm.SSM_ERR_DIMS    # 1 per lane on 8 waves
     # workspace missing or short
     short = _bwd_dims(2, 100, 70, 16)
     short.workspace_bytes -= 4

@@ -65,8 +65,8 @@ CASES = [
     # forced states per lane
     (1, 80, 64, 4, "f32", 0, True, False, False, 0, 1),
     (1, 80, 64, 16, "f32", 0, True, False, False, 0, 4),
-    (1, 80, 64, 16, "f32", 0, True, False, False, 0, 8),
-    (1, 80, 64, 16, "f32", 0, True, False, False, 0, 16),
+    (1, 80, 64, 40, "f32", 0, True, False, False, 0, 8),
+    (1, 80, 64, 100, "f32", 0, True, False, False, 0, 16),
     (1, 77, 64, 24, "bf16", 0, True, True, True, 0, 4),
 ]
 
