@@ -71,6 +71,8 @@ def _load():
         lib.oracle_sigmoid.restype = ctypes.c_double
         lib.oracle_selective_scan_bwd.argtypes = [i64, i64, i64, i64] + [dp] * 20 + [ctypes.c_int]
         lib.oracle_selective_scan_bwd.restype = ctypes.c_int
+        lib.oracle_causal_conv1d.argtypes = [i64, i64, i64, i64] + [dp] * 4 + [ctypes.c_int] + [dp] * 2
+        lib.oracle_causal_conv1d.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -219,3 +221,26 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, dy=None,
     if code != OK:
         raise OracleError(code, "selective_scan_bwd")
     return out
+
+
+def causal_conv1d(x, w, bias=None, state=None, silu=True):
+    """fp64 causal depthwise convolution (width K = w.shape[1]) with optional SiLU.
+
+    x (batch, dim, L); w (dim, K); bias (dim,); state (batch, dim, K-1) = the inputs
+    before the sequence, oldest first (None = zeros).  Returns (out, state_out) with
+    state_out the last K-1 inputs (the history a following call continues from)."""
+    x, w, bias, state = _f64(x), _f64(w), _f64(bias), _f64(state)
+    batch, dim, L = x.shape
+    K = w.shape[1]
+    if w.shape != (dim, K) or (bias is not None and bias.shape != (dim,)):
+        raise ValueError("w must be (dim, K) and bias (dim,)")
+    if state is not None and state.shape != (batch, dim, K - 1):
+        raise ValueError("state must be (batch, dim, K-1)")
+    out = np.zeros((batch, dim, L))
+    st = np.zeros((batch, dim, max(K - 1, 1)))
+    code = _load().oracle_causal_conv1d(batch, L, dim, K, _ptr(x), _ptr(w), _ptr(bias),
+                                        _ptr(state) if K > 1 else None, int(bool(silu)), _ptr(out),
+                                        _ptr(st) if K > 1 else None)
+    if code != OK:
+        raise OracleError(code, "causal_conv1d")
+    return out, st[..., : K - 1]

@@ -395,3 +395,53 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N,
     free(acc);
     return OR_OK;
 }
+
+/*
+ * Causal depthwise convolution of the scan's input, the "local convolution" that a
+ * real Mamba layer places before the scan ([QT], the remark after the runnable
+ * scalar model), with an optional SiLU (the activation [GS] §3.1 uses in the block).
+ * Per row (b, d) and t = 0 .. L-1, with width K:
+ *     pre[t] = bias[d] + sum_{k=0}^{K-1} w[d,k] * xs(t - (K-1) + k)
+ *     out[t] = SiLU(pre[t]) if silu else pre[t]
+ * where xs(s) = x[b,d,s] for s >= 0 and, for s < 0, the carried history
+ * state[b,d,(K-1)+s] (the K-1 inputs before the sequence, oldest first), or 0 without a
+ * state.  The conv state is part of what recurrent decoding keeps per layer ([QT],
+ * the paragraph on inference memory).  state_out (nullable) receives the K-1 inputs
+ * xs(L-K+1) .. xs(L-1), the history the next call continues from.
+ * Layouts: x, out (batch, dim, L); w (dim, K); bias (dim,) nullable; state, state_out
+ * (batch, dim, K-1).  K must be 1 .. 8.  Non-finite inputs are refused.
+ */
+int oracle_causal_conv1d(int64_t batch, int64_t L, int64_t dim, int64_t K, const double* x, const double* w,
+                         const double* bias, const double* state, int silu, double* out, double* state_out)
+{
+    if (batch <= 0 || L <= 0 || dim <= 0) return OR_ERR_EMPTY;
+    if (K < 1 || K > 8) return OR_ERR_EMPTY;
+    if (!x || !w || !out) return OR_ERR_NULL;
+    const int64_t H = K - 1;
+    if (!all_finite(x, batch * dim * L) || !all_finite(w, dim * K) || (bias && !all_finite(bias, dim)) ||
+        (state && H > 0 && !all_finite(state, batch * dim * H)))
+        return OR_ERR_NONFINITE;
+    for (int64_t r = 0; r < batch * dim; ++r) {
+        const int64_t d = r % dim;
+        for (int64_t t = 0; t < L; ++t) {
+            double acc = bias ? bias[d] : 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t s = t - H + k;
+                double xv = 0.0;
+                if (s >= 0) xv = x[r * L + s];
+                else if (state) xv = state[r * H + (H + s)];
+                acc += w[d * K + k] * xv;
+            }
+            out[r * L + t] = silu ? oracle_silu(acc) : acc;
+        }
+        if (state_out)
+            for (int64_t j = 0; j < H; ++j) {
+                const int64_t s = L - H + j;
+                double xv = 0.0;
+                if (s >= 0) xv = x[r * L + s];
+                else if (state) xv = state[r * H + (H + s)];
+                state_out[r * H + j] = xv;
+            }
+    }
+    return OR_OK;
+}
