@@ -219,6 +219,81 @@ def decode_step_bench(batch: int, steps: int = 200, warmup: int = 50):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
 
 
+def fused_conv_bench(x, dev, width: int = 4, steps: int = 100, warmup: int = 30):
+    """Time ssm_selective_scan_fwd_conv on the same inputs (u taken as the
+    convolution's input x, a width-`width` SiLU front end, u not written out) and the
+    fused decode step (convolution history + scan state updated in place)."""
+    import torch
+    import selective_state_space_79_amd as ssm
+    from selective_state_space_79_amd.inputs import io_to_device, make_conv, make_inputs
+
+    w, bb, _ = make_conv(x, width, seed=62)
+    wt, bt = torch.from_numpy(w).cuda(), torch.from_numpy(bb).cuda()
+    conv = ssm.SsmConv(wt.data_ptr(), bt.data_ptr(), width, 1)
+    y = torch.empty_like(dev["u"])
+    dims = ssm.dims_for(dev["u"], dev["B"], dev["A"])
+    stream = torch.cuda.current_stream()
+    p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    args = (p(dev["u"]), ctypes.byref(conv), None, p(dev["delta"]), p(dev["A"]), p(dev["B"]), p(dev["C"]),
+            p(dev["D"]), p(dev["z"]), p(dev["dt_bias"]), None, None, p(y), None, ctypes.byref(dims),
+            ctypes.c_void_p(stream.cuda_stream))
+    fn = ssm.load_library().ssm_selective_scan_fwd_conv
+
+    def timed(call, n, nw):
+        for _ in range(nw):
+            st = call()
+            if st != 0:
+                raise ssm.SsmError(st, "fused conv")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(lambda: fn(*args), steps, warmup)
+    nbytes = algorithmic_bytes(x) + 4 * x.dim * (width + 1)
+    out = {"workload": f"{x.batch}x{x.L}x{x.dim}, N {x.N}, {x.io} I/O, width-{width} SiLU front end fused",
+           "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3),
+           "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": nbytes}
+    decode = []
+    for batch in (64, 256):
+        xd = make_inputs(batch, 1, x.dim, x.N, seed=63, io=x.io)
+        dd = {k: v for k, v in to_device_cols(xd).items()}
+        wd, bd, st = make_conv(xd, width, seed=64, with_state=True)
+        cst = io_to_device(xd, st)
+        h = torch.zeros((batch, x.dim, x.N), dtype=torch.float32, device="cuda:0")
+        yd = torch.empty_like(dd["u"])
+        wdt, bdt = torch.from_numpy(wd).cuda(), torch.from_numpy(bd).cuda()
+        cv = ssm.SsmConv(wdt.data_ptr(), bdt.data_ptr(), width, 1)
+        sd = ssm.make_dims(batch, 1, x.dim, x.N, io_dtype=ssm.SSM_BF16 if x.io == "bf16" else ssm.SSM_F32)
+        a2 = (p(dd["u"]), ctypes.byref(cv), p(cst), p(dd["delta"]), p(dev["A"]), p(dd["B"]), p(dd["C"]), p(dev["D"]),
+              p(dd["z"]), p(dev["dt_bias"]), p(h), None, p(yd), ctypes.byref(sd), ctypes.c_void_p(stream.cuda_stream))
+        f2 = ssm.load_library().ssm_selective_scan_step_conv
+        us = timed(lambda: f2(*a2), 200, 50) * 1e3
+        esz = 2 if x.io == "bf16" else 4
+        # state read and written; A; x, delta, z read and y written; B, C; D, dt_bias;
+        # the convolution history read and written; its weights and bias
+        nb = (8 * batch * x.dim * x.N + 4 * x.dim * x.N + 4 * esz * batch * x.dim + 2 * esz * batch * x.N
+              + 8 * x.dim + 2 * esz * batch * x.dim * (width - 1) + 4 * x.dim * (width + 1))
+        decode.append({"sequences": batch, "us_per_step": round(us, 3), "tokens_per_s": round(batch / (us * 1e-6), 1),
+                       "gbs": round(nb / (us * 1e-6) / 1e9, 1), "hbm_frac": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "algorithmic_bytes": nb})
+    out["decode_step"] = decode
+    return out
+
+
+def to_device_cols(xd):
+    """Device tensors of a one-token input set, the token axis dropped: (batch, dim)
+    and (batch, N)."""
+    from selective_state_space_79_amd.inputs import to_device
+
+    dev = to_device(xd, "cuda:0")
+    return {k: (dev[k][..., 0].contiguous() if k in ("u", "delta", "z", "B", "C") else dev[k]) for k in dev}
+
+
 # minimal VALU operations per state update of the backward pass: the forward recompute
 # with its read-out (mul, exp2, mul, fma, fma), the reverse step (g = ds*C + e: fma;
 # e = a*g: mul; a*h_prev: mul; g*(a*h_prev): mul; dA, sum A*.., sum g*B: 3 fma;
@@ -397,6 +472,8 @@ def main():
     }
     if args.workload == 3:
         rec["decode_step"] = [decode_step_bench(64), decode_step_bench(256)]
+    if args.workload == 3:
+        rec["fused_conv"] = fused_conv_bench(x, dev)
     if not args.no_backward:
         rec["backward"] = backward_bench(x, dev)
     if not args.no_cpu_baseline:

@@ -135,6 +135,49 @@ SSM_API int ssm_selective_scan_step(const void* u, const void* delta, const floa
                                     const float* D, const void* z, const float* dt_bias, float* h, void* y,
                                     const ssm_dims* dims, void* stream);
 
+/* The fused front end: a causal depthwise convolution of the scan's input, the "local
+ * convolution" a real Mamba layer places before the scan (qubittool.com
+ * "Mamba 与状态空间模型：机制、演进与工程选型", the remark after the runnable scalar
+ * model), optionally followed by SiLU.  With x the convolution's input, per batch row b,
+ * channel d and step t:
+ *     u[b,d,t] = act(bias[d] + sum_{k=0}^{width-1} weight[d,k] * x[b,d,t-width+1+k])
+ * where x before the first step is the carried history (conv_state, the width-1 inputs
+ * before the sequence, oldest first) or 0.  The conv state is part of the per-layer
+ * state recurrent decoding keeps (the same page, on inference memory).
+ *   weight: float32 (dim, width), required;  bias: float32 (dim,), nullable;
+ *   width: 1 .. 4;  silu: 1 = SiLU after the convolution, 0 = none. */
+typedef struct ssm_conv {
+    const float* weight;
+    const float* bias;
+    int32_t width;
+    int32_t silu;
+} ssm_conv;
+
+/* ssm_selective_scan_fwd_state on u = act(conv(x)): x (batch, dim, seqlen) in io_dtype
+ * takes the place of u; conv_state (batch, dim, width-1) in io_dtype is the history
+ * before x (nullable: zeros).  u is formed inside the scan's staging in float32 and is
+ * not rounded before the scan; u_out (nullable, (batch, dim, seqlen) in io_dtype)
+ * receives it rounded to io_dtype.  The state after this call's last input, for a
+ * following call, is the last width-1 columns of x (with the history when seqlen <
+ * width-1).  Same workspace, layouts and rules as the plain forward; u_out may overlap
+ * no other array.  conv NULL gives SSM_ERR_NULL, a width outside 1..4 or silu not 0/1
+ * SSM_ERR_DIMS. */
+SSM_API int ssm_selective_scan_fwd_conv(const void* x, const ssm_conv* conv, const void* conv_state, const void* delta,
+                                        const float* A, const void* B, const void* C, const float* D, const void* z,
+                                        const float* dt_bias, const float* h0, void* u_out, void* y, float* h_last,
+                                        const ssm_dims* dims, void* stream);
+
+/* One decoding step of the fused front end and the scan: x (batch, dim) in io_dtype is
+ * the new input; conv_state (batch, dim, width-1) in io_dtype holds the previous
+ * width-1 inputs, oldest first, and is shifted in place (required when width > 1);
+ * u = act(conv) feeds the step exactly as u does in ssm_selective_scan_step (h updated
+ * in place, y written); u_out (nullable) receives u rounded to io_dtype.  Equal, step
+ * by step, to ssm_selective_scan_fwd_conv over the same inputs. */
+SSM_API int ssm_selective_scan_step_conv(const void* x, const ssm_conv* conv, void* conv_state, const void* delta,
+                                         const float* A, const void* B, const void* C, const float* D, const void* z,
+                                         const float* dt_bias, float* h, void* u_out, void* y, const ssm_dims* dims,
+                                         void* stream);
+
 /* Largest dstate the backward pass accepts. */
 #define SSM_MAX_DSTATE_BWD 128
 

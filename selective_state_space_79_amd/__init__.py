@@ -37,7 +37,8 @@ SSM_MAX_CHUNKS = 1024
 
 EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_fwd_state", "ssm_selective_scan_step",
             "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan", "ssm_status_string",
-            "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd_plan")
+            "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd_plan",
+            "ssm_selective_scan_fwd_conv", "ssm_selective_scan_step_conv")
 SSM_MAX_DSTATE_BWD = 128
 
 
@@ -81,6 +82,12 @@ class SsmGrads(ctypes.Structure):
                 ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddt_bias", "dh0")]
 
 
+class SsmConv(ctypes.Structure):
+    """Mirror of ``ssm_conv`` in include/ssm.h."""
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("width", ctypes.c_int32),
+                ("silu", ctypes.c_int32)]
+
+
 class SsmError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {ssm_status_string(status)} (status {status})")
@@ -114,6 +121,10 @@ def load_library():
         lib.ssm_selective_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.ssm_selective_scan_bwd_plan.argtypes = [ctypes.POINTER(SsmDims), ctypes.POINTER(SsmPlan)]
         lib.ssm_selective_scan_bwd_plan.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd_conv.argtypes = [vp, ctypes.POINTER(SsmConv)] + [vp] * 12 + [ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_fwd_conv.restype = ctypes.c_int
+        lib.ssm_selective_scan_step_conv.argtypes = [vp, ctypes.POINTER(SsmConv)] + [vp] * 11 + [ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_step_conv.restype = ctypes.c_int
         lib.ssm_status_string.argtypes = [ctypes.c_int]
         lib.ssm_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -324,3 +335,86 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, dy, h
     if st != SSM_OK:
         raise SsmError(st, "ssm_selective_scan_bwd")
     return out
+
+
+def _conv_struct(weight, bias, silu):
+    return SsmConv(weight.data_ptr(), bias.data_ptr() if bias is not None else None, weight.shape[1], int(bool(silu)))
+
+
+def ssm_selective_scan_fwd_conv(x, conv: SsmConv, conv_state, delta, A, B, C, D, z, dt_bias, h0, u_out, y, h_last,
+                                dims: SsmDims, stream=None) -> int:
+    """C entry point of the scan with the fused convolution front end; returns the status."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    return int(load_library().ssm_selective_scan_fwd_conv(
+        _ptr(x), ctypes.byref(conv), _ptr(conv_state), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(dt_bias), _ptr(h0), _ptr(u_out), _ptr(y), _ptr(h_last), ctypes.byref(dims),
+        ctypes.c_void_p(stream.cuda_stream)))
+
+
+def ssm_selective_scan_step_conv(x, conv: SsmConv, conv_state, delta, A, B, C, D, z, dt_bias, h, u_out, y,
+                                 dims: SsmDims, stream=None) -> int:
+    """C entry point of one fused convolution + scan decoding step; returns the status."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    return int(load_library().ssm_selective_scan_step_conv(
+        _ptr(x), ctypes.byref(conv), _ptr(conv_state), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(dt_bias), _ptr(h), _ptr(u_out), _ptr(y), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
+def selective_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, dt_bias=None, *, silu=True,
+                            conv_state=None, h0=None, return_state=False, return_u=False, out=None, workspace=None,
+                            nchunks=0, states_per_lane=0, stream=None):
+    """Scan of u = act(conv(x)) with the convolution fused into the scan's staging.
+    conv_weight float32 (dim, width <= 4), conv_bias float32 (dim,) or None.  Returns y,
+    or a tuple (y, h_last, u) with the pieces asked for by return_state / return_u."""
+    import torch
+
+    _check_tensors(x, dict(x=x, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h0=h0,
+                           conv_weight=conv_weight, conv_bias=conv_bias, conv_state=conv_state),
+                   f32_names=("A", "D", "dt_bias", "h0", "conv_weight", "conv_bias"))
+    dims = dims_for(x, B, A, nchunks=nchunks, states_per_lane=states_per_lane)
+    if out is None:
+        out = torch.empty_like(x)
+    h_last = torch.empty((x.shape[0], x.shape[1], B.shape[1]), dtype=torch.float32, device=x.device) \
+        if return_state else None
+    u = torch.empty_like(x) if return_u else None
+    need = ssm_selective_scan_workspace_bytes(dims)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        dims.workspace = workspace.data_ptr()
+        dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    conv = _conv_struct(conv_weight, conv_bias, silu)
+    st = ssm_selective_scan_fwd_conv(x, conv, conv_state, delta, A, B, C, D, z, dt_bias, h0, u, out, h_last, dims,
+                                     stream)
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_selective_scan_fwd_conv")
+    if not (return_state or return_u):
+        return out
+    return tuple(v for v, want in ((out, True), (h_last, return_state), (u, return_u)) if want)
+
+
+def selective_scan_step_conv(x, conv_weight, conv_bias, conv_state, delta, A, B, C, D, z, dt_bias, h, *, silu=True,
+                             return_u=False, out=None, stream=None):
+    """One decoding step with the fused convolution: conv_state (batch, dim, width-1)
+    and h are updated in place.  Returns y (and u when return_u)."""
+    import torch
+
+    _check_tensors(x, dict(x=x, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h=h,
+                           conv_weight=conv_weight, conv_bias=conv_bias, conv_state=conv_state),
+                   f32_names=("A", "D", "dt_bias", "h", "conv_weight", "conv_bias"))
+    io = SSM_BF16 if x.dtype == torch.bfloat16 else SSM_F32
+    dims = make_dims(x.shape[0], 1, x.shape[1], B.shape[1], nheads=A.shape[0] if A.dim() == 1 else 0, io_dtype=io)
+    if out is None:
+        out = torch.empty_like(x)
+    u = torch.empty_like(x) if return_u else None
+    conv = _conv_struct(conv_weight, conv_bias, silu)
+    st = ssm_selective_scan_step_conv(x, conv, conv_state, delta, A, B, C, D, z, dt_bias, h, u, out, dims, stream)
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_selective_scan_step_conv")
+    return (out, u) if return_u else out

@@ -37,6 +37,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "ssm.h"
 
 #include "scan_common.h"
@@ -66,9 +68,18 @@ struct Params {
     float* ws_H;          // [groups][nchunks][np][64] piece end states from zero (pass 1)
     float* ws_S;          // [groups][nchunks][64]     sum of dt2 over each piece (pass 1)
     float* ws_Hin;        // [groups][nchunks][np][64] true starting state of each piece
+    // fused front end (conv_w != nullptr): the rows at `u` hold the convolution's input
+    // x and the scan's input is u = act(conv_b + sum_k conv_w[d,k] x[t-K+1+k])
+    const float* conv_w;     // (dim, conv_k)
+    const float* conv_b;     // nullable
+    const void* conv_state;  // nullable: (batch, dim, conv_k-1) inputs before the sequence
+    void* u_out;             // nullable: u, rounded to the I/O type (full mode)
+    int32_t conv_k;          // 1 .. kMaxConv
+    int32_t conv_silu;       // 1: SiLU after the convolution
 };
 
 enum Mode { kFull = 0, kAggregate = 1 };
+constexpr int kMaxConv = 4;   // widest fused convolution: its history fits one 4-element halo
 
 // LDS layout of one tile buffer (floats); rows of 64 channels are padded to kRow or
 // kRowY entries so that the staging writes and epilogue reads, whose lanes span 4
@@ -227,6 +238,20 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
         if constexpr (SCALAR) sv_ah[k] = sv_ok[k] ? p.A[d / p.head_dim] : 0.0f;
         sv_row[k] = (int64_t(b) * p.dim + (sv_ok[k] ? d : 0)) * p.L;
     }
+    // ---- fused convolution: tap j of a vector's halo-extended window multiplies
+    //      x[t - 3 + j] (taps before the first weight are 0)
+    const bool conv = p.conv_w != nullptr;
+    float sv_cw[KX][kMaxConv], sv_cb[KX];
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+        const int64_t d = c0 + sv_ch[k];
+#pragma unroll
+        for (int j = 0; j < kMaxConv; ++j) {
+            const int kk = j - (kMaxConv - p.conv_k);
+            sv_cw[k][j] = (conv && sv_ok[k] && kk >= 0) ? p.conv_w[d * p.conv_k + kk] : 0.0f;
+        }
+        sv_cb[k] = (conv && sv_ok[k] && p.conv_b) ? p.conv_b[d] : 0.0f;
+    }
 
     // ---- B/C staging constants: row vectors v = stid + k*NS, B rows first, then C
     const IO* bc_row[KBV > 0 ? KBV : 1];
@@ -287,6 +312,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
 
     Vec<IO> nu[KX], ndl[KX], nz[KX], nbc[KBV > 0 ? KBV : 1];
     IO nbce[KBE > 0 ? KBE : 1];
+    IO nhalo[KX][kMaxConv];   // fused convolution: x[t-4 .. t-1] before each vector
 
     // ---- global -> registers for the tile starting at t0 (staging threads)
     auto issue_loads = [&](int64_t t0) {
@@ -297,6 +323,19 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
                 nu[k] = load_vec<IO, VEC>(gu + sv_row[k], t, tend, sv_ok[k]);
                 ndl[k] = load_vec<IO, VEC>(gdl + sv_row[k], t, tend, sv_ok[k]);
                 if (has_z) nz[k] = load_vec<IO, VEC>(gz + sv_row[k], t, tend, sv_ok[k]);
+                if (conv) {
+                    // the 4 inputs before the vector (t is a multiple of the vector width,
+                    // so t >= 4 unless t == 0, whose history stage takes from conv_state)
+                    const IO* src = gu + sv_row[k] + (t >= kMaxConv ? t - kMaxConv : 0);
+                    if constexpr (VEC) {
+                        using R = typename std::conditional<sizeof(IO) == 2, uint2, uint4>::type;
+                        const R raw = *reinterpret_cast<const R*>(src);
+                        __builtin_memcpy(nhalo[k], &raw, sizeof(R));
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < kMaxConv; ++j) nhalo[k][j] = src[j];
+                    }
+                }
             }
         }
 #pragma unroll
@@ -315,8 +354,45 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
         float* sSk = sBC + NBC + G * T * kRowY;
         float* sGt = sSk + T * kRowY;
         const bool full_tile = t0 + T <= tend;
+        float uval[KX][VW];   // the scan's input u of each vector element
+#pragma unroll
+        for (int k = 0; k < KX; ++k) {
+#pragma unroll
+            for (int e = 0; e < VW; ++e) uval[k][e] = IOT<IO>::to_f32(nu[k].e[e]);
+            if (conv && sv_on[k]) {
+                const int64_t t = t0 + sv_tv[k] * VW;
+                float xx[kMaxConv + VW];
+#pragma unroll
+                for (int j = 0; j < kMaxConv; ++j) xx[j] = (t >= kMaxConv) ? IOT<IO>::to_f32(nhalo[k][j]) : 0.0f;
+                if (t == 0 && p.conv_state && sv_ok[k] && p.conv_k > 1) {
+                    // history before the sequence: the last conv_k-1 inputs, oldest first
+                    const int64_t d = c0 + sv_ch[k];
+                    const IO* st = static_cast<const IO*>(p.conv_state) + (int64_t(b) * p.dim + d) * (p.conv_k - 1);
+#pragma unroll
+                    for (int j = 0; j < kMaxConv; ++j) {
+                        const int q = j - (kMaxConv - (p.conv_k - 1));
+                        if (q >= 0) xx[j] = IOT<IO>::to_f32(st[q]);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < VW; ++e) xx[kMaxConv + e] = uval[k][e];
+#pragma unroll
+                for (int e = 0; e < VW; ++e) {
+                    float acc = sv_cb[k];
+#pragma unroll
+                    for (int j = 0; j < kMaxConv; ++j) acc = fmaf(sv_cw[k][j], xx[e + 1 + j], acc);
+                    uval[k][e] = p.conv_silu ? silu_f32(acc) : acc;
+                }
+                if (kFullMode && p.u_out) {
+                    Vec<IO> ov;
+#pragma unroll
+                    for (int e = 0; e < VW; ++e) ov.e[e] = IOT<IO>::from_f32(uval[k][e]);
+                    store_vec<IO, VEC>(static_cast<IO*>(p.u_out) + sv_row[k], t, tend, sv_ok[k], ov);
+                }
+            }
+        }
         auto elem = [&](int k, int e, bool in) {
-            const float uu = IOT<IO>::to_f32(nu[k].e[e]);
+            const float uu = uval[k][e];
             const float dt2 = in ? softplus_log2(IOT<IO>::to_f32(ndl[k].e[e]) + sv_bias[k]) : 0.0f;
             float first = dt2;
             if constexpr (SCALAR && kFullMode) first = __builtin_amdgcn_exp2f(dt2 * sv_ah[k]);
@@ -545,7 +621,45 @@ struct StepParams {
     float* h;             // (batch, dim, N), updated in place
     void* y;
     int64_t batch, dim, N, head_dim;
+    // fused front end (conv_w != nullptr): `u` holds the new input x, conv_state the
+    // previous conv_k-1 inputs (oldest first, updated in place), u = act(conv)
+    const float* conv_w;  // (dim, conv_k)
+    const float* conv_b;  // nullable
+    void* conv_state;     // (batch, dim, conv_k-1), may be nullptr when conv_k == 1
+    void* u_out;          // nullable
+    int32_t conv_k;
+    int32_t conv_silu;
 };
+
+// The scan input of row i (batch*dim + d) for this token: the stored u, or the fused
+// convolution of the row's history and its new input.  When `update` is set (one lane
+// per row) the history is shifted in place and u is written to u_out; all lanes of a
+// row run in the same wave, so every lane reads the history before it is written.
+template <typename IO>
+__device__ inline float step_input(const StepParams& p, int64_t i, int64_t d, bool update) {
+    const float x = IOT<IO>::to_f32(static_cast<const IO*>(p.u)[i]);
+    if (!p.conv_w) return x;
+    const int K = p.conv_k;
+    const float* w = p.conv_w + d * K;
+    IO* st = static_cast<IO*>(p.conv_state) + i * (K - 1);
+    float acc = p.conv_b ? p.conv_b[d] : 0.0f;
+    float hist[kMaxConv];
+#pragma unroll
+    for (int j = 0; j < kMaxConv - 1; ++j) hist[j] = (j < K - 1) ? IOT<IO>::to_f32(st[j]) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxConv - 1; ++j)
+        if (j < K - 1) acc = fmaf(w[j], hist[j], acc);
+    acc = fmaf(w[K - 1], x, acc);
+    const float u = p.conv_silu ? silu_f32(acc) : acc;
+    if (update) {
+#pragma unroll
+        for (int j = 0; j + 1 < kMaxConv - 1; ++j)
+            if (j + 1 < K - 1) st[j] = IOT<IO>::from_f32(hist[j + 1]);
+        if (K > 1) st[K - 2] = static_cast<const IO*>(p.u)[i];
+        if (p.u_out) static_cast<IO*>(p.u_out)[i] = IOT<IO>::from_f32(u);
+    }
+    return u;
+}
 
 // 4 consecutive values of an I/O row as fp32 (16-byte or 8-byte aligned)
 __device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -557,7 +671,7 @@ __device__ inline float4 load4(const uint16_t* p) {
 
 template <typename IO, bool SCALAR>
 __device__ inline void step_row_prologue(const StepParams& p, int64_t i, int64_t d, float& uu, float& dt2) {
-    uu = IOT<IO>::to_f32(static_cast<const IO*>(p.u)[i]);
+    uu = step_input<IO>(p, i, d, true);
     const float dr = IOT<IO>::to_f32(static_cast<const IO*>(p.delta)[i]) + (p.bias ? p.bias[d] : 0.0f);
     dt2 = softplus_log2(dr);
 }
@@ -593,7 +707,7 @@ __global__ void __launch_bounds__(256) scan_step_rows_kernel(StepParams p) {
         bv[k] = load4(static_cast<const IO*>(p.Bm) + b * p.N + n0);
         cv[k] = load4(static_cast<const IO*>(p.Cm) + b * p.N + n0);
         if constexpr (!SCALAR) ar[k] = *reinterpret_cast<const float4*>(p.A + d * p.N + n0);
-        uu[k] = IOT<IO>::to_f32(static_cast<const IO*>(p.u)[ri[k]]);
+        uu[k] = step_input<IO>(p, ri[k], ri[k] % p.dim, live[k] && q == 0);
         dr[k] = IOT<IO>::to_f32(static_cast<const IO*>(p.delta)[ri[k]]) + (p.bias ? p.bias[d] : 0.0f);
         zz[k] = p.z ? IOT<IO>::to_f32(static_cast<const IO*>(p.z)[ri[k]]) : 0.0f;
     }
@@ -855,9 +969,15 @@ size_t ssm_selective_scan_workspace_bytes(const ssm_dims* dims) {
     return pl.ws_bytes;
 }
 
-int ssm_selective_scan_fwd_state(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                                 const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
-                                 float* h_last, const ssm_dims* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward entry points share this: the plain scan (conv == nullptr) or the scan of
+// u = act(conv(x)) with x at `u` (conv != nullptr).
+int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+             const void* z, const float* dt_bias, const float* h0, void* y, float* h_last, const ssm_dims* dims,
+             void* stream, const ssm_conv* conv, const void* conv_state, void* u_out) {
     if (!dims) return SSM_ERR_NULL;
     Plan pl;
     int st = make_plan(dims, &pl);
@@ -887,12 +1007,32 @@ int ssm_selective_scan_fwd_state(const void* u, const void* delta, const float* 
                    overlaps(h_last, nh, dt_bias, nd)))
         return SSM_ERR_ALIAS;
 
+    if (conv) {
+        if (!conv->weight) return SSM_ERR_NULL;
+        if (conv->width < 1 || conv->width > kMaxConv || (conv->silu != 0 && conv->silu != 1)) return SSM_ERR_DIMS;
+        const size_t nw = size_t(dims->dim) * conv->width * 4;
+        const size_t ns = size_t(dims->batch) * dims->dim * (conv->width - 1) * esz;
+        if (misaligned(conv->weight, 4) || misaligned(conv->bias, 4) || misaligned(conv_state, esz) ||
+            misaligned(u_out, esz))
+            return SSM_ERR_ALIGN;
+        // u_out is an output like y: it may overlap no input and no other output
+        const void* ins[] = {u, delta, z, B, C, A, D, dt_bias, h0, conv->weight, conv->bias, conv_state};
+        const size_t sizes[] = {nel, nel, nel, nbc, nbc, na, nd, nd, nh, nw, nd, ns};
+        for (int k = 0; k < 12; ++k)
+            if (overlaps(u_out, nel, ins[k], sizes[k]) || overlaps(y, nel, ins[k], sizes[k]) ||
+                (h_last && k >= 9 && overlaps(h_last, nh, ins[k], sizes[k])))
+                return SSM_ERR_ALIAS;
+        if (overlaps(u_out, nel, y, nel) || overlaps(u_out, nel, h_last, nh)) return SSM_ERR_ALIAS;
+    } else if (conv_state || u_out) {
+        return SSM_ERR_DIMS;
+    }
+
     if (pl.ws_bytes > 0) {
         if (!dims->workspace || dims->workspace_bytes < pl.ws_bytes ||
             (reinterpret_cast<uintptr_t>(dims->workspace) % 256) != 0)
             return SSM_ERR_WORKSPACE;
         if (overlaps(dims->workspace, pl.ws_bytes, y, nel) || overlaps(dims->workspace, pl.ws_bytes, h0, nh) ||
-            overlaps(dims->workspace, pl.ws_bytes, h_last, nh))
+            overlaps(dims->workspace, pl.ws_bytes, h_last, nh) || overlaps(dims->workspace, pl.ws_bytes, u_out, nel))
             return SSM_ERR_ALIAS;
     }
 
@@ -923,6 +1063,12 @@ int ssm_selective_scan_fwd_state(const void* u, const void* delta, const float* 
     p.np = pl.G * pl.spl;
     p.h0 = h0;
     p.h_last = h_last;
+    p.conv_w = conv ? conv->weight : nullptr;
+    p.conv_b = conv ? conv->bias : nullptr;
+    p.conv_state = conv ? conv_state : nullptr;
+    p.u_out = conv ? u_out : nullptr;
+    p.conv_k = conv ? conv->width : 0;
+    p.conv_silu = conv ? conv->silu : 0;
     p.ws_H = p.ws_S = p.ws_Hin = nullptr;
     if (pl.ws_bytes > 0) {
         const size_t per = size_t(dims->batch) * pl.nblk_d * pl.nchunks * kLanes;
@@ -937,15 +1083,37 @@ int ssm_selective_scan_fwd_state(const void* u, const void* delta, const float* 
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+int ssm_selective_scan_fwd_state(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                 const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
+                                 float* h_last, const ssm_dims* dims, void* stream) {
+    return fwd_impl(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, dims, stream, nullptr, nullptr, nullptr);
+}
+
+int ssm_selective_scan_fwd_conv(const void* x, const ssm_conv* conv, const void* conv_state, const void* delta,
+                                const float* A, const void* B, const void* C, const float* D, const void* z,
+                                const float* dt_bias, const float* h0, void* u_out, void* y, float* h_last,
+                                const ssm_dims* dims, void* stream) {
+    if (!conv) return SSM_ERR_NULL;
+    return fwd_impl(x, delta, A, B, C, D, z, dt_bias, h0, y, h_last, dims, stream, conv, conv_state, u_out);
+}
+
 int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                            const float* D, const void* z, const float* dt_bias, void* y, const ssm_dims* dims,
                            void* stream) {
     return ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, nullptr, y, nullptr, dims, stream);
 }
 
-int ssm_selective_scan_step(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                            const float* D, const void* z, const float* dt_bias, float* h, void* y,
-                            const ssm_dims* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int step_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+              const void* z, const float* dt_bias, float* h, void* y, const ssm_dims* dims, void* stream,
+              const ssm_conv* conv, void* conv_state, void* u_out) {
     const int st = validate_dims(dims);
     if (st != SSM_OK) return st;
     if (dims->seqlen != 1) return SSM_ERR_DIMS;
@@ -965,6 +1133,29 @@ int ssm_selective_scan_step(const void* u, const void* delta, const float* A, co
     for (int k = 0; k < 8; ++k)
         if (overlaps(y, nel, ins[k], sizes[k]) || overlaps(h, nh, ins[k], sizes[k])) return SSM_ERR_ALIAS;
     if (overlaps(y, nel, h, nh)) return SSM_ERR_ALIAS;
+    if (conv) {
+        if (!conv->weight) return SSM_ERR_NULL;
+        if (conv->width < 1 || conv->width > kMaxConv || (conv->silu != 0 && conv->silu != 1)) return SSM_ERR_DIMS;
+        if (conv->width > 1 && !conv_state) return SSM_ERR_NULL;
+        if (misaligned(conv->weight, 4) || misaligned(conv->bias, 4) || misaligned(conv_state, esz) ||
+            misaligned(u_out, esz))
+            return SSM_ERR_ALIGN;
+        const size_t nw = size_t(dims->dim) * conv->width * 4;
+        const size_t ns = size_t(dims->batch) * dims->dim * (conv->width - 1) * esz;
+        // conv_state is read and written (in place); u_out is written: neither may
+        // overlap any other array
+        const void* all[] = {u, delta, z, B, C, A, D, dt_bias, conv->weight, conv->bias, h, y};
+        const size_t all_sz[] = {nel, nel, nel, nbc, nbc, na, nd, nd, nw, nd, nh, nel};
+        for (int k = 0; k < 12; ++k)
+            if (overlaps(conv_state, ns, all[k], all_sz[k]) || overlaps(u_out, nel, all[k], all_sz[k]))
+                return SSM_ERR_ALIAS;
+        if ((overlaps(conv_state, ns, u_out, nel)) ||
+            overlaps(h, nh, conv->weight, nw) || overlaps(h, nh, conv->bias, nd) ||
+            overlaps(y, nel, conv->weight, nw) || overlaps(y, nel, conv->bias, nd))
+            return SSM_ERR_ALIAS;
+    } else if (conv_state || u_out) {
+        return SSM_ERR_DIMS;
+    }
 
     StepParams p;
     p.u = u;
@@ -981,6 +1172,12 @@ int ssm_selective_scan_step(const void* u, const void* delta, const float* A, co
     p.dim = dims->dim;
     p.N = dims->dstate;
     p.head_dim = dims->nheads > 0 ? dims->dim / dims->nheads : 0;
+    p.conv_w = conv ? conv->weight : nullptr;
+    p.conv_b = conv ? conv->bias : nullptr;
+    p.conv_state = conv ? conv_state : nullptr;
+    p.u_out = conv ? u_out : nullptr;
+    p.conv_k = conv ? conv->width : 0;
+    p.conv_silu = conv ? conv->silu : 0;
     // the vector form reads 4 entries at once: rows of h and A 16-byte aligned, of B and C 4*esz
     const bool vec4 = dims->dstate % 4 == 0 && !misaligned(h, 16) && !misaligned(B, 4 * esz) &&
                       !misaligned(C, 4 * esz) && (dims->nheads > 0 || !misaligned(A, 16));
@@ -993,6 +1190,24 @@ int ssm_selective_scan_step(const void* u, const void* delta, const float* A, co
     else
         e = scalar ? launch_step<float, true>(p, vec4, s) : launch_step<float, false>(p, vec4, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_selective_scan_step(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const void* z, const float* dt_bias, float* h, void* y,
+                            const ssm_dims* dims, void* stream) {
+    return step_impl(u, delta, A, B, C, D, z, dt_bias, h, y, dims, stream, nullptr, nullptr, nullptr);
+}
+
+int ssm_selective_scan_step_conv(const void* x, const ssm_conv* conv, void* conv_state, const void* delta,
+                                 const float* A, const void* B, const void* C, const float* D, const void* z,
+                                 const float* dt_bias, float* h, void* u_out, void* y, const ssm_dims* dims,
+                                 void* stream) {
+    if (!conv) return SSM_ERR_NULL;
+    return step_impl(x, delta, A, B, C, D, z, dt_bias, h, y, dims, stream, conv, conv_state, u_out);
 }
 
 }  // extern "C"

@@ -164,3 +164,19 @@ def io_to_device(x: ScanInputs, a: np.ndarray, device="cuda"):
     if x.io == "bf16":
         return torch.from_numpy(bf16_bits(a)).view(torch.bfloat16).to(device)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def make_conv(x: ScanInputs, width: int, *, seed: int, with_bias: bool = True, with_state: bool = False):
+    """Seeded parameters of the fused convolution front end for the inputs x (whose u
+    then plays the convolution's input): weight (dim, width) ~ N(0, 1/width) float32,
+    bias (dim,) ~ N(0, 0.1^2) float32 or None, and optionally a history conv_state
+    (batch, dim, width-1) ~ N(0, 1) in the I/O type.  Returns (weight, bias, state)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = (rng.standard_normal((x.dim, width)) / math.sqrt(width)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(x.dim)).astype(np.float32) if with_bias else None
+    st = None
+    if with_state:
+        st = rng.standard_normal((x.batch, x.dim, width - 1), dtype=np.float32)
+        if x.io == "bf16":
+            st = round_to_bf16(st)
+    return w, b, st

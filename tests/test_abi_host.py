@@ -261,3 +261,38 @@ def test_backward_refusals():
     g = ssm.SsmGrads(0x40000000, 0x41000000, 0x42000000, 0x43000000, 0x80000000, None, None, None, None)
     assert _bwd(d, g) == ssm.SSM_ERR_ALIAS
     assert _bwd(ssm.make_dims(0, 100, 70, 16)) == ssm.SSM_ERR_EMPTY
+
+
+# ---------------------------------------------------------------- fused convolution front end
+
+def test_conv_entry_points_refuse_bad_arguments():
+    lib = ssm.load_library()
+    p = lambda a: ctypes.c_void_p(a) if a else None
+    dims = ssm.make_dims(2, 64, 70, 16)
+    W = 0x50000000
+
+    def fwd(conv, conv_state=None, u_out=None, y=FAKE + 0x500000):
+        return lib.ssm_selective_scan_fwd_conv(
+            p(FAKE), ctypes.byref(conv) if conv is not None else None, p(conv_state), p(FAKE + 0x100000),
+            p(FAKE + 0x200000), p(FAKE + 0x300000), p(FAKE + 0x400000), None, None, None, None, p(u_out), p(y),
+            None, ctypes.byref(dims), None)
+
+    assert fwd(None) == ssm.SSM_ERR_NULL
+    assert fwd(ssm.SsmConv(None, None, 4, 1)) == ssm.SSM_ERR_NULL
+    assert fwd(ssm.SsmConv(W, None, 0, 1)) == ssm.SSM_ERR_DIMS
+    assert fwd(ssm.SsmConv(W, None, 5, 1)) == ssm.SSM_ERR_DIMS
+    assert fwd(ssm.SsmConv(W, None, 4, 2)) == ssm.SSM_ERR_DIMS
+    assert fwd(ssm.SsmConv(W + 2, None, 4, 1)) == ssm.SSM_ERR_ALIGN
+    assert fwd(ssm.SsmConv(W, None, 4, 1), u_out=FAKE + 0x500000) == ssm.SSM_ERR_ALIAS   # u_out is y
+    assert fwd(ssm.SsmConv(W, None, 4, 1), u_out=FAKE) == ssm.SSM_ERR_ALIAS              # u_out is x
+    sdims = ssm.make_dims(2, 1, 70, 16)
+
+    def step(conv, conv_state, u_out=None):
+        return lib.ssm_selective_scan_step_conv(
+            p(FAKE), ctypes.byref(conv), p(conv_state), p(FAKE + 0x100000), p(FAKE + 0x200000), p(FAKE + 0x300000),
+            p(FAKE + 0x400000), None, None, None, p(0x60000000), p(u_out), p(FAKE + 0x500000), ctypes.byref(sdims),
+            None)
+
+    assert step(ssm.SsmConv(W, None, 4, 1), None) == ssm.SSM_ERR_NULL       # width > 1 needs a state
+    assert step(ssm.SsmConv(W, None, 4, 1), FAKE) == ssm.SSM_ERR_ALIAS      # state overlaps x
+    assert step(ssm.SsmConv(W, None, 9, 1), 0x70000000) == ssm.SSM_ERR_DIMS
