@@ -94,9 +94,11 @@ def cpu_baseline(x, rows_batches: int, repeats: int = 3):
 PROFILE_COMMANDS = {
     "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/stats -o scan -- python3 bench.py",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/fetch -o scan -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward --no-decode",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/write -o scan -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward --no-decode",
+    "conv_stats": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/convstats -o conv -- "
+                  "python3 bench.py --steps 200 --warmup 50 --no-cpu-baseline --no-backward --no-decode --fused-conv",
     "copyfetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/copyfetch -o copy -- "
                  "python3 bench.py --calibrate-copy",
     "copywrite": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/copywrite -o copy -- "
@@ -176,6 +178,22 @@ def summarize_profiles(d):
     with open(os.path.join(ROOT, "profiles", "scan_fwd_mamba13b.md"), "w") as f:
         f.write("\n".join(md))
     print(json.dumps({"traffic_bytes_per_launch": rd + wr, "ratio_to_algorithmic": (rd + wr) / alg}))
+    conv_stats = os.path.join(d, "convstats", "conv_kernel_stats.csv")
+    if os.path.exists(conv_stats):
+        rows = list(csv.DictReader(open(conv_stats)))
+        md = ["# Fused convolution front end + scan, mamba-1.3b-layer workload (4 x 4096 x 4096, N=16, bf16, "
+              "width-4 SiLU convolution): rocprofv3 summary", "",
+              f"Kernel source sha256[:16]: `{kernel_hash()}`", "",
+              "The run times the plain scan first (`--steps` calls) and then the fused front end (100 calls of "
+              "`ssm_selective_scan_fwd_conv`, then the fused decode step); both scans launch the same kernel, so "
+              "its calls here are the two kinds together.", "",
+              "Command (from the repository root on the GPU box):", "",
+              "    " + PROFILE_COMMANDS["conv_stats"].format(d="gpurun_out/prof"), "",
+              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+        for r in rows:
+            md.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+        with open(os.path.join(ROOT, "profiles", "scan_fwd_conv_mamba13b.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
 
 
 def decode_step_bench(batch: int, steps: int = 200, warmup: int = 50):
@@ -360,6 +378,10 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="1..5; the reported line is workload 3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
+    ap.add_argument("--fused-conv", action="store_true",
+                    help="also time the fused convolution front end (same scan kernel, so off by default: "
+                         "its launches would mix into the scan kernel's profile)")
     ap.add_argument("--cpu-batches", type=int, default=4, help="batch rows in the oracle's timing sample")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 2 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs in DIR")
@@ -470,9 +492,9 @@ def main():
         "timing": {"ms_events": ms_events, "ms_wall": ms_wall, "input_gen_s": round(gen_s, 2),
                    "kernel_source_sha256_16": kernel_hash(), "device": torch.cuda.get_device_name(0)},
     }
-    if args.workload == 3:
+    if args.workload == 3 and not args.no_decode:
         rec["decode_step"] = [decode_step_bench(64), decode_step_bench(256)]
-    if args.workload == 3:
+    if args.fused_conv:
         rec["fused_conv"] = fused_conv_bench(x, dev)
     if not args.no_backward:
         rec["backward"] = backward_bench(x, dev)
