@@ -244,3 +244,61 @@ def causal_conv1d(x, w, bias=None, state=None, silu=True):
     if code != OK:
         raise OracleError(code, "causal_conv1d")
     return out, st[..., : K - 1]
+
+
+def ssd_matrix_form(u, delta, A, B, C, D=None, z=None, dt_bias=None, h0=None):
+    """fp64 quadratic form of the scalar-decay scan with one step size per head.
+
+    State space duality (yo3nglau.github.io "Mamba 与状态空间模型：面试问题与推荐回答"
+    Q10): when the state matrix is a scalar times the identity, the recurrence
+    h_t = a_t h_{t-1} + B_t u_t, y_t = C_t . h_t equals one matrix product of the
+    inputs with a causal (lower-triangular) mask whose entries are the read-write
+    products C_t . B_s times the decay accumulated between s and t.  Written out for
+    head h with step sizes dt_t = softplus(delta[b,h,t] + dt_bias[h]) and decay
+    exp(dt_t A[h]) per step (cum_t = sum_{k<=t} dt_k A[h]):
+
+        M[t, s] = (C_t . B_s) * exp(cum_t - cum_s) * dt_s        for s <= t, else 0
+        y[p, t] = sum_s M[t, s] u[p, s] + exp(cum_t) C_t . h0[p]
+        h_last[p] = exp(cum_{L-1}) h0[p] + sum_s exp(cum_{L-1} - cum_s) dt_s u[p, s] B_s
+
+    then y = (y + D u) * SiLU(z) as in the recurrence.  Shapes: u, z (batch, H*P, L)
+    with head h owning channels h*P .. h*P+P-1; delta (batch, H, L); A, dt_bias (H,);
+    B, C (batch, N, L); D (H*P,); h0 (batch, H*P, N).  Returns (y, h_last).  Plain
+    numpy matrix products over the whole sequence: small L only.
+    """
+    u, delta, A, B, C = (np.asarray(x, dtype=np.float64) for x in (u, delta, A, B, C))
+    D, z, dt_bias, h0 = (None if x is None else np.asarray(x, dtype=np.float64) for x in (D, z, dt_bias, h0))
+    batch, dim, L = u.shape
+    H = delta.shape[1]
+    N = B.shape[1]
+    if delta.shape != (batch, H, L) or A.shape != (H,) or dim % H:
+        raise ValueError("delta must be (batch, H, L), A (H,) and dim a multiple of H")
+    if B.shape != (batch, N, L) or C.shape != (batch, N, L):
+        raise ValueError("B and C must be (batch, N, L)")
+    P = dim // H
+    bias = np.zeros(H) if dt_bias is None else dt_bias
+    causal = np.tri(L, dtype=bool)
+    y = np.zeros((batch, dim, L))
+    h_last = np.zeros((batch, dim, N))
+    for b in range(batch):
+        G = C[b].T @ B[b]                                   # G[t, s] = C_t . B_s
+        for h in range(H):
+            dt = np.logaddexp(0.0, delta[b, h] + bias[h])   # softplus
+            cum = np.cumsum(dt * A[h])
+            diff = cum[:, None] - cum[None, :]
+            decay = np.where(causal, np.exp(np.where(causal, diff, 0.0)), 0.0)
+            M = G * decay * dt[None, :]
+            ch = slice(h * P, (h + 1) * P)
+            U = u[b, ch]                                    # (P, L)
+            Y = U @ M.T
+            last = U @ (B[b] * (np.exp(cum[-1] - cum) * dt)[None, :]).T     # (P, N)
+            if h0 is not None:
+                Y += (h0[b, ch] @ C[b]) * np.exp(cum)[None, :]
+                last += np.exp(cum[-1]) * h0[b, ch]
+            y[b, ch] = Y
+            h_last[b, ch] = last
+    if D is not None:
+        y += D[None, :, None] * u
+    if z is not None:
+        y *= z / (1.0 + np.exp(-z))
+    return y, h_last

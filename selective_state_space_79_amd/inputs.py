@@ -180,3 +180,87 @@ def make_conv(x: ScanInputs, width: int, *, seed: int, with_bias: bool = True, w
         if x.io == "bf16":
             st = round_to_bf16(st)
     return w, b, st
+
+
+# The scalar-decay workload with one step size per head, the form the chunked
+# state-space-duality path takes (Mamba-2 layout: 64 heads of 64 channels, N = 128).
+SSD_WORKLOADS = {
+    5: dict(name="scalar-decay-large-state-head-dt", batch=2, L=8192, nheads=64, headdim=64, N=128,
+            dt_range=(1e-3, 1e-1)),
+}
+
+
+@dataclasses.dataclass
+class SsdInputs:
+    """Inputs of the scalar-decay scan with per-head step sizes (all bf16-exact float32
+    except A, D and dt_bias).  Head h owns channels h*headdim .. h*headdim+headdim-1."""
+    batch: int
+    L: int
+    nheads: int
+    headdim: int
+    N: int
+    u: np.ndarray        # (batch, dim, L)
+    delta: np.ndarray    # (batch, nheads, L)  raw step input, before bias and softplus
+    z: np.ndarray        # (batch, dim, L)
+    B: np.ndarray        # (batch, N, L)
+    C: np.ndarray        # (batch, N, L)
+    A: np.ndarray        # (nheads,)  a_h < 0
+    D: np.ndarray        # (dim,)
+    dt_bias: np.ndarray  # (nheads,)
+
+    @property
+    def dim(self) -> int:
+        return self.nheads * self.headdim
+
+    @property
+    def updates(self) -> int:
+        return self.batch * self.L * self.dim * self.N
+
+    def per_channel(self) -> ScanInputs:
+        """The same inputs laid out for the per-channel scan: each head's step input,
+        bias and decay repeated over its channels (a copy, no arithmetic)."""
+        rep = lambda a, axis: np.ascontiguousarray(np.repeat(a, self.headdim, axis=axis))
+        return ScanInputs(self.batch, self.L, self.dim, self.N, self.nheads, "bf16", self.u, rep(self.delta, 1),
+                          self.z, self.B, self.C, self.A, self.D, rep(self.dt_bias, 0))
+
+
+def make_ssd_inputs(batch: int, L: int, nheads: int, headdim: int, N: int, *, seed: int, dt_range=(1e-3, 1e-1),
+                    a_range=(1.0, 16.0)) -> SsdInputs:
+    """Seeded bf16 inputs with one step size per head.  Same recipe as make_inputs in
+    scalar-decay mode except that delta_raw is (batch, nheads, L) and dt_h is drawn per
+    head: draw order u, delta_raw, z, B, C (standard normal, rounded to bf16), D (N(0,1)
+    float32), dt_h (log-uniform on dt_range), a_h = -U(a_range); dt_bias[h] =
+    log(expm1(dt_h))."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dim = nheads * headdim
+
+    def draw(shape):
+        return round_to_bf16(rng.standard_normal(shape, dtype=np.float32))
+
+    u = draw((batch, dim, L))
+    delta = draw((batch, nheads, L))
+    z = draw((batch, dim, L))
+    B = draw((batch, N, L))
+    C = draw((batch, N, L))
+    D = rng.standard_normal(dim, dtype=np.float32)
+    lo, hi = dt_range
+    dt = np.exp(rng.uniform(math.log(lo), math.log(hi), size=nheads))
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+    A = (-rng.uniform(a_range[0], a_range[1], size=nheads)).astype(np.float32)
+    return SsdInputs(batch, L, nheads, headdim, N, u, delta, z, B, C, A, D, dt_bias)
+
+
+def make_ssd_workload(index: int = 5, seed: int | None = None) -> SsdInputs:
+    w = SSD_WORKLOADS[index]
+    return make_ssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["N"],
+                           seed=WORKLOAD_SEEDS[index] if seed is None else seed, dt_range=w["dt_range"])
+
+
+def ssd_to_device(x: SsdInputs, device="cuda"):
+    """Upload to torch tensors: u/delta/z/B/C bf16, A/D/dt_bias float32."""
+    import torch
+
+    bf = lambda a: torch.from_numpy(bf16_bits(a)).view(torch.bfloat16).to(device)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    return dict(u=bf(x.u), delta=bf(x.delta), z=bf(x.z), B=bf(x.B), C=bf(x.C), A=f32(x.A), D=f32(x.D),
+                dt_bias=f32(x.dt_bias))
