@@ -261,6 +261,69 @@ SSM_API int ssm_selective_scan_plan(const ssm_dims* dims, ssm_plan* plan);
  * ssm_selective_scan_bwd_workspace_bytes; time_tile is the recompute interval). */
 SSM_API int ssm_selective_scan_bwd_plan(const ssm_dims* dims, ssm_plan* plan);
 
+/* ------------------------------------------------------------------------------
+ * Scalar decay with one step size per head: the chunked state-space-duality form.
+ *
+ * When the state matrix of a head is a scalar times the identity (A = a_h * I,
+ * yo3nglau.github.io "Mamba 与状态空间模型：面试问题与推荐回答" Q9) and the head's
+ * channels share one step size per token, the scan is a masked linear attention and
+ * can be computed chunk by chunk with matrix products (the same page, Q10: the
+ * duality of SSMs and attention, and the chunked algorithm that processes token
+ * blocks on chip).  ssm_ssd_fwd computes, for head h owning channels
+ * d = h*headdim .. h*headdim+headdim-1:
+ *
+ *   dt       = softplus(delta[b,h,t] + dt_bias[h])
+ *   h[d,n]   = exp(dt * A[h]) * h[d,n] + dt * B[b,n,t] * u[b,d,t]
+ *   y[b,d,t] = (sum_n C[b,n,t] * h[d,n] + D[d] * u[b,d,t]) * SiLU(z[b,d,t])
+ *
+ * i.e. ssm_selective_scan_fwd_state in scalar-decay mode with delta and dt_bias
+ * repeated over each head's channels; the result is the same up to float rounding.
+ * The products run on the matrix cores with fp32 accumulation; operands that are not
+ * bf16 inputs are split into two bf16 parts, so the arithmetic error stays near fp32
+ * scan level rather than bf16 level.
+ *
+ * Layouts (row-major, no padding; dim = nheads * headdim):
+ *   u, z, y : (batch, dim, seqlen) bf16
+ *   delta   : (batch, nheads, seqlen) bf16 -- the raw step input, one per head
+ *   B, C    : (batch, dstate, seqlen) bf16, shared by every head
+ *   A       : float32 (nheads,)
+ *   dt_bias : float32 (nheads,), nullable (0)
+ *   D       : float32 (dim,), nullable (no skip);  z nullable (no gate)
+ *   h0      : float32 (batch, dim, dstate), nullable (zeros) -- the state before the
+ *             first step;  h_last: same layout, nullable -- the state after the last
+ *             step.  h_last may not overlap h0 or any array.
+ * Supported: io_dtype SSM_BF16, headdim 64, dstate 64 or 128 (else SSM_ERR_DTYPE /
+ * SSM_ERR_DIMS).  Each sequence is cut into nsegments pieces of whole 64-step chunks
+ * (0: library choice); the pieces' end states travel through the workspace.
+ * Ownership, asynchrony and the other error rules are those of ssm_selective_scan_fwd
+ * (y may not overlap an input: SSM_ERR_ALIAS).
+ */
+typedef struct ssm_ssd_dims {
+    int64_t batch;           /* >= 1 */
+    int64_t seqlen;          /* >= 1 */
+    int64_t nheads;          /* >= 1 */
+    int64_t headdim;         /* channels per head; 64 */
+    int64_t dstate;          /* N: 64 or 128 */
+    int32_t io_dtype;        /* SSM_BF16 */
+    int32_t nsegments;       /* 0: library choice; k in 1 .. SSM_MAX_CHUNKS forces k pieces
+                                (clamped to the number of 64-step chunks) */
+    int32_t reserved;        /* must be 0 */
+    int32_t reserved2;       /* ignored (padding) */
+    void* workspace;         /* device memory for the pieces' end states, 256-byte aligned;
+                                may be NULL when the required size is 0 */
+    size_t workspace_bytes;
+} ssm_ssd_dims;
+
+/* Bytes of workspace ssm_ssd_fwd needs: 4 * batch * dim * dstate per piece boundary
+ * plus one float per head and boundary (0 with a single piece, and for a dims that
+ * ssm_ssd_fwd would refuse). */
+SSM_API size_t ssm_ssd_fwd_workspace_bytes(const ssm_ssd_dims* dims);
+
+/* Enqueue the scalar-decay per-head-step forward pass.  Returns an ssm_status value. */
+SSM_API int ssm_ssd_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                        const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
+                        float* h_last, const ssm_ssd_dims* dims, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

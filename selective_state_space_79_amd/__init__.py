@@ -1,17 +1,16 @@
 """Python binding of libssm.so, the MI355X selective scan (forward, decode step,
-backward).
+backward, fused convolution front end, and the chunked scalar-decay pass with
+per-head step sizes).
 
 Argument marshalling only: every step of the scan runs in the HIP kernels of
-``csrc/scan_fwd.hip`` and ``csrc/scan_bwd.hip`` behind the C ABI of ``include/ssm.h``.  There is no CPU or
-PyTorch fallback: if the library is missing, every call raises.
+``csrc/scan_fwd.hip``, ``csrc/scan_bwd.hip`` and ``csrc/ssd_fwd.hip`` behind the C ABI
+of ``include/ssm.h``.  There is no CPU or PyTorch fallback: if the library is missing,
+every call raises.
 
-The functions carry the C names (``ssm_selective_scan_fwd``,
-``ssm_selective_scan_fwd_state``, ``ssm_selective_scan_step``,
-``ssm_selective_scan_bwd``, ``ssm_selective_scan_workspace_bytes``,
-``ssm_selective_scan_bwd_workspace_bytes``, ``ssm_selective_scan_plan``,
-``ssm_selective_scan_bwd_plan``, ``ssm_status_string``); ``selective_scan_fwd``,
-``selective_scan_step`` and ``selective_scan_bwd`` additionally allocate outputs and
-the workspace through PyTorch's caching allocator.
+The ``ssm_*`` functions carry the C names (see ``EXPORTED``) and take raw device
+tensors; ``selective_scan_fwd``, ``selective_scan_step``, ``selective_scan_bwd``,
+``selective_scan_fwd_conv``, ``selective_scan_step_conv`` and ``ssd_fwd`` additionally
+allocate outputs and the workspace through PyTorch's caching allocator.
 """
 from __future__ import annotations
 
@@ -38,7 +37,8 @@ SSM_MAX_CHUNKS = 1024
 EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_fwd_state", "ssm_selective_scan_step",
             "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan", "ssm_status_string",
             "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd_plan",
-            "ssm_selective_scan_fwd_conv", "ssm_selective_scan_step_conv")
+            "ssm_selective_scan_fwd_conv", "ssm_selective_scan_step_conv", "ssm_ssd_fwd",
+            "ssm_ssd_fwd_workspace_bytes")
 SSM_MAX_DSTATE_BWD = 128
 
 
@@ -88,6 +88,23 @@ class SsmConv(ctypes.Structure):
                 ("silu", ctypes.c_int32)]
 
 
+class SsmSsdDims(ctypes.Structure):
+    """Mirror of ``ssm_ssd_dims`` in include/ssm.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("nsegments", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class SsmError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {ssm_status_string(status)} (status {status})")
@@ -125,6 +142,10 @@ def load_library():
         lib.ssm_selective_scan_fwd_conv.restype = ctypes.c_int
         lib.ssm_selective_scan_step_conv.argtypes = [vp, ctypes.POINTER(SsmConv)] + [vp] * 11 + [ctypes.POINTER(SsmDims), vp]
         lib.ssm_selective_scan_step_conv.restype = ctypes.c_int
+        lib.ssm_ssd_fwd.argtypes = [vp] * 11 + [ctypes.POINTER(SsmSsdDims), vp]
+        lib.ssm_ssd_fwd.restype = ctypes.c_int
+        lib.ssm_ssd_fwd_workspace_bytes.argtypes = [ctypes.POINTER(SsmSsdDims)]
+        lib.ssm_ssd_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.ssm_status_string.argtypes = [ctypes.c_int]
         lib.ssm_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -418,3 +439,58 @@ def selective_scan_step_conv(x, conv_weight, conv_bias, conv_state, delta, A, B,
     if st != SSM_OK:
         raise SsmError(st, "ssm_selective_scan_step_conv")
     return (out, u) if return_u else out
+
+
+def make_ssd_dims(batch, seqlen, nheads, dstate, *, headdim=64, io_dtype=SSM_BF16, nsegments=0, workspace=0,
+                  workspace_bytes=0, reserved=0) -> SsmSsdDims:
+    return SsmSsdDims(batch, seqlen, nheads, headdim, dstate, io_dtype, nsegments, reserved, 0, workspace or None,
+                      workspace_bytes)
+
+
+def ssm_ssd_fwd_workspace_bytes(dims: SsmSsdDims) -> int:
+    return int(load_library().ssm_ssd_fwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def ssm_ssd_fwd(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, dims: SsmSsdDims, stream=None) -> int:
+    """C entry point of the chunked scalar-decay pass with per-head step sizes; returns
+    the status.  u, z, y (batch, nheads*headdim, L), delta (batch, nheads, L), B, C
+    (batch, N, L) bf16; A, dt_bias float32 (nheads,); D float32 (dim,); h0, h_last
+    float32 (batch, dim, N) or None."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device)
+    return int(load_library().ssm_ssd_fwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y),
+        _ptr(h_last), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
+def ssd_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, h0=None, return_state=False, out=None,
+            workspace=None, nsegments=0, stream=None):
+    """Allocate y (and the workspace) and run ssm_ssd_fwd.  Returns y, or (y, h_last)
+    with return_state=True.  Raises SsmError on a refused call."""
+    import torch
+
+    _check_tensors(u, dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h0=h0))
+    if u.dim() != 3 or delta.dim() != 3 or B.dim() != 3 or A.dim() != 1:
+        raise ValueError("u (batch, dim, L), delta (batch, nheads, L), B (batch, N, L) and A (nheads,) expected")
+    if u.dtype != torch.bfloat16:
+        raise TypeError("the chunked pass takes bf16 inputs")
+    batch, dim, L = u.shape
+    nheads = delta.shape[1]
+    if dim % nheads:
+        raise ValueError("dim must be a multiple of nheads")
+    dims = make_ssd_dims(batch, L, nheads, B.shape[1], headdim=dim // nheads, nsegments=nsegments)
+    if out is None:
+        out = torch.empty_like(u)
+    h_last = torch.empty((batch, dim, B.shape[1]), dtype=torch.float32, device=u.device) if return_state else None
+    need = ssm_ssd_fwd_workspace_bytes(dims)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+        dims.workspace = workspace.data_ptr()
+        dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = ssm_ssd_fwd(u, delta, A, B, C, D, z, dt_bias, h0, out, h_last, dims, stream)
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_ssd_fwd")
+    return (out, h_last) if return_state else out

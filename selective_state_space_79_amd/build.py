@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", name) for name in ("scan_fwd.hip", "scan_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("scan_fwd.hip", "scan_bwd.hip", "ssd_fwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
 
@@ -25,6 +25,7 @@ HIP_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden",
     "-I", INCLUDE,
 ]

@@ -1,0 +1,741 @@
+// ssd_fwd.hip -- the scalar-decay selective scan with one step size per head, computed
+// in its chunked state-space-duality form with every contraction on the gfx950 matrix
+// cores (v_mfma_f32_16x16x32_bf16).
+//
+// What it computes is the recurrence of ssm.h for a head h whose channels share the
+// decay A = a_h * I and the step size dt[b,h,t] = softplus(delta[b,h,t] + dt_bias[h])
+// (the entry point ssm_ssd_fwd).  When the state matrix is a scalar times the
+// identity, the scan equals a masked linear attention, and a chunked algorithm can
+// process blocks of tokens on chip (yo3nglau.github.io "Mamba 与状态空间模型：面试问题与
+// 推荐回答" Q10).  For a chunk of kQ steps entered with the per-head state Hin
+// (N x P, one column per channel) and cum_t = sum_{k<=t} dt_k a_h inside the chunk:
+//
+//   y[t,p] = sum_{s<=t} G[t,s] exp(cum_t - cum_s) dt_s u[s,p]  +  exp(cum_t) sum_n C[n,t] Hin[n,p]
+//   Hout   = exp(cum_last) Hin + sum_s exp(cum_last - cum_s) dt_s B[:,s] u[s,:]
+//
+// with G[t,s] = sum_n C[n,t] B[n,s]; then y = (y + D u) SiLU(z) as in the recurrence.
+// The four products (G, the masked-decay product, the read of Hin, the chunk's state
+// contribution) are MFMA tiles.  G's operands are the bf16 inputs themselves; the
+// other products multiply a bf16 input by an fp32 value (the decayed mask, the
+// weighted inputs, the state), which is split into a high and a low bf16 part and
+// multiplied twice, so the operand carries ~2^-16 relative error instead of bf16's
+// 2^-9 (plain bf16 operands exceed a 2e-2 output error on the N = 128 workload).
+// Products accumulate in fp32.
+//
+// Work split: a sequence is cut into segments of whole chunks.  ssd_state_kernel
+// computes each segment's end state from a zero start (and its total decay);
+// ssd_out_kernel composes the states of the segments before its own with h0, then
+// walks its chunks in order, producing y and carrying the state in registers.  In
+// both, wave w of a workgroup owns the head's channels 16w .. 16w+15: their state
+// columns (all N rows), the chunk's state contribution to them, and their outputs.
+// The masked decay matrix of a chunk is shared by all channels: its 10 lower-
+// triangular 16x16 tiles are computed once, spread over the waves, and exchanged
+// through LDS.  The next chunk's inputs are loaded into registers while the current
+// one is computed.
+#include "scan_common.h"
+
+#include <algorithm>
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kQ = 64;                  // steps per chunk
+constexpr int kP = 64;                  // channels per head
+constexpr int kWaves = 4;               // wave w owns channels 16w .. 16w+15
+constexpr int kThreads = kWaves * kLanes;
+constexpr int kRow = kQ + 8;            // LDS row (bf16): 144 bytes, 36 dwords
+static_assert(kQ == kLanes, "one step per lane in the step-size prefix");
+
+// LDS, in bf16 units: B[n][s], C[n][t], u[p][s], and the masked decay matrix
+// M[t][s] as high and low bf16 parts; then the fp32 step arrays.
+template <int N> struct OutLds {
+    static constexpr int Bn = 0;
+    static constexpr int Cn = Bn + N * kRow;
+    static constexpr int U = Cn + N * kRow;
+    static constexpr int Mhi = U + kP * kRow;
+    static constexpr int Mlo = Mhi + kQ * kRow;
+    static constexpr int F = Mlo + kQ * kRow;
+    static constexpr size_t bytes = size_t(F) * 2 + (4 * kQ + 4) * sizeof(float);
+};
+template <int N> struct StateLds {
+    static constexpr int Bn = 0;
+    static constexpr int U = Bn + N * kRow;
+    static constexpr int F = U + kP * kRow;
+    static constexpr size_t bytes = size_t(F) * 2 + (4 * kQ + 4) * sizeof(float);
+};
+// fp32 step arrays (offsets in floats): cum (log2 units), dt, the state weights
+// exp(cum_last - cum_s) dt_s, the read-out decays exp(cum_t), and cum_last.
+constexpr int kFCum = 0, kFDt = kQ, kFW = 2 * kQ, kFE = 3 * kQ, kFTot = 4 * kQ;
+
+struct SsdParams {
+    const uint16_t* u;
+    const uint16_t* delta;
+    const float* A;
+    const uint16_t* B;
+    const uint16_t* C;
+    const float* D;
+    const uint16_t* z;       // NULL: no gate
+    const float* dt_bias;
+    const float* h0;
+    uint16_t* y;
+    float* h_last;
+    float* seg_state;        // (nseg-1, batch*nheads) blocks of P*N fp32, in lane order
+    float* seg_decay;        // (nseg-1, batch*nheads) fp32, log2 units
+    int64_t L, nheads, bh_total;
+    int nseg, cps, nchunks;
+};
+
+// ------------------------------------------------------------------ state row order
+// A 32-wide block kb of the contraction over the state index feeds MFMA slot j of
+// lane group g from row
+//     nrow(kb, g, half, j) = 32 kb + 16 (g / 2) + 8 half + (g % 2) + 2 j,
+// half = 0 for slots 0..3 and 1 for slots 4..7.  Any fixed order is correct as long
+// as both operands use it; this one makes the transposed LDS reads of B and C (four
+// rows two apart) and the row reads of B in the state product (rows of both
+// parities) free of bank conflicts at a 36-dword row stride.  The state tile nb of a
+// wave holds, at row m = 4 g + r of its MFMA result, state index
+// nrow(nb / 2, g, nb % 2, r): the same order, so the tiles 2kb and 2kb+1 of a lane
+// are exactly the B operand slots of block kb when the state is read out.
+__device__ constexpr int nrow(int kb, int g, int half, int j) {
+    return 32 * kb + 16 * (g >> 1) + 8 * half + (g & 1) + 2 * j;
+}
+
+__device__ inline float bf_half(uint32_t word, int hi) {
+    return __uint_as_float(hi ? (word & 0xFFFF0000u) : (word << 16));
+}
+
+__device__ inline uint16_t bf_bits(float v) {
+    const __bf16 b = static_cast<__bf16>(v);   // round to nearest even
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ inline f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 lds16(const uint16_t* q) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q));
+}
+
+// Transposed operand read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
+// 4a + c receives, as element j, element c of the four bf16 that lane 4j + a of the
+// group addresses.  With lane 16g + 4j + a addressing row nrow(kb, g, half, j) at
+// column col0 + 4a of a [row][col] array, lane 16g + i therefore gets the four rows'
+// entries at column col0 + i: an operand whose column is the lane and whose
+// contraction index is the row.
+__device__ inline bf16x8 lds_tr(const uint16_t* base, int kb, int col0, int lane) {
+    const int g = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + nrow(kb, g, 0, j) * kRow + col0 + 4 * a));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + nrow(kb, g, 1, j) * kRow + col0 + 4 * a));
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in fp32).
+template <int K>
+__device__ inline void split(const float (&x)[K], __bf16 (&hi)[K], __bf16 (&lo)[K]) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        hi[j] = static_cast<__bf16>(x[j]);
+        lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(hi[j]));
+    }
+}
+
+// ------------------------------------------------------------------ global I/O
+// 8 bf16 of a row starting at step t (zeros past L).  VEC: 16-byte loads, which the
+// host allows only when L % 8 == 0 and the arrays are 16-byte aligned, so a vector is
+// either wholly inside the row or wholly past its end.
+template <bool VEC>
+__device__ inline u32x4 ld8(const uint16_t* __restrict__ row, int64_t t, int64_t L) {
+    if constexpr (VEC) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (t < L) v = *reinterpret_cast<const u32x4*>(row + t);
+        return v;
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = (t + 2 * j < L) ? row[t + 2 * j] : 0u;
+            const uint32_t b = (t + 2 * j + 1 < L) ? row[t + 2 * j + 1] : 0u;
+            w[j] = a | (b << 16);
+        }
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+template <bool VEC>
+__device__ inline u32x2 ld4(const uint16_t* __restrict__ row, int64_t t, int64_t L) {
+    if constexpr (VEC) {
+        u32x2 v = {0u, 0u};
+        if (t < L) v = *reinterpret_cast<const u32x2*>(row + t);
+        return v;
+    } else {
+        uint32_t w[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t a = (t + 2 * j < L) ? row[t + 2 * j] : 0u;
+            const uint32_t b = (t + 2 * j + 1 < L) ? row[t + 2 * j + 1] : 0u;
+            w[j] = a | (b << 16);
+        }
+        return u32x2{w[0], w[1]};
+    }
+}
+
+template <bool VEC>
+__device__ inline void st4(uint16_t* __restrict__ row, int64_t t, int64_t L, u32x2 v) {
+    if constexpr (VEC) {
+        if (t < L) *reinterpret_cast<u32x2*>(row + t) = v;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (t + j < L) row[t + j] = uint16_t(j & 1 ? v[j >> 1] >> 16 : v[j >> 1] & 0xFFFFu);
+    }
+}
+
+// Raw buffer descriptors: a workgroup-uniform base and byte size in scalar
+// registers, a 32-bit per-lane byte offset and a uniform scalar offset (the chunk's
+// first step) per access; a read past the size returns zeros.  Word 3 selects 32-bit
+// data format, untyped.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// A chunk's inputs in registers: 16-byte pieces of the rows of B (and C) and u (8
+// pieces per row), thread tid taking pieces tid, tid + 256, ...; and the raw step
+// input of step t0 + lane.  Consecutive lanes take consecutive pieces of one row, so
+// loads and LDS stores are contiguous.  A thread's pieces all start at step
+// t0 + 8 (tid % 8): with VEC they are either all inside their rows or all past the
+// end, and `ok` records which, so that the pieces past the end (the next row's data,
+// or zeros past the block) are stored to LDS as zeros a chunk later, with no compare
+// between a load and its use.
+template <int N, bool WITH_C>
+struct Chunk {
+    static constexpr int kBC = (WITH_C ? 2 : 1) * N * (kQ / 8) / kThreads;
+    static constexpr int kU = kP * (kQ / 8) / kThreads;
+    u32x4 bc[kBC];
+    u32x4 u[kU];
+    bool ok;
+    uint32_t draw;
+};
+
+// Per-thread addressing of the chunk loads, fixed for the whole sequence.
+template <int N, bool WITH_C>
+struct ChunkSrc {
+    using Ch = Chunk<N, WITH_C>;
+    Rsrc rb, rc, ru, rd;
+    uint32_t off_bc[Ch::kBC];   // byte offsets of the pieces at step 0
+    uint32_t off_u[Ch::kU];
+};
+
+template <int N, bool WITH_C>
+__device__ inline void init_src(ChunkSrc<N, WITH_C>& a, const SsdParams& p, int64_t b, int64_t bh, int tid) {
+    using Ch = Chunk<N, WITH_C>;
+    const uint32_t L32 = uint32_t(p.L);
+    a.rb = make_rsrc(p.B + b * N * p.L, 2 * N * p.L);
+    a.rc = make_rsrc(p.C + b * N * p.L, 2 * N * p.L);
+    a.ru = make_rsrc(p.u + bh * kP * p.L, 2 * kP * p.L);
+    a.rd = make_rsrc(p.delta + bh * p.L, 2 * p.L);
+#pragma unroll
+    for (int q = 0; q < Ch::kBC; ++q) {
+        const int k = (tid + q * kThreads) % (N * (kQ / 8));
+        a.off_bc[q] = 2u * (uint32_t(k >> 3) * L32 + uint32_t(k & 7) * 8u);
+    }
+#pragma unroll
+    for (int q = 0; q < Ch::kU; ++q) {
+        const int i = tid + q * kThreads;
+        a.off_u[q] = 2u * (uint32_t(i >> 3) * L32 + uint32_t(i & 7) * 8u);
+    }
+}
+
+template <int N, bool WITH_C, bool VEC>
+__device__ inline void load_chunk(Chunk<N, WITH_C>& c, const ChunkSrc<N, WITH_C>& a, const SsdParams& p, int64_t b,
+                                  int64_t bh, int64_t t0, int tid) {
+    using Ch = Chunk<N, WITH_C>;
+    if constexpr (VEC) {
+        const int so = int(2 * t0);
+#pragma unroll
+        for (int q = 0; q < Ch::kBC; ++q) {
+            const bool isC = (tid + q * kThreads) >= N * (kQ / 8);
+            c.bc[q] = __builtin_amdgcn_raw_buffer_load_b128(isC ? a.rc : a.rb, a.off_bc[q], so, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < Ch::kU; ++q) c.u[q] = __builtin_amdgcn_raw_buffer_load_b128(a.ru, a.off_u[q], so, 0);
+        c.ok = t0 + (tid & 7) * 8 < p.L;
+        c.draw = __builtin_amdgcn_raw_buffer_load_b16(a.rd, 2u * uint32_t(tid & 63), so, 0);
+    } else {
+#pragma unroll
+        for (int q = 0; q < Ch::kBC; ++q) {
+            const int i = tid + q * kThreads;
+            const int arr = i / (N * (kQ / 8)), k = i % (N * (kQ / 8));
+            c.bc[q] = ld8<false>((arr ? p.C : p.B) + (b * N + (k >> 3)) * p.L, t0 + (k & 7) * 8, p.L);
+        }
+#pragma unroll
+        for (int q = 0; q < Ch::kU; ++q) {
+            const int i = tid + q * kThreads;
+            c.u[q] = ld8<false>(p.u + (bh * kP + (i >> 3)) * p.L, t0 + (i & 7) * 8, p.L);
+        }
+        c.ok = true;
+        const int64_t t = t0 + (tid & 63);
+        c.draw = t < p.L ? p.delta[bh * p.L + t] : 0;
+    }
+}
+
+template <int N, bool WITH_C>
+__device__ inline void store_chunk(const Chunk<N, WITH_C>& c, uint16_t* lds, int bn, int cn, int un, int tid,
+                                   bool full) {
+    using Ch = Chunk<N, WITH_C>;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // `full` (the whole chunk inside the sequence) is uniform: no per-piece select then
+    const bool ok = full || c.ok;
+#pragma unroll
+    for (int q = 0; q < Ch::kBC; ++q) {
+        const int i = tid + q * kThreads;
+        const int arr = i / (N * (kQ / 8)), k = i % (N * (kQ / 8));
+        u32x4* dst = reinterpret_cast<u32x4*>(lds + (arr ? cn : bn) + (k >> 3) * kRow + (k & 7) * 8);
+        if (full) *dst = c.bc[q];
+        else *dst = ok ? c.bc[q] : zero;
+    }
+#pragma unroll
+    for (int q = 0; q < Ch::kU; ++q) {
+        const int i = tid + q * kThreads;
+        u32x4* dst = reinterpret_cast<u32x4*>(lds + un + (i >> 3) * kRow + (i & 7) * 8);
+        if (full) *dst = c.u[q];
+        else *dst = ok ? c.u[q] : zero;
+    }
+}
+
+// One wave, one step per lane: step sizes (in log2 units, dl2 = dt / ln 2, so that the
+// decay exp(dt a) is exp2(dl2 a)), their decay prefix inside the chunk, and the
+// per-step weights.  Steps past L get dt = 0: they leave the state unchanged and add
+// nothing, so the last chunk needs no other masking.
+__device__ inline void stage_steps(uint32_t draw, bool valid, float a, float bias, float* sf, int lane) {
+    const float dl2 = valid ? softplus_log2(__uint_as_float(draw << 16) + bias) : 0.0f;
+    float cum = dl2 * a;
+#pragma unroll
+    for (int o = 1; o < kLanes; o <<= 1) {
+        const float v = __shfl_up(cum, o);
+        if (lane >= o) cum += v;
+    }
+    const float tot = __shfl(cum, kLanes - 1);
+    const float dt = dl2 * kLn2;
+    sf[kFCum + lane] = cum;
+    sf[kFDt + lane] = dt;
+    sf[kFW + lane] = __builtin_amdgcn_exp2f(tot - cum) * dt;
+    sf[kFE + lane] = __builtin_amdgcn_exp2f(cum);
+    if (lane == 0) sf[kFTot] = tot;
+}
+
+// ------------------------------------------------------------------ the state
+// H[nb] (nb < N/16) is the wave's state tile nb: result row m = 4 lg + r holds state
+// index nrow(nb / 2, lg, nb % 2, r), column lr holds channel 16 w + lr.
+//
+// The chunk's contribution: H <- exp2(cum_last) H + B[n][s] X[s][p], X[s][p] = w_s u[s][p],
+// contracted over the chunk's 64 steps in two 32-step blocks.
+template <int N>
+__device__ inline void chunk_state(f32x4 (&H)[N / 16], const uint16_t* sBn, const uint16_t* sU, const float* sf,
+                                   int w, int lr, int lg) {
+    const float dec = __builtin_amdgcn_exp2f(sf[kFTot]);
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) H[nb] *= dec;
+#pragma unroll
+    for (int kb = 0; kb < kQ / 32; ++kb) {
+        const int s0 = 32 * kb + 8 * lg;
+        const u32x4 uv = *reinterpret_cast<const u32x4*>(sU + (16 * w + lr) * kRow + s0);
+        float xv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = sf[kFW + s0 + j] * bf_half(uv[j >> 1], j & 1);
+        __bf16 xh[8], xl[8];
+        split<8>(xv, xh, xl);
+        bf16x8 xo_h, xo_l;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            xo_h[j] = xh[j];
+            xo_l[j] = xl[j];
+        }
+#pragma unroll
+        for (int nb = 0; nb < N / 16; ++nb) {
+            const bf16x8 bo = lds16(sBn + nrow(nb >> 1, lr >> 2, nb & 1, lr & 3) * kRow + s0);
+            H[nb] = mfma(bo, xo_h, H[nb]);
+            H[nb] = mfma(bo, xo_l, H[nb]);
+        }
+    }
+}
+
+// Block k of the workspace's segment states holds tile nb of wave w at
+// ((k * NB + nb) * 4 + w) * 64 + lane, four floats each (the register layout).
+template <int N>
+__device__ inline int64_t seg_index(int64_t k, int nb, int w, int lane) {
+    return (((k * (N / 16) + nb) * kWaves + w) * kLanes + lane) * 4;
+}
+
+// ------------------------------------------------------------------ pass 1: segment end states
+template <int N, bool VEC>
+__global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
+    using Lay = StateLds<N>;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    float* sf = reinterpret_cast<float*>(lds + Lay::F);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int nsm = p.nseg - 1;
+    const int seg = int(blockIdx.x % unsigned(nsm));
+    const int64_t bh = blockIdx.x / unsigned(nsm);
+    const int64_t b = bh / p.nheads, h = bh % p.nheads;
+    const float a = p.A[h];
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+
+    f32x4 H[N / 16];
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) H[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float dsum = 0.0f;
+    const int c0 = seg * p.cps, c1 = min(c0 + p.cps, p.nchunks);
+    Chunk<N, false> nx;
+    ChunkSrc<N, false> src;
+    init_src<N, false>(src, p, b, bh, tid);
+    load_chunk<N, false, VEC>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    for (int c = c0; c < c1; ++c) {
+        const int64_t t0 = int64_t(c) * kQ;
+        __syncthreads();
+        store_chunk<N, false>(nx, lds, Lay::Bn, 0, Lay::U, tid, t0 + kQ <= p.L);
+        if (w == 0) stage_steps(nx.draw, t0 + l < p.L, a, bias, sf, l);
+        if (c + 1 < c1) load_chunk<N, false, VEC>(nx, src, p, b, bh, t0 + kQ, tid);
+        __syncthreads();
+        dsum += sf[kFTot];
+        chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
+    }
+    const int64_t k = int64_t(seg) * p.bh_total + bh;
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb)
+        *reinterpret_cast<f32x4*>(p.seg_state + seg_index<N>(k, nb, w, l)) = H[nb];
+    if (tid == 0) p.seg_decay[k] = dsum;
+}
+
+// ------------------------------------------------------------------ pass 2: outputs
+// The 10 lower-triangular 16x16 tiles (t block tb, s block sb <= tb) of a chunk's
+// masked decay matrix, numbered row by row; wave w computes tiles w, w + 4 and w + 8.
+__device__ inline int tile_t(int ti) { return (ti >= 1) + (ti >= 3) + (ti >= 6); }
+__device__ inline int tile_s(int ti) { const int tb = tile_t(ti); return ti - tb * (tb + 1) / 2; }
+
+template <int N, bool VEC, bool GATE>
+__global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
+    using Lay = OutLds<N>;
+    constexpr int NK = N / 32;    // 32-wide blocks of the state index
+    constexpr int NB = N / 16;    // state tiles per wave
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    float* sf = reinterpret_cast<float*>(lds + Lay::F);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int seg = int(blockIdx.x % unsigned(p.nseg));
+    const int64_t bh = blockIdx.x / unsigned(p.nseg);
+    const int64_t b = bh / p.nheads, h = bh % p.nheads;
+    const float a = p.A[h];
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const int pc = 16 * w + lr;                          // the lane's channel within the head
+    const float Dp = p.D ? p.D[h * kP + pc] : 0.0f;
+    const uint16_t* zb = p.z + bh * kP * p.L;            // the head's rows
+    uint16_t* yb = p.y + bh * kP * p.L;
+    const Rsrc rz = make_rsrc(GATE ? zb : p.u, 2 * kP * p.L);
+    const Rsrc ry = make_rsrc(yb, 2 * kP * p.L);
+    const uint32_t prow = uint32_t(pc) * uint32_t(p.L);
+    const uint32_t lane_off = 2u * (prow + 4u * uint32_t(lg));   // bytes: channel pc, step 4 lg
+
+    // state entering the segment: h0 carried through the segments before it
+    f32x4 H[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.h0) {
+            const float* hr = p.h0 + (bh * kP + pc) * N + nrow(nb >> 1, lg, nb & 1, 0);
+            v = f32x4{hr[0], hr[2], hr[4], hr[6]};
+        }
+        for (int j = 0; j < seg; ++j) {
+            const int64_t k = int64_t(j) * p.bh_total + bh;
+            const float dec = __builtin_amdgcn_exp2f(p.seg_decay[k]);
+            v = dec * v + *reinterpret_cast<const f32x4*>(p.seg_state + seg_index<N>(k, nb, w, l));
+        }
+        H[nb] = v;
+    }
+    // the tiles of M above the diagonal that the 32-step contraction blocks include
+    // (t block 0 x s block 1, t block 2 x s block 3) stay zero
+    for (int i = tid; i < 2 * 16 * 16; i += kThreads) {
+        const int blk = i >> 8, r = (i >> 4) & 15, col = i & 15;
+        const int off = (32 * blk + r) * kRow + 32 * blk + 16 + col;
+        lds[Lay::Mhi + off] = 0;
+        lds[Lay::Mlo + off] = 0;
+    }
+
+    const int c0 = seg * p.cps, c1 = min(c0 + p.cps, p.nchunks);
+    Chunk<N, true> nx;
+    ChunkSrc<N, true> src;
+    init_src<N, true>(src, p, b, bh, tid);
+    load_chunk<N, true, VEC>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    for (int c = c0; c < c1; ++c) {
+        const int64_t t0 = int64_t(c) * kQ;
+        __syncthreads();
+        store_chunk<N, true>(nx, lds, Lay::Bn, Lay::Cn, Lay::U, tid, t0 + kQ <= p.L);
+        if (w == 0) stage_steps(nx.draw, t0 + l < p.L, a, bias, sf, l);
+        if (c + 1 < c1) load_chunk<N, true, VEC>(nx, src, p, b, bh, t0 + kQ, tid);
+        // gate inputs of the lane's outputs: steps 16 tb + 4 lg .. +3 of channel pc (a
+        // step past L reads the row's last four; its output is not stored)
+        u32x2 zr[4];
+        if constexpr (GATE) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                if constexpr (VEC)
+                    zr[tb] = __builtin_amdgcn_raw_buffer_load_b64(rz, lane_off + 32u * tb, int(2 * t0), 0);
+                else
+                    zr[tb] = ld4<false>(zb + prow, t0 + 16 * tb + 4 * lg, p.L);
+            }
+        }
+        __syncthreads();
+
+        // masked decay tiles: M[t][s] = GT[s][t] exp2(cum_t - cum_s) dt_s for s <= t,
+        // GT[s][t] = sum_n B[n][s] C[n][t]; result row 4 lg + r is step s, column lr step t
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int ti = w + 4 * k;
+            if (ti < 10) {
+                const int tb = tile_t(ti), sb = tile_s(ti);
+                f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kb = 0; kb < NK; ++kb)
+                    g = mfma(lds_tr(lds + Lay::Bn, kb, 16 * sb, l), lds_tr(lds + Lay::Cn, kb, 16 * tb, l), g);
+                const int t = 16 * tb + lr;
+                const float cum_t = sf[kFCum + t];
+                float m[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * sb + 4 * lg + r;
+                    const float e = __builtin_amdgcn_exp2f(cum_t - sf[kFCum + s]) * sf[kFDt + s];
+                    m[r] = s <= t ? g[r] * e : 0.0f;
+                }
+                __bf16 mh[4], ml[4];
+                split<4>(m, mh, ml);
+                uint16_t hb[4], lb[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    hb[r] = __builtin_bit_cast(uint16_t, mh[r]);
+                    lb[r] = __builtin_bit_cast(uint16_t, ml[r]);
+                }
+                const int off = t * kRow + 16 * sb + 4 * lg;
+                *reinterpret_cast<u32x2*>(lds + Lay::Mhi + off) =
+                    u32x2{hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16)};
+                *reinterpret_cast<u32x2*>(lds + Lay::Mlo + off) =
+                    u32x2{lb[0] | (uint32_t(lb[1]) << 16), lb[2] | (uint32_t(lb[3]) << 16)};
+            }
+        }
+
+        // read-out of the chunk's starting state: yo[tb][t][p] = sum_n C[n][t] H[n][p]
+        f32x4 yo[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) yo[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < NK; ++kb) {
+            float hv[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hv[r] = H[2 * kb][r];
+                hv[4 + r] = H[2 * kb + 1][r];
+            }
+            __bf16 hh[8], hl[8];
+            split<8>(hv, hh, hl);
+            bf16x8 ho_h, ho_l;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                ho_h[j] = hh[j];
+                ho_l[j] = hl[j];
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const bf16x8 co = lds_tr(lds + Lay::Cn, kb, 16 * tb, l);
+                yo[tb] = mfma(co, ho_h, yo[tb]);
+                yo[tb] = mfma(co, ho_l, yo[tb]);
+            }
+        }
+
+        chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
+        __syncthreads();   // M complete
+
+        // within the chunk: yd[tb][t][p] = sum_{s} M[t][s] u[s][p] over the 32-step
+        // blocks that reach the diagonal of t block tb
+        f32x4 yd[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            yd[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb <= tb / 2; ++kb) {
+                const int s0 = 32 * kb + 8 * lg;
+                const bf16x8 uo = lds16(lds + Lay::U + pc * kRow + s0);
+                const int moff = (16 * tb + lr) * kRow + s0;
+                yd[tb] = mfma(lds16(lds + Lay::Mhi + moff), uo, yd[tb]);
+                yd[tb] = mfma(lds16(lds + Lay::Mlo + moff), uo, yd[tb]);
+            }
+        }
+
+        // y = (yd + exp(cum_t) yo + D u) SiLU(z); the lane owns steps 16 tb + 4 lg + r
+        const bool full = VEC && t0 + kQ <= p.L;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int tq = 16 * tb + 4 * lg;
+            const f32x4 e4 = *reinterpret_cast<const f32x4*>(sf + kFE + tq);
+            const u32x2 uu = *reinterpret_cast<const u32x2*>(lds + Lay::U + pc * kRow + tq);
+            uint32_t o[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float v[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = 2 * q + e;
+                    float x = fmaf(e4[r], yo[tb][r], yd[tb][r]);
+                    x = fmaf(Dp, bf_half(uu[q], e), x);
+                    if constexpr (GATE) x *= silu_f32(bf_half(zr[tb][q], e));
+                    v[e] = x;
+                }
+                o[q] = uint32_t(bf_bits(v[0])) | (uint32_t(bf_bits(v[1])) << 16);
+            }
+            if (full)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{o[0], o[1]}, ry, lane_off + 32u * tb, int(2 * t0), 0);
+            else
+                st4<false>(yb + prow, t0 + tq, p.L, u32x2{o[0], o[1]});
+        }
+    }
+
+    if (p.h_last && seg == p.nseg - 1) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float* hr = p.h_last + (bh * kP + pc) * N + nrow(nb >> 1, lg, nb & 1, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hr[2 * r] = H[nb][r];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host side
+struct SsdPlan {
+    int nseg, cps, nchunks;
+    int64_t bh_total;
+    size_t ws_bytes, state_floats;
+};
+
+inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int ssd_plan(const ssm_ssd_dims* d, SsdPlan* pl) {
+    if (!d) return SSM_ERR_NULL;
+    if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1) return SSM_ERR_EMPTY;
+    if (d->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (d->headdim != kP || (d->dstate != 64 && d->dstate != 128)) return SSM_ERR_DIMS;
+    if (d->nsegments < 0 || d->nsegments > SSM_MAX_CHUNKS || d->reserved != 0) return SSM_ERR_DIMS;
+    const int64_t lim = int64_t(1) << 40;
+    if (d->batch > lim / d->nheads) return SSM_ERR_DIMS;
+    const int64_t bh = d->batch * d->nheads;
+    if (bh > lim / (kP * d->seqlen) || bh > lim / (d->dstate * kP)) return SSM_ERR_DIMS;
+    if (d->batch > lim / (d->dstate * d->seqlen)) return SSM_ERR_DIMS;
+    // kernels address a head's (64, L) block of u, z and y and a batch row's (N, L)
+    // block of B and C through buffer descriptors of at most 2^31 - 1 bytes
+    if (d->seqlen > (int64_t(1) << 31) / (2 * kP) || d->seqlen > (int64_t(1) << 31) / (2 * d->dstate))
+        return SSM_ERR_DIMS;
+    const int64_t nchunks = cdiv(d->seqlen, kQ);
+    if (nchunks > (int64_t(1) << 30)) return SSM_ERR_DIMS;
+    // default: enough workgroups to give every compute unit one (the output pass holds
+    // one workgroup per CU at N = 128)
+    int64_t nseg = d->nsegments ? d->nsegments : cdiv(256, bh);
+    nseg = std::min<int64_t>(std::max<int64_t>(nseg, 1), nchunks);
+    const int64_t cps = cdiv(nchunks, nseg);
+    nseg = cdiv(nchunks, cps);
+    if (nseg * bh > int64_t(INT32_MAX)) return SSM_ERR_DIMS;
+    pl->nseg = int(nseg);
+    pl->cps = int(cps);
+    pl->nchunks = int(nchunks);
+    pl->bh_total = bh;
+    pl->state_floats = size_t(nseg - 1) * size_t(bh) * size_t(kP) * size_t(d->dstate);  // P*N per head
+    pl->ws_bytes = nseg > 1 ? round256(pl->state_floats * 4) + round256(size_t(nseg - 1) * size_t(bh) * 4) : 0;
+    return SSM_OK;
+}
+
+template <int N, bool VEC>
+int ssd_launch(const SsdParams& p, const SsdPlan& pl, hipStream_t s) {
+    if (pl.nseg > 1) {
+        hipLaunchKernelGGL((ssd_state_kernel<N, VEC>), dim3(unsigned((pl.nseg - 1) * pl.bh_total)), dim3(kThreads),
+                           StateLds<N>::bytes, s, p);
+    }
+    const dim3 grid(unsigned(pl.nseg * pl.bh_total));
+    if (p.z)
+        hipLaunchKernelGGL((ssd_out_kernel<N, VEC, true>), grid, dim3(kThreads), OutLds<N>::bytes, s, p);
+    else
+        hipLaunchKernelGGL((ssd_out_kernel<N, VEC, false>), grid, dim3(kThreads), OutLds<N>::bytes, s, p);
+    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" SSM_API size_t ssm_ssd_fwd_workspace_bytes(const ssm_ssd_dims* dims) {
+    SsdPlan pl;
+    return ssd_plan(dims, &pl) == SSM_OK ? pl.ws_bytes : 0;
+}
+
+extern "C" SSM_API int ssm_ssd_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                   const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
+                                   float* h_last, const ssm_ssd_dims* dims, void* stream) {
+    SsdPlan pl;
+    const int st = ssd_plan(dims, &pl);
+    if (st != SSM_OK) return st;
+    if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+    for (const void* q : {u, delta, B, C, z, static_cast<const void*>(y)})
+        if (misaligned(q, 2)) return SSM_ERR_ALIGN;
+    for (const void* q : {static_cast<const void*>(A), static_cast<const void*>(D),
+                          static_cast<const void*>(dt_bias)})
+        if (misaligned(q, 4)) return SSM_ERR_ALIGN;
+    if (misaligned(h0, 4) || misaligned(h_last, 4)) return SSM_ERR_ALIGN;
+
+    const int64_t N = dims->dstate, L = dims->seqlen, H = dims->nheads, dim = H * kP;
+    const size_t io = size_t(dims->batch * dim * L) * 2, dl = size_t(dims->batch * H * L) * 2;
+    const size_t bc = size_t(dims->batch * N * L) * 2, stb = size_t(dims->batch * dim * N) * 4;
+    const size_t hb = size_t(H) * 4, db = size_t(dim) * 4;
+    const struct {
+        const void* q;
+        size_t n;
+    } ins[] = {{u, io}, {delta, dl}, {B, bc}, {C, bc}, {z, io}, {A, hb}, {D, db}, {dt_bias, hb}, {h0, stb}};
+    for (const auto& in : ins) {
+        if (overlaps(y, io, in.q, in.n)) return SSM_ERR_ALIAS;
+        if (overlaps(h_last, stb, in.q, in.n)) return SSM_ERR_ALIAS;
+    }
+    if (overlaps(h_last, stb, y, io)) return SSM_ERR_ALIAS;
+
+    SsdParams p{};
+    if (pl.ws_bytes) {
+        if (!dims->workspace || dims->workspace_bytes < pl.ws_bytes || misaligned(dims->workspace, 256))
+            return SSM_ERR_WORKSPACE;
+        p.seg_state = static_cast<float*>(dims->workspace);
+        p.seg_decay = reinterpret_cast<float*>(static_cast<char*>(dims->workspace) + round256(pl.state_floats * 4));
+    }
+    p.u = static_cast<const uint16_t*>(u);
+    p.delta = static_cast<const uint16_t*>(delta);
+    p.A = A;
+    p.B = static_cast<const uint16_t*>(B);
+    p.C = static_cast<const uint16_t*>(C);
+    p.D = D;
+    p.z = static_cast<const uint16_t*>(z);
+    p.dt_bias = dt_bias;
+    p.h0 = h0;
+    p.y = static_cast<uint16_t*>(y);
+    p.h_last = h_last;
+    p.L = L;
+    p.nheads = H;
+    p.bh_total = pl.bh_total;
+    p.nseg = pl.nseg;
+    p.cps = pl.cps;
+    p.nchunks = pl.nchunks;
+
+    bool vec = L % 8 == 0;
+    for (const void* q : {u, B, C, z, static_cast<const void*>(y)}) vec = vec && !misaligned(q, 16);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (N == 128) return vec ? ssd_launch<128, true>(p, pl, s) : ssd_launch<128, false>(p, pl, s);
+    return vec ? ssd_launch<64, true>(p, pl, s) : ssd_launch<64, false>(p, pl, s);
+}

@@ -296,3 +296,63 @@ def test_conv_entry_points_refuse_bad_arguments():
     assert step(ssm.SsmConv(W, None, 4, 1), None) == ssm.SSM_ERR_NULL       # width > 1 needs a state
     assert step(ssm.SsmConv(W, None, 4, 1), FAKE) == ssm.SSM_ERR_ALIAS      # state overlaps x
     assert step(ssm.SsmConv(W, None, 9, 1), 0x70000000) == ssm.SSM_ERR_DIMS
+
+
+def _ssd_call(dims, u=FAKE, delta=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000,
+              D=None, z=None, bias=None, h0=None, y=FAKE + 0x500000, h_last=None):
+    lib = ssm.load_library()
+    args = [None if a is None else ctypes.c_void_p(a) for a in (u, delta, A, B, C, D, z, bias, h0, y, h_last)]
+    return lib.ssm_ssd_fwd(*args, ctypes.byref(dims) if dims is not None else None, None)
+
+
+def _ssd_dims(**kw):
+    base = dict(batch=1, seqlen=64, nheads=2, dstate=64)
+    base.update({k: kw.pop(k) for k in list(kw) if k in base})
+    return ssm.make_ssd_dims(base["batch"], base["seqlen"], base["nheads"], base["dstate"], **kw)
+
+
+def test_ssd_refusals():
+    E = ssm
+    assert _ssd_call(None) == E.SSM_ERR_NULL
+    for field in ("batch", "seqlen", "nheads", "dstate"):
+        assert _ssd_call(_ssd_dims(**{field: 0})) == E.SSM_ERR_EMPTY
+    assert _ssd_call(_ssd_dims(headdim=0)) == E.SSM_ERR_EMPTY
+    assert _ssd_call(_ssd_dims(io_dtype=E.SSM_F32)) == E.SSM_ERR_DTYPE
+    assert _ssd_call(_ssd_dims(io_dtype=9)) == E.SSM_ERR_DTYPE
+    assert _ssd_call(_ssd_dims(headdim=32)) == E.SSM_ERR_DIMS
+    for n in (16, 32, 96, 256):
+        assert _ssd_call(_ssd_dims(dstate=n)) == E.SSM_ERR_DIMS
+    assert _ssd_call(_ssd_dims(nsegments=-1)) == E.SSM_ERR_DIMS
+    assert _ssd_call(_ssd_dims(nsegments=E.SSM_MAX_CHUNKS + 1)) == E.SSM_ERR_DIMS
+    assert _ssd_call(_ssd_dims(reserved=1)) == E.SSM_ERR_DIMS
+    assert _ssd_call(_ssd_dims(batch=1 << 30, seqlen=1 << 20)) == E.SSM_ERR_DIMS
+    for name in ("u", "delta", "A", "B", "C", "y"):
+        assert _ssd_call(_ssd_dims(), **{name: None}) == E.SSM_ERR_NULL
+    assert _ssd_call(_ssd_dims(), u=FAKE + 1) == E.SSM_ERR_ALIGN
+    assert _ssd_call(_ssd_dims(), A=FAKE + 0x200002) == E.SSM_ERR_ALIGN
+    assert _ssd_call(_ssd_dims(), h0=FAKE + 0x600002) == E.SSM_ERR_ALIGN
+    assert _ssd_call(_ssd_dims(), h_last=FAKE + 0x700002) == E.SSM_ERR_ALIGN
+    assert _ssd_call(_ssd_dims(), y=FAKE) == E.SSM_ERR_ALIAS
+    assert _ssd_call(_ssd_dims(), z=FAKE + 0x600000, y=FAKE + 0x600000 + 64) == E.SSM_ERR_ALIAS
+    assert _ssd_call(_ssd_dims(), h0=FAKE + 0x600000, h_last=FAKE + 0x600000) == E.SSM_ERR_ALIAS
+    assert _ssd_call(_ssd_dims(), h_last=FAKE + 0x500000) == E.SSM_ERR_ALIAS
+    # a forced second segment needs a workspace
+    d = _ssd_dims(seqlen=256, nsegments=2)
+    assert _ssd_call(d) == E.SSM_ERR_WORKSPACE
+    need = ssm.ssm_ssd_fwd_workspace_bytes(d)
+    d.workspace, d.workspace_bytes = FAKE + 0x800000, need - 1
+    assert _ssd_call(d) == E.SSM_ERR_WORKSPACE
+    d.workspace, d.workspace_bytes = FAKE + 0x800000 + 128, need
+    assert _ssd_call(d) == E.SSM_ERR_WORKSPACE
+
+
+def test_ssd_workspace_sizes():
+    r = lambda x: (x + 255) // 256 * 256
+    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(nsegments=1)) == 0
+    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(seqlen=64, nsegments=4)) == 0   # one chunk: one piece
+    d = _ssd_dims(batch=2, seqlen=8192, nheads=64, dstate=128, nsegments=4)
+    assert ssm.ssm_ssd_fwd_workspace_bytes(d) == r(3 * 128 * 64 * 128 * 4) + r(3 * 128 * 4)
+    # pieces are whole chunks: 10 chunks in 4 pieces of 3 chunks leave 4 pieces
+    d = _ssd_dims(batch=1, seqlen=640, nheads=1, dstate=64, nsegments=4)
+    assert ssm.ssm_ssd_fwd_workspace_bytes(d) == r(3 * 64 * 64 * 4) + r(3 * 4)
+    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(dstate=32)) == 0
