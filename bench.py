@@ -94,11 +94,11 @@ def cpu_baseline(x, rows_batches: int, repeats: int = 3):
 PROFILE_COMMANDS = {
     "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/stats -o scan -- python3 bench.py",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/fetch -o scan -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward --no-decode",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward --no-decode --no-ssd",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/write -o scan -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward --no-decode",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward --no-decode --no-ssd",
     "conv_stats": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/convstats -o conv -- "
-                  "python3 bench.py --steps 200 --warmup 50 --no-cpu-baseline --no-backward --no-decode --fused-conv",
+                  "python3 bench.py --steps 200 --warmup 50 --no-cpu-baseline --no-backward --no-decode --no-ssd --fused-conv",
     "copyfetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/copyfetch -o copy -- "
                  "python3 bench.py --calibrate-copy",
     "copywrite": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/copywrite -o copy -- "
@@ -370,6 +370,91 @@ def backward_bench(x, dev, steps: int = 30, warmup: int = 5):
             "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def ssd_bench(steps: int = 50, warmup: int = 10):
+    """Time ssm_ssd_fwd, the chunked state-space-duality pass, on the scalar-decay
+    large-state workload with one step size per head (batch 2, L 8192, 64 heads x 64
+    channels, N 128, bf16 I/O); one call = both of its kernels.  The per-channel scan
+    (ssm_selective_scan_fwd in scalar-decay mode) is timed on the same inputs, each
+    head's step input repeated over its channels."""
+    import torch
+    import selective_state_space_79_amd as ssm
+    from selective_state_space_79_amd.inputs import SSD_WORKLOADS, make_ssd_workload, ssd_to_device, to_device
+
+    x = make_ssd_workload()
+    d = ssd_to_device(x, "cuda:0")
+    y = torch.empty_like(d["u"])
+    dims = ssm.make_ssd_dims(x.batch, x.L, x.nheads, x.N, headdim=x.headdim)
+    need = ssm.ssm_ssd_fwd_workspace_bytes(dims)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda:0")
+    dims.workspace, dims.workspace_bytes = ws.data_ptr(), need
+    stream = torch.cuda.current_stream()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (p(d["u"]), p(d["delta"]), p(d["A"]), p(d["B"]), p(d["C"]), p(d["D"]), p(d["z"]), p(d["dt_bias"]), None,
+            p(y), None, ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream))
+    fn = ssm.load_library().ssm_ssd_fwd
+
+    def timed(call, n, w):
+        for _ in range(w):
+            st = call()
+            if st != 0:
+                raise ssm.SsmError(st, "bench call")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(lambda: fn(*args), steps, warmup)
+    # the per-channel scan on the same inputs
+    sc = to_device(x.per_channel(), "cuda:0")
+    ys = torch.empty_like(sc["u"])
+    sdims = ssm.dims_for(sc["u"], sc["B"], sc["A"])
+    splan = ssm.ssm_selective_scan_plan(sdims).as_dict()
+    sws = torch.empty(max(splan["workspace_bytes"], 1), dtype=torch.uint8, device="cuda:0")
+    sdims.workspace, sdims.workspace_bytes = sws.data_ptr(), splan["workspace_bytes"]
+    sargs = (p(sc["u"]), p(sc["delta"]), p(sc["A"]), p(sc["B"]), p(sc["C"]), p(sc["D"]), p(sc["z"]),
+             p(sc["dt_bias"]), p(ys), ctypes.byref(sdims), ctypes.c_void_p(stream.cuda_stream))
+    sfn = ssm.load_library().ssm_selective_scan_fwd
+    ms_scan = timed(lambda: sfn(*sargs), max(steps // 5, 5), 3)
+    del sc, ys, sws
+
+    # algorithmic bytes: u, z read and y written per (b,t,d); the step input per
+    # (b,h,t); B and C per (b,t,n); A, dt_bias per head and D per channel
+    nbytes = (3 * 2 * x.batch * x.L * x.dim + 2 * x.batch * x.nheads * x.L + 2 * 2 * x.batch * x.N * x.L
+              + 4 * (2 * x.nheads + x.dim))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # matrix work the chunked method issues per head and 64-step chunk: 10 lower-
+    # triangular 16x16 tiles of C^T B (N-deep), the masked product (6 16x32 blocks per
+    # 16 channels, two bf16 parts), the state read and the state update (N x 64 x 64
+    # each, two parts); the end states of all but the last segment repeat the update
+    seg = ssm.ssm_ssd_fwd_workspace_bytes(dims)
+    nseg = 1
+    if seg:
+        per_seg = -(-(x.batch * x.nheads * x.headdim * x.N * 4) // 256) * 256
+        nseg = 1 + seg // per_seg
+    chunks = x.batch * x.nheads * -(-x.L // 64)
+    mac_chunk = 10 * 256 * x.N + 2 * 4 * 6 * 16 * 16 * 32 + 2 * 64 * 64 * x.N + 2 * x.N * 64 * 64
+    mac_state = 2 * x.N * 64 * 64 * (nseg - 1) / nseg
+    tflops = 2 * chunks * (mac_chunk + mac_state) / (ms * 1e-3) / 1e12
+    return {"workload": f"{SSD_WORKLOADS[5]['name']}: batch {x.batch}, L {x.L}, {x.nheads} heads x {x.headdim}, "
+                        f"N {x.N}, bf16 I/O, one step size per head",
+            "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3), "segments": nseg,
+            "hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes},
+            "mfma": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "note": "bf16 matrix FLOPs the chunked method issues (operands split in two bf16 parts)"},
+            "per_channel_scan_same_inputs": {"ms_per_call": round(ms_scan, 4),
+                                             "updates_per_s": x.updates / (ms_scan * 1e-3),
+                                             "speedup_of_chunked": round(ms_scan / ms, 2)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -379,6 +464,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
+    ap.add_argument("--no-ssd", action="store_true",
+                    help="skip the chunked scalar-decay (per-head step) pass on the large-state workload")
     ap.add_argument("--fused-conv", action="store_true",
                     help="also time the fused convolution front end (same scan kernel, so off by default: "
                          "its launches would mix into the scan kernel's profile)")
@@ -498,6 +585,10 @@ def main():
         rec["fused_conv"] = fused_conv_bench(x, dev)
     if not args.no_backward:
         rec["backward"] = backward_bench(x, dev)
+    if not args.no_ssd:
+        del dev, y
+        torch.cuda.empty_cache()
+        rec["ssd"] = ssd_bench()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_batches)
     print(json.dumps(rec), flush=True)

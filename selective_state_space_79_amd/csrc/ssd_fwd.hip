@@ -94,17 +94,24 @@ struct SsdParams {
 // ------------------------------------------------------------------ state row order
 // A 32-wide block kb of the contraction over the state index feeds MFMA slot j of
 // lane group g from row
-//     nrow(kb, g, half, j) = 32 kb + 16 (g / 2) + 8 half + (g % 2) + 2 j,
+//     nrow(kb, g, half, j) = 32 kb + 16 half + 8 (g % 2) + g / 2 + 2 j,
 // half = 0 for slots 0..3 and 1 for slots 4..7.  Any fixed order is correct as long
-// as both operands use it; this one makes the transposed LDS reads of B and C (four
-// rows two apart) and the row reads of B in the state product (rows of both
-// parities) free of bank conflicts at a 36-dword row stride.  The state tile nb of a
-// wave holds, at row m = 4 g + r of its MFMA result, state index
-// nrow(nb / 2, g, nb % 2, r): the same order, so the tiles 2kb and 2kb+1 of a lane
-// are exactly the B operand slots of block kb when the state is read out.
+// as both operands use it.  This one keeps the LDS reads free of bank conflicts with
+// 64 four-byte banks and a 36-dword row stride, where row r starts at bank
+// 4 * (9 r mod 16): a transposed read (two lane groups, rows 2 apart in each, 8 rows
+// apart between the groups) and a 16-lane row read in the state product (rows of all
+// 16 residues mod 16) both touch every bank once.  The state tile nb of a wave holds,
+// at row m = 4 g + r of its MFMA result, state index nrow(nb / 2, g, nb % 2, r): the
+// same order, so the tiles 2kb and 2kb+1 of a lane are exactly the B operand slots of
+// block kb when the state is read out.
 __device__ constexpr int nrow(int kb, int g, int half, int j) {
-    return 32 * kb + 16 * (g >> 1) + 8 * half + (g & 1) + 2 * j;
+    return 32 * kb + 16 * half + 8 * (g & 1) + (g >> 1) + 2 * j;
 }
+
+// Row of piece k (16 bytes, 8 steps) of a chunk's [row][step] array: lanes 8s .. 8s+7 of
+// each 16 take the 8 pieces of one row, and the two halves of the 16 take rows 8
+// apart, whose starts are 32 banks apart.
+__device__ constexpr int piece_row(int k) { return 16 * (k >> 7) + ((k >> 4) & 7) + 8 * ((k >> 3) & 1); }
 
 __device__ inline float bf_half(uint32_t word, int hi) {
     return __uint_as_float(hi ? (word & 0xFFFF0000u) : (word << 16));
@@ -248,12 +255,12 @@ __device__ inline void init_src(ChunkSrc<N, WITH_C>& a, const SsdParams& p, int6
 #pragma unroll
     for (int q = 0; q < Ch::kBC; ++q) {
         const int k = (tid + q * kThreads) % (N * (kQ / 8));
-        a.off_bc[q] = 2u * (uint32_t(k >> 3) * L32 + uint32_t(k & 7) * 8u);
+        a.off_bc[q] = 2u * (uint32_t(piece_row(k)) * L32 + uint32_t(k & 7) * 8u);
     }
 #pragma unroll
     for (int q = 0; q < Ch::kU; ++q) {
         const int i = tid + q * kThreads;
-        a.off_u[q] = 2u * (uint32_t(i >> 3) * L32 + uint32_t(i & 7) * 8u);
+        a.off_u[q] = 2u * (uint32_t(piece_row(i)) * L32 + uint32_t(i & 7) * 8u);
     }
 }
 
@@ -277,12 +284,12 @@ __device__ inline void load_chunk(Chunk<N, WITH_C>& c, const ChunkSrc<N, WITH_C>
         for (int q = 0; q < Ch::kBC; ++q) {
             const int i = tid + q * kThreads;
             const int arr = i / (N * (kQ / 8)), k = i % (N * (kQ / 8));
-            c.bc[q] = ld8<false>((arr ? p.C : p.B) + (b * N + (k >> 3)) * p.L, t0 + (k & 7) * 8, p.L);
+            c.bc[q] = ld8<false>((arr ? p.C : p.B) + (b * N + piece_row(k)) * p.L, t0 + (k & 7) * 8, p.L);
         }
 #pragma unroll
         for (int q = 0; q < Ch::kU; ++q) {
             const int i = tid + q * kThreads;
-            c.u[q] = ld8<false>(p.u + (bh * kP + (i >> 3)) * p.L, t0 + (i & 7) * 8, p.L);
+            c.u[q] = ld8<false>(p.u + (bh * kP + piece_row(i)) * p.L, t0 + (i & 7) * 8, p.L);
         }
         c.ok = true;
         const int64_t t = t0 + (tid & 63);
@@ -301,17 +308,35 @@ __device__ inline void store_chunk(const Chunk<N, WITH_C>& c, uint16_t* lds, int
     for (int q = 0; q < Ch::kBC; ++q) {
         const int i = tid + q * kThreads;
         const int arr = i / (N * (kQ / 8)), k = i % (N * (kQ / 8));
-        u32x4* dst = reinterpret_cast<u32x4*>(lds + (arr ? cn : bn) + (k >> 3) * kRow + (k & 7) * 8);
+        u32x4* dst = reinterpret_cast<u32x4*>(lds + (arr ? cn : bn) + piece_row(k) * kRow + (k & 7) * 8);
         if (full) *dst = c.bc[q];
         else *dst = ok ? c.bc[q] : zero;
     }
 #pragma unroll
     for (int q = 0; q < Ch::kU; ++q) {
         const int i = tid + q * kThreads;
-        u32x4* dst = reinterpret_cast<u32x4*>(lds + un + (i >> 3) * kRow + (i & 7) * 8);
+        u32x4* dst = reinterpret_cast<u32x4*>(lds + un + piece_row(i) * kRow + (i & 7) * 8);
         if (full) *dst = c.u[q];
         else *dst = ok ? c.u[q] : zero;
     }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4
+// and 8 inside each row of 16 lanes (a lane shifted in from outside its row reads 0),
+// then lane 15 is added to row 1 (and lane 47 to row 3), and lane 31 to rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_in(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+}
+
+__device__ inline float wave_prefix_sum(float v) {
+    v += dpp_in<0x111, 0xF>(v);   // row_shr:1
+    v += dpp_in<0x112, 0xF>(v);   // row_shr:2
+    v += dpp_in<0x114, 0xF>(v);   // row_shr:4
+    v += dpp_in<0x118, 0xF>(v);   // row_shr:8
+    v += dpp_in<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_in<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
 }
 
 // One wave, one step per lane: step sizes (in log2 units, dl2 = dt / ln 2, so that the
@@ -320,13 +345,8 @@ __device__ inline void store_chunk(const Chunk<N, WITH_C>& c, uint16_t* lds, int
 // nothing, so the last chunk needs no other masking.
 __device__ inline void stage_steps(uint32_t draw, bool valid, float a, float bias, float* sf, int lane) {
     const float dl2 = valid ? softplus_log2(__uint_as_float(draw << 16) + bias) : 0.0f;
-    float cum = dl2 * a;
-#pragma unroll
-    for (int o = 1; o < kLanes; o <<= 1) {
-        const float v = __shfl_up(cum, o);
-        if (lane >= o) cum += v;
-    }
-    const float tot = __shfl(cum, kLanes - 1);
+    const float cum = wave_prefix_sum(dl2 * a);
+    const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kLanes - 1));
     const float dt = dl2 * kLn2;
     sf[kFCum + lane] = cum;
     sf[kFDt + lane] = dt;
@@ -476,23 +496,34 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
     ChunkSrc<N, true> src;
     init_src<N, true>(src, p, b, bh, tid);
     load_chunk<N, true, VEC>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    // gate inputs of the lane's outputs, steps 16 tb + 4 lg .. +3 of channel pc, loaded a
+    // chunk ahead after the chunk's other inputs (loads complete in order, so waiting
+    // for them never waits for a later chunk's).  A step past L reads other data or
+    // zeros; its output is not stored.
+    u32x2 zn[4];
+    auto load_z = [&](int64_t t0) {
+        if constexpr (GATE) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                if constexpr (VEC)
+                    zn[tb] = __builtin_amdgcn_raw_buffer_load_b64(rz, lane_off + 32u * tb, int(2 * t0), 0);
+                else
+                    zn[tb] = ld4<false>(zb + prow, t0 + 16 * tb + 4 * lg, p.L);
+            }
+        }
+    };
+    load_z(int64_t(c0) * kQ);
     for (int c = c0; c < c1; ++c) {
         const int64_t t0 = int64_t(c) * kQ;
         __syncthreads();
         store_chunk<N, true>(nx, lds, Lay::Bn, Lay::Cn, Lay::U, tid, t0 + kQ <= p.L);
         if (w == 0) stage_steps(nx.draw, t0 + l < p.L, a, bias, sf, l);
-        if (c + 1 < c1) load_chunk<N, true, VEC>(nx, src, p, b, bh, t0 + kQ, tid);
-        // gate inputs of the lane's outputs: steps 16 tb + 4 lg .. +3 of channel pc (a
-        // step past L reads the row's last four; its output is not stored)
         u32x2 zr[4];
-        if constexpr (GATE) {
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                if constexpr (VEC)
-                    zr[tb] = __builtin_amdgcn_raw_buffer_load_b64(rz, lane_off + 32u * tb, int(2 * t0), 0);
-                else
-                    zr[tb] = ld4<false>(zb + prow, t0 + 16 * tb + 4 * lg, p.L);
-            }
+        for (int tb = 0; tb < 4; ++tb) zr[tb] = zn[tb];
+        if (c + 1 < c1) {
+            load_chunk<N, true, VEC>(nx, src, p, b, bh, t0 + kQ, tid);
+            load_z(t0 + kQ);
         }
         __syncthreads();
 
@@ -643,9 +674,9 @@ int ssd_plan(const ssm_ssd_dims* d, SsdPlan* pl) {
         return SSM_ERR_DIMS;
     const int64_t nchunks = cdiv(d->seqlen, kQ);
     if (nchunks > (int64_t(1) << 30)) return SSM_ERR_DIMS;
-    // default: enough workgroups to give every compute unit one (the output pass holds
-    // one workgroup per CU at N = 128)
-    int64_t nseg = d->nsegments ? d->nsegments : cdiv(256, bh);
+    // default: enough workgroups for two per compute unit (the output pass holds two
+    // per CU at N = 128)
+    int64_t nseg = d->nsegments ? d->nsegments : cdiv(512, bh);
     nseg = std::min<int64_t>(std::max<int64_t>(nseg, 1), nchunks);
     const int64_t cps = cdiv(nchunks, nseg);
     nseg = cdiv(nchunks, cps);
