@@ -293,8 +293,10 @@ SSM_API int ssm_selective_scan_bwd_plan(const ssm_dims* dims, ssm_plan* plan);
  *             first step;  h_last: same layout, nullable -- the state after the last
  *             step.  h_last may not overlap h0 or any array.
  * Supported: io_dtype SSM_BF16, headdim 64, dstate 64 or 128 (else SSM_ERR_DTYPE /
- * SSM_ERR_DIMS).  Each sequence is cut into nsegments pieces of whole 64-step chunks
- * (0: library choice); the pieces' end states travel through the workspace.
+ * SSM_ERR_DIMS); seqlen * max(64, dstate) * 2 < 2^31.  Each sequence is cut into
+ * nsegments pieces of whole 64-step chunks (0: library choice); C^T B of each chunk
+ * and the pieces' end states travel through the workspace (required, 256-byte
+ * aligned, ssm_ssd_fwd_workspace_bytes(dims) bytes).
  * Ownership, asynchrony and the other error rules are those of ssm_selective_scan_fwd
  * (y may not overlap an input: SSM_ERR_ALIAS).
  */
@@ -309,14 +311,15 @@ typedef struct ssm_ssd_dims {
                                 (clamped to the number of 64-step chunks) */
     int32_t reserved;        /* must be 0 */
     int32_t reserved2;       /* ignored (padding) */
-    void* workspace;         /* device memory for the pieces' end states, 256-byte aligned;
-                                may be NULL when the required size is 0 */
+    void* workspace;         /* device memory for C^T B per chunk and the pieces' end
+                                states, 256-byte aligned */
     size_t workspace_bytes;
 } ssm_ssd_dims;
 
-/* Bytes of workspace ssm_ssd_fwd needs: 4 * batch * dim * dstate per piece boundary
- * plus one float per head and boundary (0 with a single piece, and for a dims that
- * ssm_ssd_fwd would refuse). */
+/* Bytes of workspace ssm_ssd_fwd needs (never 0 for a valid dims; 0 for a dims that
+ * ssm_ssd_fwd would refuse): 10240 bytes per batch row and 64-step chunk for C^T B of
+ * the chunk (shared by all heads), then 4 * batch * dim * dstate bytes per piece
+ * boundary and one float per head and boundary, each part rounded up to 256 bytes. */
 SSM_API size_t ssm_ssd_fwd_workspace_bytes(const ssm_ssd_dims* dims);
 
 /* Enqueue the scalar-decay per-head-step forward pass.  Returns an ssm_status value. */

@@ -22,8 +22,9 @@
 // 2^-9 (plain bf16 operands exceed a 2e-2 output error on the N = 128 workload).
 // Products accumulate in fp32.
 //
-// Work split: a sequence is cut into segments of whole chunks.  ssd_state_kernel
-// computes each segment's end state from a zero start (and its total decay);
+// Work split: ssd_gram_kernel forms C^T B of every chunk once for all heads.  A sequence
+// is cut into segments of whole chunks.  ssd_state_kernel computes each segment's end
+// state from a zero start (and its total decay);
 // ssd_out_kernel composes the states of the segments before its own with h0, then
 // walks its chunks in order, producing y and carrying the state in registers.  In
 // both, wave w of a workgroup owns the head's channels 16w .. 16w+15: their state
@@ -85,11 +86,20 @@ struct SsdParams {
     const float* h0;
     uint16_t* y;
     float* h_last;
+    float* gram;             // (batch, nchunks, 10 tiles, 64 lanes, 4) fp32: C^T B per chunk
     float* seg_state;        // (nseg-1, batch*nheads) blocks of P*N fp32, in lane order
     float* seg_decay;        // (nseg-1, batch*nheads) fp32, log2 units
     int64_t L, nheads, bh_total;
     int nseg, cps, nchunks;
 };
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also orders global memory,
+// which makes every wave wait for all of its outstanding global loads -- including the
+// next chunk's prefetch, issued just before -- at every barrier.  No wave of these
+// kernels reads global memory another wave wrote, so waiting for the wave's own LDS
+// operations (lgkmcnt) before s_barrier is enough; the memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ------------------------------------------------------------------ state row order
 // A 32-wide block kb of the contraction over the state index feeds MFMA slot j of
@@ -264,36 +274,46 @@ __device__ inline void init_src(ChunkSrc<N, WITH_C>& a, const SsdParams& p, int6
     }
 }
 
-template <int N, bool WITH_C, bool VEC>
+// PART 0 loads everything; the output pass spreads its loads over the chunk's compute
+// phases instead (1: B pieces, 2: C pieces, 3: u and the step input), so that the
+// vector-memory requests of all waves do not queue up at once.
+template <int N, bool WITH_C, bool VEC, int PART = 0>
 __device__ inline void load_chunk(Chunk<N, WITH_C>& c, const ChunkSrc<N, WITH_C>& a, const SsdParams& p, int64_t b,
                                   int64_t bh, int64_t t0, int tid) {
     using Ch = Chunk<N, WITH_C>;
+    constexpr int q0 = PART == 2 ? Ch::kBC / 2 : 0;
+    constexpr int q1 = PART == 0 ? Ch::kBC : PART == 1 ? Ch::kBC / 2 : PART == 2 ? Ch::kBC : 0;
+    constexpr bool with_u = PART == 0 || PART == 3;
     if constexpr (VEC) {
         const int so = int(2 * t0);
 #pragma unroll
-        for (int q = 0; q < Ch::kBC; ++q) {
+        for (int q = q0; q < q1; ++q) {
             const bool isC = (tid + q * kThreads) >= N * (kQ / 8);
             c.bc[q] = __builtin_amdgcn_raw_buffer_load_b128(isC ? a.rc : a.rb, a.off_bc[q], so, 0);
         }
+        if constexpr (with_u) {
 #pragma unroll
-        for (int q = 0; q < Ch::kU; ++q) c.u[q] = __builtin_amdgcn_raw_buffer_load_b128(a.ru, a.off_u[q], so, 0);
-        c.ok = t0 + (tid & 7) * 8 < p.L;
-        c.draw = __builtin_amdgcn_raw_buffer_load_b16(a.rd, 2u * uint32_t(tid & 63), so, 0);
+            for (int q = 0; q < Ch::kU; ++q) c.u[q] = __builtin_amdgcn_raw_buffer_load_b128(a.ru, a.off_u[q], so, 0);
+            c.ok = t0 + (tid & 7) * 8 < p.L;
+            c.draw = __builtin_amdgcn_raw_buffer_load_b16(a.rd, 2u * uint32_t(tid & 63), so, 0);
+        }
     } else {
 #pragma unroll
-        for (int q = 0; q < Ch::kBC; ++q) {
+        for (int q = q0; q < q1; ++q) {
             const int i = tid + q * kThreads;
             const int arr = i / (N * (kQ / 8)), k = i % (N * (kQ / 8));
             c.bc[q] = ld8<false>((arr ? p.C : p.B) + (b * N + piece_row(k)) * p.L, t0 + (k & 7) * 8, p.L);
         }
+        if constexpr (with_u) {
 #pragma unroll
-        for (int q = 0; q < Ch::kU; ++q) {
-            const int i = tid + q * kThreads;
-            c.u[q] = ld8<false>(p.u + (bh * kP + piece_row(i)) * p.L, t0 + (i & 7) * 8, p.L);
+            for (int q = 0; q < Ch::kU; ++q) {
+                const int i = tid + q * kThreads;
+                c.u[q] = ld8<false>(p.u + (bh * kP + piece_row(i)) * p.L, t0 + (i & 7) * 8, p.L);
+            }
+            c.ok = true;
+            const int64_t t = t0 + (tid & 63);
+            c.draw = t < p.L ? p.delta[bh * p.L + t] : 0;
         }
-        c.ok = true;
-        const int64_t t = t0 + (tid & 63);
-        c.draw = t < p.L ? p.delta[bh * p.L + t] : 0;
     }
 }
 
@@ -398,6 +418,48 @@ __device__ inline int64_t seg_index(int64_t k, int nb, int w, int lane) {
     return (((k * (N / 16) + nb) * kWaves + w) * kLanes + lane) * 4;
 }
 
+// ------------------------------------------------------------------ pass 0: C^T B per chunk
+// The 10 lower-triangular 16x16 tiles (t block tb, s block sb <= tb) of a chunk's
+// matrices, numbered row by row; wave w of a workgroup handles tiles w, w + 4, w + 8.
+__device__ inline int tile_t(int ti) { return (ti >= 1) + (ti >= 3) + (ti >= 6); }
+__device__ inline int tile_s(int ti) { const int tb = tile_t(ti); return ti - tb * (tb + 1) / 2; }
+constexpr int kTiles = 10;
+
+// G[t][s] = sum_n C[n][t] B[n][s] does not depend on the head, so it is formed once per
+// (batch row, chunk) and stored as GT tiles in the register layout the output pass uses:
+// tile ti of chunk c of batch row b at ((b * nchunks + c) * 10 + ti) * 64 + lane, four
+// floats per lane (result row 4 lg + r is step s, column lr step t).
+template <int N, bool VEC>
+__global__ void __launch_bounds__(kThreads) ssd_gram_kernel(SsdParams p) {
+    constexpr int NK = N / 32;
+    constexpr int kPieces = N * (kQ / 8);
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int c = int(blockIdx.x % unsigned(p.nchunks));
+    const int64_t b = blockIdx.x / unsigned(p.nchunks);
+    const int64_t t0 = int64_t(c) * kQ;
+    for (int i = tid; i < 2 * kPieces; i += kThreads) {
+        const int arr = i / kPieces, k = i % kPieces;
+        const uint16_t* row = (arr ? p.C : p.B) + (b * N + piece_row(k)) * p.L;
+        *reinterpret_cast<u32x4*>(lds + arr * N * kRow + piece_row(k) * kRow + (k & 7) * 8) =
+            ld8<VEC>(row, t0 + (k & 7) * 8, p.L);
+    }
+    lds_barrier();
+    float* out = p.gram + (b * p.nchunks + c) * (kTiles * 256);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int ti = w + 4 * k;
+        if (ti < kTiles) {
+            const int tb = tile_t(ti), sb = tile_s(ti);
+            f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb)
+                g = mfma(lds_tr(lds, kb, 16 * sb, l), lds_tr(lds + N * kRow, kb, 16 * tb, l), g);
+            *reinterpret_cast<f32x4*>(out + (ti * 64 + l) * 4) = g;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ pass 1: segment end states
 template <int N, bool VEC>
 __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
@@ -423,11 +485,11 @@ __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
     load_chunk<N, false, VEC>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
     for (int c = c0; c < c1; ++c) {
         const int64_t t0 = int64_t(c) * kQ;
-        __syncthreads();
+        lds_barrier();
         store_chunk<N, false>(nx, lds, Lay::Bn, 0, Lay::U, tid, t0 + kQ <= p.L);
         if (w == 0) stage_steps(nx.draw, t0 + l < p.L, a, bias, sf, l);
         if (c + 1 < c1) load_chunk<N, false, VEC>(nx, src, p, b, bh, t0 + kQ, tid);
-        __syncthreads();
+        lds_barrier();
         dsum += sf[kFTot];
         chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
     }
@@ -439,10 +501,6 @@ __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
 }
 
 // ------------------------------------------------------------------ pass 2: outputs
-// The 10 lower-triangular 16x16 tiles (t block tb, s block sb <= tb) of a chunk's
-// masked decay matrix, numbered row by row; wave w computes tiles w, w + 4 and w + 8.
-__device__ inline int tile_t(int ti) { return (ti >= 1) + (ti >= 3) + (ti >= 6); }
-__device__ inline int tile_s(int ti) { const int tb = tile_t(ti); return ti - tb * (tb + 1) / 2; }
 
 template <int N, bool VEC, bool GATE>
 __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
@@ -513,31 +571,41 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
         }
     };
     load_z(int64_t(c0) * kQ);
+    // this wave's tiles of C^T B (tiles w, w + 4, w + 8 < 10), also a chunk ahead; a
+    // wave without a third tile reads the next tile (or zeros past the end) unused
+    const Rsrc rg = make_rsrc(p.gram + b * p.nchunks * (kTiles * 256), int64_t(p.nchunks) * kTiles * 1024);
+    u32x4 gn[3];
+    auto load_g = [&](int c) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            gn[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, uint32_t(((w + 4 * k) * 64 + l) * 16), c * kTiles * 1024, 0);
+    };
+    load_g(c0);
     for (int c = c0; c < c1; ++c) {
         const int64_t t0 = int64_t(c) * kQ;
-        __syncthreads();
+        lds_barrier();
         store_chunk<N, true>(nx, lds, Lay::Bn, Lay::Cn, Lay::U, tid, t0 + kQ <= p.L);
         if (w == 0) stage_steps(nx.draw, t0 + l < p.L, a, bias, sf, l);
         u32x2 zr[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) zr[tb] = zn[tb];
-        if (c + 1 < c1) {
-            load_chunk<N, true, VEC>(nx, src, p, b, bh, t0 + kQ, tid);
-            load_z(t0 + kQ);
-        }
-        __syncthreads();
+        f32x4 gr[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) gr[k] = __builtin_bit_cast(f32x4, gn[k]);
+        // the next chunk's inputs, spread over this chunk's phases (after the segment's last
+        // chunk they are the next segment's or past the end: read but unused; buffer reads
+        // past a block return zeros, flat reads past L are not made)
+        load_g(c + 1);
+        lds_barrier();
 
         // masked decay tiles: M[t][s] = GT[s][t] exp2(cum_t - cum_s) dt_s for s <= t,
         // GT[s][t] = sum_n B[n][s] C[n][t]; result row 4 lg + r is step s, column lr step t
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             const int ti = w + 4 * k;
-            if (ti < 10) {
+            if (ti < kTiles) {
                 const int tb = tile_t(ti), sb = tile_s(ti);
-                f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int kb = 0; kb < NK; ++kb)
-                    g = mfma(lds_tr(lds + Lay::Bn, kb, 16 * sb, l), lds_tr(lds + Lay::Cn, kb, 16 * tb, l), g);
+                const f32x4 g = gr[k];
                 const int t = 16 * tb + lr;
                 const float cum_t = sf[kFCum + t];
                 float m[4];
@@ -562,6 +630,8 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
                     u32x2{lb[0] | (uint32_t(lb[1]) << 16), lb[2] | (uint32_t(lb[3]) << 16)};
             }
         }
+
+        load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, t0 + kQ, tid);
 
         // read-out of the chunk's starting state: yo[tb][t][p] = sum_n C[n][t] H[n][p]
         f32x4 yo[4];
@@ -591,8 +661,10 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             }
         }
 
+        load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, t0 + kQ, tid);
         chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
-        __syncthreads();   // M complete
+        load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, t0 + kQ, tid);
+        lds_barrier();   // M complete
 
         // within the chunk: yd[tb][t][p] = sum_{s} M[t][s] u[s][p] over the 32-step
         // blocks that reach the diagonal of t block tb
@@ -609,6 +681,8 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
                 yd[tb] = mfma(lds16(lds + Lay::Mlo + moff), uo, yd[tb]);
             }
         }
+
+        load_z(t0 + kQ);
 
         // y = (yd + exp(cum_t) yo + D u) SiLU(z); the lane owns steps 16 tb + 4 lg + r
         const bool full = VEC && t0 + kQ <= p.L;
@@ -652,7 +726,7 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
 struct SsdPlan {
     int nseg, cps, nchunks;
     int64_t bh_total;
-    size_t ws_bytes, state_floats;
+    size_t ws_bytes, state_floats, gram_bytes;
 };
 
 inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -673,7 +747,7 @@ int ssd_plan(const ssm_ssd_dims* d, SsdPlan* pl) {
     if (d->seqlen > (int64_t(1) << 31) / (2 * kP) || d->seqlen > (int64_t(1) << 31) / (2 * d->dstate))
         return SSM_ERR_DIMS;
     const int64_t nchunks = cdiv(d->seqlen, kQ);
-    if (nchunks > (int64_t(1) << 30)) return SSM_ERR_DIMS;
+    if (nchunks > (int64_t(1) << 30) || d->batch * nchunks > int64_t(INT32_MAX)) return SSM_ERR_DIMS;
     // default: enough workgroups for two per compute unit (the output pass holds two
     // per CU at N = 128)
     int64_t nseg = d->nsegments ? d->nsegments : cdiv(512, bh);
@@ -686,12 +760,16 @@ int ssd_plan(const ssm_ssd_dims* d, SsdPlan* pl) {
     pl->nchunks = int(nchunks);
     pl->bh_total = bh;
     pl->state_floats = size_t(nseg - 1) * size_t(bh) * size_t(kP) * size_t(d->dstate);  // P*N per head
-    pl->ws_bytes = nseg > 1 ? round256(pl->state_floats * 4) + round256(size_t(nseg - 1) * size_t(bh) * 4) : 0;
+    pl->gram_bytes = round256(size_t(d->batch) * size_t(nchunks) * kTiles * 1024);
+    pl->ws_bytes = pl->gram_bytes +
+                   (nseg > 1 ? round256(pl->state_floats * 4) + round256(size_t(nseg - 1) * size_t(bh) * 4) : 0);
     return SSM_OK;
 }
 
 template <int N, bool VEC>
 int ssd_launch(const SsdParams& p, const SsdPlan& pl, hipStream_t s) {
+    hipLaunchKernelGGL((ssd_gram_kernel<N, VEC>), dim3(unsigned(pl.bh_total / p.nheads * pl.nchunks)), dim3(kThreads),
+                       size_t(2 * N * kRow * 2), s, p);
     if (pl.nseg > 1) {
         hipLaunchKernelGGL((ssd_state_kernel<N, VEC>), dim3(unsigned((pl.nseg - 1) * pl.bh_total)), dim3(kThreads),
                            StateLds<N>::bytes, s, p);
@@ -740,11 +818,13 @@ extern "C" SSM_API int ssm_ssd_fwd(const void* u, const void* delta, const float
     if (overlaps(h_last, stb, y, io)) return SSM_ERR_ALIAS;
 
     SsdParams p{};
-    if (pl.ws_bytes) {
-        if (!dims->workspace || dims->workspace_bytes < pl.ws_bytes || misaligned(dims->workspace, 256))
-            return SSM_ERR_WORKSPACE;
-        p.seg_state = static_cast<float*>(dims->workspace);
-        p.seg_decay = reinterpret_cast<float*>(static_cast<char*>(dims->workspace) + round256(pl.state_floats * 4));
+    if (!dims->workspace || dims->workspace_bytes < pl.ws_bytes || misaligned(dims->workspace, 256))
+        return SSM_ERR_WORKSPACE;
+    {
+        char* ws = static_cast<char*>(dims->workspace);
+        p.gram = reinterpret_cast<float*>(ws);
+        p.seg_state = reinterpret_cast<float*>(ws + pl.gram_bytes);
+        p.seg_decay = reinterpret_cast<float*>(ws + pl.gram_bytes + round256(pl.state_floats * 4));
     }
     p.u = static_cast<const uint16_t*>(u);
     p.delta = static_cast<const uint16_t*>(delta);

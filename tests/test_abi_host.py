@@ -336,7 +336,7 @@ def test_ssd_refusals():
     assert _ssd_call(_ssd_dims(), z=FAKE + 0x600000, y=FAKE + 0x600000 + 64) == E.SSM_ERR_ALIAS
     assert _ssd_call(_ssd_dims(), h0=FAKE + 0x600000, h_last=FAKE + 0x600000) == E.SSM_ERR_ALIAS
     assert _ssd_call(_ssd_dims(), h_last=FAKE + 0x500000) == E.SSM_ERR_ALIAS
-    # a forced second segment needs a workspace
+    # a forced second segment needs a larger workspace
     d = _ssd_dims(seqlen=256, nsegments=2)
     assert _ssd_call(d) == E.SSM_ERR_WORKSPACE
     need = ssm.ssm_ssd_fwd_workspace_bytes(d)
@@ -348,11 +348,14 @@ def test_ssd_refusals():
 
 def test_ssd_workspace_sizes():
     r = lambda x: (x + 255) // 256 * 256
-    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(nsegments=1)) == 0
-    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(seqlen=64, nsegments=4)) == 0   # one chunk: one piece
+    gram = lambda batch, L: r(batch * ((L + 63) // 64) * 10 * 1024)
+    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(nsegments=1)) == gram(1, 64)
+    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(seqlen=64, nsegments=4)) == gram(1, 64)  # one chunk: one piece
     d = _ssd_dims(batch=2, seqlen=8192, nheads=64, dstate=128, nsegments=4)
-    assert ssm.ssm_ssd_fwd_workspace_bytes(d) == r(3 * 128 * 64 * 128 * 4) + r(3 * 128 * 4)
+    assert ssm.ssm_ssd_fwd_workspace_bytes(d) == gram(2, 8192) + r(3 * 128 * 64 * 128 * 4) + r(3 * 128 * 4)
     # pieces are whole chunks: 10 chunks in 4 pieces of 3 chunks leave 4 pieces
     d = _ssd_dims(batch=1, seqlen=640, nheads=1, dstate=64, nsegments=4)
-    assert ssm.ssm_ssd_fwd_workspace_bytes(d) == r(3 * 64 * 64 * 4) + r(3 * 4)
+    assert ssm.ssm_ssd_fwd_workspace_bytes(d) == gram(1, 640) + r(3 * 64 * 64 * 4) + r(3 * 4)
     assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(dstate=32)) == 0
+    # the workspace is always required
+    assert _ssd_call(_ssd_dims(nsegments=1)) == ssm.SSM_ERR_WORKSPACE
