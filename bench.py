@@ -106,6 +106,8 @@ PROFILE_COMMANDS = {
                  "python3 bench.py --calibrate-copy",
 }
 COPY_BYTES = 2 << 30
+# output directory the profile commands write to (relative to the repository root)
+PROFILE_DIR = "rocprof_out"
 
 
 def calibrate_copy():
@@ -153,7 +155,7 @@ def summarize_profiles(d):
            "fetch_scale": ffac, "write_scale": wfac, "hbm_read_bytes_per_launch": rd,
            "hbm_write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
            "algorithmic_read_bytes": alg_read, "algorithmic_write_bytes": alg_write, "algorithmic_bytes": alg,
-           "commands": [PROFILE_COMMANDS[k].format(d="gpurun_out/prof") for k in ("fetch", "write", "copyfetch", "copywrite")]}
+           "commands": [PROFILE_COMMANDS[k].format(d=PROFILE_DIR) for k in ("fetch", "write", "copyfetch", "copywrite")]}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
@@ -163,7 +165,7 @@ def summarize_profiles(d):
           f"Kernel source sha256[:16]: `{kernel_hash()}`", "",
           "## Kernel time (`--kernel-trace --stats`)", "",
           "Command (from the repository root on the GPU box):", "",
-          "    " + PROFILE_COMMANDS["stats"].format(d="gpurun_out/prof"), "",
+          "    " + PROFILE_COMMANDS["stats"].format(d=PROFILE_DIR), "",
           "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in rows:
         md.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
@@ -189,7 +191,7 @@ def summarize_profiles(d):
               "`ssm_selective_scan_fwd_conv`, then the fused decode step); both scans launch the same kernel, so "
               "its calls here are the two kinds together.", "",
               "Command (from the repository root on the GPU box):", "",
-              "    " + PROFILE_COMMANDS["conv_stats"].format(d="gpurun_out/prof"), "",
+              "    " + PROFILE_COMMANDS["conv_stats"].format(d=PROFILE_DIR), "",
               "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
         for r in rows:
             md.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
@@ -210,7 +212,7 @@ def summarize_profiles(d):
               "`ssd_out_kernel`.  The scalar-decay rows of `scan_fwd_kernel` are the per-channel scan timed on the "
               "same inputs for comparison.", "",
               "Command (from the repository root on the GPU box):", "",
-              "    " + PROFILE_COMMANDS["stats"].format(d="gpurun_out/prof"), "",
+              "    " + PROFILE_COMMANDS["stats"].format(d=PROFILE_DIR), "",
               "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
         for r in rows:
             md.append(f"| `{r['Name'][:120]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
@@ -504,7 +506,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this build "
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the library "
               "has no multi-GPU path; the scan is sharded over batch/channels with no communication when it is "
               "run once per GPU.", file=sys.stderr)
         sys.exit(2)
