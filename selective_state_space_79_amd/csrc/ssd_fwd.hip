@@ -36,6 +36,7 @@
 #include "scan_common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace {
 
@@ -43,6 +44,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -127,11 +130,6 @@ __device__ inline float bf_half(uint32_t word, int hi) {
     return __uint_as_float(hi ? (word & 0xFFFF0000u) : (word << 16));
 }
 
-__device__ inline uint16_t bf_bits(float v) {
-    const __bf16 b = static_cast<__bf16>(v);   // round to nearest even
-    return __builtin_bit_cast(uint16_t, b);
-}
-
 __device__ inline f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -157,14 +155,28 @@ __device__ inline bf16x8 lds_tr(const uint16_t* base, int kb, int col0, int lane
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in fp32).
+// Two floats to packed bf16 (round to nearest even): one v_cvt_pk_bf16_f32.
+__device__ inline uint32_t pack_bf16(float x0, float x1) {
+    const f32x2 x = {x0, x1};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// x = hi + lo for K (even) floats with hi = bf16(x) and lo = bf16(x - hi) (x - hi is
+// exact in fp32), packed two per word: per pair one conversion for hi, the two hi
+// values back to fp32 by a shift and a mask, two subtractions, one conversion for lo.
 template <int K>
-__device__ inline void split(const float (&x)[K], __bf16 (&hi)[K], __bf16 (&lo)[K]) {
+__device__ inline void split(const float (&x)[K], uint32_t (&hi)[K / 2], uint32_t (&lo)[K / 2]) {
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-        hi[j] = static_cast<__bf16>(x[j]);
-        lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(hi[j]));
+    for (int j = 0; j < K / 2; ++j) {
+        const uint32_t h = pack_bf16(x[2 * j], x[2 * j + 1]);
+        hi[j] = h;
+        lo[j] = pack_bf16(x[2 * j] - __uint_as_float(h << 16), x[2 * j + 1] - __uint_as_float(h & 0xFFFF0000u));
     }
+}
+
+__device__ inline bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 // ------------------------------------------------------------------ global I/O
@@ -288,7 +300,10 @@ __device__ inline void load_chunk(Chunk<N, WITH_C>& c, const ChunkSrc<N, WITH_C>
         const int so = int(2 * t0);
 #pragma unroll
         for (int q = q0; q < q1; ++q) {
-            const bool isC = (tid + q * kThreads) >= N * (kQ / 8);
+            // pieces tid + 256 q: all B's without C, else the first kBC/2 values of q are
+            // B's and the rest C's (a compile-time choice, so the descriptor stays in
+            // scalar registers)
+            const bool isC = WITH_C && q >= Ch::kBC / 2;
             c.bc[q] = __builtin_amdgcn_raw_buffer_load_b128(isC ? a.rc : a.rb, a.off_bc[q], so, 0);
         }
         if constexpr (with_u) {
@@ -394,14 +409,9 @@ __device__ inline void chunk_state(f32x4 (&H)[N / 16], const uint16_t* sBn, cons
         float xv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) xv[j] = sf[kFW + s0 + j] * bf_half(uv[j >> 1], j & 1);
-        __bf16 xh[8], xl[8];
+        uint32_t xh[4], xl[4];
         split<8>(xv, xh, xl);
-        bf16x8 xo_h, xo_l;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            xo_h[j] = xh[j];
-            xo_l[j] = xl[j];
-        }
+        const bf16x8 xo_h = as_bf16x8(xh), xo_l = as_bf16x8(xl);
 #pragma unroll
         for (int nb = 0; nb < N / 16; ++nb) {
             const bf16x8 bo = lds16(sBn + nrow(nb >> 1, lr >> 2, nb & 1, lr & 3) * kRow + s0);
@@ -553,11 +563,17 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
     Chunk<N, true> nx;
     ChunkSrc<N, true> src;
     init_src<N, true>(src, p, b, bh, tid);
-    load_chunk<N, true, VEC>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
-    // gate inputs of the lane's outputs, steps 16 tb + 4 lg .. +3 of channel pc, loaded a
-    // chunk ahead after the chunk's other inputs (loads complete in order, so waiting
-    // for them never waits for a later chunk's).  A step past L reads other data or
-    // zeros; its output is not stored.
+    // this wave's tiles of C^T B (tiles w, w + 4, w + 8 < 10); a wave without a third
+    // tile reads the next tile (or zeros past the end) unused
+    const Rsrc rg = make_rsrc(p.gram + b * p.nchunks * (kTiles * 256), int64_t(p.nchunks) * kTiles * 1024);
+    u32x4 gn[3];
+    auto load_g = [&](int c) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            gn[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, uint32_t(((w + 4 * k) * 64 + l) * 16), c * kTiles * 1024, 0);
+    };
+    // gate inputs of the lane's outputs, steps 16 tb + 4 lg .. +3 of channel pc.  A step
+    // past L reads other data or zeros; its output is not stored.
     u32x2 zn[4];
     auto load_z = [&](int64_t t0) {
         if constexpr (GATE) {
@@ -570,32 +586,31 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             }
         }
     };
-    load_z(int64_t(c0) * kQ);
-    // this wave's tiles of C^T B (tiles w, w + 4, w + 8 < 10), also a chunk ahead; a
-    // wave without a third tile reads the next tile (or zeros past the end) unused
-    const Rsrc rg = make_rsrc(p.gram + b * p.nchunks * (kTiles * 256), int64_t(p.nchunks) * kTiles * 1024);
-    u32x4 gn[3];
-    auto load_g = [&](int c) {
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            gn[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, uint32_t(((w + 4 * k) * 64 + l) * 16), c * kTiles * 1024, 0);
-    };
+    // The first chunk's inputs, in the order the chunk loop issues the next chunk's (u
+    // and the step input -- read from HBM, so first --, then the C^T B tiles, B, C and
+    // the gate inputs): loads complete in order, and with the same order before the loop
+    // as inside it the compiler can wait for exactly the loads each use needs.
+    load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
     load_g(c0);
-    for (int c = c0; c < c1; ++c) {
+    load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    load_z(int64_t(c0) * kQ);
+    // One chunk.  FULL: the chunk lies wholly inside the sequence, so every global
+    // access takes one straight path (with a per-element tail path the compiler would
+    // drain all outstanding loads and stores at the top of every chunk); the sequence's
+    // ragged last chunk, if any, runs the checked copy after the loop.
+    auto chunk = [&](const int c, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const int64_t t0 = int64_t(c) * kQ;
         lds_barrier();
-        store_chunk<N, true>(nx, lds, Lay::Bn, Lay::Cn, Lay::U, tid, t0 + kQ <= p.L);
-        if (w == 0) stage_steps(nx.draw, t0 + l < p.L, a, bias, sf, l);
-        u32x2 zr[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) zr[tb] = zn[tb];
-        f32x4 gr[3];
-#pragma unroll
-        for (int k = 0; k < 3; ++k) gr[k] = __builtin_bit_cast(f32x4, gn[k]);
-        // the next chunk's inputs, spread over this chunk's phases (after the segment's last
-        // chunk they are the next segment's or past the end: read but unused; buffer reads
-        // past a block return zeros, flat reads past L are not made)
-        load_g(c + 1);
+        store_chunk<N, true>(nx, lds, Lay::Bn, Lay::Cn, Lay::U, tid, FULL);
+        if (w == 0) stage_steps(nx.draw, FULL || t0 + l < p.L, a, bias, sf, l);
+        load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, t0 + kQ, tid);
+        // The next chunk's inputs are loaded over this chunk's phases, each after the
+        // last use of the registers it replaces, so no copies (and no early waits) are
+        // needed between iterations.  After the segment's last chunk they are the next
+        // segment's or past the end: read but unused (buffer reads past a block return
+        // zeros; flat reads past L are not made).
         lds_barrier();
 
         // masked decay tiles: M[t][s] = GT[s][t] exp2(cum_t - cum_s) dt_s for s <= t,
@@ -605,7 +620,7 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             const int ti = w + 4 * k;
             if (ti < kTiles) {
                 const int tb = tile_t(ti), sb = tile_s(ti);
-                const f32x4 g = gr[k];
+                const f32x4 g = __builtin_bit_cast(f32x4, gn[k]);
                 const int t = 16 * tb + lr;
                 const float cum_t = sf[kFCum + t];
                 float m[4];
@@ -615,22 +630,15 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
                     const float e = __builtin_amdgcn_exp2f(cum_t - sf[kFCum + s]) * sf[kFDt + s];
                     m[r] = s <= t ? g[r] * e : 0.0f;
                 }
-                __bf16 mh[4], ml[4];
+                uint32_t mh[2], ml[2];
                 split<4>(m, mh, ml);
-                uint16_t hb[4], lb[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    hb[r] = __builtin_bit_cast(uint16_t, mh[r]);
-                    lb[r] = __builtin_bit_cast(uint16_t, ml[r]);
-                }
                 const int off = t * kRow + 16 * sb + 4 * lg;
-                *reinterpret_cast<u32x2*>(lds + Lay::Mhi + off) =
-                    u32x2{hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16)};
-                *reinterpret_cast<u32x2*>(lds + Lay::Mlo + off) =
-                    u32x2{lb[0] | (uint32_t(lb[1]) << 16), lb[2] | (uint32_t(lb[3]) << 16)};
+                *reinterpret_cast<u32x2*>(lds + Lay::Mhi + off) = u32x2{mh[0], mh[1]};
+                *reinterpret_cast<u32x2*>(lds + Lay::Mlo + off) = u32x2{ml[0], ml[1]};
             }
         }
 
+        load_g(c + 1);
         load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, t0 + kQ, tid);
 
         // read-out of the chunk's starting state: yo[tb][t][p] = sum_n C[n][t] H[n][p]
@@ -645,14 +653,9 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
                 hv[r] = H[2 * kb][r];
                 hv[4 + r] = H[2 * kb + 1][r];
             }
-            __bf16 hh[8], hl[8];
+            uint32_t hh[4], hl[4];
             split<8>(hv, hh, hl);
-            bf16x8 ho_h, ho_l;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                ho_h[j] = hh[j];
-                ho_l[j] = hl[j];
-            }
+            const bf16x8 ho_h = as_bf16x8(hh), ho_l = as_bf16x8(hl);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 const bf16x8 co = lds_tr(lds + Lay::Cn, kb, 16 * tb, l);
@@ -663,7 +666,6 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
 
         load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, t0 + kQ, tid);
         chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
-        load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, t0 + kQ, tid);
         lds_barrier();   // M complete
 
         // within the chunk: yd[tb][t][p] = sum_{s} M[t][s] u[s][p] over the 32-step
@@ -682,10 +684,8 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             }
         }
 
-        load_z(t0 + kQ);
-
         // y = (yd + exp(cum_t) yo + D u) SiLU(z); the lane owns steps 16 tb + 4 lg + r
-        const bool full = VEC && t0 + kQ <= p.L;
+        constexpr bool full = VEC && FULL;
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             const int tq = 16 * tb + 4 * lg;
@@ -700,17 +700,22 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
                     const int r = 2 * q + e;
                     float x = fmaf(e4[r], yo[tb][r], yd[tb][r]);
                     x = fmaf(Dp, bf_half(uu[q], e), x);
-                    if constexpr (GATE) x *= silu_f32(bf_half(zr[tb][q], e));
+                    if constexpr (GATE) x *= silu_f32(bf_half(zn[tb][q], e));
                     v[e] = x;
                 }
-                o[q] = uint32_t(bf_bits(v[0])) | (uint32_t(bf_bits(v[1])) << 16);
+                o[q] = pack_bf16(v[0], v[1]);
             }
-            if (full)
+            if constexpr (full)
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{o[0], o[1]}, ry, lane_off + 32u * tb, int(2 * t0), 0);
             else
                 st4<false>(yb + prow, t0 + tq, p.L, u32x2{o[0], o[1]});
         }
-    }
+        load_z(t0 + kQ);
+    };
+    const int c_full = std::min<int64_t>(c1, p.L / kQ);   // chunks wholly inside L
+    int c = c0;
+    for (; c < c_full; ++c) chunk(c, std::true_type{});
+    for (; c < c1; ++c) chunk(c, std::false_type{});
 
     if (p.h_last && seg == p.nseg - 1) {
 #pragma unroll
