@@ -286,9 +286,9 @@ __device__ inline void init_src(ChunkSrc<N, WITH_C>& a, const SsdParams& p, int6
     }
 }
 
-// PART 0 loads everything; the output pass spreads its loads over the chunk's compute
-// phases instead (1: B pieces, 2: C pieces, 3: u and the step input), so that the
-// vector-memory requests of all waves do not queue up at once.
+// PART 0 loads everything; the passes spread their loads over the chunk's phases
+// instead (1: the first half of the B/C pieces -- B's -- 2: the second half -- C's, or
+// B's when there is no C -- 3: u and the step input).
 template <int N, bool WITH_C, bool VEC, int PART = 0>
 __device__ inline void load_chunk(Chunk<N, WITH_C>& c, const ChunkSrc<N, WITH_C>& a, const SsdParams& p, int64_t b,
                                   int64_t bh, int64_t t0, int tid) {
@@ -489,17 +489,27 @@ __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
     for (int nb = 0; nb < N / 16; ++nb) H[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float dsum = 0.0f;
     const int c0 = seg * p.cps, c1 = min(c0 + p.cps, p.nchunks);
+    // Every chunk of a segment before the last lies wholly inside the sequence (the last
+    // segment holds the last chunk), so no chunk here needs masking, and the next chunk
+    // (the following segment's first after this segment's last) is always in bounds.
+    // Loads are issued in one order throughout -- u and the step input (from HBM)
+    // first, then B -- and each after the last use of the registers it refills.
     Chunk<N, false> nx;
     ChunkSrc<N, false> src;
     init_src<N, false>(src, p, b, bh, tid);
-    load_chunk<N, false, VEC>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    load_chunk<N, false, VEC, 3>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads in the loop's order
+    load_chunk<N, false, VEC, 1>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    load_chunk<N, false, VEC, 2>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
     for (int c = c0; c < c1; ++c) {
         const int64_t t0 = int64_t(c) * kQ;
         lds_barrier();
-        store_chunk<N, false>(nx, lds, Lay::Bn, 0, Lay::U, tid, t0 + kQ <= p.L);
-        if (w == 0) stage_steps(nx.draw, t0 + l < p.L, a, bias, sf, l);
-        if (c + 1 < c1) load_chunk<N, false, VEC>(nx, src, p, b, bh, t0 + kQ, tid);
+        store_chunk<N, false>(nx, lds, Lay::Bn, 0, Lay::U, tid, true);
+        if (w == 0) stage_steps(nx.draw, true, a, bias, sf, l);
+        load_chunk<N, false, VEC, 3>(nx, src, p, b, bh, t0 + kQ, tid);
         lds_barrier();
+        load_chunk<N, false, VEC, 1>(nx, src, p, b, bh, t0 + kQ, tid);
+        load_chunk<N, false, VEC, 2>(nx, src, p, b, bh, t0 + kQ, tid);
         dsum += sf[kFTot];
         chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
     }
@@ -591,9 +601,13 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
     // the gate inputs): loads complete in order, and with the same order before the loop
     // as inside it the compiler can wait for exactly the loads each use needs.
     load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads in the loop's order
     load_g(c0);
+    __builtin_amdgcn_sched_barrier(0);
     load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    __builtin_amdgcn_sched_barrier(0);
     load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    __builtin_amdgcn_sched_barrier(0);
     load_z(int64_t(c0) * kQ);
     // One chunk.  FULL: the chunk lies wholly inside the sequence, so every global
     // access takes one straight path (with a per-element tail path the compiler would
