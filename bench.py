@@ -397,7 +397,7 @@ def backward_bench(x, dev, steps: int = 30, warmup: int = 5):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def ssd_bench(steps: int = 50, warmup: int = 10):
+def ssd_bench(steps: int = 100, warmup: int = 30):
     """Time ssm_ssd_fwd, the chunked state-space-duality pass, on the scalar-decay
     large-state workload with one step size per head (batch 2, L 8192, 64 heads x 64
     channels, N 128, bf16 I/O); one call = both of its kernels.  The per-channel scan
