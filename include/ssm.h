@@ -298,7 +298,7 @@ SSM_API int ssm_selective_scan_bwd_plan(const ssm_dims* dims, ssm_plan* plan);
  * and the pieces' end states travel through the workspace (required, 256-byte
  * aligned, ssm_ssd_fwd_workspace_bytes(dims) bytes).
  * Ownership, asynchrony and the other error rules are those of ssm_selective_scan_fwd
- * (y may not overlap an input: SSM_ERR_ALIAS).
+ * (y may not overlap an input, and the workspace no input or output: SSM_ERR_ALIAS).
  */
 typedef struct ssm_ssd_dims {
     int64_t batch;           /* >= 1 */

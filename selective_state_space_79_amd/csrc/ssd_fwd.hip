@@ -839,6 +839,11 @@ extern "C" SSM_API int ssm_ssd_fwd(const void* u, const void* delta, const float
     SsdParams p{};
     if (!dims->workspace || dims->workspace_bytes < pl.ws_bytes || misaligned(dims->workspace, 256))
         return SSM_ERR_WORKSPACE;
+    // the workspace is written: it may overlap no input or output
+    for (const auto& in : ins)
+        if (overlaps(dims->workspace, pl.ws_bytes, in.q, in.n)) return SSM_ERR_ALIAS;
+    if (overlaps(dims->workspace, pl.ws_bytes, y, io) || overlaps(dims->workspace, pl.ws_bytes, h_last, stb))
+        return SSM_ERR_ALIAS;
     {
         char* ws = static_cast<char*>(dims->workspace);
         p.gram = reinterpret_cast<float*>(ws);

@@ -357,5 +357,10 @@ def test_ssd_workspace_sizes():
     d = _ssd_dims(batch=1, seqlen=640, nheads=1, dstate=64, nsegments=4)
     assert ssm.ssm_ssd_fwd_workspace_bytes(d) == gram(1, 640) + r(3 * 64 * 64 * 4) + r(3 * 4)
     assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(dstate=32)) == 0
-    # the workspace is always required
+    # the workspace is always required, and may overlap no input or output
     assert _ssd_call(_ssd_dims(nsegments=1)) == ssm.SSM_ERR_WORKSPACE
+    d = _ssd_dims(nsegments=1)
+    d.workspace, d.workspace_bytes = FAKE + 0x800000, ssm.ssm_ssd_fwd_workspace_bytes(d)
+    assert _ssd_call(d, u=FAKE + 0x800000 + 4096) == ssm.SSM_ERR_ALIAS
+    assert _ssd_call(d, y=FAKE + 0x800000 + 256) == ssm.SSM_ERR_ALIAS
+    assert _ssd_call(d, h_last=FAKE + 0x800000) == ssm.SSM_ERR_ALIAS
