@@ -457,18 +457,15 @@ def ssd_bench(steps: int = 100, warmup: int = 30):
     # triangular 16x16 tiles of C^T B (N-deep), the masked product (6 16x32 blocks per
     # 16 channels, two bf16 parts), the state read and the state update (N x 64 x 64
     # each, two parts); the end states of all but the last segment repeat the update
-    seg = ssm.ssm_ssd_fwd_workspace_bytes(dims)
-    nseg = 1
-    if seg:
-        per_seg = -(-(x.batch * x.nheads * x.headdim * x.N * 4) // 256) * 256
-        nseg = 1 + seg // per_seg
+    plan = ssm.ssm_ssd_fwd_plan(dims).as_dict()
+    nseg = plan["nsegments"]
     chunks = x.batch * x.nheads * -(-x.L // 64)
     mac_chunk = 10 * 256 * x.N + 2 * 4 * 6 * 16 * 16 * 32 + 2 * 64 * 64 * x.N + 2 * x.N * 64 * 64
     mac_state = 2 * x.N * 64 * 64 * (nseg - 1) / nseg
     tflops = 2 * chunks * (mac_chunk + mac_state) / (ms * 1e-3) / 1e12
     return {"workload": f"{SSD_WORKLOADS[5]['name']}: batch {x.batch}, L {x.L}, {x.nheads} heads x {x.headdim}, "
                         f"N {x.N}, bf16 I/O, one step size per head",
-            "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3), "segments": nseg,
+            "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3), "plan": plan,
             "hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes},
             "mfma": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

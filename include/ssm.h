@@ -318,9 +318,23 @@ typedef struct ssm_ssd_dims {
 
 /* Bytes of workspace ssm_ssd_fwd needs (never 0 for a valid dims; 0 for a dims that
  * ssm_ssd_fwd would refuse): 10240 bytes per batch row and 64-step chunk for C^T B of
- * the chunk (shared by all heads), then 4 * batch * dim * dstate bytes per piece
- * boundary and one float per head and boundary, each part rounded up to 256 bytes. */
+ * the chunk (shared by all heads), then 4 * batch * dim * dstate bytes and one float per
+ * head for each piece before the last (ssm_ssd_fwd_plan), each part rounded up to 256
+ * bytes. */
 SSM_API size_t ssm_ssd_fwd_workspace_bytes(const ssm_ssd_dims* dims);
+
+/* How ssm_ssd_fwd would run dims: pieces per sequence, 64-step chunks per piece (the
+ * last piece may have fewer), the chunk length and count, and the workspace size.
+ * Returns an ssm_status value; fills *plan only on SSM_OK.  Pure host function. */
+typedef struct ssm_ssd_plan {
+    int32_t nsegments;
+    int32_t chunks_per_segment;
+    int32_t chunk_len;
+    int32_t reserved;
+    int64_t nchunks;
+    size_t workspace_bytes;
+} ssm_ssd_plan;
+SSM_API int ssm_ssd_fwd_plan(const ssm_ssd_dims* dims, ssm_ssd_plan* plan);
 
 /* Enqueue the scalar-decay per-head-step forward pass.  Returns an ssm_status value. */
 SSM_API int ssm_ssd_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,

@@ -38,7 +38,7 @@ EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_fwd_state", "ssm_selec
             "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan", "ssm_status_string",
             "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd_plan",
             "ssm_selective_scan_fwd_conv", "ssm_selective_scan_step_conv", "ssm_ssd_fwd",
-            "ssm_ssd_fwd_workspace_bytes")
+            "ssm_ssd_fwd_workspace_bytes", "ssm_ssd_fwd_plan")
 SSM_MAX_DSTATE_BWD = 128
 
 
@@ -105,6 +105,21 @@ class SsmSsdDims(ctypes.Structure):
     ]
 
 
+class SsmSsdPlan(ctypes.Structure):
+    """Mirror of ``ssm_ssd_plan`` in include/ssm.h."""
+    _fields_ = [
+        ("nsegments", ctypes.c_int32),
+        ("chunks_per_segment", ctypes.c_int32),
+        ("chunk_len", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("nchunks", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 class SsmError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {ssm_status_string(status)} (status {status})")
@@ -146,6 +161,8 @@ def load_library():
         lib.ssm_ssd_fwd.restype = ctypes.c_int
         lib.ssm_ssd_fwd_workspace_bytes.argtypes = [ctypes.POINTER(SsmSsdDims)]
         lib.ssm_ssd_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssm_ssd_fwd_plan.argtypes = [ctypes.POINTER(SsmSsdDims), ctypes.POINTER(SsmSsdPlan)]
+        lib.ssm_ssd_fwd_plan.restype = ctypes.c_int
         lib.ssm_status_string.argtypes = [ctypes.c_int]
         lib.ssm_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -449,6 +466,14 @@ def make_ssd_dims(batch, seqlen, nheads, dstate, *, headdim=64, io_dtype=SSM_BF1
 
 def ssm_ssd_fwd_workspace_bytes(dims: SsmSsdDims) -> int:
     return int(load_library().ssm_ssd_fwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def ssm_ssd_fwd_plan(dims: SsmSsdDims) -> SsmSsdPlan:
+    plan = SsmSsdPlan()
+    st = load_library().ssm_ssd_fwd_plan(ctypes.byref(dims), ctypes.byref(plan))
+    if st != SSM_OK:
+        raise SsmError(st, "ssm_ssd_fwd_plan")
+    return plan
 
 
 def ssm_ssd_fwd(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, dims: SsmSsdDims, stream=None) -> int:

@@ -488,7 +488,7 @@ __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb) H[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float dsum = 0.0f;
-    const int c0 = seg * p.cps, c1 = min(c0 + p.cps, p.nchunks);
+    const int c0 = seg * p.cps, c1 = c0 + p.cps;
     // Every chunk of a segment before the last lies wholly inside the sequence (the last
     // segment holds the last chunk), so no chunk here needs masking, and the next chunk
     // (the following segment's first after this segment's last) is always in bounds.
@@ -802,6 +802,20 @@ int ssd_launch(const SsdParams& p, const SsdPlan& pl, hipStream_t s) {
 }
 
 }  // namespace
+
+extern "C" SSM_API int ssm_ssd_fwd_plan(const ssm_ssd_dims* dims, ssm_ssd_plan* plan) {
+    SsdPlan pl;
+    const int st = ssd_plan(dims, &pl);
+    if (st != SSM_OK) return st;
+    if (!plan) return SSM_ERR_NULL;
+    plan->nsegments = pl.nseg;
+    plan->chunks_per_segment = pl.cps;
+    plan->chunk_len = kQ;
+    plan->reserved = 0;
+    plan->nchunks = pl.nchunks;
+    plan->workspace_bytes = pl.ws_bytes;
+    return SSM_OK;
+}
 
 extern "C" SSM_API size_t ssm_ssd_fwd_workspace_bytes(const ssm_ssd_dims* dims) {
     SsdPlan pl;

@@ -349,14 +349,30 @@ def test_ssd_refusals():
 def test_ssd_workspace_sizes():
     r = lambda x: (x + 255) // 256 * 256
     gram = lambda batch, L: r(batch * ((L + 63) // 64) * 10 * 1024)
-    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(nsegments=1)) == gram(1, 64)
-    assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(seqlen=64, nsegments=4)) == gram(1, 64)  # one chunk: one piece
-    d = _ssd_dims(batch=2, seqlen=8192, nheads=64, dstate=128, nsegments=4)
-    assert ssm.ssm_ssd_fwd_workspace_bytes(d) == gram(2, 8192) + r(3 * 128 * 64 * 128 * 4) + r(3 * 128 * 4)
+
+    def expect(batch, L, H, N, nseg):
+        pl = ssm.ssm_ssd_fwd_plan(_ssd_dims(batch=batch, seqlen=L, nheads=H, dstate=N, nsegments=nseg))
+        nchunks = (L + 63) // 64
+        assert pl.nchunks == nchunks and pl.chunk_len == 64
+        assert pl.nsegments == -(-nchunks // pl.chunks_per_segment)
+        sub = pl.nsegments - 1
+        size = gram(batch, L) + (r(sub * batch * H * 64 * N * 4) + r(sub * batch * H * 4) if sub else 0)
+        assert pl.workspace_bytes == size
+        assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(batch=batch, seqlen=L, nheads=H, dstate=N, nsegments=nseg)) == size
+        return pl
+
+    assert expect(1, 64, 2, 64, 1).nsegments == 1
+    assert expect(1, 64, 2, 64, 4).nsegments == 1                 # one chunk: one piece
+    pl = expect(2, 8192, 64, 128, 4)
+    assert (pl.nsegments, pl.chunks_per_segment) == (4, 32)
     # pieces are whole chunks: 10 chunks in 4 pieces of 3 chunks leave 4 pieces
-    d = _ssd_dims(batch=1, seqlen=640, nheads=1, dstate=64, nsegments=4)
-    assert ssm.ssm_ssd_fwd_workspace_bytes(d) == gram(1, 640) + r(3 * 64 * 64 * 4) + r(3 * 4)
+    pl = expect(1, 640, 1, 64, 4)
+    assert (pl.nsegments, pl.chunks_per_segment) == (4, 3)
+    expect(1, 1000, 2, 128, 3)
+    assert expect(2, 8192, 64, 128, 0).nsegments == 4             # default: two workgroups per CU
     assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(dstate=32)) == 0
+    with pytest.raises(ssm.SsmError):
+        ssm.ssm_ssd_fwd_plan(_ssd_dims(dstate=32))
     # the workspace is always required, and may overlap no input or output
     assert _ssd_call(_ssd_dims(nsegments=1)) == ssm.SSM_ERR_WORKSPACE
     d = _ssd_dims(nsegments=1)
