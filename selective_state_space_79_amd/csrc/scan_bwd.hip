@@ -40,6 +40,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ssm.h"
 
 #include "scan_common.h"
@@ -667,6 +669,391 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------- gradient pass with
+// separate roles (16 state entries per channel).  Four walking waves (wave w holds
+// entries 4w..4w+3 of all 64 channels) walk tile k while four helper waves finish
+// tile k-1 and stage tile k+1, so the staging and finishing work fills the issue slots
+// the walk leaves on each SIMD instead of running between barriers.  Tiles are
+// double-buffered in LDS and there is one barrier per tile.  A helper thread stages and
+// finishes the same elements (4 consecutive steps of one channel), so finishing tile
+// k-1 and then staging tile k+1 into the same buffer needs no barrier between them;
+// the per-element values finishing needs besides the walk's sums (u, sigmoid of the
+// step input, the gate's derivative) stay in the helper's registers, one set per
+// buffer.  The walk keeps the tile's recomputed states and decays in VGPRs, so the
+// reverse step does not evaluate the exponential again.
+namespace wsg {
+constexpr int SPL = 4, G = 4, H = 4, T = 16, NP = G * SPL, EPT = T / H, NTH = H * kLanes;
+constexpr int kW = T * kLanes * 4;        // (dt2, dt2*u, ds, scalar decay) per step and channel
+constexpr int kBC = T * NP * 2;           // (B*ln2, C) per step and entry
+constexpr int kSlab = G * T * kLanes;     // per-wave sums over the wave's entries, per step and channel
+constexpr int kDBC = 2 * NP * T;          // the tile's dB (unscaled), dC summed over the 64 channels
+constexpr int kBuf = kW + kBC + 3 * kSlab + kDBC;
+constexpr int kThreads = (G + H) * kLanes;
+constexpr size_t kLdsBytes = size_t(2 * kBuf) * sizeof(float);
+constexpr int KB = (2 * NP * T + NTH - 1) / NTH;   // B/C values per helper thread and tile
+}  // namespace wsg
+
+template <typename IO, bool SCALAR, bool VEC>
+__global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdParams p) {
+    using namespace wsg;
+    static_assert(KB * NTH == 2 * NP * T, "the tile's B and C values must split evenly over the helpers");
+    extern __shared__ float smem[];
+    const int tid = threadIdx.x;
+    const int wv = tid / kLanes;
+    const int lane = tid % kLanes;
+    const bool walker = wv < G;                   // wave-uniform
+    const int64_t bid = blockIdx.x;
+    const int cblk = int(bid % p.nblk_d);
+    const int b = int((bid / p.nblk_d) % p.batch);
+    const int piece = int(bid / (int64_t(p.nblk_d) * p.batch)) + p.piece_base;
+    const int64_t blk = int64_t(b) * p.nblk_d + cblk;
+    const int64_t c0 = int64_t(cblk) * kLanes;
+    const int64_t tbeg = int64_t(piece) * p.chunk_len;
+    const int64_t tend = (tbeg + p.chunk_len < p.L) ? tbeg + p.chunk_len : p.L;
+    const int ntiles = int((tend - tbeg + T - 1) / T);
+    const int64_t tile0 = tbeg / T;
+    auto kt_of = [&](int i) { return ntiles - 1 - i; };   // tiles in reverse order
+    auto buf = [&](int par) { return smem + par * kBuf; };
+
+    // ================================================================ walkers
+    // lane = channel c0 + lane, entries n = 4*wv + j
+    const int64_t dch = c0 + lane;
+    const bool lane_ok = dch < p.dim;
+    float Ar[SPL], e[SPL], dAacc[SPL], hst[SPL], ckn[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const int64_t n = int64_t(wv) * SPL + j;
+        Ar[j] = 0.0f;
+        if (walker && lane_ok) {
+            if constexpr (SCALAR) Ar[j] = p.A[dch / p.head_dim];
+            else if (n < p.N) Ar[j] = p.A[dch * p.N + n];
+        }
+        e[j] = dAacc[j] = hst[j] = ckn[j] = 0.0f;
+    }
+    if (walker) {
+        if (p.nchunks > 1) {
+            const int64_t sb = ((blk * p.nchunks + piece) * NP + int64_t(wv) * SPL) * kLanes + lane;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) e[j] = p.rEin[sb + int64_t(j) * kLanes];
+        } else if (p.dh_last && lane_ok) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t n = int64_t(wv) * SPL + j;
+                if (n < p.N) e[j] = p.dh_last[(int64_t(b) * p.dim + dch) * p.N + n];
+            }
+        }
+    }
+    auto load_ck = [&](int kt) {
+        const float* ck = p.ck + ((blk * p.ntiles_seq + tile0 + kt) * NP + int64_t(wv) * SPL) * kLanes + lane;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) ckn[j] = ck[int64_t(j) * kLanes];
+    };
+
+    struct StepOps {
+        float4 W;
+        float Bv[SPL], Cv[SPL];
+    };
+    auto read_step = [&](const float* bf, int t, StepOps& o) {
+        o.W = reinterpret_cast<const float4*>(bf)[t * kLanes + lane];
+        const float4* q = reinterpret_cast<const float4*>(bf + kW + t * NP * 2 + wv * SPL * 2);
+        const float4 v0 = q[0], v1 = q[1];
+        o.Bv[0] = v0.x; o.Cv[0] = v0.y; o.Bv[1] = v0.z; o.Cv[1] = v0.w;
+        o.Bv[2] = v1.x; o.Cv[2] = v1.y; o.Bv[3] = v1.z; o.Cv[3] = v1.w;
+    };
+
+    // sum 8 per-lane values over the wave's 64 lanes (channels) in registers, in a
+    // fixed order.  Value v < 4 is dB of entry 4*wv+v, v >= 4 dC of entry 4*wv+v-4.
+    //   1. v_permlane32_swap on value pairs (2k, 2k+1), then add: register k holds
+    //      value 2k in lanes 0-31 and 2k+1 in lanes 32-63, each lane m the sum of
+    //      lanes m and m^32;
+    //   2. v_permlane16_swap on register pairs, then add: two registers whose 16-lane
+    //      rows hold values (0, 2, 1, 3) and (4, 6, 5, 7), each lane the sum of 4;
+    //   3. within each row, lanes 0-7 keep the first register plus its other half-row
+    //      and lanes 8-15 the second (a row rotation by 8): each lane the sum of 8;
+    //   4. DPP quad swaps and the half-row mirror sum the 8 lanes of each group.
+    // Group g = lane / 8 then holds value (g % 2) * 4 + ((g / 2) % 2) * 2 + g / 4.
+    const bool lo8 = (lane & 8) == 0;
+    const int red_v = ((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + (lane >> 5);
+    auto swap_add = [](float x, float y, auto swap) {
+        const auto r = swap(__float_as_uint(x), __float_as_uint(y));
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    };
+    auto p32 = [](unsigned x, unsigned y) { return __builtin_amdgcn_permlane32_swap(x, y, false, false); };
+    auto p16 = [](unsigned x, unsigned y) { return __builtin_amdgcn_permlane16_swap(x, y, false, false); };
+    auto reduce8 = [&](const float (&pv)[kRound], float* sdBC, int t) {
+        const float r0 = swap_add(pv[0], pv[1], p32), r1 = swap_add(pv[2], pv[3], p32);
+        const float r2 = swap_add(pv[4], pv[5], p32), r3 = swap_add(pv[6], pv[7], p32);
+        const float s0 = swap_add(r0, r1, p16), s1 = swap_add(r2, r3, p16);
+        float sum = (lo8 ? s0 : s1) + dpp_move<0x128>(lo8 ? s1 : s0);   // row_ror:8
+        sum += dpp_move<0xB1>(sum);    // quad_perm [1,0,3,2]
+        sum += dpp_move<0x4E>(sum);    // quad_perm [2,3,0,1]
+        sum += dpp_move<0x141>(sum);   // row_half_mirror
+        if ((lane & 7) == 0) sdBC[((red_v / SPL) * NP + wv * SPL + (red_v % SPL)) * T + t] = sum;
+    };
+
+    auto walk = [&](float* bf) {
+        float* sP = bf + kW + kBC;
+        float* sdBC = sP + 3 * kSlab;
+        float Hs[T][SPL], Aa[T][SPL];
+        {
+            float hh[SPL];
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) hh[j] = hst[j];
+            StepOps cur, nxt;
+            read_step(bf, 0, cur);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                if (t + 1 < T) read_step(bf, t + 1, nxt);
+                float yp = 0.0f;
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) {
+                    const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[j]);
+                    hh[j] = fmaf(a, hh[j], cur.W.y * cur.Bv[j]);
+                    Hs[t][j] = hh[j];
+                    Aa[t][j] = a;
+                    yp = fmaf(cur.Cv[j], hh[j], yp);
+                }
+                sP[(wv * T + t) * kLanes + lane] = yp;
+                cur = nxt;
+            }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        StepOps cur, nxt;
+        read_step(bf, T - 1, cur);
+#pragma unroll
+        for (int t = T - 1; t >= 0; --t) {
+            if (t > 0) read_step(bf, t - 1, nxt);
+            float s1 = 0.0f, s2 = 0.0f, pv[kRound];
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const float a = Aa[t][j];
+                const float hp = t > 0 ? Hs[t > 0 ? t - 1 : 0][j] : hst[j];
+                const float g = fmaf(cur.W.z, cur.Cv[j], e[j]);
+                const float t1 = g * (a * hp);
+                dAacc[j] = fmaf(cur.W.x, t1, dAacc[j]);
+                s1 = fmaf(Ar[j], t1, s1);
+                s2 = fmaf(g, cur.Bv[j], s2);
+                e[j] = a * g;
+                pv[j] = g * cur.W.y;                 // dB (unscaled)
+                pv[SPL + j] = cur.W.z * Hs[t][j];    // dC
+            }
+            sP[kSlab + (wv * T + t) * kLanes + lane] = s1;
+            sP[2 * kSlab + (wv * T + t) * kLanes + lane] = s2;
+            reduce8(pv, sdBC, t);
+            cur = nxt;
+        }
+    };
+
+    // ================================================================ helpers
+    // helper hw = wv - G, thread ht: channel c0 + lane, steps 4*hw .. 4*hw+3 of a tile
+    const int ht = tid - G * kLanes;              // negative on walkers (unused there)
+    const int e_seg = walker ? 0 : wv - G;
+    const int64_t e_d = c0 + lane;
+    const bool e_ok = !walker && e_d < p.dim;
+    const float e_bias = (e_ok && p.bias) ? p.bias[e_d] : 0.0f;
+    const float e_skip = (e_ok && p.Dskip) ? p.Dskip[e_d] : 0.0f;
+    const float e_ah = (SCALAR && e_ok) ? p.A[e_d / p.head_dim] : 0.0f;
+    const int64_t e_row = (int64_t(b) * p.dim + (e_ok ? e_d : 0)) * p.L;
+    const bool has_z = p.z != nullptr;
+    const IO* __restrict__ gu = static_cast<const IO*>(p.u);
+    const IO* __restrict__ gdl = static_cast<const IO*>(p.delta);
+    const IO* __restrict__ gz = static_cast<const IO*>(p.z);
+    const IO* __restrict__ gdy = static_cast<const IO*>(p.dy);
+    const IO* __restrict__ gB = static_cast<const IO*>(p.Bm);
+    const IO* __restrict__ gC = static_cast<const IO*>(p.Cm);
+
+    // B/C value v = ht + k*NTH -> (B or C, entry n, step t of the tile)
+    const IO* bc_ptr[KB];
+    int bc_slot[KB], bc_t[KB];
+    bool bc_ok[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        const int v = (walker ? 0 : ht) + k * NTH;
+        const int isC = v / (NP * T);
+        const int n = (v / T) % NP;
+        bc_t[k] = v % T;
+        bc_ok[k] = !walker && n < p.N;
+        bc_ptr[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bc_ok[k] ? n : 0)) * p.L + bc_t[k];
+        bc_slot[k] = (bc_t[k] * NP + n) * 2 + isC;
+    }
+
+    InSeg<IO, EPT, VEC> nu, ndl, nz, ndy;
+    IO nbc[KB];
+    auto issue_loads = [&](int kt) {
+        const int64_t t0 = tbeg + int64_t(kt) * T;
+        const int64_t t = t0 + e_seg * EPT;
+        nu = load_seg<IO, EPT, VEC>(gu + e_row, t, tend, e_ok);
+        ndl = load_seg<IO, EPT, VEC>(gdl + e_row, t, tend, e_ok);
+        ndy = load_seg<IO, EPT, VEC>(gdy + e_row, t, tend, e_ok);
+        nz = load_seg<IO, EPT, VEC>((has_z ? gz : gdy) + e_row, t, tend, e_ok && has_z);
+#pragma unroll
+        for (int k = 0; k < KB; ++k) nbc[k] = *((bc_ok[k] && t0 + bc_t[k] < tend) ? bc_ptr[k] + t0 : gB);
+    };
+
+    // finishing inputs kept from staging: u, sigmoid(delta + bias), dy * SiLU'(z);
+    // set P belongs to the tiles staged into buffer P
+    float Fu[2][EPT], Fsg[2][EPT], Fdz[2][EPT];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) Fu[s][k] = Fsg[s][k] = Fdz[s][k] = 0.0f;
+
+    // registers -> LDS buffer P for tile kt; steps beyond the piece's end are identity
+    // steps (dt2 = 0, x = 0, ds = 0, decay 1)
+    auto stage = [&](int kt, auto par) {
+        constexpr int P = decltype(par)::value;
+        float* bf = buf(P);
+        const int64_t t0 = tbeg + int64_t(kt) * T;
+        float4* sW = reinterpret_cast<float4*>(bf);
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int tl = e_seg * EPT + k;
+            const bool in = e_ok && t0 + tl < tend;
+            const float uu = in ? nu.get(k) : 0.0f;
+            const float r = in ? ndl.get(k) + e_bias : 0.0f;
+            const float dt2 = in ? softplus_log2(r) : 0.0f;
+            const float decay = SCALAR ? __builtin_amdgcn_exp2f(dt2 * e_ah) : 0.0f;
+            const float dyv = in ? ndy.get(k) : 0.0f;
+            const float zz = (has_z && in) ? nz.get(k) : 0.0f;
+            const float ds = has_z ? dyv * silu_f32(zz) : dyv;
+            sW[tl * kLanes + lane] = make_float4(dt2, dt2 * uu, ds, decay);
+            Fu[P][k] = uu;
+            Fsg[P][k] = sigmoid_f32(r);
+            Fdz[P][k] = has_z ? dyv * silu_grad_f32(zz) : 0.0f;
+        }
+        float* sBC = bf + kW;
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const bool in = bc_ok[k] && t0 + bc_t[k] < tend;
+            sBC[bc_slot[k]] = in ? IOT<IO>::to_f32(nbc[k]) * ((bc_slot[k] & 1) ? 1.0f : kLn2) : 0.0f;
+        }
+    };
+
+    IO* __restrict__ gdu = static_cast<IO*>(p.du);
+    IO* __restrict__ gdd = static_cast<IO*>(p.ddelta);
+    IO* __restrict__ gdz = static_cast<IO*>(p.dz);
+    const bool write_dz = p.dz != nullptr && has_z;
+    float accD = 0.0f, accBias = 0.0f;
+    auto finish = [&](int kt, auto par) {
+        constexpr int P = decltype(par)::value;
+        const float* bf = buf(P);
+        const int64_t t0 = tbeg + int64_t(kt) * T;
+        const float4* sW = reinterpret_cast<const float4*>(bf);
+        const float* sP = bf + kW + kBC;
+        const float* sdBC = sP + 3 * kSlab;
+        Seg<IO, EPT> odu, odd, odz;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int tl = e_seg * EPT + k;
+            const int idx = tl * kLanes + lane;
+            const bool in = e_ok && t0 + tl < tend;
+            const float4 Wv = sW[idx];
+            float yp = sP[idx], s1 = sP[kSlab + idx], s2 = sP[2 * kSlab + idx];
+#pragma unroll
+            for (int w = 1; w < G; ++w) {
+                const int o = w * T * kLanes + idx;
+                yp += sP[o];
+                s1 += sP[kSlab + o];
+                s2 += sP[2 * kSlab + o];
+            }
+            const float uu = Fu[P][k];
+            const float ddt = fmaf(uu * kLog2e, s2, s1);
+            const float dd = ddt * Fsg[P][k];
+            const float dui = fmaf(e_skip, Wv.z, Wv.x * s2);
+            const float dzi = Fdz[P][k] * fmaf(e_skip, uu, yp);
+            if (in) {
+                accD = fmaf(Wv.z, uu, accD);
+                accBias += dd;
+            }
+            odu.e[k] = IOT<IO>::from_f32(dui);
+            odd.e[k] = IOT<IO>::from_f32(dd);
+            odz.e[k] = IOT<IO>::from_f32(dzi);
+        }
+        const int64_t t = t0 + e_seg * EPT;
+        store_seg<IO, EPT, VEC>(gdu + e_row, t, tend, e_ok, odu);
+        store_seg<IO, EPT, VEC>(gdd + e_row, t, tend, e_ok, odd);
+        if (write_dz) store_seg<IO, EPT, VEC>(gdz + e_row, t, tend, e_ok, odz);
+        for (int i = ht; i < 2 * int(p.N) * T; i += NTH) {
+            const int isC = i / (int(p.N) * T);
+            const int rem = i % (int(p.N) * T);
+            const int n = rem / T, tt = rem % T;
+            if (t0 + tt < tend)
+                p.pBC[(((int64_t(cblk) * p.batch + b) * 2 + isC) * p.N + n) * p.L + t0 + tt] = sdBC[(isC * NP + n) * T + tt];
+        }
+    };
+
+    // ================================================================ pipeline
+    // period i: walkers walk tile i (buffer i % 2); helpers finish tile i-1 and stage
+    // tile i+1 (both buffer (i+1) % 2), then prefetch tile i+2.  The two roles run
+    // separate loops with the same number of barriers, so neither keeps the other's
+    // registers live.
+    if (walker) {
+        load_ck(kt_of(0));
+        __syncthreads();
+        for (int i = 0; i <= ntiles; ++i) {
+            if (i < ntiles) {
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) hst[j] = ckn[j];
+                if (i + 1 < ntiles) load_ck(kt_of(i + 1));
+                walk(buf(i & 1));
+            }
+            __syncthreads();
+        }
+    } else {
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        issue_loads(kt_of(0));
+        stage(kt_of(0), P0{});
+        if (ntiles > 1) issue_loads(kt_of(1));
+        __syncthreads();
+        auto period = [&](int i, auto par) {
+            using Q = std::integral_constant<int, 1 - decltype(par)::value>;
+            if (i >= 1) finish(kt_of(i - 1), Q{});
+            if (i + 1 < ntiles) {
+                stage(kt_of(i + 1), Q{});
+                if (i + 2 < ntiles) issue_loads(kt_of(i + 2));
+            }
+            __syncthreads();
+        };
+        for (int i = 0; i <= ntiles; i += 2) {
+            period(i, P0{});
+            if (i + 1 <= ntiles) period(i + 1, P1{});
+        }
+    }
+
+    // ================================================================ results
+    if (walker && lane_ok) {
+        float* pa = p.pA + ((int64_t(piece) * p.batch + b) * p.dim + dch) * NP + int64_t(wv) * SPL;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) pa[j] = dAacc[j];
+        if (piece == 0 && p.dh0) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t n = int64_t(wv) * SPL + j;
+                if (n < p.N) p.dh0[(int64_t(b) * p.dim + dch) * p.N + n] = e[j];
+            }
+        }
+    }
+    // per-channel sums of the helper threads of a channel, in step-segment order
+    float* fin = smem;   // [2][H][64]
+    if (!walker) {
+        fin[e_seg * kLanes + lane] = accD;
+        fin[(H + e_seg) * kLanes + lane] = accBias;
+    }
+    __syncthreads();
+    if (tid < kLanes && c0 + tid < p.dim) {
+        float sd = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int sg = 0; sg < H; ++sg) {
+            sd += fin[sg * kLanes + tid];
+            sb += fin[(H + sg) * kLanes + tid];
+        }
+        const int64_t o = (int64_t(piece) * p.batch + b) * p.dim + c0 + tid;
+        p.pD[o] = sd;
+        p.pbias[o] = sb;
+    }
+}
+
 // Piece carries, one thread per (group, state entry, lane), in sequence order:
 //   forward:  Hin[0] = h0 (or 0),     Hin[c+1] = exp2(A*S[c]) Hin[c] + H[c]
 //   reverse:  Ein[P-1] = dh_last (or 0), Ein[c-1] = exp2(A*S[c]) Ein[c] + G[c]
@@ -764,6 +1151,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_heads_kernel(BwdParams p, floa
 // ------------------------------------------------------------------ host side
 struct BwdPlan {
     int spl, G, nch, T;
+    bool ws;    // gradient pass with separate walking and helper waves (16 state entries)
     int64_t chunk_len, nblk_d, groups, ntiles_seq;
     size_t off_ck, off_bc, off_a, off_d, off_bias, off_fh, off_fs, off_fhin, off_rg, off_rs, off_rein, ws_bytes;
     size_t lds_grad, lds_fwd;
@@ -844,14 +1232,16 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
         off += st_bytes;
     }
     pl->ws_bytes = off;
-    pl->lds_grad = bwd_lds_floats(pl->G, spl, kGrad) * f;
+    static_assert(wsg::T == bwd_tile(wsg::NP), "both gradient kernels read the same checkpoints");
+    pl->ws = spl == 2 && pl->G == 8;
+    pl->lds_grad = pl->ws ? wsg::kLdsBytes : bwd_lds_floats(pl->G, spl, kGrad) * f;
     pl->lds_fwd = bwd_lds_floats(pl->G, spl, kCkpt) * f;
     return SSM_OK;
 }
 
 template <typename IO, int SPL, int G, bool SCALAR, bool VEC>
-hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, float* dA, float* dB, float* dC, float* dD, float* dbias,
-                      hipStream_t s) {
+hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, float* dA, float* dB, float* dC, float* dD,
+                      float* dbias, hipStream_t s) {
     const dim3 block(unsigned(G * kLanes));
     const int64_t groups = pl.groups;
     if (pl.nch > 1) {
@@ -869,7 +1259,14 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, float* dA, float* dB, floa
     p.piece_base = 0;
     const dim3 grid(unsigned(groups * pl.nch));
     hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt, VEC>), grid, block, pl.lds_fwd, s, p);
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kGrad, VEC>), grid, block, pl.lds_grad, s, p);
+    if constexpr (SPL == wsg::NP / G && G == 8) {
+        if (vec_g)
+            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, true>), grid, dim3(wsg::kThreads), pl.lds_grad, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, false>), grid, dim3(wsg::kThreads), pl.lds_grad, s, p);
+    } else {
+        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kGrad, VEC>), grid, block, pl.lds_grad, s, p);
+    }
     const int64_t nbc = int64_t(p.batch) * 2 * p.N * p.L;
     hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned(cdiv(nbc, 256))), dim3(256), 0, s, p, dB, dC, nbc);
     const int64_t npar = p.dim * p.N;
@@ -885,10 +1282,10 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, float* dA, float* dB, floa
 // The (entries per lane, waves) pairs the planner produces: 1..4 entries with 4 waves
 // (dstate <= 16, or forced), and 2..16 entries with 8 waves.
 template <typename IO, bool SCALAR, bool VEC>
-hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, float* dA, float* dB, float* dC, float* dD,
-                            float* dbias, hipStream_t s) {
+hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, bool vec_g, float* dA, float* dB, float* dC,
+                            float* dD, float* dbias, hipStream_t s) {
 #define SSM_BWD_CASE(S_, G_)                                                              \
-    if (pl.spl == S_ && pl.G == G_) return bwd_launch<IO, S_, G_, SCALAR, VEC>(p, pl, dA, dB, dC, dD, dbias, s);
+    if (pl.spl == S_ && pl.G == G_) return bwd_launch<IO, S_, G_, SCALAR, VEC>(p, pl, vec_g, dA, dB, dC, dD, dbias, s);
     SSM_BWD_CASE(1, 4)
     SSM_BWD_CASE(2, 4)
     SSM_BWD_CASE(4, 4)
@@ -901,10 +1298,10 @@ hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, float* dA, fl
 }
 
 template <typename IO, bool SCALAR>
-hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, bool vec, float* dA, float* dB, float* dC,
-                        float* dD, float* dbias, hipStream_t s) {
-    return vec ? bwd_dispatch_vec<IO, SCALAR, true>(p, pl, dA, dB, dC, dD, dbias, s)
-               : bwd_dispatch_vec<IO, SCALAR, false>(p, pl, dA, dB, dC, dD, dbias, s);
+hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, bool vec, bool vec_g, float* dA, float* dB,
+                        float* dC, float* dD, float* dbias, hipStream_t s) {
+    return vec ? bwd_dispatch_vec<IO, SCALAR, true>(p, pl, vec_g, dA, dB, dC, dD, dbias, s)
+               : bwd_dispatch_vec<IO, SCALAR, false>(p, pl, vec_g, dA, dB, dC, dD, dbias, s);
 }
 
 }  // namespace
@@ -976,12 +1373,17 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
         (reinterpret_cast<uintptr_t>(dims->workspace) % 256) != 0)
         return SSM_ERR_WORKSPACE;
 
-    // each thread moves T/G consecutive elements of a row at once when the rows allow it
-    const int64_t ept = pl.T / pl.G;
-    const size_t seg = size_t(ept) * esz;
-    auto aligned = [seg](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) % seg) == 0; };
-    const bool vec = (dims->seqlen % ept) == 0 && aligned(u) && aligned(delta) && aligned(z) && aligned(dy) &&
-                     aligned(grads->du) && aligned(grads->ddelta) && aligned(dz);
+    // each thread moves ept consecutive elements of a row at once when the rows allow
+    // it: T/G in the checkpoint and aggregate passes, T/4 in the gradient pass with
+    // helper waves
+    auto rows_allow = [&](int64_t ept) {
+        const size_t seg = size_t(ept) * esz;
+        auto aligned = [seg](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) % seg) == 0; };
+        return (dims->seqlen % ept) == 0 && aligned(u) && aligned(delta) && aligned(z) && aligned(dy) &&
+               aligned(grads->du) && aligned(grads->ddelta) && aligned(dz);
+    };
+    const bool vec = rows_allow(pl.T / pl.G);
+    const bool vec_g = pl.ws ? rows_allow(wsg::EPT) : vec;
 
     BwdParams p;
     p.u = u;
@@ -1030,11 +1432,11 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     const bool scalar = dims->nheads > 0;
     hipError_t e;
     if (dims->io_dtype == SSM_BF16)
-        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, vec, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
-                   : bwd_dispatch<uint16_t, false>(p, pl, vec, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, vec, vec_g, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<uint16_t, false>(p, pl, vec, vec_g, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
     else
-        e = scalar ? bwd_dispatch<float, true>(p, pl, vec, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
-                   : bwd_dispatch<float, false>(p, pl, vec, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+        e = scalar ? bwd_dispatch<float, true>(p, pl, vec, vec_g, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<float, false>(p, pl, vec, vec_g, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
