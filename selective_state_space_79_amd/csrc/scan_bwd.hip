@@ -123,6 +123,10 @@ template <> struct RawOf<2> { using T = uint16_t; };
 template <> struct RawOf<4> { using T = uint32_t; };
 template <> struct RawOf<8> { using T = uint2; };
 template <> struct RawOf<16> { using T = uint4; };
+struct Raw32 {
+    uint4 lo, hi;
+};
+template <> struct RawOf<32> { using T = Raw32; };
 
 // Output elements of one thread's segment.
 template <typename IO, int EPT> struct Seg {
@@ -1054,6 +1058,168 @@ __global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdPara
     }
 }
 
+// ---------------------------------------------------------------- checkpoint pass with
+// separate roles (16 state entries per channel): four walking waves (4 entries per
+// lane) walk 32-step tiles forward and write the state at the start of every 16-step
+// tile of the gradient pass, while four helper waves stage the next tile's step sizes,
+// weighted inputs and B.  Tiles are double-buffered in LDS, one barrier per tile.
+namespace wsc {
+constexpr int SPL = 4, G = 4, H = 4, T = 32, TC = 16, NP = G * SPL, EPT = T / H, NTH = H * kLanes;
+constexpr int kRowB = 20;                  // B row stride (floats): 16-byte aligned, few bank conflicts
+constexpr int kX = T * kLanes * 2;         // (dt2 or the scalar decay, dt2*u) per step and channel
+constexpr int kB = T * kRowB;              // B*ln2 per step and entry
+constexpr int kBuf = kX + kB;
+constexpr int kThreads = (G + H) * kLanes;
+constexpr size_t kLdsBytes = size_t(2 * kBuf) * sizeof(float);
+constexpr int KB = (T * NP + NTH - 1) / NTH;
+}  // namespace wsc
+
+template <typename IO, bool SCALAR, bool VEC>
+__global__ void __launch_bounds__(wsc::kThreads) scan_bwd_ckpt_ws_kernel(BwdParams p) {
+    using namespace wsc;
+    static_assert(KB * NTH == T * NP, "the tile's B values must split evenly over the helpers");
+    static_assert(T % TC == 0, "checkpoint tiles must nest in walk tiles");
+    extern __shared__ float smem[];
+    const int tid = threadIdx.x;
+    const int wv = tid / kLanes;
+    const int lane = tid % kLanes;
+    const bool walker = wv < G;
+    const int64_t bid = blockIdx.x;
+    const int cblk = int(bid % p.nblk_d);
+    const int b = int((bid / p.nblk_d) % p.batch);
+    const int piece = int(bid / (int64_t(p.nblk_d) * p.batch)) + p.piece_base;
+    const int64_t blk = int64_t(b) * p.nblk_d + cblk;
+    const int64_t c0 = int64_t(cblk) * kLanes;
+    const int64_t tbeg = int64_t(piece) * p.chunk_len;
+    const int64_t tend = (tbeg + p.chunk_len < p.L) ? tbeg + p.chunk_len : p.L;
+    const int ntiles = int((tend - tbeg + T - 1) / T);
+    auto buf = [&](int par) { return smem + par * kBuf; };
+
+    if (walker) {
+        const int64_t dch = c0 + lane;
+        const bool lane_ok = dch < p.dim;
+        float Ar[SPL], h[SPL];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const int64_t n = int64_t(wv) * SPL + j;
+            Ar[j] = 0.0f;
+            h[j] = 0.0f;
+            if (lane_ok) {
+                if constexpr (SCALAR) Ar[j] = p.A[dch / p.head_dim];
+                else if (n < p.N) Ar[j] = p.A[dch * p.N + n];
+            }
+        }
+        if (p.nchunks > 1) {
+            const int64_t sb = ((blk * p.nchunks + piece) * NP + int64_t(wv) * SPL) * kLanes + lane;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) h[j] = p.fHin[sb + int64_t(j) * kLanes];
+        } else if (p.h0 && lane_ok) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t n = int64_t(wv) * SPL + j;
+                if (n < p.N) h[j] = p.h0[(int64_t(b) * p.dim + dch) * p.N + n];
+            }
+        }
+        __syncthreads();
+        for (int i = 0; i < ntiles; ++i) {
+            const float* bf = buf(i & 1);
+            const float2* sx = reinterpret_cast<const float2*>(bf) + lane;
+            const float4* sb4 = reinterpret_cast<const float4*>(bf + kX + wv * SPL);
+            const int64_t t0 = tbeg + int64_t(i) * T;
+            float2 xc = sx[0], xn;
+            float4 bc = sb4[0], bn;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                if (t % TC == 0 && t0 + t < tend) {
+                    float* ck = p.ck + ((blk * p.ntiles_seq + (t0 + t) / TC) * NP + int64_t(wv) * SPL) * kLanes + lane;
+#pragma unroll
+                    for (int j = 0; j < SPL; ++j) ck[int64_t(j) * kLanes] = h[j];
+                }
+                if (t + 1 < T) {
+                    xn = sx[(t + 1) * kLanes];
+                    bn = sb4[(t + 1) * (kRowB / 4)];
+                }
+                const float bv[SPL] = {bc.x, bc.y, bc.z, bc.w};
+#pragma unroll
+                for (int j = 0; j < SPL; ++j) {
+                    const float a = SCALAR ? xc.x : __builtin_amdgcn_exp2f(xc.x * Ar[j]);
+                    h[j] = fmaf(a, h[j], xc.y * bv[j]);
+                }
+                xc = xn;
+                bc = bn;
+            }
+            __syncthreads();
+        }
+    } else {
+        const int e_seg = wv - G;
+        const int ht = tid - G * kLanes;
+        const int64_t e_d = c0 + lane;
+        const bool e_ok = e_d < p.dim;
+        const float e_bias = (e_ok && p.bias) ? p.bias[e_d] : 0.0f;
+        const float e_ah = (SCALAR && e_ok) ? p.A[e_d / p.head_dim] : 0.0f;
+        const int64_t e_row = (int64_t(b) * p.dim + (e_ok ? e_d : 0)) * p.L;
+        const IO* __restrict__ gu = static_cast<const IO*>(p.u);
+        const IO* __restrict__ gdl = static_cast<const IO*>(p.delta);
+        const IO* __restrict__ gB = static_cast<const IO*>(p.Bm);
+        // B value v = ht + k*NTH -> (entry n, step t of the tile)
+        const IO* bp[KB];
+        int bslot[KB], bt[KB];
+        bool bok[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int v = ht + k * NTH;
+            const int n = v / T;
+            bt[k] = v % T;
+            bok[k] = n < p.N;
+            bp[k] = gB + (int64_t(b) * p.N + (bok[k] ? n : 0)) * p.L + bt[k];
+            bslot[k] = bt[k] * kRowB + n;
+        }
+        InSeg<IO, EPT, VEC> nu, ndl;
+        IO nb[KB];
+        auto issue_loads = [&](int kt) {
+            const int64_t t0 = tbeg + int64_t(kt) * T;
+            const int64_t t = t0 + e_seg * EPT;
+            nu = load_seg<IO, EPT, VEC>(gu + e_row, t, tend, e_ok);
+            ndl = load_seg<IO, EPT, VEC>(gdl + e_row, t, tend, e_ok);
+#pragma unroll
+            for (int k = 0; k < KB; ++k) nb[k] = *((bok[k] && t0 + bt[k] < tend) ? bp[k] + t0 : gB);
+        };
+        // steps beyond the piece's end are identity steps (decay 1, input 0)
+        auto stage = [&](int kt) {
+            float* bf = buf(kt & 1);
+            const int64_t t0 = tbeg + int64_t(kt) * T;
+            float2* sx = reinterpret_cast<float2*>(bf);
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const int tl = e_seg * EPT + k;
+                const bool in = e_ok && t0 + tl < tend;
+                const float uu = in ? nu.get(k) : 0.0f;
+                const float r = in ? ndl.get(k) + e_bias : 0.0f;
+                const float dt2 = in ? softplus_log2(r) : 0.0f;
+                const float first = SCALAR ? __builtin_amdgcn_exp2f(dt2 * e_ah) : dt2;
+                sx[tl * kLanes + lane] = make_float2(first, dt2 * uu);
+            }
+            float* sB = bf + kX;
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const bool in = bok[k] && t0 + bt[k] < tend;
+                sB[bslot[k]] = in ? IOT<IO>::to_f32(nb[k]) * kLn2 : 0.0f;
+            }
+        };
+        issue_loads(0);
+        stage(0);
+        if (ntiles > 1) issue_loads(1);
+        __syncthreads();
+        for (int i = 0; i < ntiles; ++i) {
+            if (i + 1 < ntiles) {
+                stage(i + 1);
+                if (i + 2 < ntiles) issue_loads(i + 2);
+            }
+            __syncthreads();
+        }
+    }
+}
+
 // Piece carries, one thread per (group, state entry, lane), in sequence order:
 //   forward:  Hin[0] = h0 (or 0),     Hin[c+1] = exp2(A*S[c]) Hin[c] + H[c]
 //   reverse:  Ein[P-1] = dh_last (or 0), Ein[c-1] = exp2(A*S[c]) Ein[c] + G[c]
@@ -1240,8 +1406,8 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
 }
 
 template <typename IO, int SPL, int G, bool SCALAR, bool VEC>
-hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, float* dA, float* dB, float* dC, float* dD,
-                      float* dbias, hipStream_t s) {
+hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, float* dA, float* dB, float* dC,
+                      float* dD, float* dbias, hipStream_t s) {
     const dim3 block(unsigned(G * kLanes));
     const int64_t groups = pl.groups;
     if (pl.nch > 1) {
@@ -1258,7 +1424,14 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, float* dA, flo
     }
     p.piece_base = 0;
     const dim3 grid(unsigned(groups * pl.nch));
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt, VEC>), grid, block, pl.lds_fwd, s, p);
+    if constexpr (SPL == wsc::NP / G && G == 8) {
+        if (vec_c)
+            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true>), grid, dim3(wsc::kThreads), wsc::kLdsBytes, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, false>), grid, dim3(wsc::kThreads), wsc::kLdsBytes, s, p);
+    } else {
+        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt, VEC>), grid, block, pl.lds_fwd, s, p);
+    }
     if constexpr (SPL == wsg::NP / G && G == 8) {
         if (vec_g)
             hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, true>), grid, dim3(wsg::kThreads), pl.lds_grad, s, p);
@@ -1282,10 +1455,11 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, float* dA, flo
 // The (entries per lane, waves) pairs the planner produces: 1..4 entries with 4 waves
 // (dstate <= 16, or forced), and 2..16 entries with 8 waves.
 template <typename IO, bool SCALAR, bool VEC>
-hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, bool vec_g, float* dA, float* dB, float* dC,
-                            float* dD, float* dbias, hipStream_t s) {
-#define SSM_BWD_CASE(S_, G_)                                                              \
-    if (pl.spl == S_ && pl.G == G_) return bwd_launch<IO, S_, G_, SCALAR, VEC>(p, pl, vec_g, dA, dB, dC, dD, dbias, s);
+hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, bool vec_g, bool vec_c, float* dA, float* dB,
+                            float* dC, float* dD, float* dbias, hipStream_t s) {
+#define SSM_BWD_CASE(S_, G_)                                                                               \
+    if (pl.spl == S_ && pl.G == G_)                                                                        \
+        return bwd_launch<IO, S_, G_, SCALAR, VEC>(p, pl, vec_g, vec_c, dA, dB, dC, dD, dbias, s);
     SSM_BWD_CASE(1, 4)
     SSM_BWD_CASE(2, 4)
     SSM_BWD_CASE(4, 4)
@@ -1298,10 +1472,10 @@ hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, bool vec_g, f
 }
 
 template <typename IO, bool SCALAR>
-hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, bool vec, bool vec_g, float* dA, float* dB,
-                        float* dC, float* dD, float* dbias, hipStream_t s) {
-    return vec ? bwd_dispatch_vec<IO, SCALAR, true>(p, pl, vec_g, dA, dB, dC, dD, dbias, s)
-               : bwd_dispatch_vec<IO, SCALAR, false>(p, pl, vec_g, dA, dB, dC, dD, dbias, s);
+hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, bool vec, bool vec_g, bool vec_c, float* dA,
+                        float* dB, float* dC, float* dD, float* dbias, hipStream_t s) {
+    return vec ? bwd_dispatch_vec<IO, SCALAR, true>(p, pl, vec_g, vec_c, dA, dB, dC, dD, dbias, s)
+               : bwd_dispatch_vec<IO, SCALAR, false>(p, pl, vec_g, vec_c, dA, dB, dC, dD, dbias, s);
 }
 
 }  // namespace
@@ -1374,8 +1548,8 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
         return SSM_ERR_WORKSPACE;
 
     // each thread moves ept consecutive elements of a row at once when the rows allow
-    // it: T/G in the checkpoint and aggregate passes, T/4 in the gradient pass with
-    // helper waves
+    // it: T/G in the aggregate passes (and the checkpoint and gradient passes without
+    // helper waves); 4 in the gradient pass and 8 in the checkpoint pass with helpers
     auto rows_allow = [&](int64_t ept) {
         const size_t seg = size_t(ept) * esz;
         auto aligned = [seg](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) % seg) == 0; };
@@ -1384,6 +1558,7 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     };
     const bool vec = rows_allow(pl.T / pl.G);
     const bool vec_g = pl.ws ? rows_allow(wsg::EPT) : vec;
+    const bool vec_c = pl.ws ? rows_allow(wsc::EPT) : vec;
 
     BwdParams p;
     p.u = u;
@@ -1432,11 +1607,11 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     const bool scalar = dims->nheads > 0;
     hipError_t e;
     if (dims->io_dtype == SSM_BF16)
-        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, vec, vec_g, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
-                   : bwd_dispatch<uint16_t, false>(p, pl, vec, vec_g, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, vec, vec_g, vec_c, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<uint16_t, false>(p, pl, vec, vec_g, vec_c, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
     else
-        e = scalar ? bwd_dispatch<float, true>(p, pl, vec, vec_g, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
-                   : bwd_dispatch<float, false>(p, pl, vec, vec_g, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+        e = scalar ? bwd_dispatch<float, true>(p, pl, vec, vec_g, vec_c, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<float, false>(p, pl, vec, vec_g, vec_c, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
