@@ -31,6 +31,10 @@
 //      per-wave LDS transpose, 16 values at a time, in a fixed order;
 //   3. reduce kernels add the per-workgroup partials of dB, dC, dA, dD and ddt_bias
 //      in a fixed order.
+// With 9..16 state entries per channel the checkpoint and gradient passes run with
+// separate roles instead: four walking waves (4 entries per lane) beside four helper
+// waves that stage and finish, over double-buffered tiles (scan_bwd_ckpt_ws_kernel,
+// scan_bwd_grad_ws_kernel).
 // Long sequences are cut into pieces exactly as in the forward: the pieces' start
 // states come from a forward aggregate pass and carry, their incoming gradients from
 // a reverse aggregate pass (e from zero at the piece end, and the dt2 sum) and a
