@@ -343,7 +343,7 @@ def to_device_cols(xd):
 BWD_OPS_PER_UPDATE = 16
 
 
-def backward_bench(x, dev, steps: int = 30, warmup: int = 5):
+def backward_bench(x, dev, steps: int = 40, warmup: int = 15):
     """Time ssm_selective_scan_bwd on the same inputs (cotangent dy seeded, no dh_last):
     one call = every kernel of the backward (state checkpoints, reverse gradient walk,
     reductions of the partial sums)."""
