@@ -386,12 +386,45 @@ def backward_bench(x, dev, steps: int = 40, warmup: int = 15):
     nbytes = (7 * esz * x.batch * x.L * x.dim + (2 * esz + 8) * x.batch * x.N * x.L
               + 8 * (x.A.size + 2 * x.dim))
     tops = BWD_OPS_PER_UPDATE * x.updates / (ms * 1e-3) / 1e12
-    return {"workload": f"{x.batch}x{x.L}x{x.dim}, N {x.N}, {x.io} I/O: gradients of every input",
-            "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3), "plan": plan,
-            "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
-                         "unit": "TFLOP/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
-                         "note": f"{BWD_OPS_PER_UPDATE} fp32 VALU lane operations per state update"},
-            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    rec = {"workload": f"{x.batch}x{x.L}x{x.dim}, N {x.N}, {x.io} I/O: gradients of every input",
+           "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3), "plan": plan,
+           "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                        "unit": "TFLOP/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
+                        "note": f"{BWD_OPS_PER_UPDATE} fp32 VALU lane operations per state update"},
+           "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+    # training with saved checkpoints: the forward keeps the state every 16 steps and
+    # the backward starts from them instead of recomputing them
+    nck = ssm.ssm_selective_scan_ckpt_bytes(dims)
+    if nck:
+        ck = torch.empty(nck // 4, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(dev["u"])
+        fargs = (p(dev["u"]), p(dev["delta"]), p(dev["A"]), p(dev["B"]), p(dev["C"]), p(dev["D"]), p(dev["z"]),
+                 p(dev["dt_bias"]), None, p(y), None, p(ck), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream))
+        bargs = args[:11] + (p(ck),) + args[11:]
+        lib = ssm.load_library()
+
+        def timed(fn, a, name):
+            for _ in range(warmup):
+                st = fn(*a)
+                if st != 0:
+                    raise ssm.SsmError(st, name)
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(steps):
+                fn(*a)
+            t1.record(stream)
+            t1.synchronize()
+            return t0.elapsed_time(t1) / steps
+
+        f_ms = timed(lib.ssm_selective_scan_fwd_ckpt, fargs, "ssm_selective_scan_fwd_ckpt")
+        b_ms = timed(lib.ssm_selective_scan_bwd_ckpt, bargs, "ssm_selective_scan_bwd_ckpt")
+        rec["with_forward_checkpoints"] = {
+            "fwd_ckpt_ms": round(f_ms, 4), "bwd_ckpt_ms": round(b_ms, 4), "checkpoint_bytes": nck,
+            "note": "ssm_selective_scan_fwd_ckpt keeps the state every 16 steps; ssm_selective_scan_bwd_ckpt "
+                    "starts from them and skips its own recomputation walk"}
+    return rec
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0

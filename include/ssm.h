@@ -239,6 +239,40 @@ SSM_API int ssm_selective_scan_bwd(const void* u, const void* delta, const float
                                    const void* dy, const float* dh_last, const ssm_grads* grads,
                                    const ssm_dims* dims, void* stream);
 
+/* ------------------------------------------------------------------------------
+ * Training with saved state checkpoints.  The backward needs the forward's states;
+ * like Mamba's kernels it recomputes them instead of storing every step
+ * (yo3nglau.github.io "Mamba 与状态空间模型：面试问题与推荐回答" Q7).  It recomputes each
+ * 16-step interval from the state at the interval's start, and ordinarily first
+ * re-walks the sequence to find those states.  A forward that is run anyway (a
+ * training step) can keep them instead, and the backward then skips that walk.
+ *
+ * Checkpoint buffer: float32 [batch][ceil(dim/64)][ceil(seqlen/16)][16][64]; element
+ * (b, c, k, n, l) is the state h[b, 64c+l, n] before step 16k (k = 0: h0 or zeros).
+ * Elements with n >= dstate or 64c+l >= dim are written by the forward and ignored by
+ * the backward.  Supported: 9 <= dstate <= 16 with dims->states_per_lane = 0. */
+
+/* Bytes of the checkpoint buffer for dims; 0 when dims is invalid or not supported. */
+SSM_API size_t ssm_selective_scan_ckpt_bytes(const ssm_dims* dims);
+
+/* ssm_selective_scan_fwd_state that also writes the checkpoints to ckpt (required,
+ * 4-byte aligned, ssm_selective_scan_ckpt_bytes(dims) bytes, overlapping no input, no
+ * other output and no workspace: SSM_ERR_ALIAS).  y and h_last are bitwise those of
+ * ssm_selective_scan_fwd_state.  Unsupported dims give SSM_ERR_DIMS. */
+SSM_API int ssm_selective_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                                        const void* C, const float* D, const void* z, const float* dt_bias,
+                                        const float* h0, void* y, float* h_last, float* ckpt,
+                                        const ssm_dims* dims, void* stream);
+
+/* ssm_selective_scan_bwd with the checkpoints that ssm_selective_scan_fwd_ckpt wrote
+ * for the same inputs (ckpt: required, 4-byte aligned, read only; no output may
+ * overlap it).  Same workspace and results up to float rounding; unsupported dims
+ * give SSM_ERR_DIMS. */
+SSM_API int ssm_selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                                        const void* C, const float* D, const void* z, const float* dt_bias,
+                                        const float* h0, const void* dy, const float* dh_last, const float* ckpt,
+                                        const ssm_grads* grads, const ssm_dims* dims, void* stream);
+
 /* Static English text for a status value. */
 SSM_API const char* ssm_status_string(int status);
 

@@ -38,7 +38,8 @@ EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_fwd_state", "ssm_selec
             "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_plan", "ssm_status_string",
             "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd_plan",
             "ssm_selective_scan_fwd_conv", "ssm_selective_scan_step_conv", "ssm_ssd_fwd",
-            "ssm_ssd_fwd_workspace_bytes", "ssm_ssd_fwd_plan")
+            "ssm_ssd_fwd_workspace_bytes", "ssm_ssd_fwd_plan", "ssm_selective_scan_ckpt_bytes",
+            "ssm_selective_scan_fwd_ckpt", "ssm_selective_scan_bwd_ckpt")
 SSM_MAX_DSTATE_BWD = 128
 
 
@@ -163,6 +164,12 @@ def load_library():
         lib.ssm_ssd_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.ssm_ssd_fwd_plan.argtypes = [ctypes.POINTER(SsmSsdDims), ctypes.POINTER(SsmSsdPlan)]
         lib.ssm_ssd_fwd_plan.restype = ctypes.c_int
+        lib.ssm_selective_scan_ckpt_bytes.argtypes = [ctypes.POINTER(SsmDims)]
+        lib.ssm_selective_scan_ckpt_bytes.restype = ctypes.c_size_t
+        lib.ssm_selective_scan_fwd_ckpt.argtypes = [vp] * 12 + [ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_fwd_ckpt.restype = ctypes.c_int
+        lib.ssm_selective_scan_bwd_ckpt.argtypes = [vp] * 12 + [ctypes.POINTER(SsmGrads), ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_bwd_ckpt.restype = ctypes.c_int
         lib.ssm_status_string.argtypes = [ctypes.c_int]
         lib.ssm_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -236,6 +243,23 @@ def ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last
         _ptr(h_last), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
 
 
+def ssm_selective_scan_ckpt_bytes(dims: SsmDims) -> int:
+    return int(load_library().ssm_selective_scan_ckpt_bytes(ctypes.byref(dims)))
+
+
+def ssm_selective_scan_fwd_ckpt(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, ckpt, dims: SsmDims,
+                                stream=None) -> int:
+    """C entry point of the forward that also keeps the state checkpoints (float32
+    buffer of ssm_selective_scan_ckpt_bytes(dims) bytes)."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device)
+    return int(load_library().ssm_selective_scan_fwd_ckpt(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y),
+        _ptr(h_last), _ptr(ckpt), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
 def ssm_selective_scan_step(u, delta, A, B, C, D, z, dt_bias, h, y, dims: SsmDims, stream=None) -> int:
     """C entry point of one decoding step; h float32 (batch, dim, N) is updated in place."""
     import torch
@@ -283,16 +307,20 @@ def _check_tensors(u, tensors, f32_names=("A", "D", "dt_bias", "h0", "h")):
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, h0=None, return_state=False, out=None,
-                       workspace=None, nchunks=0, states_per_lane=0, stream=None):
+                       workspace=None, nchunks=0, states_per_lane=0, ckpt=None, stream=None):
     """Allocate y (and the workspace, if the plan needs one) and run the scan.
 
     Tensors must be contiguous CUDA tensors with the layouts of include/ssm.h.
     h0: optional float32 (batch, dim, N) starting state.  With return_state=True the
-    final state is returned too, as (y, h_last).  Raises SsmError on a refused call.
+    final state is returned too, as (y, h_last).  ckpt: optional float32 device tensor
+    of ssm_selective_scan_ckpt_bytes(dims) bytes that receives the state checkpoints
+    for selective_scan_bwd (ssm_selective_scan_fwd_ckpt).  Raises SsmError on a
+    refused call.
     """
     import torch
 
-    _check_tensors(u, dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h0=h0))
+    _check_tensors(u, dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h0=h0, ckpt=ckpt),
+                   f32_names=("A", "D", "dt_bias", "h0", "ckpt"))
     dims = dims_for(u, B, A, nchunks=nchunks, states_per_lane=states_per_lane)
     if out is None:
         out = torch.empty_like(u)
@@ -305,10 +333,26 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, h0=No
             workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
         dims.workspace = workspace.data_ptr()
         dims.workspace_bytes = workspace.numel() * workspace.element_size()
-    st = ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, h0, out, h_last, dims, stream)
-    if st != SSM_OK:
-        raise SsmError(st, "ssm_selective_scan_fwd_state")
+    if ckpt is not None:
+        st = ssm_selective_scan_fwd_ckpt(u, delta, A, B, C, D, z, dt_bias, h0, out, h_last, ckpt, dims, stream)
+        if st != SSM_OK:
+            raise SsmError(st, "ssm_selective_scan_fwd_ckpt")
+    else:
+        st = ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, h0, out, h_last, dims, stream)
+        if st != SSM_OK:
+            raise SsmError(st, "ssm_selective_scan_fwd_state")
     return (out, h_last) if return_state else out
+
+
+def new_ckpt(u, B, A):
+    """A float32 device tensor for the state checkpoints of a forward on these shapes
+    (raises SsmError when the shapes have no checkpoint form)."""
+    import torch
+
+    n = ssm_selective_scan_ckpt_bytes(dims_for(u, B, A))
+    if n == 0:
+        raise SsmError(SSM_ERR_DIMS, "ssm_selective_scan_ckpt_bytes")
+    return torch.empty(n // 4, dtype=torch.float32, device=u.device)
 
 
 def selective_scan_step(u, delta, A, B, C, D, z, dt_bias, h, *, out=None, stream=None):
@@ -341,16 +385,30 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, gr
         _ptr(dh_last), ctypes.byref(grads), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
 
 
+def ssm_selective_scan_bwd_ckpt(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, ckpt, grads: SsmGrads,
+                                dims: SsmDims, stream=None) -> int:
+    """C entry point of the backward from the forward's state checkpoints."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device)
+    return int(load_library().ssm_selective_scan_bwd_ckpt(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(dy),
+        _ptr(dh_last), _ptr(ckpt), ctypes.byref(grads), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
 def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, dy, h0=None, dh_last=None,
-                       nchunks=0, states_per_lane=0, workspace=None, stream=None) -> dict:
+                       nchunks=0, states_per_lane=0, workspace=None, ckpt=None, stream=None) -> dict:
     """Gradients of sum(dy * y) + sum(dh_last * h_last) for the forward with the same
     inputs.  Allocates the outputs (and the workspace) with torch; returns a dict with
     du, ddelta (u's dtype), dA, dB, dC, dD, ddt_bias, dh0 (float32) and dz (when z is
-    given).  Raises SsmError on a refused call."""
+    given).  ckpt: the checkpoints a selective_scan_fwd(..., ckpt=...) call kept for
+    the same inputs (the backward then skips recomputing them).  Raises SsmError on a
+    refused call."""
     import torch
 
     _check_tensors(u, dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, h0=h0, dy=dy,
-                           dh_last=dh_last), f32_names=("A", "D", "dt_bias", "h0", "dh_last"))
+                           dh_last=dh_last, ckpt=ckpt), f32_names=("A", "D", "dt_bias", "h0", "dh_last", "ckpt"))
     dims = dims_for(u, B, A, nchunks=nchunks, states_per_lane=states_per_lane)
     batch, dim, L = u.shape
     N = B.shape[1]
@@ -369,9 +427,14 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, *, dy, h
     dims.workspace = workspace.data_ptr()
     dims.workspace_bytes = workspace.numel() * workspace.element_size()
     g = SsmGrads(*[out[k].data_ptr() if k in out else None for k, _ in SsmGrads._fields_])
-    st = ssm_selective_scan_bwd(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, g, dims, stream)
-    if st != SSM_OK:
-        raise SsmError(st, "ssm_selective_scan_bwd")
+    if ckpt is not None:
+        st = ssm_selective_scan_bwd_ckpt(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, ckpt, g, dims, stream)
+        if st != SSM_OK:
+            raise SsmError(st, "ssm_selective_scan_bwd_ckpt")
+    else:
+        st = ssm_selective_scan_bwd(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, g, dims, stream)
+        if st != SSM_OK:
+            raise SsmError(st, "ssm_selective_scan_bwd")
     return out
 
 

@@ -751,6 +751,9 @@ __global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdPara
             }
         }
     }
+    bool ck_ok[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) ck_ok[j] = lane_ok && int64_t(wv) * SPL + j < p.N;
     auto load_ck = [&](int kt) {
         const float* ck = p.ck + ((blk * p.ntiles_seq + tile0 + kt) * NP + int64_t(wv) * SPL) * kLanes + lane;
 #pragma unroll
@@ -1000,8 +1003,10 @@ __global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdPara
         __syncthreads();
         for (int i = 0; i <= ntiles; ++i) {
             if (i < ntiles) {
+                // checkpoint entries of absent channels and padding entries are not
+                // used (they may hold anything when the checkpoints come from the caller)
 #pragma unroll
-                for (int j = 0; j < SPL; ++j) hst[j] = ckn[j];
+                for (int j = 0; j < SPL; ++j) hst[j] = ck_ok[j] ? ckn[j] : 0.0f;
                 if (i + 1 < ntiles) load_ck(kt_of(i + 1));
                 walk(buf(i & 1));
             }
@@ -1409,26 +1414,31 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
     return SSM_OK;
 }
 
+// ext_ck: the checkpoints at p.ck come from the caller (the forward kept them), so the
+// forward aggregate, the forward carry and the checkpoint pass are skipped.
 template <typename IO, int SPL, int G, bool SCALAR, bool VEC>
-hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, float* dA, float* dB, float* dC,
-                      float* dD, float* dbias, hipStream_t s) {
+hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, bool ext_ck, float* dA, float* dB,
+                      float* dC, float* dD, float* dbias, hipStream_t s) {
     const dim3 block(unsigned(G * kLanes));
     const int64_t groups = pl.groups;
     if (pl.nch > 1) {
         const dim3 grid1(unsigned(groups * (pl.nch - 1)));
         p.piece_base = 0;
-        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kFwdAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
+        if (!ext_ck)
+            hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kFwdAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
         p.piece_base = 1;
         hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kRevAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
         p.piece_base = 0;
         const int64_t total = groups * p.np * kLanes;
         const dim3 gridc(unsigned(cdiv(total, 256)));
-        hipLaunchKernelGGL(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 0);
+        if (!ext_ck) hipLaunchKernelGGL(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 0);
         hipLaunchKernelGGL(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 1);
     }
     p.piece_base = 0;
     const dim3 grid(unsigned(groups * pl.nch));
-    if constexpr (SPL == wsc::NP / G && G == 8) {
+    if (ext_ck) {
+        // nothing to recompute
+    } else if constexpr (SPL == wsc::NP / G && G == 8) {
         if (vec_c)
             hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true>), grid, dim3(wsc::kThreads), wsc::kLdsBytes, s, p);
         else
@@ -1459,11 +1469,11 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, fl
 // The (entries per lane, waves) pairs the planner produces: 1..4 entries with 4 waves
 // (dstate <= 16, or forced), and 2..16 entries with 8 waves.
 template <typename IO, bool SCALAR, bool VEC>
-hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, bool vec_g, bool vec_c, float* dA, float* dB,
-                            float* dC, float* dD, float* dbias, hipStream_t s) {
+hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, bool vec_g, bool vec_c, bool ext_ck, float* dA,
+                            float* dB, float* dC, float* dD, float* dbias, hipStream_t s) {
 #define SSM_BWD_CASE(S_, G_)                                                                               \
     if (pl.spl == S_ && pl.G == G_)                                                                        \
-        return bwd_launch<IO, S_, G_, SCALAR, VEC>(p, pl, vec_g, vec_c, dA, dB, dC, dD, dbias, s);
+        return bwd_launch<IO, S_, G_, SCALAR, VEC>(p, pl, vec_g, vec_c, ext_ck, dA, dB, dC, dD, dbias, s);
     SSM_BWD_CASE(1, 4)
     SSM_BWD_CASE(2, 4)
     SSM_BWD_CASE(4, 4)
@@ -1476,10 +1486,10 @@ hipError_t bwd_dispatch_vec(const BwdParams& p, const BwdPlan& pl, bool vec_g, b
 }
 
 template <typename IO, bool SCALAR>
-hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, bool vec, bool vec_g, bool vec_c, float* dA,
-                        float* dB, float* dC, float* dD, float* dbias, hipStream_t s) {
-    return vec ? bwd_dispatch_vec<IO, SCALAR, true>(p, pl, vec_g, vec_c, dA, dB, dC, dD, dbias, s)
-               : bwd_dispatch_vec<IO, SCALAR, false>(p, pl, vec_g, vec_c, dA, dB, dC, dD, dbias, s);
+hipError_t bwd_dispatch(const BwdParams& p, const BwdPlan& pl, bool vec, bool vec_g, bool vec_c, bool ext_ck,
+                        float* dA, float* dB, float* dC, float* dD, float* dbias, hipStream_t s) {
+    return vec ? bwd_dispatch_vec<IO, SCALAR, true>(p, pl, vec_g, vec_c, ext_ck, dA, dB, dC, dD, dbias, s)
+               : bwd_dispatch_vec<IO, SCALAR, false>(p, pl, vec_g, vec_c, ext_ck, dA, dB, dC, dD, dbias, s);
 }
 
 }  // namespace
@@ -1509,15 +1519,20 @@ int ssm_selective_scan_bwd_plan(const ssm_dims* dims, ssm_plan* plan) {
     return SSM_OK;
 }
 
-int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                           const float* D, const void* z, const float* dt_bias, const float* h0, const void* dy,
-                           const float* dh_last, const ssm_grads* grads, const ssm_dims* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+             const void* z, const float* dt_bias, const float* h0, const void* dy, const float* dh_last,
+             const ssm_grads* grads, const ssm_dims* dims, void* stream, bool with_ckpt, const float* ckpt) {
     if (!dims || !grads) return SSM_ERR_NULL;
     BwdPlan pl;
     int st = make_bwd_plan(dims, &pl);
     if (st != SSM_OK) return st;
+    if (with_ckpt && (ssm_selective_scan_ckpt_bytes(dims) == 0 || !pl.ws)) return SSM_ERR_DIMS;
     if (!u || !delta || !A || !B || !C || !dy || !grads->du || !grads->ddelta || !grads->dA || !grads->dB ||
-        !grads->dC)
+        !grads->dC || (with_ckpt && !ckpt))
         return SSM_ERR_NULL;
     void* dz = z ? grads->dz : nullptr;
     const size_t esz = dims->io_dtype == SSM_BF16 ? 2 : 4;
@@ -1526,7 +1541,7 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
         misaligned(dz, esz) || misaligned(A, 4) || misaligned(D, 4) || misaligned(dt_bias, 4) ||
         misaligned(h0, 4) || misaligned(dh_last, 4) || misaligned(grads->dA, 4) || misaligned(grads->dB, 4) ||
         misaligned(grads->dC, 4) || misaligned(grads->dD, 4) || misaligned(grads->ddt_bias, 4) ||
-        misaligned(grads->dh0, 4))
+        misaligned(grads->dh0, 4) || misaligned(ckpt, 4))
         return SSM_ERR_ALIGN;
 
     const size_t nel = size_t(dims->batch) * dims->dim * dims->seqlen * esz;
@@ -1535,12 +1550,13 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     const size_t na = (dims->nheads > 0 ? size_t(dims->nheads) : size_t(dims->dim) * dims->dstate) * 4;
     const size_t nd = size_t(dims->dim) * 4;
     const size_t nh = size_t(dims->batch) * dims->dim * dims->dstate * 4;
-    const void* ins[] = {u, delta, z, B, C, A, D, dt_bias, h0, dy, dh_last};
-    const size_t in_sz[] = {nel, nel, nel, nbc, nbc, na, nd, nd, nh, nel, nh};
+    const size_t nck = with_ckpt ? ssm_selective_scan_ckpt_bytes(dims) : 0;
+    const void* ins[] = {u, delta, z, B, C, A, D, dt_bias, h0, dy, dh_last, with_ckpt ? ckpt : nullptr};
+    const size_t in_sz[] = {nel, nel, nel, nbc, nbc, na, nd, nd, nh, nel, nh, nck};
     const void* outs[] = {grads->du, grads->ddelta, dz, grads->dA, grads->dB, grads->dC, grads->dD,
                           grads->ddt_bias, grads->dh0, dims->workspace};
     const size_t out_sz[] = {nel, nel, nel, na, nbc4, nbc4, nd, nd, nh, pl.ws_bytes};
-    constexpr int kIn = 11, kOut = 10;
+    constexpr int kIn = 12, kOut = 10;
     for (int i = 0; i < kOut; ++i) {
         for (int k = 0; k < kIn; ++k)
             if (overlaps(outs[i], out_sz[i], ins[k], in_sz[k])) return SSM_ERR_ALIAS;
@@ -1593,7 +1609,7 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     p.piece_base = 0;
     char* ws = static_cast<char*>(dims->workspace);
     auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-    p.ck = at(pl.off_ck);
+    p.ck = with_ckpt ? const_cast<float*>(ckpt) : at(pl.off_ck);   // read only when given
     p.pBC = at(pl.off_bc);
     p.pA = at(pl.off_a);
     p.pD = at(pl.off_d);
@@ -1611,12 +1627,29 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     const bool scalar = dims->nheads > 0;
     hipError_t e;
     if (dims->io_dtype == SSM_BF16)
-        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, vec, vec_g, vec_c, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
-                   : bwd_dispatch<uint16_t, false>(p, pl, vec, vec_g, vec_c, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+        e = scalar ? bwd_dispatch<uint16_t, true>(p, pl, vec, vec_g, vec_c, with_ckpt, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<uint16_t, false>(p, pl, vec, vec_g, vec_c, with_ckpt, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
     else
-        e = scalar ? bwd_dispatch<float, true>(p, pl, vec, vec_g, vec_c, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
-                   : bwd_dispatch<float, false>(p, pl, vec, vec_g, vec_c, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
+        e = scalar ? bwd_dispatch<float, true>(p, pl, vec, vec_g, vec_c, with_ckpt, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s)
+                   : bwd_dispatch<float, false>(p, pl, vec, vec_g, vec_c, with_ckpt, grads->dA, grads->dB, grads->dC, grads->dD, grads->ddt_bias, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* dt_bias, const float* h0, const void* dy,
+                           const float* dh_last, const ssm_grads* grads, const ssm_dims* dims, void* stream) {
+    return bwd_impl(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, grads, dims, stream, false, nullptr);
+}
+
+int ssm_selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* dt_bias, const float* h0, const void* dy,
+                                const float* dh_last, const float* ckpt, const ssm_grads* grads, const ssm_dims* dims,
+                                void* stream) {
+    return bwd_impl(u, delta, A, B, C, D, z, dt_bias, h0, dy, dh_last, grads, dims, stream, true, ckpt);
 }
 
 }  // extern "C"

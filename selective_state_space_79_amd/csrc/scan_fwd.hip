@@ -76,7 +76,13 @@ struct Params {
     void* u_out;             // nullable: u, rounded to the I/O type (full mode)
     int32_t conv_k;          // 1 .. kMaxConv
     int32_t conv_silu;       // 1: SiLU after the convolution
+    // state checkpoints (kernels instantiated with checkpoints only, 16 padded state
+    // entries): [groups][ntiles_ck][16][64], the state before every 16th step
+    float* ckpt;
+    int64_t ntiles_ck;       // ceil(L / 16)
 };
+
+constexpr int kCkptSteps = 16;   // steps between state checkpoints
 
 enum Mode { kFull = 0, kAggregate = 1 };
 constexpr int kMaxConv = 4;   // widest fused convolution: its history fits one 4-element halo
@@ -140,13 +146,15 @@ inline size_t lds_floats_g(int G, int spl, bool full) {
 // One launch processes, for every (batch, channel block, piece), the piece's time
 // tiles in order.  MODE kFull reads out and stores y (starting from ws_Hin when the
 // piece is not the first); MODE kAggregate only records the piece's end state from
-// zero and its dt2 sum.
+// zero and its dt2 sum.  With CK (full mode, 16 padded entries) the walkers also
+// write their state before every 16th step to p.ckpt, the checkpoints the backward's
+// gradient pass starts its tiles from.
 //
 // The G walking waves each carry SPL state entries of every channel; entries
 // n >= N are padding with A = 0 and B = C = 0, which stay zero.  Staged steps beyond
 // the piece's end are identity steps (dt2 = 0, x = 0), so the walk always runs
 // whole tiles.
-template <typename IO, int SPL, bool SCALAR, int MODE, bool VEC, int G>
+template <typename IO, int SPL, bool SCALAR, int MODE, bool VEC, int G, bool CK = false>
 __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(Params p) {
     using S = Shape<G, SPL>;
     constexpr int NP_ = G * SPL;
@@ -174,6 +182,8 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     constexpr float kLn2f = kLn2;
     constexpr int BUF = T * kRow * 2 + NBC + (kFullMode ? (G + 2) * T * kRowY : 0);   // floats per buffer
     static_assert(T % 8 == 0, "time tile must hold whole vectors and step groups");
+    static_assert(!CK || (MODE == kFull && NP_ == 16 && T % kCkptSteps == 0 && kCkptSteps % QB == 0),
+                  "checkpoints: full mode, 16 padded entries, whole checkpoint intervals per tile");
 
     extern __shared__ float smem[];
     const int tid = threadIdx.x;
@@ -436,12 +446,19 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
 
     // ---- walk one tile from LDS buffer `buf` (walking waves): SPL state entries per
     //      lane, sequential in t; the LDS operands of QB steps are read up front
-    auto walk = [&](float* buf) {
+    auto walk = [&](float* buf, int64_t t0) {
         const float2* dxp = reinterpret_cast<const float2*>(buf) + lane;
         const float* bcp = buf + T * kRow * 2 + w * T * BCW;
         float* yo = buf + T * kRow * 2 + NBC + w * T * kRowY + lane;
 #pragma unroll
         for (int t = 0; t < T; t += QB) {
+            if constexpr (CK) {
+                if (t % kCkptSteps == 0 && t0 + t < tend) {
+                    float* ck = p.ckpt + ((blk * p.ntiles_ck + (t0 + t) / kCkptSteps) * NP + int64_t(w) * SPL) * kLanes + lane;
+#pragma unroll
+                    for (int j = 0; j < SPL; ++j) ck[int64_t(j) * kLanes] = h[j];
+                }
+            }
             float2 dx[QB];
             BCVec<SPL> bc[QB];
 #pragma unroll
@@ -529,7 +546,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
             float* oth = smem + ((kt + 1) & 1) * BUF;
             const int64_t t0 = tbeg + int64_t(kt) * T;
             if (walker) {
-                walk(cur);
+                walk(cur, t0);
             } else {
                 if (kt >= 1) finish(oth, t0 - T, kt - 1);
                 if (kt + 1 < ntiles) {
@@ -547,7 +564,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
             stage(smem, t0);
             if (kt + 1 < ntiles) issue_loads(t0 + T);   // prefetch the next tile
             __syncthreads();
-            walk(smem);
+            walk(smem, t0);
             __syncthreads();
             finish(smem, t0, kt);
         }
@@ -877,7 +894,7 @@ int make_plan(const ssm_dims* d, Plan* pl) {
 }
 
 // ------------------------------------------------------------------ host side: launching
-template <typename IO, int SPL, bool SCALAR, bool VEC, int G>
+template <typename IO, int SPL, bool SCALAR, bool VEC, int G, bool CK = false>
 hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
     using S = Shape<G, SPL>;
     if (pl.G != G || pl.T != S::T || p.np != G * SPL) return hipErrorInvalidConfiguration;
@@ -892,7 +909,7 @@ hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
         const int64_t total = groups * p.np * kLanes;
         hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, p, total);
     }
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, G>), dim3(unsigned(pl.blocks)), block, lds_full,
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, G, CK>), dim3(unsigned(pl.blocks)), block, lds_full,
                        stream, p);
     return hipGetLastError();
 }
@@ -925,6 +942,24 @@ hipError_t dispatch_nt(const Params& p, const Plan& pl, bool vec, hipStream_t s)
 template <typename IO>
 hipError_t dispatch(const Params& p, const Plan& pl, bool vec, hipStream_t s) {
     return pl.scalar ? dispatch_nt<IO, true>(p, pl, vec, s) : dispatch_nt<IO, false>(p, pl, vec, s);
+}
+
+// Plans with a checkpointing kernel: the automatic plans for 9..16 state entries
+// (diagonal decay: 4 walking waves of 4 entries; scalar decay: 8 of 2).
+inline bool ckpt_plan(const Plan& pl) {
+    return pl.G * pl.spl == 16 && ((!pl.scalar && pl.spl == 4 && pl.G == 4) || (pl.scalar && pl.spl == 2 && pl.G == 8));
+}
+
+template <typename IO, bool VEC>
+hipError_t dispatch_ckpt_vec(const Params& p, const Plan& pl, hipStream_t s) {
+    if (!pl.scalar && pl.spl == 4 && pl.G == 4) return launch_all<IO, 4, false, VEC, 4, true>(p, pl, s);
+    if (pl.scalar && pl.spl == 2 && pl.G == 8) return launch_all<IO, 2, true, VEC, 8, true>(p, pl, s);
+    return hipErrorInvalidConfiguration;
+}
+
+template <typename IO>
+hipError_t dispatch_ckpt(const Params& p, const Plan& pl, bool vec, hipStream_t s) {
+    return vec ? dispatch_ckpt_vec<IO, true>(p, pl, s) : dispatch_ckpt_vec<IO, false>(p, pl, s);
 }
 
 }  // namespace
@@ -977,17 +1012,19 @@ namespace {
 // u = act(conv(x)) with x at `u` (conv != nullptr).
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
              const void* z, const float* dt_bias, const float* h0, void* y, float* h_last, const ssm_dims* dims,
-             void* stream, const ssm_conv* conv, const void* conv_state, void* u_out) {
+             void* stream, const ssm_conv* conv, const void* conv_state, void* u_out, bool with_ckpt = false,
+             float* ckpt = nullptr) {
     if (!dims) return SSM_ERR_NULL;
     Plan pl;
     int st = make_plan(dims, &pl);
     if (st != SSM_OK) return st;
-    if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+    if (with_ckpt && (ssm_selective_scan_ckpt_bytes(dims) == 0 || !ckpt_plan(pl))) return SSM_ERR_DIMS;
+    if (!u || !delta || !A || !B || !C || !y || (with_ckpt && !ckpt)) return SSM_ERR_NULL;
 
     const size_t esz = dims->io_dtype == SSM_BF16 ? 2 : 4;
     if (misaligned(u, esz) || misaligned(delta, esz) || misaligned(z, esz) || misaligned(B, esz) ||
         misaligned(C, esz) || misaligned(y, esz) || misaligned(A, 4) || misaligned(D, 4) || misaligned(dt_bias, 4) ||
-        misaligned(h0, 4) || misaligned(h_last, 4))
+        misaligned(h0, 4) || misaligned(h_last, 4) || misaligned(ckpt, 4))
         return SSM_ERR_ALIGN;
 
     const size_t nel = size_t(dims->batch) * dims->dim * dims->seqlen * esz;
@@ -1036,6 +1073,17 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
             return SSM_ERR_ALIAS;
     }
 
+    if (with_ckpt) {
+        // the checkpoints are an output: they may overlap no input, no other output
+        // and no workspace
+        const size_t nck = ssm_selective_scan_ckpt_bytes(dims);
+        const void* all[] = {u, delta, z, B, C, A, D, dt_bias, h0, y, h_last};
+        const size_t all_sz[] = {nel, nel, nel, nbc, nbc, na, nd, nd, nh, nel, nh};
+        for (int k = 0; k < 11; ++k)
+            if (overlaps(ckpt, nck, all[k], all_sz[k])) return SSM_ERR_ALIAS;
+        if (pl.ws_bytes > 0 && overlaps(ckpt, nck, dims->workspace, pl.ws_bytes)) return SSM_ERR_ALIAS;
+    }
+
     // vector (16-byte) loads need 16-byte aligned rows: aligned base pointers and a
     // row length that is a whole number of vectors
     const size_t vw = 16 / esz;
@@ -1069,6 +1117,8 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     p.u_out = conv ? u_out : nullptr;
     p.conv_k = conv ? conv->width : 0;
     p.conv_silu = conv ? conv->silu : 0;
+    p.ckpt = with_ckpt ? ckpt : nullptr;
+    p.ntiles_ck = cdiv(dims->seqlen, kCkptSteps);
     p.ws_H = p.ws_S = p.ws_Hin = nullptr;
     if (pl.ws_bytes > 0) {
         const size_t per = size_t(dims->batch) * pl.nblk_d * pl.nchunks * kLanes;
@@ -1079,7 +1129,11 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = dims->io_dtype == SSM_BF16 ? dispatch<uint16_t>(p, pl, vec, s) : dispatch<float>(p, pl, vec, s);
+    hipError_t e;
+    if (with_ckpt)
+        e = dims->io_dtype == SSM_BF16 ? dispatch_ckpt<uint16_t>(p, pl, vec, s) : dispatch_ckpt<float>(p, pl, vec, s);
+    else
+        e = dims->io_dtype == SSM_BF16 ? dispatch<uint16_t>(p, pl, vec, s) : dispatch<float>(p, pl, vec, s);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -1105,6 +1159,20 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
                            const float* D, const void* z, const float* dt_bias, void* y, const ssm_dims* dims,
                            void* stream) {
     return ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, nullptr, y, nullptr, dims, stream);
+}
+
+size_t ssm_selective_scan_ckpt_bytes(const ssm_dims* dims) {
+    if (validate_dims(dims) != SSM_OK) return 0;
+    if (dims->dstate < 9 || dims->dstate > 16 || dims->states_per_lane != 0) return 0;
+    return size_t(dims->batch) * size_t(cdiv(dims->dim, kLanes)) * size_t(cdiv(dims->seqlen, kCkptSteps)) * 16 *
+           kLanes * sizeof(float);
+}
+
+int ssm_selective_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
+                                float* h_last, float* ckpt, const ssm_dims* dims, void* stream) {
+    return fwd_impl(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, dims, stream, nullptr, nullptr, nullptr, true,
+                    ckpt);
 }
 
 }  // extern "C"

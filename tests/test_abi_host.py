@@ -263,6 +263,51 @@ def test_backward_refusals():
     assert _bwd(ssm.make_dims(0, 100, 70, 16)) == ssm.SSM_ERR_EMPTY
 
 
+# ---------------------------------------------------------------- state checkpoints
+
+def _fwd_ck(dims, ckpt=0x60000000, y=FAKE + 0x500000):
+    p = lambda a: ctypes.c_void_p(a) if a else None
+    return ssm.load_library().ssm_selective_scan_fwd_ckpt(
+        p(FAKE), p(FAKE + 0x100000), p(FAKE + 0x200000), p(FAKE + 0x300000), p(FAKE + 0x400000), None, None, None,
+        None, p(y), None, p(ckpt), ctypes.byref(dims), None)
+
+
+def _bwd_ck(dims, ckpt=0x60000000):
+    base = 0x40000000
+    g = ssm.SsmGrads(base, base + 0x1000000, base + 0x2000000, base + 0x3000000, base + 0x4000000, None, None, None,
+                     None)
+    p = lambda a: ctypes.c_void_p(a) if a else None
+    return ssm.load_library().ssm_selective_scan_bwd_ckpt(
+        p(FAKE), p(FAKE + 0x100000), p(FAKE + 0x200000), p(FAKE + 0x300000), p(FAKE + 0x400000), None, None, None,
+        None, p(FAKE + 0x500000), None, p(ckpt), ctypes.byref(g), ctypes.byref(dims), None)
+
+
+def test_checkpoint_sizes_and_refusals():
+    """Checkpoints: batch x 64-channel blocks x 16-step intervals x 16 entries x 64
+    lanes x 4 bytes, for 9..16 state entries with the automatic plan only; every
+    refusal comes before anything is enqueued."""
+    assert ssm.ssm_selective_scan_ckpt_bytes(ssm.make_dims(4, 4096, 4096, 16)) == 4 * 64 * 256 * 16 * 64 * 4
+    assert ssm.ssm_selective_scan_ckpt_bytes(ssm.make_dims(2, 100, 70, 12)) == 2 * 2 * 7 * 16 * 64 * 4
+    assert ssm.ssm_selective_scan_ckpt_bytes(ssm.make_dims(1, 17, 64, 9, nheads=2)) == 2 * 16 * 64 * 4
+    for args, kw in [((1, 100, 64, 8), {}), ((1, 100, 64, 17), {}), ((1, 100, 64, 16), dict(states_per_lane=4)),
+                     ((0, 100, 64, 16), {}), ((1, 100, 64, 16), dict(io_dtype=9))]:
+        assert ssm.ssm_selective_scan_ckpt_bytes(ssm.make_dims(*args, **kw)) == 0
+    d = ssm.make_dims(2, 100, 70, 16)
+    assert _fwd_ck(d, ckpt=None) == ssm.SSM_ERR_NULL
+    assert _fwd_ck(ssm.make_dims(1, 100, 64, 8)) == ssm.SSM_ERR_DIMS
+    assert _fwd_ck(ssm.make_dims(1, 100, 64, 16, states_per_lane=2)) == ssm.SSM_ERR_DIMS
+    assert _fwd_ck(d, ckpt=0x60000002) == ssm.SSM_ERR_ALIGN
+    assert _fwd_ck(d, ckpt=FAKE + 0x500000) == ssm.SSM_ERR_ALIAS      # the checkpoints are y
+    assert _fwd_ck(d, ckpt=FAKE - 0x100) == ssm.SSM_ERR_ALIAS         # they run into u
+    bd = _bwd_dims(2, 100, 70, 16)
+    assert _bwd_ck(bd, ckpt=None) == ssm.SSM_ERR_NULL
+    assert _bwd_ck(_bwd_dims(1, 100, 64, 8)) == ssm.SSM_ERR_DIMS
+    assert _bwd_ck(_bwd_dims(1, 100, 64, 40)) == ssm.SSM_ERR_DIMS
+    assert _bwd_ck(bd, ckpt=0x60000002) == ssm.SSM_ERR_ALIGN
+    assert _bwd_ck(bd, ckpt=0x40000000) == ssm.SSM_ERR_ALIAS          # du written over them
+    assert _bwd_ck(bd, ckpt=0x80000000) == ssm.SSM_ERR_ALIAS          # the workspace
+
+
 # ---------------------------------------------------------------- fused convolution front end
 
 def test_conv_entry_points_refuse_bad_arguments():
