@@ -414,8 +414,8 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
     //      [v][lane]; lane 8o+q then sums lanes 8q..8q+7 of value o, and the 8 lanes of
     //      an output combine their partials with DPP (quad swaps, then the half-row
     //      mirror), so every lane of the group holds the same total.  A wave's LDS
-    //      operations complete in issue order, so the reads see this round's writes and
-    //      the next round's writes cannot overtake these reads.
+    //      operations complete in issue order, so the reads see this batch's writes and
+    //      the next batch's writes cannot overtake these reads.
     float* red = sRed + w * kRound * kLanes;
     auto flush = [&](const float (&pv)[kRound], int t_base, int j0) {
 #pragma unroll
