@@ -444,6 +444,10 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
         o.W = swl[t * kLanes];
         read_bc(t, o.Bv, o.Cv);
     };
+    auto get_bc = [&](const StepOps& o, int j, float& Bj, float& Cj) {
+        Bj = o.Bv[j];
+        Cj = o.Cv[j];
+    };
     auto grad_tile = [&]() {
         float hsb[NSB > 1 ? NSB - 1 : 1][SPL];
         if constexpr (NSB > 1) {
@@ -457,8 +461,10 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 if (t + 1 < (NSB - 1) * TS) read_step(t + 1, nxt);
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) {
+                    float Bj, Cj;
+                    get_bc(cur, j, Bj, Cj);
                     const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[j]);
-                    hh[j] = fmaf(a, hh[j], cur.W.y * cur.Bv[j]);
+                    hh[j] = fmaf(a, hh[j], cur.W.y * Bj);
                 }
                 if ((t + 1) % TS == 0) {
 #pragma unroll
@@ -486,10 +492,12 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                     float yp = 0.0f;
 #pragma unroll
                     for (int j = 0; j < SPL; ++j) {
+                        float Bj, Cj;
+                        get_bc(cur, j, Bj, Cj);
                         const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[j]);
-                        hh[j] = fmaf(a, hh[j], cur.W.y * cur.Bv[j]);
+                        hh[j] = fmaf(a, hh[j], cur.W.y * Bj);
                         H[ts][j] = hh[j];
-                        yp = fmaf(cur.Cv[j], hh[j], yp);
+                        yp = fmaf(Cj, hh[j], yp);
                     }
                     sP[(w * T + t) * kLanes + lane] = yp;
                     cur = nxt;
@@ -509,13 +517,15 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 const int s = ts % RS;
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) {
+                    float Bj, Cj;
+                    get_bc(cur, j, Bj, Cj);
                     const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[j]);
                     const float hp = ts > 0 ? H[ts > 0 ? ts - 1 : 0][j] : hb[j];
-                    const float g = fmaf(cur.W.z, cur.Cv[j], e[j]);
+                    const float g = fmaf(cur.W.z, Cj, e[j]);
                     const float t1 = g * (a * hp);
                     dAacc[j] = fmaf(cur.W.x, t1, dAacc[j]);
                     s1 = fmaf(Ar[j], t1, s1);
-                    s2 = fmaf(g, cur.Bv[j], s2);
+                    s2 = fmaf(g, Bj, s2);
                     e[j] = a * g;
                     const int jj = j % JR;
                     pv[(s * 2) * JR + jj] = g * cur.W.y;              // dB (unscaled)
@@ -531,6 +541,112 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 }
                 cur = nxt;
             }
+        }
+    };
+
+    // ---- the gradient walk with 8 or more entries per lane: the entries in groups of
+    //      4, each group recomputing the tile's states from the checkpoint and walking
+    //      back through them, so only one group's states are live in VGPRs (a whole
+    //      tile of 8 or 16 entries did not fit and spilled).  The group loop is not
+    //      unrolled (unrolled, the compiler interleaved the groups and spilled more);
+    //      the group always works on entries 0..3 of the per-entry arrays, which are
+    //      rotated by 4 after each group and so return to their order after the last.
+    //      The per-step sums over entries (read-out, sum A g a h, sum g B') are
+    //      accumulated over the groups in the wave's LDS slab rows.  Each
+    //      phase addresses the LDS step operands through its own opaque zero offset:
+    //      with equal addresses the compiler kept the recompute's B and C values for
+    //      the reverse walk instead of reading them again, and spilled them.
+    auto grad_tile_grouped = [&]() {
+        constexpr int GS = 4, NG = SPL / GS;
+        static_assert(SPL < 8 || (SPL % GS == 0 && JR == GS && RS == 1), "one reduction round per step and group");
+        // per-step sums of this wave: the first group writes its slab rows, later
+        // groups add to them
+        float* const yrow = sP + (w * T) * kLanes + lane;
+        auto rotate = [](float (&v)[SPL]) {
+            float first[GS];
+#pragma unroll
+            for (int k = 0; k < GS; ++k) first[k] = v[k];
+#pragma unroll
+            for (int k = 0; k + GS < SPL; ++k) v[k] = v[k + GS];
+#pragma unroll
+            for (int k = 0; k < GS; ++k) v[SPL - GS + k] = first[k];
+        };
+        // the step's operands for the group: (dt2, x, ds, decay) and (B, C) of its 4
+        // entries, read one step ahead
+        struct GOps {
+            float4 W, bc0, bc1;
+        };
+        auto gread = [&](int off, int t, int j0, GOps& o) {
+            o.W = swl[off + t * kLanes];
+            const float4* q = reinterpret_cast<const float4*>(sbw + off + t * NP * 2 + 2 * j0);
+            o.bc0 = q[0];
+            o.bc1 = q[1];
+        };
+        auto bj = [](const GOps& o, int jj) { return jj == 0 ? o.bc0.x : jj == 1 ? o.bc0.z : jj == 2 ? o.bc1.x : o.bc1.z; };
+        auto cj = [](const GOps& o, int jj) { return jj == 0 ? o.bc0.y : jj == 1 ? o.bc0.w : jj == 2 ? o.bc1.y : o.bc1.w; };
+#pragma unroll 1
+        for (int gi = 0; gi < NG; ++gi) {
+            const int j0 = gi * GS;       // the group's first entry
+            const bool first = gi == 0;
+            float H[T][GS];
+            {
+                int off = 0;
+                asm volatile("" : "+v"(off));
+                float hh[GS];
+#pragma unroll
+                for (int jj = 0; jj < GS; ++jj) hh[jj] = hst[jj];
+                GOps cur, nxt;
+                gread(off, 0, j0, cur);
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    if (t + 1 < T) gread(off, t + 1, j0, nxt);
+                    float yp = first ? 0.0f : yrow[t * kLanes];
+#pragma unroll
+                    for (int jj = 0; jj < GS; ++jj) {
+                        const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[jj]);
+                        hh[jj] = fmaf(a, hh[jj], cur.W.y * bj(cur, jj));
+                        H[t][jj] = hh[jj];
+                        yp = fmaf(cj(cur, jj), hh[jj], yp);
+                    }
+                    yrow[t * kLanes] = yp;
+                    cur = nxt;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            int off = 0;
+            asm volatile("" : "+v"(off));
+            float pv[kRound];
+            GOps cur, nxt;
+            gread(off, T - 1, j0, cur);
+#pragma unroll
+            for (int t = T - 1; t >= 0; --t) {
+                if (t > 0) gread(off, t - 1, j0, nxt);
+                float s1 = first ? 0.0f : yrow[kSlab + t * kLanes];
+                float s2 = first ? 0.0f : yrow[2 * kSlab + t * kLanes];
+#pragma unroll
+                for (int jj = 0; jj < GS; ++jj) {
+                    const float Bj = bj(cur, jj), Cj = cj(cur, jj);
+                    const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[jj]);
+                    const float hp = t > 0 ? H[t > 0 ? t - 1 : 0][jj] : hst[jj];
+                    const float g = fmaf(cur.W.z, Cj, e[jj]);
+                    const float t1 = g * (a * hp);
+                    dAacc[jj] = fmaf(cur.W.x, t1, dAacc[jj]);
+                    s1 = fmaf(Ar[jj], t1, s1);
+                    s2 = fmaf(g, Bj, s2);
+                    e[jj] = a * g;
+                    pv[jj] = g * cur.W.y;              // dB (unscaled)
+                    pv[GS + jj] = cur.W.z * H[t][jj];  // dC
+                }
+                yrow[kSlab + t * kLanes] = s1;
+                yrow[2 * kSlab + t * kLanes] = s2;
+                flush(pv, t, j0);
+                cur = nxt;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            rotate(e);
+            rotate(dAacc);
+            rotate(hst);
+            if constexpr (!SCALAR) rotate(Ar);
         }
     };
 
@@ -628,7 +744,10 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
         }
         if (i + 1 < ntiles) issue_loads(kRev ? kt - 1 : kt + 1);
         __syncthreads();
-        if constexpr (kG) grad_tile();
+        if constexpr (kG) {
+            if constexpr (SPL >= 8) grad_tile_grouped();   // 8 or 16 entries per lane
+            else grad_tile();
+        }
         else if constexpr (MODE == kRevAgg) rev_tile();
         else fwd_tile(kt);
         __syncthreads();
