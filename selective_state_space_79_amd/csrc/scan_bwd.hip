@@ -433,6 +433,27 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
         }
     };
 
+    // ---- the same 8-value channel sum in registers (lane-swap butterfly, see the
+    //      role-split gradient pass): dB of entries j0..j0+3 of this wave, then dC
+    const bool lo8 = (lane & 8) == 0;
+    const int red_v = ((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + (lane >> 5);
+    auto reduce8 = [&](const float (&pv)[kRound], int t, int j0) {
+        auto swap_add = [](float x, float y, auto swap) {
+            const auto r = swap(__float_as_uint(x), __float_as_uint(y));
+            return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        };
+        auto p32 = [](unsigned x, unsigned y) { return __builtin_amdgcn_permlane32_swap(x, y, false, false); };
+        auto p16 = [](unsigned x, unsigned y) { return __builtin_amdgcn_permlane16_swap(x, y, false, false); };
+        const float r0 = swap_add(pv[0], pv[1], p32), r1 = swap_add(pv[2], pv[3], p32);
+        const float r2 = swap_add(pv[4], pv[5], p32), r3 = swap_add(pv[6], pv[7], p32);
+        const float s0 = swap_add(r0, r1, p16), s1 = swap_add(r2, r3, p16);
+        float sum = (lo8 ? s0 : s1) + dpp_move<0x128>(lo8 ? s1 : s0);   // row_ror:8
+        sum += dpp_move<0xB1>(sum);
+        sum += dpp_move<0x4E>(sum);
+        sum += dpp_move<0x141>(sum);
+        if ((lane & 7) == 0) sdBC[((red_v / 4) * NP + w * SPL + j0 + (red_v % 4)) * T + t] = sum;
+    };
+
     // ---- the gradient walk of one tile (all waves); hst holds the tile's start state.
     //      Both walks read the LDS operands of the next step before the arithmetic of
     //      the current one, so that the LDS latency overlaps the work.
@@ -623,23 +644,35 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 if (t > 0) gread(off, t - 1, j0, nxt);
                 float s1 = first ? 0.0f : yrow[kSlab + t * kLanes];
                 float s2 = first ? 0.0f : yrow[2 * kSlab + t * kLanes];
+                float t1s = 0.0f;   // scalar decay: sum over the group of g * a * h_prev
 #pragma unroll
                 for (int jj = 0; jj < GS; ++jj) {
                     const float Bj = bj(cur, jj), Cj = cj(cur, jj);
                     const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[jj]);
                     const float hp = t > 0 ? H[t > 0 ? t - 1 : 0][jj] : hst[jj];
                     const float g = fmaf(cur.W.z, Cj, e[jj]);
-                    const float t1 = g * (a * hp);
-                    dAacc[jj] = fmaf(cur.W.x, t1, dAacc[jj]);
-                    s1 = fmaf(Ar[jj], t1, s1);
+                    if constexpr (SCALAR) {
+                        t1s = fmaf(g, a * hp, t1s);
+                    } else {
+                        const float t1 = g * (a * hp);
+                        dAacc[jj] = fmaf(cur.W.x, t1, dAacc[jj]);
+                        s1 = fmaf(Ar[jj], t1, s1);
+                    }
                     s2 = fmaf(g, Bj, s2);
                     e[jj] = a * g;
                     pv[jj] = g * cur.W.y;              // dB (unscaled)
                     pv[GS + jj] = cur.W.z * H[t][jj];  // dC
                 }
+                if constexpr (SCALAR) {
+                    // the head's rate is every entry's: its dA goes to the group's first
+                    // entry (a padding entry only when the whole group is padding, whose
+                    // terms are zero); the head sum adds all entries
+                    dAacc[0] = fmaf(cur.W.x, t1s, dAacc[0]);
+                    s1 = fmaf(Ar[0], t1s, s1);
+                }
                 yrow[kSlab + t * kLanes] = s1;
                 yrow[2 * kSlab + t * kLanes] = s2;
-                flush(pv, t, j0);
+                reduce8(pv, t, j0);
                 cur = nxt;
                 __builtin_amdgcn_sched_barrier(0);
             }
