@@ -589,6 +589,218 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     }
 }
 
+// ------------------------------------------------------------------ pass 1 on the matrix cores
+// With one decay rate a_h per head, the end state of a piece from zero is
+//   H[d,n] = ln2 * sum_t x[d,t] * 2^(a_h * sum_{s>t} dt2[d,s]) * B[n,t],   x = dt2 * u
+// (dt2 = dt / ln 2: step sizes in log2 units, as in the walk, which folds the ln 2
+// into B),
+// i.e. for each 64-channel block the product of a (channels x steps) weight matrix and
+// the (steps x states) matrix B: a dense contraction over the steps.  Chunk by chunk of
+// 64 steps, H <- 2^(a_h * S_chunk) H + W_chunk B_chunk on v_mfma_f32_16x16x32_bf16,
+// with the fp32 weights split into two bf16 parts (B is a bf16 input, exact).  Same
+// outputs as scan_fwd_kernel<kAggregate>: ws_H and ws_S (the piece's sum of dt2).
+//
+// Wave w owns channels 16w..16w+15.  As the A operand, lane l supplies channel
+// 16w + l%16 at steps 8(l/16)..+7 (k-step 0) and 32 + 8(l/16)..+7 (k-step 1) of the
+// chunk; it computes those 16 weights itself.  The suffix sums over the chunk come
+// from the 8 group totals of its channel, exchanged through LDS among the 4 lanes of
+// the channel (all in the same wave).  The result rows are channels 4(l/16)..+3 of
+// column n = 16j + l%16, so the chunk's decay scales each accumulator row.
+namespace agg {
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+constexpr int kQ = 64;             // steps per chunk
+constexpr int kRowB = kQ + 8;      // B row stride in LDS (bf16): 144 bytes, so the 16 rows
+                                   // a 16-lane group reads start in distinct bank quads
+constexpr int kThreads = 256;
+
+__device__ inline uint32_t pack2(float x0, float x1) {
+    const f32x2 x = {x0, x1};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+// x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) for 8 floats, packed two per word
+__device__ inline void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t hw = pack2(x[2 * j], x[2 * j + 1]);
+        h[j] = hw;
+        l[j] = pack2(x[2 * j] - __uint_as_float(hw << 16), x[2 * j + 1] - __uint_as_float(hw & 0xFFFF0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+}  // namespace agg
+
+template <int N>
+__global__ void __launch_bounds__(agg::kThreads) scan_agg_mfma_kernel(Params p) {
+    using namespace agg;
+    constexpr int NT = N / 16;                    // 16-state column tiles
+    constexpr int KBV = N * (kQ / 8) / kThreads;  // 16-byte B vectors per thread and chunk
+    static_assert(N % 16 == 0 && KBV * kThreads == N * (kQ / 8), "B vectors must split evenly");
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][N * kRowB];
+    __shared__ __attribute__((aligned(16))) float sTot[kLanes * 8];
+    __shared__ __attribute__((aligned(16))) float sDec[kLanes];
+
+    const int tid = threadIdx.x;
+    const int wv = tid / kLanes, lane = tid % kLanes, g = lane / 16;
+    const int64_t bid = blockIdx.x;
+    const int cblk = int(bid % p.nblk_d);
+    const int b = int((bid / p.nblk_d) % p.batch);
+    const int piece = int(bid / (int64_t(p.nblk_d) * p.batch));
+    const int64_t blk = int64_t(b) * p.nblk_d + cblk;
+    const int64_t c0 = int64_t(cblk) * kLanes;
+    const int64_t tbeg = int64_t(piece) * p.chunk_len;
+    const int64_t tend = (tbeg + p.chunk_len < p.L) ? tbeg + p.chunk_len : p.L;
+    const int nq = int((tend - tbeg + kQ - 1) / kQ);
+
+    // A side: channel chl of the block, steps 8g..8g+7 and 32+8g..32+8g+7 of each chunk
+    const int chl = 16 * wv + (lane % 16);
+    const int64_t d = c0 + chl;
+    const bool dok = d < p.dim;
+    const float a_h = dok ? p.A[d / p.head_dim] : 0.0f;
+    const float bias = (dok && p.bias) ? p.bias[d] : 0.0f;
+    const int64_t row = (int64_t(b) * p.dim + (dok ? d : 0)) * p.L;
+    const uint16_t* __restrict__ urow = static_cast<const uint16_t*>(p.u) + row;
+    const uint16_t* __restrict__ drow = static_cast<const uint16_t*>(p.delta) + row;
+    // B side: vector v = tid + k*256 is row n = v/8, steps 8(v%8)..+7 of the chunk
+    const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.Bm) + int64_t(b) * N * p.L;
+
+    // loads never branch: an 8-step group wholly outside the piece reads the row start
+    // and is masked where it is used (pieces hold whole 8-step groups)
+    auto a_off = [&](int q, int grp) {
+        const int64_t t = tbeg + int64_t(q) * kQ + grp * 32 + 8 * g;
+        return t < tend ? t : int64_t(0);
+    };
+    // (the prefetched 16-byte vectors are native vector types: with HIP's uint4, a
+    //  struct, the compiler kept them in scratch memory)
+    const int bcol = 8 * (tid % 8);      // every vector of a thread has the same steps
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float ssum = 0.0f, scomp = 0.0f;   // compensated sum of dt2 over the piece
+
+    u32x4 d0 = *reinterpret_cast<const u32x4*>(drow + a_off(0, 0));
+    u32x4 u0 = *reinterpret_cast<const u32x4*>(urow + a_off(0, 0));
+    u32x4 d1 = *reinterpret_cast<const u32x4*>(drow + a_off(0, 1));
+    u32x4 u1 = *reinterpret_cast<const u32x4*>(urow + a_off(0, 1));
+    u32x4 d0n, u0n, d1n, u1n, bv[KBV];
+    {
+        const int64_t t = tbeg + bcol;
+#pragma unroll
+        for (int k = 0; k < KBV; ++k)
+            bv[k] = *reinterpret_cast<const u32x4*>(gB + int64_t((tid + k * kThreads) / 8) * p.L + (t < tend ? t : 0));
+#pragma unroll
+        for (int k = 0; k < KBV; ++k)
+            *reinterpret_cast<u32x4*>(&sB[0][((tid + k * kThreads) / 8) * kRowB + bcol]) = bv[k];
+    }
+    __syncthreads();
+    for (int q = 0; q < nq; ++q) {
+        if (q + 1 < nq) {
+            d0n = *reinterpret_cast<const u32x4*>(drow + a_off(q + 1, 0));
+            u0n = *reinterpret_cast<const u32x4*>(urow + a_off(q + 1, 0));
+            d1n = *reinterpret_cast<const u32x4*>(drow + a_off(q + 1, 1));
+            u1n = *reinterpret_cast<const u32x4*>(urow + a_off(q + 1, 1));
+            const int64_t t = tbeg + int64_t(q + 1) * kQ + bcol;
+#pragma unroll
+            for (int k = 0; k < KBV; ++k)
+                bv[k] = *reinterpret_cast<const u32x4*>(gB + int64_t((tid + k * kThreads) / 8) * p.L + (t < tend ? t : 0));
+        }
+        // dt2 and x = dt2*u of the lane's two 8-step groups; steps outside the piece
+        // are identity steps (dt2 = 0, x = 0)
+        float dt[2][8], x[2][8], tot[2];
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+            const int64_t t = tbeg + int64_t(q) * kQ + grp * 32 + 8 * g;
+            const bool in = dok && t < tend;
+            uint16_t dr[8], uu[8];
+            const u32x4 dv = grp == 0 ? d0 : d1, uv = grp == 0 ? u0 : u1;
+            __builtin_memcpy(dr, &dv, 16);
+            __builtin_memcpy(uu, &uv, 16);
+            tot[grp] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float r = IOT<uint16_t>::to_f32(dr[j]) + bias;
+                dt[grp][j] = in ? softplus_log2(r) : 0.0f;
+                x[grp][j] = dt[grp][j] * (in ? IOT<uint16_t>::to_f32(uu[j]) : 0.0f);
+                tot[grp] += dt[grp][j];
+            }
+        }
+        // the channel's 8 group totals in step order: groups 0..3 are the first groups
+        // of lanes g = 0..3, groups 4..7 their second
+        sTot[chl * 8 + g] = tot[0];
+        sTot[chl * 8 + 4 + g] = tot[1];
+        __builtin_amdgcn_wave_barrier();   // the wave's LDS writes complete before its reads
+        const f32x4 t03 = *reinterpret_cast<const f32x4*>(&sTot[chl * 8]);
+        const f32x4 t47 = *reinterpret_cast<const f32x4*>(&sTot[chl * 8 + 4]);
+        const float G[8] = {t03[0], t03[1], t03[2], t03[3], t47[0], t47[1], t47[2], t47[3]};
+        float after[8];   // after[k] = sum of the groups after group k
+        after[7] = 0.0f;
+#pragma unroll
+        for (int k = 6; k >= 0; --k) after[k] = after[k + 1] + G[k + 1];
+        const float schunk = after[0] + G[0];
+        // weights w_t = x_t * 2^(a_h * sum of dt2 after step t within the chunk)
+        bf16x8 ahi[2], alo[2];
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+            // after[grp*4 + g] without indexing by the lane's group (that would put
+            // the array in scratch memory)
+            const int k0 = grp * 4;
+            float suffix = g == 0 ? after[k0] : g == 1 ? after[k0 + 1] : g == 2 ? after[k0 + 2] : after[k0 + 3];
+            float w[8];
+#pragma unroll
+            for (int j = 7; j >= 0; --j) {
+                w[j] = x[grp][j] * __builtin_amdgcn_exp2f(a_h * suffix);
+                suffix += dt[grp][j];
+            }
+            split8(w, ahi[grp], alo[grp]);
+        }
+        // the chunk's decay of the rows this lane accumulates (channels 4g..4g+3)
+        if (g == 0) sDec[chl] = __builtin_amdgcn_exp2f(a_h * schunk);
+        __builtin_amdgcn_wave_barrier();
+        const f32x4 dec = *reinterpret_cast<const f32x4*>(&sDec[16 * wv + 4 * g]);
+        {
+            const float yk = schunk - scomp;
+            const float tk = ssum + yk;
+            scomp = (tk - ssum) - yk;
+            ssum = tk;
+        }
+        const uint16_t* bb = sB[q & 1] + (lane % 16) * kRowB + 8 * g;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            acc[j] *= dec;
+            const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bb + 16 * j * kRowB);
+            const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bb + 16 * j * kRowB + 32);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[0], b0, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[0], b0, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[1], b1, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[1], b1, acc[j], 0, 0, 0);
+        }
+        if (q + 1 < nq) {
+            uint16_t* sb = sB[(q + 1) & 1];
+#pragma unroll
+            for (int k = 0; k < KBV; ++k)
+                *reinterpret_cast<u32x4*>(&sb[((tid + k * kThreads) / 8) * kRowB + bcol]) = bv[k];
+            d0 = d0n;
+            u0 = u0n;
+            d1 = d1n;
+            u1 = u1n;
+        }
+        __syncthreads();
+    }
+
+    // H rows 16w+4g..+3 of column n = 16j + l%16, in the [n][64 channels] layout
+    float* hout = p.ws_H + (blk * p.nchunks + piece) * int64_t(N) * kLanes;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        *reinterpret_cast<f32x4*>(hout + int64_t(16 * j + lane % 16) * kLanes + 16 * wv + 4 * g) = acc[j] * kLn2;
+    if (g == 0) p.ws_S[(blk * p.nchunks + piece) * kLanes + chl] = ssum;
+}
+
 // Compose the pieces' affine maps in sequence order: one thread per (group, state, lane).
 //   Hin[0] = h0 (or 0);  Hin[c+1] = exp2(A * S2[c]) * Hin[c] + H[c]     (S2 = sum of dt2)
 __global__ void __launch_bounds__(256) scan_carry_kernel(Params p, int64_t total) {
@@ -903,9 +1115,24 @@ hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
     const size_t lds_agg = lds_floats_g(G, SPL, false) * sizeof(float);
     if (pl.nchunks > 1) {
         const int64_t groups = int64_t(p.batch) * p.nblk_d;
-        // pass 1 on every piece but the last
+        // pass 1 on every piece but the last: on the matrix cores when the decay is a
+        // scalar per head and the rows allow 16-byte loads, else by walking
         const dim3 grid1(unsigned(groups * (pl.nchunks - 1)));
-        hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kAggregate, VEC, G>), grid1, block, lds_agg, stream, p);
+        bool done = false;
+        if constexpr (SCALAR && VEC && std::is_same<IO, uint16_t>::value) {
+            if (p.np == p.N) {
+                const dim3 ablock(agg::kThreads);
+                done = true;
+                switch (p.N) {
+                    case 32: hipLaunchKernelGGL(scan_agg_mfma_kernel<32>, grid1, ablock, 0, stream, p); break;
+                    case 64: hipLaunchKernelGGL(scan_agg_mfma_kernel<64>, grid1, ablock, 0, stream, p); break;
+                    case 128: hipLaunchKernelGGL(scan_agg_mfma_kernel<128>, grid1, ablock, 0, stream, p); break;
+                    default: done = false;
+                }
+            }
+        }
+        if (!done)
+            hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kAggregate, VEC, G>), grid1, block, lds_agg, stream, p);
         const int64_t total = groups * p.np * kLanes;
         hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, p, total);
     }

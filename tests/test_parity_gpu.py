@@ -70,6 +70,10 @@ RAGGED = [
     (2, 777, 100, 16, "f32", 0, True, True, True, 5, 0),
     (1, 999, 64, 4, "bf16", 0, True, True, True, 31, 0),
     (1, 512, 64, 128, "bf16", 4, True, True, True, 3, 0),
+    # scalar decay, bf16, pieces: the pieces' end states on the matrix cores (32 and 64
+    # states; channels beyond dim in the last block; pieces not whole 64-step chunks)
+    (2, 1024, 64, 32, "bf16", 2, True, True, True, 5, 0),
+    (1, 640, 96, 64, "bf16", 3, False, True, True, 4, 0),
     (1, 300, 65, 16, "f32", 0, True, True, True, 7, 0),
     # forced states per lane
     (1, 80, 64, 16, "bf16", 0, True, True, True, 0, 1),
