@@ -78,6 +78,8 @@ struct BwdParams {
     int64_t L, dim, N, head_dim, chunk_len, ntiles_seq;
     int32_t nchunks, nblk_d, batch, np;
     int32_t piece_base;    // first piece index of the launch
+    int32_t mfma_agg;      // piece aggregates on the matrix cores (scalar decay, bf16
+                           // rows that allow 16-byte loads, 32/64/128 states)
     float* ck;             // [groups][ntiles_seq][np][64]   tile start states
     float* pBC;            // [nblk_d][batch][2][N][L]       per-block dB (unscaled), dC
     float* pA;             // [nchunks][batch][dim][np]      per-piece dA / ln 2
@@ -1583,11 +1585,43 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, bo
     const int64_t groups = pl.groups;
     if (pl.nch > 1) {
         const dim3 grid1(unsigned(groups * (pl.nch - 1)));
+        bool mfma_fwd = false, mfma_rev = false;
+        if (p.mfma_agg) {
+            ssm_detail::PieceStatesArgs a;
+            a.delta = p.delta;
+            a.A = p.A;
+            a.bias = p.bias;
+            a.L = p.L;
+            a.dim = p.dim;
+            a.nstate = p.N;
+            a.head_dim = p.head_dim;
+            a.chunk_len = p.chunk_len;
+            a.nchunks = p.nchunks;
+            a.nblk_d = p.nblk_d;
+            a.batch = p.batch;
+            if (!ext_ck) {
+                a.x = p.u;
+                a.z = nullptr;
+                a.BC = p.Bm;
+                a.piece_base = 0;
+                a.H = p.fH;
+                a.S = p.fS;
+                mfma_fwd = ssm_detail::launch_piece_states(a, false, pl.nch - 1, s);
+            }
+            a.x = p.dy;
+            a.z = p.z;
+            a.BC = p.Cm;
+            a.piece_base = 1;
+            a.H = p.rG;
+            a.S = p.rS;
+            mfma_rev = ssm_detail::launch_piece_states(a, true, pl.nch - 1, s);
+        }
         p.piece_base = 0;
-        if (!ext_ck)
+        if (!ext_ck && !mfma_fwd)
             hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kFwdAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
         p.piece_base = 1;
-        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kRevAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
+        if (!mfma_rev)
+            hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kRevAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
         p.piece_base = 0;
         const int64_t total = groups * p.np * kLanes;
         const dim3 gridc(unsigned(cdiv(total, 256)));
@@ -1767,6 +1801,13 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     p.batch = int32_t(dims->batch);
     p.np = pl.G * pl.spl;
     p.piece_base = 0;
+    {
+        auto a16 = [](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) % 16) == 0; };
+        const int64_t N = dims->dstate;
+        p.mfma_agg = dims->nheads > 0 && dims->io_dtype == SSM_BF16 && p.np == N &&
+                     (N == 32 || N == 64 || N == 128) && dims->seqlen % 8 == 0 && a16(u) && a16(delta) &&
+                     a16(z) && a16(dy) && a16(B) && a16(C);
+    }
     char* ws = static_cast<char*>(dims->workspace);
     auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
     p.ck = with_ckpt ? const_cast<float*>(ckpt) : at(pl.off_ck);   // read only when given

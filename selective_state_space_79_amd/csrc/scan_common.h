@@ -140,3 +140,30 @@ inline int validate_dims(const ssm_dims* d) {
 }
 
 }  // namespace
+
+// Piece end states on the matrix cores (scalar decay, bf16 rows that allow 16-byte
+// loads, nstate in {32, 64, 128}); defined in scan_fwd.hip, used by the forward's and
+// the backward's piece carries.
+//   forward (reverse = 0), pieces piece_base..:  H[d,n] = state after the piece from a
+//     zero start, S[d] = the piece's sum of dt2 (step sizes in log2 units);
+//   reverse (reverse = 1): H[d,n] = the gradient reaching the piece's first state from
+//     the piece alone, sum_t 2^(a_h * sum_{s<=t} dt2_s) * ds_t * C[n,t] with
+//     ds = dy * SiLU(z) (dy without z), and S[d] as above.
+// H and S in the carry layouts [groups][nchunks][nstate][64] and [groups][nchunks][64].
+namespace ssm_detail {
+struct PieceStatesArgs {
+    const void* x;        // forward: u; reverse: dy
+    const void* delta;
+    const void* z;        // reverse: gate input, nullable
+    const void* BC;       // forward: B; reverse: C
+    const float* A;       // (nheads,)
+    const float* bias;    // nullable
+    int64_t L, dim, nstate, head_dim, chunk_len;
+    int32_t nchunks, nblk_d, batch, piece_base;
+    float* H;
+    float* S;
+};
+// Launches one workgroup per (batch row, 64-channel block, piece) for npieces pieces
+// from piece_base; returns false (launching nothing) when nstate is not supported.
+bool launch_piece_states(const PieceStatesArgs& a, bool reverse, int64_t npieces, hipStream_t s);
+}  // namespace ssm_detail

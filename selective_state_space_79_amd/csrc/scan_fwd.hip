@@ -590,6 +590,9 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
 }
 
 // ------------------------------------------------------------------ pass 1 on the matrix cores
+// (Forward mode; the reverse mode, for the backward, is described with
+// launch_piece_states in scan_common.h: the same contraction with ds against C,
+// the chunks taken from the piece's end and prefix sums in place of suffix sums.)
 // With one decay rate a_h per head, the end state of a piece from zero is
 //   H[d,n] = ln2 * sum_t x[d,t] * 2^(a_h * sum_{s>t} dt2[d,s]) * B[n,t],   x = dt2 * u
 // (dt2 = dt / ln 2: step sizes in log2 units, as in the walk, which folds the ln 2
@@ -635,8 +638,8 @@ __device__ inline void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
 }
 }  // namespace agg
 
-template <int N>
-__global__ void __launch_bounds__(agg::kThreads) scan_agg_mfma_kernel(Params p) {
+template <int N, bool REV>
+__global__ void __launch_bounds__(agg::kThreads) scan_piece_states_kernel(ssm_detail::PieceStatesArgs p) {
     using namespace agg;
     constexpr int NT = N / 16;                    // 16-state column tiles
     constexpr int KBV = N * (kQ / 8) / kThreads;  // 16-byte B vectors per thread and chunk
@@ -650,7 +653,7 @@ __global__ void __launch_bounds__(agg::kThreads) scan_agg_mfma_kernel(Params p) 
     const int64_t bid = blockIdx.x;
     const int cblk = int(bid % p.nblk_d);
     const int b = int((bid / p.nblk_d) % p.batch);
-    const int piece = int(bid / (int64_t(p.nblk_d) * p.batch));
+    const int piece = int(bid / (int64_t(p.nblk_d) * p.batch)) + p.piece_base;
     const int64_t blk = int64_t(b) * p.nblk_d + cblk;
     const int64_t c0 = int64_t(cblk) * kLanes;
     const int64_t tbeg = int64_t(piece) * p.chunk_len;
@@ -664,15 +667,19 @@ __global__ void __launch_bounds__(agg::kThreads) scan_agg_mfma_kernel(Params p) 
     const float a_h = dok ? p.A[d / p.head_dim] : 0.0f;
     const float bias = (dok && p.bias) ? p.bias[d] : 0.0f;
     const int64_t row = (int64_t(b) * p.dim + (dok ? d : 0)) * p.L;
-    const uint16_t* __restrict__ urow = static_cast<const uint16_t*>(p.u) + row;
+    const uint16_t* __restrict__ urow = static_cast<const uint16_t*>(p.x) + row;   // u, or dy
     const uint16_t* __restrict__ drow = static_cast<const uint16_t*>(p.delta) + row;
-    // B side: vector v = tid + k*256 is row n = v/8, steps 8(v%8)..+7 of the chunk
-    const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.Bm) + int64_t(b) * N * p.L;
+    const bool has_z = REV && p.z != nullptr;
+    const uint16_t* __restrict__ zrow = static_cast<const uint16_t*>(has_z ? p.z : p.x) + row;
+    // B (or C) side: vector v = tid + k*256 is row n = v/8, steps 8(v%8)..+7 of the chunk
+    const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.BC) + int64_t(b) * N * p.L;
 
     // loads never branch: an 8-step group wholly outside the piece reads the row start
     // and is masked where it is used (pieces hold whole 8-step groups)
-    auto a_off = [&](int q, int grp) {
-        const int64_t t = tbeg + int64_t(q) * kQ + grp * 32 + 8 * g;
+    // chunk i of the loop: chunks in step order, or from the piece's end (reverse)
+    auto chunk_of = [&](int i) { return REV ? nq - 1 - i : i; };
+    auto a_off = [&](int i, int grp) {
+        const int64_t t = tbeg + int64_t(chunk_of(i)) * kQ + grp * 32 + 8 * g;
         return t < tend ? t : int64_t(0);
     };
     // (the prefetched 16-byte vectors are native vector types: with HIP's uint4, a
@@ -688,9 +695,14 @@ __global__ void __launch_bounds__(agg::kThreads) scan_agg_mfma_kernel(Params p) 
     u32x4 u0 = *reinterpret_cast<const u32x4*>(urow + a_off(0, 0));
     u32x4 d1 = *reinterpret_cast<const u32x4*>(drow + a_off(0, 1));
     u32x4 u1 = *reinterpret_cast<const u32x4*>(urow + a_off(0, 1));
+    u32x4 z0 = {0u, 0u, 0u, 0u}, z1 = z0, z0n = z0, z1n = z0;
+    if constexpr (REV) {
+        z0 = *reinterpret_cast<const u32x4*>(zrow + a_off(0, 0));
+        z1 = *reinterpret_cast<const u32x4*>(zrow + a_off(0, 1));
+    }
     u32x4 d0n, u0n, d1n, u1n, bv[KBV];
     {
-        const int64_t t = tbeg + bcol;
+        const int64_t t = tbeg + int64_t(chunk_of(0)) * kQ + bcol;
 #pragma unroll
         for (int k = 0; k < KBV; ++k)
             bv[k] = *reinterpret_cast<const u32x4*>(gB + int64_t((tid + k * kThreads) / 8) * p.L + (t < tend ? t : 0));
@@ -705,28 +717,38 @@ __global__ void __launch_bounds__(agg::kThreads) scan_agg_mfma_kernel(Params p) 
             u0n = *reinterpret_cast<const u32x4*>(urow + a_off(q + 1, 0));
             d1n = *reinterpret_cast<const u32x4*>(drow + a_off(q + 1, 1));
             u1n = *reinterpret_cast<const u32x4*>(urow + a_off(q + 1, 1));
-            const int64_t t = tbeg + int64_t(q + 1) * kQ + bcol;
+            if constexpr (REV) {
+                z0n = *reinterpret_cast<const u32x4*>(zrow + a_off(q + 1, 0));
+                z1n = *reinterpret_cast<const u32x4*>(zrow + a_off(q + 1, 1));
+            }
+            const int64_t t = tbeg + int64_t(chunk_of(q + 1)) * kQ + bcol;
 #pragma unroll
             for (int k = 0; k < KBV; ++k)
                 bv[k] = *reinterpret_cast<const u32x4*>(gB + int64_t((tid + k * kThreads) / 8) * p.L + (t < tend ? t : 0));
         }
-        // dt2 and x = dt2*u of the lane's two 8-step groups; steps outside the piece
-        // are identity steps (dt2 = 0, x = 0)
+        // dt2 and the weighted value (forward: x = dt2*u; reverse: ds = dy*SiLU(z)) of
+        // the lane's two 8-step groups; steps outside the piece are identity steps
+        // (dt2 = 0, value 0)
         float dt[2][8], x[2][8], tot[2];
 #pragma unroll
         for (int grp = 0; grp < 2; ++grp) {
-            const int64_t t = tbeg + int64_t(q) * kQ + grp * 32 + 8 * g;
+            const int64_t t = tbeg + int64_t(chunk_of(q)) * kQ + grp * 32 + 8 * g;
             const bool in = dok && t < tend;
-            uint16_t dr[8], uu[8];
-            const u32x4 dv = grp == 0 ? d0 : d1, uv = grp == 0 ? u0 : u1;
+            uint16_t dr[8], uu[8], zz[8];
+            const u32x4 dv = grp == 0 ? d0 : d1, uv = grp == 0 ? u0 : u1, zv = grp == 0 ? z0 : z1;
             __builtin_memcpy(dr, &dv, 16);
             __builtin_memcpy(uu, &uv, 16);
+            __builtin_memcpy(zz, &zv, 16);
             tot[grp] = 0.0f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float r = IOT<uint16_t>::to_f32(dr[j]) + bias;
                 dt[grp][j] = in ? softplus_log2(r) : 0.0f;
-                x[grp][j] = dt[grp][j] * (in ? IOT<uint16_t>::to_f32(uu[j]) : 0.0f);
+                const float v = in ? IOT<uint16_t>::to_f32(uu[j]) : 0.0f;
+                if constexpr (REV)
+                    x[grp][j] = has_z ? v * silu_f32(IOT<uint16_t>::to_f32(zz[j])) : v;
+                else
+                    x[grp][j] = dt[grp][j] * v;
                 tot[grp] += dt[grp][j];
             }
         }
@@ -738,24 +760,39 @@ __global__ void __launch_bounds__(agg::kThreads) scan_agg_mfma_kernel(Params p) 
         const f32x4 t03 = *reinterpret_cast<const f32x4*>(&sTot[chl * 8]);
         const f32x4 t47 = *reinterpret_cast<const f32x4*>(&sTot[chl * 8 + 4]);
         const float G[8] = {t03[0], t03[1], t03[2], t03[3], t47[0], t47[1], t47[2], t47[3]};
-        float after[8];   // after[k] = sum of the groups after group k
+        // forward: after[k] = sum of the groups after group k; reverse: before[k] =
+        // sum of the groups before group k
+        float after[8], before[8];
         after[7] = 0.0f;
+        before[0] = 0.0f;
 #pragma unroll
         for (int k = 6; k >= 0; --k) after[k] = after[k + 1] + G[k + 1];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) before[k] = before[k - 1] + G[k - 1];
         const float schunk = after[0] + G[0];
-        // weights w_t = x_t * 2^(a_h * sum of dt2 after step t within the chunk)
+        // weights: forward w_t = x_t * 2^(a_h * sum of dt2 after step t within the
+        // chunk); reverse w_t = ds_t * 2^(a_h * sum of dt2 up to and including step t)
         bf16x8 ahi[2], alo[2];
 #pragma unroll
         for (int grp = 0; grp < 2; ++grp) {
-            // after[grp*4 + g] without indexing by the lane's group (that would put
-            // the array in scratch memory)
+            // the group's base without indexing by the lane's group (that would put
+            // the arrays in scratch memory)
             const int k0 = grp * 4;
-            float suffix = g == 0 ? after[k0] : g == 1 ? after[k0 + 1] : g == 2 ? after[k0 + 2] : after[k0 + 3];
+            const float (&base)[8] = REV ? before : after;
+            float part = g == 0 ? base[k0] : g == 1 ? base[k0 + 1] : g == 2 ? base[k0 + 2] : base[k0 + 3];
             float w[8];
+            if constexpr (REV) {
 #pragma unroll
-            for (int j = 7; j >= 0; --j) {
-                w[j] = x[grp][j] * __builtin_amdgcn_exp2f(a_h * suffix);
-                suffix += dt[grp][j];
+                for (int j = 0; j < 8; ++j) {
+                    part += dt[grp][j];
+                    w[j] = x[grp][j] * __builtin_amdgcn_exp2f(a_h * part);
+                }
+            } else {
+#pragma unroll
+                for (int j = 7; j >= 0; --j) {
+                    w[j] = x[grp][j] * __builtin_amdgcn_exp2f(a_h * part);
+                    part += dt[grp][j];
+                }
             }
             split8(w, ahi[grp], alo[grp]);
         }
@@ -789,16 +826,20 @@ __global__ void __launch_bounds__(agg::kThreads) scan_agg_mfma_kernel(Params p) 
             u0 = u0n;
             d1 = d1n;
             u1 = u1n;
+            z0 = z0n;
+            z1 = z1n;
         }
         __syncthreads();
     }
 
     // H rows 16w+4g..+3 of column n = 16j + l%16, in the [n][64 channels] layout
-    float* hout = p.ws_H + (blk * p.nchunks + piece) * int64_t(N) * kLanes;
+    // (the forward's B carries the ln 2 of the log2 step sizes; the reverse's C none)
+    float* hout = p.H + (blk * p.nchunks + piece) * int64_t(N) * kLanes;
+    const float scale = REV ? 1.0f : kLn2;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-        *reinterpret_cast<f32x4*>(hout + int64_t(16 * j + lane % 16) * kLanes + 16 * wv + 4 * g) = acc[j] * kLn2;
-    if (g == 0) p.ws_S[(blk * p.nchunks + piece) * kLanes + chl] = ssum;
+        *reinterpret_cast<f32x4*>(hout + int64_t(16 * j + lane % 16) * kLanes + 16 * wv + 4 * g) = acc[j] * scale;
+    if (g == 0) p.S[(blk * p.nchunks + piece) * kLanes + chl] = ssum;
 }
 
 // Compose the pieces' affine maps in sequence order: one thread per (group, state, lane).
@@ -1121,14 +1162,25 @@ hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
         bool done = false;
         if constexpr (SCALAR && VEC && std::is_same<IO, uint16_t>::value) {
             if (p.np == p.N) {
-                const dim3 ablock(agg::kThreads);
-                done = true;
-                switch (p.N) {
-                    case 32: hipLaunchKernelGGL(scan_agg_mfma_kernel<32>, grid1, ablock, 0, stream, p); break;
-                    case 64: hipLaunchKernelGGL(scan_agg_mfma_kernel<64>, grid1, ablock, 0, stream, p); break;
-                    case 128: hipLaunchKernelGGL(scan_agg_mfma_kernel<128>, grid1, ablock, 0, stream, p); break;
-                    default: done = false;
-                }
+                ssm_detail::PieceStatesArgs a;
+                a.x = p.u;
+                a.delta = p.delta;
+                a.z = nullptr;
+                a.BC = p.Bm;
+                a.A = p.A;
+                a.bias = p.bias;
+                a.L = p.L;
+                a.dim = p.dim;
+                a.nstate = p.N;
+                a.head_dim = p.head_dim;
+                a.chunk_len = p.chunk_len;
+                a.nchunks = p.nchunks;
+                a.nblk_d = p.nblk_d;
+                a.batch = p.batch;
+                a.piece_base = 0;
+                a.H = p.ws_H;
+                a.S = p.ws_S;
+                done = ssm_detail::launch_piece_states(a, false, pl.nchunks - 1, stream);
             }
         }
         if (!done)
@@ -1506,3 +1558,25 @@ int ssm_selective_scan_step_conv(const void* x, const ssm_conv* conv, void* conv
 }
 
 }  // extern "C"
+
+namespace ssm_detail {
+
+bool launch_piece_states(const PieceStatesArgs& a, bool reverse, int64_t npieces, hipStream_t s) {
+    const dim3 grid(unsigned(int64_t(a.batch) * a.nblk_d * npieces)), block(agg::kThreads);
+#define SSM_PIECE_CASE(N_)                                                                              \
+    case N_:                                                                                            \
+        if (reverse)                                                                                    \
+            hipLaunchKernelGGL((scan_piece_states_kernel<N_, true>), grid, block, 0, s, a);             \
+        else                                                                                            \
+            hipLaunchKernelGGL((scan_piece_states_kernel<N_, false>), grid, block, 0, s, a);            \
+        return true;
+    switch (a.nstate) {
+        SSM_PIECE_CASE(32)
+        SSM_PIECE_CASE(64)
+        SSM_PIECE_CASE(128)
+        default: return false;
+    }
+#undef SSM_PIECE_CASE
+}
+
+}  // namespace ssm_detail

@@ -65,6 +65,10 @@ CASES = [
     (2, 1000, 64, 16, "bf16", 0, False, True, True, 5, 0),
     (1, 999, 65, 4, "bf16", 0, True, False, False, 31, 0),
     (1, 512, 64, 128, "bf16", 8, True, True, True, 3, 0),
+    # scalar decay, bf16, pieces: the pieces' aggregates on the matrix cores (32 and 64
+    # states; without the gate; channels beyond dim in the last block)
+    (2, 1024, 64, 32, "bf16", 2, True, True, True, 5, 0),
+    (1, 640, 96, 64, "bf16", 3, False, False, True, 4, 0),
     # forced states per lane
     (1, 80, 64, 4, "f32", 0, True, False, False, 0, 1),
     (1, 80, 64, 16, "f32", 0, True, False, False, 0, 4),
