@@ -113,7 +113,10 @@ def test_plans_of_the_five_workloads(index):
     if index == 3:
         assert plan["nchunks"] == 1 and plan["workspace_bytes"] == 0
     if index == 5:
-        assert plan["nchunks"] == 2       # 128 channel blocks would leave half of the 256 CUs idle
+        # 128 channel blocks would leave half of the 256 CUs idle; with the first pass on
+        # the matrix cores (scalar decay, bf16, 128 states) pieces are cheap and the plan
+        # aims at two workgroups per CU
+        assert plan["nchunks"] == 4
 
 
 def test_forced_options_show_in_plan():
