@@ -832,32 +832,46 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- gradient pass with
-// separate roles (16 state entries per channel).  Four walking waves (wave w holds
-// entries 4w..4w+3 of all 64 channels) walk tile k while four helper waves finish
-// tile k-1 and stage tile k+1, so the staging and finishing work fills the issue slots
-// the walk leaves on each SIMD instead of running between barriers.  Tiles are
-// double-buffered in LDS and there is one barrier per tile.  A helper thread stages and
-// finishes the same elements (4 consecutive steps of one channel), so finishing tile
-// k-1 and then staging tile k+1 into the same buffer needs no barrier between them;
-// the per-element values finishing needs besides the walk's sums (u, sigmoid of the
-// step input, the gate's derivative) stay in the helper's registers, one set per
-// buffer.  The walk keeps the tile's recomputed states and decays in VGPRs, so the
-// reverse step does not evaluate the exponential again.
-namespace wsg {
-constexpr int SPL = 4, G = 4, H = 4, T = 16, NP = G * SPL, EPT = T / H, NTH = H * kLanes;
-constexpr int kW = T * kLanes * 4;        // (dt2, dt2*u, ds, scalar decay) per step and channel
-constexpr int kBC = T * NP * 2;           // (B*ln2, C) per step and entry
-constexpr int kSlab = G * T * kLanes;     // per-wave sums over the wave's entries, per step and channel
-constexpr int kDBC = 2 * NP * T;          // the tile's dB (unscaled), dC summed over the 64 channels
-constexpr int kBuf = kW + kBC + 3 * kSlab + kDBC;
-constexpr int kThreads = (G + H) * kLanes;
-constexpr size_t kLdsBytes = size_t(2 * kBuf) * sizeof(float);
-constexpr int KB = (2 * NP * T + NTH - 1) / NTH;   // B/C values per helper thread and tile
+// separate roles.  G walking waves (wave w holds entries SPL*w..SPL*w+SPL-1 of all 64
+// channels) walk tile k while four helper waves finish tile k-1 and stage tile k+1, so
+// the staging and finishing work fills the issue slots the walk leaves on each SIMD
+// instead of running between barriers.  Tiles are double-buffered in LDS and there is
+// one barrier per tile.  A helper thread stages and finishes the same elements (T/4
+// consecutive steps of one channel), so finishing tile k-1 and then staging tile k+1
+// into the same buffer needs no barrier between them; the per-element values finishing
+// needs besides the walk's sums (u, sigmoid of the step input, the gate's derivative)
+// stay in the helper's registers, one set per buffer.
+//   SPL = 4, G = 4, T = 16 (9..16 state entries): the walk keeps the tile's recomputed
+//     states and decays in VGPRs, so the reverse step evaluates no second exponential;
+//   SPL = 16, G = 8, T = 8 (65..128 entries, scalar decay): the entries are walked in
+//     groups of 4 as in the generic kernel's grouped walk, the per-step sums over
+//     entries accumulated in the wave's slab rows.
+template <int SPL_, int G_, int T_> struct WsShape {
+    static constexpr int SPL = SPL_, G = G_, H = 4, T = T_, NP = G * SPL, EPT = T / H, NTH = H * kLanes;
+    static constexpr int kW = T * kLanes * 4;        // (dt2, dt2*u, ds, scalar decay) per step and channel
+    static constexpr int kBC = T * NP * 2;           // (B*ln2, C) per step and entry
+    static constexpr int kSlab = G * T * kLanes;     // per-wave sums over the wave's entries, per step and channel
+    static constexpr int kDBC = 2 * NP * T;          // the tile's dB (unscaled), dC summed over the 64 channels
+    static constexpr int kBuf = kW + kBC + 3 * kSlab + kDBC;
+    static constexpr int kThreads = (G + H) * kLanes;
+    static constexpr size_t kLdsBytes = size_t(2 * kBuf) * sizeof(float);
+    static constexpr int KB = (2 * NP * T + NTH - 1) / NTH;   // B/C values per helper thread and tile
+};
+namespace wsg {   // 9..16 entries
+constexpr int SPL = 4, G = 4, T = 16, NP = G * SPL, EPT = T / 4;
+using Shape = WsShape<SPL, G, T>;
 }  // namespace wsg
+namespace wsw {   // 65..128 entries, scalar decay
+using Shape = WsShape<16, 8, 8>;
+}  // namespace wsw
 
-template <typename IO, bool SCALAR, bool VEC>
-__global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdParams p) {
-    using namespace wsg;
+template <typename IO, bool SCALAR, bool VEC, int SPL_, int G_, int T_>
+__global__ void __launch_bounds__((WsShape<SPL_, G_, T_>::kThreads)) scan_bwd_grad_ws_kernel(BwdParams p) {
+    using S = WsShape<SPL_, G_, T_>;
+    constexpr int SPL = S::SPL, G = S::G, H = S::H, T = S::T, NP = S::NP, EPT = S::EPT, NTH = S::NTH;
+    constexpr int kW = S::kW, kBC = S::kBC, kSlab = S::kSlab, kBuf = S::kBuf, KB = S::KB;
+    constexpr bool kGrouped = SPL > 4;            // entries walked in groups of 4
+    static_assert(SPL == 4 || (SPL % 4 == 0 && SCALAR), "wide lanes are built for scalar decay only");
     static_assert(KB * NTH == 2 * NP * T, "the tile's B and C values must split evenly over the helpers");
     extern __shared__ float smem[];
     const int tid = threadIdx.x;
@@ -945,7 +959,7 @@ __global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdPara
     };
     auto p32 = [](unsigned x, unsigned y) { return __builtin_amdgcn_permlane32_swap(x, y, false, false); };
     auto p16 = [](unsigned x, unsigned y) { return __builtin_amdgcn_permlane16_swap(x, y, false, false); };
-    auto reduce8 = [&](const float (&pv)[kRound], float* sdBC, int t) {
+    auto reduce8 = [&](const float (&pv)[kRound], float* sdBC, int t, int j0) {
         const float r0 = swap_add(pv[0], pv[1], p32), r1 = swap_add(pv[2], pv[3], p32);
         const float r2 = swap_add(pv[4], pv[5], p32), r3 = swap_add(pv[6], pv[7], p32);
         const float s0 = swap_add(r0, r1, p16), s1 = swap_add(r2, r3, p16);
@@ -953,7 +967,7 @@ __global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdPara
         sum += dpp_move<0xB1>(sum);    // quad_perm [1,0,3,2]
         sum += dpp_move<0x4E>(sum);    // quad_perm [2,3,0,1]
         sum += dpp_move<0x141>(sum);   // row_half_mirror
-        if ((lane & 7) == 0) sdBC[((red_v / SPL) * NP + wv * SPL + (red_v % SPL)) * T + t] = sum;
+        if ((lane & 7) == 0) sdBC[((red_v / 4) * NP + wv * SPL + j0 + (red_v % 4)) * T + t] = sum;
     };
 
     auto walk = [&](float* bf) {
@@ -1004,8 +1018,101 @@ __global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdPara
             }
             sP[kSlab + (wv * T + t) * kLanes + lane] = s1;
             sP[2 * kSlab + (wv * T + t) * kLanes + lane] = s2;
-            reduce8(pv, sdBC, t);
+            reduce8(pv, sdBC, t, 0);
             cur = nxt;
+        }
+    };
+
+    // entries in groups of 4 (wide lanes, scalar decay): each group recomputes the
+    // tile's states from the checkpoint and walks back through them; the group always
+    // works on entries 0..3 of the per-entry arrays, which rotate by 4 after each group
+    // (the group loop is not unrolled); the per-step sums accumulate in the wave's slab
+    // rows; the decay is every entry's, so one running sum of g * a * h_prev per step
+    // gives both the dA term (kept in entry 0 of each group) and the sum of A g a h.
+    struct GOps {
+        float4 W, bc0, bc1;
+    };
+    auto gread = [&](const float* bf, int off, int t, int j0, GOps& o) {
+        o.W = reinterpret_cast<const float4*>(bf)[off + t * kLanes + lane];
+        const float4* q = reinterpret_cast<const float4*>(bf + off + kW + t * NP * 2 + (wv * SPL + j0) * 2);
+        o.bc0 = q[0];
+        o.bc1 = q[1];
+    };
+    auto gb = [](const GOps& o, int jj) { return jj == 0 ? o.bc0.x : jj == 1 ? o.bc0.z : jj == 2 ? o.bc1.x : o.bc1.z; };
+    auto gc = [](const GOps& o, int jj) { return jj == 0 ? o.bc0.y : jj == 1 ? o.bc0.w : jj == 2 ? o.bc1.y : o.bc1.w; };
+    auto rotate = [](float (&v)[SPL]) {
+        float first[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) first[k] = v[k];
+#pragma unroll
+        for (int k = 0; k + 4 < SPL; ++k) v[k] = v[k + 4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[SPL - 4 + k] = first[k];
+    };
+    auto walk_grouped = [&](float* bf) {
+        float* const yrow = bf + kW + kBC + (wv * T) * kLanes + lane;
+        float* sdBC = bf + kW + kBC + 3 * kSlab;
+#pragma unroll 1
+        for (int gi = 0; gi < SPL / 4; ++gi) {
+            const int j0 = gi * 4;
+            const bool first = gi == 0;
+            float Hg[T][4];
+            {
+                int off = 0;
+                asm volatile("" : "+v"(off));
+                float hh[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) hh[jj] = hst[jj];
+                GOps cur, nxt;
+                gread(bf, off, 0, j0, cur);
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    if (t + 1 < T) gread(bf, off, t + 1, j0, nxt);
+                    float yp = first ? 0.0f : yrow[t * kLanes];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        hh[jj] = fmaf(cur.W.w, hh[jj], cur.W.y * gb(cur, jj));
+                        Hg[t][jj] = hh[jj];
+                        yp = fmaf(gc(cur, jj), hh[jj], yp);
+                    }
+                    yrow[t * kLanes] = yp;
+                    cur = nxt;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            int off = 0;
+            asm volatile("" : "+v"(off));
+            float pv[kRound];
+            GOps cur, nxt;
+            gread(bf, off, T - 1, j0, cur);
+#pragma unroll
+            for (int t = T - 1; t >= 0; --t) {
+                if (t > 0) gread(bf, off, t - 1, j0, nxt);
+                float s1 = first ? 0.0f : yrow[kSlab + t * kLanes];
+                float s2 = first ? 0.0f : yrow[2 * kSlab + t * kLanes];
+                float t1s = 0.0f;
+                const float a = cur.W.w;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float hp = t > 0 ? Hg[t > 0 ? t - 1 : 0][jj] : hst[jj];
+                    const float g = fmaf(cur.W.z, gc(cur, jj), e[jj]);
+                    t1s = fmaf(g, a * hp, t1s);
+                    s2 = fmaf(g, gb(cur, jj), s2);
+                    e[jj] = a * g;
+                    pv[jj] = g * cur.W.y;              // dB (unscaled)
+                    pv[4 + jj] = cur.W.z * Hg[t][jj];  // dC
+                }
+                dAacc[0] = fmaf(cur.W.x, t1s, dAacc[0]);
+                s1 = fmaf(Ar[0], t1s, s1);
+                yrow[kSlab + t * kLanes] = s1;
+                yrow[2 * kSlab + t * kLanes] = s2;
+                reduce8(pv, sdBC, t, j0);
+                cur = nxt;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            rotate(e);
+            rotate(dAacc);
+            rotate(hst);
         }
     };
 
@@ -1162,7 +1269,8 @@ __global__ void __launch_bounds__(wsg::kThreads) scan_bwd_grad_ws_kernel(BwdPara
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) hst[j] = ck_ok[j] ? ckn[j] : 0.0f;
                 if (i + 1 < ntiles) load_ck(kt_of(i + 1));
-                walk(buf(i & 1));
+                if constexpr (kGrouped) walk_grouped(buf(i & 1));
+                else walk(buf(i & 1));
             }
             __syncthreads();
         }
@@ -1480,7 +1588,8 @@ __global__ void __launch_bounds__(256) bwd_reduce_heads_kernel(BwdParams p, floa
 // ------------------------------------------------------------------ host side
 struct BwdPlan {
     int spl, G, nch, T;
-    bool ws;    // gradient pass with separate walking and helper waves (16 state entries)
+    bool ws;       // gradient pass with separate walking and helper waves (9..16 entries)
+    bool ws_wide;  // the same for 65..128 entries with scalar decay
     int64_t chunk_len, nblk_d, groups, ntiles_seq;
     size_t off_ck, off_bc, off_a, off_d, off_bias, off_fh, off_fs, off_fhin, off_rg, off_rs, off_rein, ws_bytes;
     size_t lds_grad, lds_fwd;
@@ -1571,7 +1680,10 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
     pl->ws_bytes = off;
     static_assert(wsg::T == bwd_tile(wsg::NP), "both gradient kernels read the same checkpoints");
     pl->ws = ws;
-    pl->lds_grad = pl->ws ? wsg::kLdsBytes : bwd_lds_floats(pl->G, spl, kGrad) * f;
+    pl->ws_wide = spl == 16 && pl->G == 8 && d->nheads > 0;
+    static_assert(wsw::Shape::T == bwd_tile(wsw::Shape::NP), "both gradient kernels read the same checkpoints");
+    pl->lds_grad = pl->ws ? wsg::Shape::kLdsBytes
+                          : pl->ws_wide ? wsw::Shape::kLdsBytes : bwd_lds_floats(pl->G, spl, kGrad) * f;
     pl->lds_fwd = bwd_lds_floats(pl->G, spl, kCkpt) * f;
     return SSM_OK;
 }
@@ -1641,10 +1753,17 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, bo
         hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt, VEC>), grid, block, pl.lds_fwd, s, p);
     }
     if constexpr (SPL == wsg::NP / G && G == 8) {
+        const dim3 blk_ws(static_cast<unsigned>(wsg::Shape::kThreads), 1, 1);
         if (vec_g)
-            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, true>), grid, dim3(wsg::kThreads), pl.lds_grad, s, p);
+            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, true, 4, 4, 16>), grid, blk_ws, pl.lds_grad, s, p);
         else
-            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, false>), grid, dim3(wsg::kThreads), pl.lds_grad, s, p);
+            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, false, 4, 4, 16>), grid, blk_ws, pl.lds_grad, s, p);
+    } else if constexpr (SPL == 16 && G == 8 && SCALAR) {
+        const dim3 blk_ws(static_cast<unsigned>(wsw::Shape::kThreads), 1, 1);
+        if (vec_g)
+            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, true, 16, 8, 8>), grid, blk_ws, pl.lds_grad, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, false, 16, 8, 8>), grid, blk_ws, pl.lds_grad, s, p);
     } else {
         hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kGrad, VEC>), grid, block, pl.lds_grad, s, p);
     }
@@ -1771,7 +1890,7 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
                aligned(grads->du) && aligned(grads->ddelta) && aligned(dz);
     };
     const bool vec = rows_allow(pl.T / pl.G);
-    const bool vec_g = pl.ws ? rows_allow(wsg::EPT) : vec;
+    const bool vec_g = pl.ws ? rows_allow(wsg::EPT) : pl.ws_wide ? rows_allow(wsw::Shape::EPT) : vec;
     const bool vec_c = pl.ws ? rows_allow(wsc::EPT) : vec;
 
     BwdParams p;

@@ -69,6 +69,10 @@ CASES = [
     # states; without the gate; channels beyond dim in the last block)
     (2, 1024, 64, 32, "bf16", 2, True, True, True, 5, 0),
     (1, 640, 96, 64, "bf16", 3, False, False, True, 4, 0),
+    # 65..128 entries with scalar decay: role-split gradient pass, entries in groups of 4
+    # (padding entries inside the last groups with N = 100; float32 rows)
+    (1, 136, 64, 100, "f32", 2, True, True, True, 0, 0),
+    (2, 264, 130, 128, "bf16", 2, True, True, True, 0, 0),
     # forced states per lane
     (1, 80, 64, 4, "f32", 0, True, False, False, 0, 1),
     (1, 80, 64, 16, "f32", 0, True, False, False, 0, 4),
