@@ -1334,20 +1334,33 @@ __global__ void __launch_bounds__((WsShape<SPL_, G_, T_>::kThreads)) scan_bwd_gr
 // lane) walk 32-step tiles forward and write the state at the start of every 16-step
 // tile of the gradient pass, while four helper waves stage the next tile's step sizes,
 // weighted inputs and B.  Tiles are double-buffered in LDS, one barrier per tile.
+// Shapes: SPL = 4, G = 4 (9..16 entries, checkpoints every 16 steps) and SPL = 16,
+// G = 8 (65..128 entries with scalar decay, every 8 steps); 32-step tiles.
+template <int SPL_, int G_, int TC_> struct WscShape {
+    static constexpr int SPL = SPL_, G = G_, H = 4, T = 32, TC = TC_, NP = G * SPL, EPT = T / H, NTH = H * kLanes;
+    static constexpr int kRowB = NP + 4;       // B row stride (floats): 16-byte aligned, few bank conflicts
+    static constexpr int kX = T * kLanes * 2;  // (dt2 or the scalar decay, dt2*u) per step and channel
+    static constexpr int kB = T * kRowB;       // B*ln2 per step and entry
+    static constexpr int kBuf = kX + kB;
+    static constexpr int kThreads = (G + H) * kLanes;
+    static constexpr size_t kLdsBytes = size_t(2 * kBuf) * sizeof(float);
+    static constexpr int KB = (T * NP + NTH - 1) / NTH;
+};
 namespace wsc {
-constexpr int SPL = 4, G = 4, H = 4, T = 32, TC = 16, NP = G * SPL, EPT = T / H, NTH = H * kLanes;
-constexpr int kRowB = 20;                  // B row stride (floats): 16-byte aligned, few bank conflicts
-constexpr int kX = T * kLanes * 2;         // (dt2 or the scalar decay, dt2*u) per step and channel
-constexpr int kB = T * kRowB;              // B*ln2 per step and entry
-constexpr int kBuf = kX + kB;
-constexpr int kThreads = (G + H) * kLanes;
-constexpr size_t kLdsBytes = size_t(2 * kBuf) * sizeof(float);
-constexpr int KB = (T * NP + NTH - 1) / NTH;
+using Shape = WscShape<4, 4, 16>;
+constexpr int EPT = Shape::EPT, NP = Shape::NP;
 }  // namespace wsc
+namespace wscw {
+using Shape = WscShape<16, 8, 8>;
+}  // namespace wscw
 
-template <typename IO, bool SCALAR, bool VEC>
-__global__ void __launch_bounds__(wsc::kThreads) scan_bwd_ckpt_ws_kernel(BwdParams p) {
-    using namespace wsc;
+template <typename IO, bool SCALAR, bool VEC, int SPL_, int G_, int TC_>
+__global__ void __launch_bounds__((WscShape<SPL_, G_, TC_>::kThreads)) scan_bwd_ckpt_ws_kernel(BwdParams p) {
+    using S = WscShape<SPL_, G_, TC_>;
+    constexpr int SPL = S::SPL, G = S::G, H = S::H, T = S::T, TC = S::TC, NP = S::NP, EPT = S::EPT, NTH = S::NTH;
+    constexpr int kRowB = S::kRowB, kX = S::kX, kBuf = S::kBuf, KB = S::KB;
+    constexpr int NQ = SPL / 4;   // float4 B reads per step
+    static_assert(SPL % 4 == 0, "B is read 4 entries at a time");
     static_assert(KB * NTH == T * NP, "the tile's B values must split evenly over the helpers");
     static_assert(T % TC == 0, "checkpoint tiles must nest in walk tiles");
     extern __shared__ float smem[];
@@ -1398,7 +1411,9 @@ __global__ void __launch_bounds__(wsc::kThreads) scan_bwd_ckpt_ws_kernel(BwdPara
             const float4* sb4 = reinterpret_cast<const float4*>(bf + kX + wv * SPL);
             const int64_t t0 = tbeg + int64_t(i) * T;
             float2 xc = sx[0], xn;
-            float4 bc = sb4[0], bn;
+            float4 bc[NQ], bn[NQ];
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) bc[k] = sb4[k];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 if (t % TC == 0 && t0 + t < tend) {
@@ -1408,16 +1423,19 @@ __global__ void __launch_bounds__(wsc::kThreads) scan_bwd_ckpt_ws_kernel(BwdPara
                 }
                 if (t + 1 < T) {
                     xn = sx[(t + 1) * kLanes];
-                    bn = sb4[(t + 1) * (kRowB / 4)];
+#pragma unroll
+                    for (int k = 0; k < NQ; ++k) bn[k] = sb4[(t + 1) * (kRowB / 4) + k];
                 }
-                const float bv[SPL] = {bc.x, bc.y, bc.z, bc.w};
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) {
+                    const float4 q = bc[j / 4];
+                    const float bj = (j % 4 == 0) ? q.x : (j % 4 == 1) ? q.y : (j % 4 == 2) ? q.z : q.w;
                     const float a = SCALAR ? xc.x : __builtin_amdgcn_exp2f(xc.x * Ar[j]);
-                    h[j] = fmaf(a, h[j], xc.y * bv[j]);
+                    h[j] = fmaf(a, h[j], xc.y * bj);
                 }
                 xc = xn;
-                bc = bn;
+#pragma unroll
+                for (int k = 0; k < NQ; ++k) bc[k] = bn[k];
             }
             __syncthreads();
         }
@@ -1745,10 +1763,17 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, bo
     if (ext_ck) {
         // nothing to recompute
     } else if constexpr (SPL == wsc::NP / G && G == 8) {
+        const dim3 blk_c(static_cast<unsigned>(wsc::Shape::kThreads), 1, 1);
         if (vec_c)
-            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true>), grid, dim3(wsc::kThreads), wsc::kLdsBytes, s, p);
+            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true, 4, 4, 16>), grid, blk_c, wsc::Shape::kLdsBytes, s, p);
         else
-            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, false>), grid, dim3(wsc::kThreads), wsc::kLdsBytes, s, p);
+            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, false, 4, 4, 16>), grid, blk_c, wsc::Shape::kLdsBytes, s, p);
+    } else if constexpr (SPL == 16 && G == 8 && SCALAR) {
+        const dim3 blk_c(static_cast<unsigned>(wscw::Shape::kThreads), 1, 1);
+        if (vec_c)
+            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true, 16, 8, 8>), grid, blk_c, wscw::Shape::kLdsBytes, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, false, 16, 8, 8>), grid, blk_c, wscw::Shape::kLdsBytes, s, p);
     } else {
         hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt, VEC>), grid, block, pl.lds_fwd, s, p);
     }
@@ -1891,7 +1916,7 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     };
     const bool vec = rows_allow(pl.T / pl.G);
     const bool vec_g = pl.ws ? rows_allow(wsg::EPT) : pl.ws_wide ? rows_allow(wsw::Shape::EPT) : vec;
-    const bool vec_c = pl.ws ? rows_allow(wsc::EPT) : vec;
+    const bool vec_c = pl.ws ? rows_allow(wsc::EPT) : pl.ws_wide ? rows_allow(wscw::Shape::EPT) : vec;
 
     BwdParams p;
     p.u = u;
