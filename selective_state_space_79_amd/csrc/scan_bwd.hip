@@ -56,8 +56,6 @@ namespace {
 // state entries per channel (the per-wave partial slabs must fit the LDS)
 inline constexpr int bwd_tile(int np) { return np <= 64 ? 16 : 8; }
 constexpr int kRound = 8;    // values per cross-lane reduction round
-constexpr int kQB = 2;       // steps per scheduling group in the gradient walk: keeps the
-                             // compiler from hoisting a whole tile's LDS operands at once
 
 struct BwdParams {
     const void* u;
@@ -1357,7 +1355,7 @@ using Shape = WscShape<16, 8, 8>;
 template <typename IO, bool SCALAR, bool VEC, int SPL_, int G_, int TC_>
 __global__ void __launch_bounds__((WscShape<SPL_, G_, TC_>::kThreads)) scan_bwd_ckpt_ws_kernel(BwdParams p) {
     using S = WscShape<SPL_, G_, TC_>;
-    constexpr int SPL = S::SPL, G = S::G, H = S::H, T = S::T, TC = S::TC, NP = S::NP, EPT = S::EPT, NTH = S::NTH;
+    constexpr int SPL = S::SPL, G = S::G, T = S::T, TC = S::TC, NP = S::NP, EPT = S::EPT, NTH = S::NTH;
     constexpr int kRowB = S::kRowB, kX = S::kX, kBuf = S::kBuf, KB = S::KB;
     constexpr int NQ = SPL / 4;   // float4 B reads per step
     static_assert(SPL % 4 == 0, "B is read 4 entries at a time");
