@@ -189,9 +189,12 @@ __device__ inline void store_seg(IO* __restrict__ row, int64_t t, int64_t tend, 
     }
 }
 
+// A lane permutation inside each 16-lane row (quad swaps, half-row mirror, rotation),
+// so no lane reads outside its row; written as an update with zero fill so that the
+// compiler folds it into the add that consumes it (v_add_f32_dpp).
 template <int CTRL>
 __device__ inline float dpp_move(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 template <typename IO, int SPL, int G, bool SCALAR, int MODE, bool VEC>
