@@ -53,7 +53,7 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(launch_units: float):
+def measured_traffic():
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
     try:
@@ -600,7 +600,7 @@ def main():
     kernel_ms = ms_events
     gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     tops = OPS_PER_UPDATE * updates / (kernel_ms * 1e-3) / 1e12
-    traffic = measured_traffic(1.0) if (args.workload == 3 and plan["nchunks"] == 1) else None
+    traffic = measured_traffic() if (args.workload == 3 and plan["nchunks"] == 1) else None
     alu = {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TFLOP/s",
            "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
            "note": "FLOP = one fp32 VALU lane operation; 5 per state update (mul, exp2, mul, fma, fma); peak = "
