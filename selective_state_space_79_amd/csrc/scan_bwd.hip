@@ -1659,6 +1659,14 @@ int make_bwd_plan(const ssm_dims* d, BwdPlan* pl) {
         else
             nch = waves < 2048 ? cdiv(2048, waves) : 1;
         const int64_t max_pieces = pl->ntiles_seq / 8 > 1 ? pl->ntiles_seq / 8 : 1;
+        // then the piece count, up to twice that, that leaves no part-filled last round
+        // of gradient-pass workgroups
+        const bool wide = spl == 16 && pl->G == 8 && d->nheads > 0;
+        const size_t lds = ws ? wsg::Shape::kLdsBytes
+                              : wide ? wsw::Shape::kLdsBytes : bwd_lds_floats(pl->G, spl, kGrad) * sizeof(float);
+        const int64_t per_cu = int64_t(163840 / lds);
+        const int64_t cap = max_pieces < SSM_MAX_CHUNKS ? max_pieces : SSM_MAX_CHUNKS;
+        nch = round_friendly_pieces(pl->groups, nch, cap, 256 * (per_cu > 1 ? per_cu : 1));
         if (nch > max_pieces) nch = max_pieces;
         if (nch > SSM_MAX_CHUNKS) nch = SSM_MAX_CHUNKS;
     }

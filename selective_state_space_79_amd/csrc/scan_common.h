@@ -112,6 +112,24 @@ __device__ inline float silu_grad_f32(float v) {
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Piece count for a launch of `groups` x n equal workgroups of which `slots` run at
+// once: such a launch takes ceil(groups*n/slots) rounds of L/n steps, so the cost is
+// proportional to ceil(groups*n/slots)/n.  Returns the cheapest n in [want, 2*want]
+// (at most `cap`, at least `want`), the smallest on ties; want <= 1 is returned as is.
+inline int64_t round_friendly_pieces(int64_t groups, int64_t want, int64_t cap, int64_t slots) {
+    if (want <= 1 || groups <= 0 || slots <= 0) return want;
+    int64_t best = want, best_rounds = cdiv(groups * want, slots);
+    const int64_t hi = (2 * want < cap) ? 2 * want : cap;
+    for (int64_t n = want + 1; n <= hi; ++n) {
+        const int64_t rounds = cdiv(groups * n, slots);
+        if (rounds * best < best_rounds * n) {   // rounds/n < best_rounds/best
+            best = n;
+            best_rounds = rounds;
+        }
+    }
+    return best;
+}
+
 inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     if (!a || !b) return false;
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);

@@ -1133,6 +1133,12 @@ int make_plan(const ssm_dims* d, Plan* pl) {
                                   (N == 32 || N == 64 || N == 128) && d->seqlen % 8 == 0;
         if (cheap_pieces && groups < 2 * cus && cdiv(2 * cus, groups) > nch) nch = cdiv(2 * cus, groups);
         const int64_t max_pieces = tiles / 8 > 1 ? tiles / 8 : 1;   // keep >= 8 tiles per piece
+        // then the piece count, up to twice that, that leaves no part-filled last round
+        // of workgroups (long sequence, 32 groups of 64 channels: 12 pieces 2.60 ms, 16
+        // pieces 1.97 ms, 20 pieces 2.33 ms)
+        const int64_t per_cu = int64_t(163840 / lds_floats_g(pl->G, spl, true) / sizeof(float));
+        const int64_t cap = max_pieces < SSM_MAX_CHUNKS ? max_pieces : SSM_MAX_CHUNKS;
+        nch = round_friendly_pieces(groups, nch, cap, cus * (per_cu > 1 ? per_cu : 1));
         if (nch > max_pieces) nch = max_pieces;
         if (nch > SSM_MAX_CHUNKS) nch = SSM_MAX_CHUNKS;
     }

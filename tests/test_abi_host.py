@@ -119,6 +119,29 @@ def test_plans_of_the_five_workloads(index):
         assert plan["nchunks"] == 4
 
 
+@pytest.mark.parametrize("shape, fwd_pieces, bwd_pieces", [
+    ((1, 65536, 3072, 16), 16, 32),    # 48 channel blocks
+    ((2, 16384, 2560, 16), 9, 16),     # 80 channel blocks
+    ((3, 8192, 1024, 16), 16, 32),     # 48 channel blocks
+    ((1, 131072, 2048, 16), 16, 32),   # 32 channel blocks: already whole rounds
+])
+def test_piece_counts_fill_whole_rounds_of_workgroups(shape, fwd_pieces, bwd_pieces):
+    """With one workgroup per CU (their LDS tiles take most of its 160 KB), a launch of
+    blocks x pieces workgroups runs in ceil(blocks * pieces / 256) rounds of L / pieces
+    steps; the planners take, from their first choice up to twice it, the piece count
+    with the least of that time (48 blocks: 11 pieces make 3 rounds of L/11 where 16
+    make 3 rounds of L/16)."""
+    dims = ssm.make_dims(*shape)
+    blocks = shape[0] * -(-shape[2] // 64)
+    pf = ssm.ssm_selective_scan_plan(dims)
+    pb = ssm.ssm_selective_scan_bwd_plan(dims)
+    assert pf.lds_bytes > 80 * 1024 and pb.lds_bytes > 80 * 1024       # one workgroup per CU
+    assert (pf.nchunks, pb.nchunks) == (fwd_pieces, bwd_pieces)
+    assert pf.workgroups == blocks * fwd_pieces
+    for p in (pf, pb):
+        assert p.chunk_len * p.nchunks >= shape[1] > p.chunk_len * (p.nchunks - 1)
+
+
 def test_forced_options_show_in_plan():
     for spl in (1, 2, 4, 8, 16):
         plan = ssm.ssm_selective_scan_plan(small_dims(dstate=16, states_per_lane=spl))
