@@ -767,9 +767,20 @@ int ssd_plan(const ssm_ssd_dims* d, SsdPlan* pl) {
         return SSM_ERR_DIMS;
     const int64_t nchunks = cdiv(d->seqlen, kQ);
     if (nchunks > (int64_t(1) << 30) || d->batch * nchunks > int64_t(INT32_MAX)) return SSM_ERR_DIMS;
-    // default: enough workgroups for two per compute unit (the output pass holds two
-    // per CU at N = 128)
-    int64_t nseg = d->nsegments ? d->nsegments : cdiv(512, bh);
+    // default: whole rounds of the 512 output workgroups that run at once (two per CU at
+    // N = 128).  The most segments that fit in one round; two rounds instead when one
+    // round would stay under 80% full and two rounds take more than twice the segments.
+    // Measured at N = 128: 24 head rows, 21 segments 126 us against 22 segments (a
+    // second round of 24 workgroups) 156 us; 40 rows, 12 segments 170 us against 13
+    // segments 211 us; 192 rows, 5 segments 327 us against 2 and 3 segments 390 and
+    // 417 us.
+    int64_t nseg = d->nsegments;
+    if (nseg == 0) {
+        constexpr int64_t kSlots = 512;
+        nseg = std::max<int64_t>(kSlots / bh, 1);
+        const int64_t two_rounds = std::max<int64_t>(2 * kSlots / bh, 1);
+        if (5 * bh * nseg < 4 * kSlots && two_rounds > 2 * nseg) nseg = two_rounds;
+    }
     nseg = std::min<int64_t>(std::max<int64_t>(nseg, 1), nchunks);
     const int64_t cps = cdiv(nchunks, nseg);
     nseg = cdiv(nchunks, cps);

@@ -441,6 +441,12 @@ def test_ssd_workspace_sizes():
     assert (pl.nsegments, pl.chunks_per_segment) == (4, 3)
     expect(1, 1000, 2, 128, 3)
     assert expect(2, 8192, 64, 128, 0).nsegments == 4             # default: two workgroups per CU
+    # default segment counts fill whole rounds of 512 workgroups (two per CU): one round
+    # when it can be filled to 80%, else two rounds with more than twice the segments
+    assert expect(1, 16384, 24, 128, 0).nsegments == 20           # 21 asked (504 of 512, not 22: 528), 20 of 13 chunks
+    assert expect(1, 16384, 40, 128, 0).nsegments == 12           # 480 of 512
+    assert expect(4, 8192, 48, 128, 0).nsegments == 5             # 2 fill 75%; 5 fill 960 of 1024
+    assert expect(8, 8192, 64, 128, 0).nsegments == 1             # 512 head rows: one segment each
     assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(dstate=32)) == 0
     with pytest.raises(ssm.SsmError):
         ssm.ssm_ssd_fwd_plan(_ssd_dims(dstate=32))
