@@ -902,11 +902,13 @@ struct StepParams {
 };
 
 // The scan input of row i (batch*dim + d) for this token: the stored u, or the fused
-// convolution of the row's history and its new input.  When `update` is set (one lane
-// per row) the history is shifted in place and u is written to u_out; all lanes of a
-// row run in the same wave, so every lane reads the history before it is written.
+// convolution of the row's history and its new input.  When `update` is set the history
+// is shifted in place: lane q of the row's R lanes writes entries q, q + R, ... (so the
+// R lanes of consecutive rows store consecutive entries together) and lane 0 writes u
+// to u_out.  All lanes of a row run in the same wave, so every lane reads the history
+// before it is written.
 template <typename IO>
-__device__ inline float step_input(const StepParams& p, int64_t i, int64_t d, bool update) {
+__device__ inline float step_input(const StepParams& p, int64_t i, int64_t d, bool update, int q = 0, int R = 1) {
     const float x = IOT<IO>::to_f32(static_cast<const IO*>(p.u)[i]);
     if (!p.conv_w) return x;
     const int K = p.conv_k;
@@ -922,11 +924,19 @@ __device__ inline float step_input(const StepParams& p, int64_t i, int64_t d, bo
     acc = fmaf(w[K - 1], x, acc);
     const float u = p.conv_silu ? silu_f32(acc) : acc;
     if (update) {
+        // the shifted history: entry j takes entry j + 1, the last entry the new input
+        const IO xin = static_cast<const IO*>(p.u)[i];
 #pragma unroll
-        for (int j = 0; j + 1 < kMaxConv - 1; ++j)
-            if (j + 1 < K - 1) st[j] = IOT<IO>::from_f32(hist[j + 1]);
-        if (K > 1) st[K - 2] = static_cast<const IO*>(p.u)[i];
-        if (p.u_out) static_cast<IO*>(p.u_out)[i] = IOT<IO>::from_f32(u);
+        for (int j = 0; j < kMaxConv - 1; ++j) {
+            if (j < K - 1 && j % R == q) {
+                IO v = xin;
+#pragma unroll
+                for (int k = 0; k + 1 < kMaxConv - 1; ++k)
+                    if (j == k && k + 1 < K - 1) v = IOT<IO>::from_f32(hist[k + 1]);
+                st[j] = v;
+            }
+        }
+        if (p.u_out && q == 0) static_cast<IO*>(p.u_out)[i] = IOT<IO>::from_f32(u);
     }
     return u;
 }
@@ -977,7 +987,7 @@ __global__ void __launch_bounds__(256) scan_step_rows_kernel(StepParams p) {
         bv[k] = load4(static_cast<const IO*>(p.Bm) + b * p.N + n0);
         cv[k] = load4(static_cast<const IO*>(p.Cm) + b * p.N + n0);
         if constexpr (!SCALAR) ar[k] = *reinterpret_cast<const float4*>(p.A + d * p.N + n0);
-        uu[k] = step_input<IO>(p, ri[k], ri[k] % p.dim, live[k] && q == 0);
+        uu[k] = step_input<IO>(p, ri[k], ri[k] % p.dim, live[k], q, R);
         dr[k] = IOT<IO>::to_f32(static_cast<const IO*>(p.delta)[ri[k]]) + (p.bias ? p.bias[d] : 0.0f);
         zz[k] = p.z ? IOT<IO>::to_f32(static_cast<const IO*>(p.z)[ri[k]]) : 0.0f;
     }
