@@ -97,7 +97,9 @@ def test_fused_conv_full_size_layer():
 
 @pytest.mark.parametrize("case", [(2, 64, 16, "f32", 0, 4, True), (3, 200, 16, "bf16", 0, 4, True),
                                   (2, 129, 7, "f32", 0, 3, False), (3, 256, 128, "bf16", 4, 2, True),
-                                  (2, 96, 64, "bf16", 0, 1, True)])
+                                  (2, 96, 64, "bf16", 0, 1, True),
+                                  # 2 and 1 lanes per row: a lane writes several history entries
+                                  (2, 80, 8, "bf16", 0, 4, True), (2, 64, 4, "f32", 0, 3, True)])
 def test_fused_conv_decode_matches_oracle_and_scan(case):
     """T decode steps (conv state and scan state carried in place) against the oracle's
     steps and against one fused scan over the same tokens."""
