@@ -621,10 +621,17 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 for (int jj = 0; jj < GS; ++jj) hh[jj] = hst[jj];
                 GOps cur, nxt;
                 gread(off, 0, j0, cur);
+                // the earlier groups' partial sum of a step is read a step ahead,
+                // together with the step's operands (the rows of later steps are not
+                // written before they are read)
+                float ypc = yrow[0], ypn = 0.0f;
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    if (t + 1 < T) gread(off, t + 1, j0, nxt);
-                    float yp = first ? 0.0f : yrow[t * kLanes];
+                    if (t + 1 < T) {
+                        gread(off, t + 1, j0, nxt);
+                        ypn = yrow[(t + 1) * kLanes];
+                    }
+                    float yp = first ? 0.0f : ypc;
 #pragma unroll
                     for (int jj = 0; jj < GS; ++jj) {
                         const float a = SCALAR ? cur.W.w : __builtin_amdgcn_exp2f(cur.W.x * Ar[jj]);
@@ -634,6 +641,7 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                     }
                     yrow[t * kLanes] = yp;
                     cur = nxt;
+                    ypc = ypn;
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -642,11 +650,17 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
             float pv[kRound];
             GOps cur, nxt;
             gread(off, T - 1, j0, cur);
+            float s1c = yrow[kSlab + (T - 1) * kLanes], s2c = yrow[2 * kSlab + (T - 1) * kLanes];
+            float s1n = 0.0f, s2n = 0.0f;
 #pragma unroll
             for (int t = T - 1; t >= 0; --t) {
-                if (t > 0) gread(off, t - 1, j0, nxt);
-                float s1 = first ? 0.0f : yrow[kSlab + t * kLanes];
-                float s2 = first ? 0.0f : yrow[2 * kSlab + t * kLanes];
+                if (t > 0) {
+                    gread(off, t - 1, j0, nxt);
+                    s1n = yrow[kSlab + (t - 1) * kLanes];
+                    s2n = yrow[2 * kSlab + (t - 1) * kLanes];
+                }
+                float s1 = first ? 0.0f : s1c;
+                float s2 = first ? 0.0f : s2c;
                 float t1s = 0.0f;   // scalar decay: sum over the group of g * a * h_prev
 #pragma unroll
                 for (int jj = 0; jj < GS; ++jj) {
@@ -677,6 +691,8 @@ __global__ void __launch_bounds__(G * kLanes) scan_bwd_kernel(BwdParams p) {
                 yrow[2 * kSlab + t * kLanes] = s2;
                 reduce8(pv, t, j0);
                 cur = nxt;
+                s1c = s1n;
+                s2c = s2n;
                 __builtin_amdgcn_sched_barrier(0);
             }
             rotate(e);
@@ -1066,10 +1082,17 @@ __global__ void __launch_bounds__((WsShape<SPL_, G_, T_>::kThreads)) scan_bwd_gr
                 for (int jj = 0; jj < 4; ++jj) hh[jj] = hst[jj];
                 GOps cur, nxt;
                 gread(bf, off, 0, j0, cur);
+                // the earlier groups' partial sum of a step is read a step ahead,
+                // together with the step's operands (the rows of later steps are not
+                // written before they are read)
+                float ypc = yrow[0], ypn = 0.0f;
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    if (t + 1 < T) gread(bf, off, t + 1, j0, nxt);
-                    float yp = first ? 0.0f : yrow[t * kLanes];
+                    if (t + 1 < T) {
+                        gread(bf, off, t + 1, j0, nxt);
+                        ypn = yrow[(t + 1) * kLanes];
+                    }
+                    float yp = first ? 0.0f : ypc;
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         hh[jj] = fmaf(cur.W.w, hh[jj], cur.W.y * gb(cur, jj));
@@ -1078,6 +1101,7 @@ __global__ void __launch_bounds__((WsShape<SPL_, G_, T_>::kThreads)) scan_bwd_gr
                     }
                     yrow[t * kLanes] = yp;
                     cur = nxt;
+                    ypc = ypn;
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -1086,11 +1110,17 @@ __global__ void __launch_bounds__((WsShape<SPL_, G_, T_>::kThreads)) scan_bwd_gr
             float pv[kRound];
             GOps cur, nxt;
             gread(bf, off, T - 1, j0, cur);
+            float s1c = yrow[kSlab + (T - 1) * kLanes], s2c = yrow[2 * kSlab + (T - 1) * kLanes];
+            float s1n = 0.0f, s2n = 0.0f;
 #pragma unroll
             for (int t = T - 1; t >= 0; --t) {
-                if (t > 0) gread(bf, off, t - 1, j0, nxt);
-                float s1 = first ? 0.0f : yrow[kSlab + t * kLanes];
-                float s2 = first ? 0.0f : yrow[2 * kSlab + t * kLanes];
+                if (t > 0) {
+                    gread(bf, off, t - 1, j0, nxt);
+                    s1n = yrow[kSlab + (t - 1) * kLanes];
+                    s2n = yrow[2 * kSlab + (t - 1) * kLanes];
+                }
+                float s1 = first ? 0.0f : s1c;
+                float s2 = first ? 0.0f : s2c;
                 float t1s = 0.0f;
                 const float a = cur.W.w;
 #pragma unroll
@@ -1109,6 +1139,8 @@ __global__ void __launch_bounds__((WsShape<SPL_, G_, T_>::kThreads)) scan_bwd_gr
                 yrow[2 * kSlab + t * kLanes] = s2;
                 reduce8(pv, sdBC, t, j0);
                 cur = nxt;
+                s1c = s1n;
+                s2c = s2n;
                 __builtin_amdgcn_sched_barrier(0);
             }
             rotate(e);
