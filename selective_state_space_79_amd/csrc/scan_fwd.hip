@@ -1180,11 +1180,13 @@ hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
     if (pl.nchunks > 1) {
         const int64_t groups = int64_t(p.batch) * p.nblk_d;
         // pass 1 on every piece but the last: on the matrix cores when the decay is a
-        // scalar per head and the rows allow 16-byte loads, else by walking
+        // scalar per head and the rows allow 16-byte loads, else by walking.  The matrix
+        // form reads the scan input from `u` directly, so it is not used with the fused
+        // convolution front end (whose `u` rows hold the convolution's input).
         const dim3 grid1(unsigned(groups * (pl.nchunks - 1)));
         bool done = false;
         if constexpr (SCALAR && VEC && std::is_same<IO, uint16_t>::value) {
-            if (p.np == p.N) {
+            if (p.np == p.N && p.conv_w == nullptr) {
                 ssm_detail::PieceStatesArgs a;
                 a.x = p.u;
                 a.delta = p.delta;

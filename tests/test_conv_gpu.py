@@ -45,6 +45,10 @@ CASES = [
     (1, 1000, 64, 16, "bf16", 0, 4, True, True, True, True, 5),
     (2, 777, 100, 16, "f32", 0, 4, True, True, True, False, 3),
     (1, 5, 64, 16, "f32", 0, 4, True, True, True, False, 0),
+    # scalar decay, bf16, 64 and 128 states in pieces: the pieces' end states must come
+    # from u = act(conv(x)), not from the convolution's input x
+    (1, 512, 64, 64, "bf16", 2, 4, True, True, True, True, 4),
+    (2, 256, 128, 128, "bf16", 2, 3, True, True, False, False, 2),
 ]
 
 
