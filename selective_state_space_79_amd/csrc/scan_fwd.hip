@@ -154,7 +154,7 @@ inline size_t lds_floats_g(int G, int spl, bool full) {
 // n >= N are padding with A = 0 and B = C = 0, which stay zero.  Staged steps beyond
 // the piece's end are identity steps (dt2 = 0, x = 0), so the walk always runs
 // whole tiles.
-template <typename IO, int SPL, bool SCALAR, int MODE, bool VEC, int G, bool CK = false>
+template <typename IO, int SPL, bool SCALAR, int MODE, bool VEC, int G, bool CK = false, bool CONV = false>
 __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(Params p) {
     using S = Shape<G, SPL>;
     constexpr int NP_ = G * SPL;
@@ -250,7 +250,10 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     }
     // ---- fused convolution: tap j of a vector's halo-extended window multiplies
     //      x[t - 3 + j] (taps before the first weight are 0)
-    const bool conv = p.conv_w != nullptr;
+    // the fused front end is a template flag (launched exactly when p.conv_w is set), so
+    // that the plain scan carries none of its registers or address arithmetic
+    constexpr bool conv = CONV;
+    static_assert(!(CK && CONV), "checkpoints are kept by the plain scan only");
     float sv_cw[KX][kMaxConv], sv_cb[KX];
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
@@ -1170,7 +1173,7 @@ int make_plan(const ssm_dims* d, Plan* pl) {
 }
 
 // ------------------------------------------------------------------ host side: launching
-template <typename IO, int SPL, bool SCALAR, bool VEC, int G, bool CK = false>
+template <typename IO, int SPL, bool SCALAR, bool VEC, int G, bool CK = false, bool CONV = false>
 hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
     using S = Shape<G, SPL>;
     if (pl.G != G || pl.T != S::T || p.np != G * SPL) return hipErrorInvalidConfiguration;
@@ -1185,8 +1188,8 @@ hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
         // convolution front end (whose `u` rows hold the convolution's input).
         const dim3 grid1(unsigned(groups * (pl.nchunks - 1)));
         bool done = false;
-        if constexpr (SCALAR && VEC && std::is_same<IO, uint16_t>::value) {
-            if (p.np == p.N && p.conv_w == nullptr) {
+        if constexpr (SCALAR && VEC && !CONV && std::is_same<IO, uint16_t>::value) {
+            if (p.np == p.N) {
                 ssm_detail::PieceStatesArgs a;
                 a.x = p.u;
                 a.delta = p.delta;
@@ -1209,26 +1212,33 @@ hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
             }
         }
         if (!done)
-            hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kAggregate, VEC, G>), grid1, block, lds_agg, stream, p);
+            hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kAggregate, VEC, G, false, CONV>), grid1, block, lds_agg,
+                               stream, p);
         const int64_t total = groups * p.np * kLanes;
         hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, p, total);
     }
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, G, CK>), dim3(unsigned(pl.blocks)), block, lds_full,
-                       stream, p);
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, G, CK, CONV>), dim3(unsigned(pl.blocks)), block,
+                       lds_full, stream, p);
     return hipGetLastError();
 }
 
 // One instantiation per (states per lane, waves per workgroup) pair the planner can
 // produce: waves are 4, 8 or 16 and states per lane 1..16.
+template <typename IO, bool SCALAR, bool VEC, int G, bool CONV>
+hipError_t dispatch_spl_c(const Params& p, const Plan& pl, hipStream_t s) {
+    switch (pl.spl) {
+        case 1: return launch_all<IO, 1, SCALAR, VEC, G, false, CONV>(p, pl, s);
+        case 2: return launch_all<IO, 2, SCALAR, VEC, G, false, CONV>(p, pl, s);
+        case 4: return launch_all<IO, 4, SCALAR, VEC, G, false, CONV>(p, pl, s);
+        case 8: return launch_all<IO, 8, SCALAR, VEC, G, false, CONV>(p, pl, s);
+        default: return launch_all<IO, 16, SCALAR, VEC, G, false, CONV>(p, pl, s);
+    }
+}
+
 template <typename IO, bool SCALAR, bool VEC, int G>
 hipError_t dispatch_spl(const Params& p, const Plan& pl, hipStream_t s) {
-    switch (pl.spl) {
-        case 1: return launch_all<IO, 1, SCALAR, VEC, G>(p, pl, s);
-        case 2: return launch_all<IO, 2, SCALAR, VEC, G>(p, pl, s);
-        case 4: return launch_all<IO, 4, SCALAR, VEC, G>(p, pl, s);
-        case 8: return launch_all<IO, 8, SCALAR, VEC, G>(p, pl, s);
-        default: return launch_all<IO, 16, SCALAR, VEC, G>(p, pl, s);
-    }
+    return p.conv_w ? dispatch_spl_c<IO, SCALAR, VEC, G, true>(p, pl, s)
+                    : dispatch_spl_c<IO, SCALAR, VEC, G, false>(p, pl, s);
 }
 
 template <typename IO, bool SCALAR, bool VEC>
