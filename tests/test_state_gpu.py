@@ -33,7 +33,10 @@ def rand_state(x, seed, scale=1.0):
 
 @pytest.mark.parametrize("case", [
     (1, 200, 64, 16, "f32", 0, 0), (2, 300, 100, 16, "bf16", 0, 0), (1, 1000, 64, 16, "bf16", 0, 4),
-    (1, 500, 128, 128, "bf16", 2, 0), (1, 777, 70, 5, "f32", 0, 3), (2, 96, 64, 32, "f32", 4, 2)])
+    (1, 500, 128, 128, "bf16", 2, 0), (1, 777, 70, 5, "f32", 0, 3), (2, 96, 64, 32, "f32", 4, 2),
+    # scalar decay, bf16 rows of whole vectors, 64 and 128 states in pieces: the pieces'
+    # end states come from the matrix cores and compose with h0
+    (1, 512, 128, 128, "bf16", 2, 4), (2, 384, 64, 64, "bf16", 4, 3)])
 def test_scan_with_initial_and_final_state(case):
     import torch
     import selective_state_space_79_amd as ssm
