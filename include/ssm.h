@@ -43,7 +43,11 @@
  * NULL, meaning no skip, no gate and a zero bias.  y must not overlap any input.
  *
  * Errors: every status except SSM_ERR_HIP is returned synchronously before
- * anything is enqueued, so a refused call has no effect on the device.  Work is
+ * anything is enqueued, so a refused call has no effect on the device.
+ * SSM_ERR_HIP reports an error of this call's own launches only: an entry point
+ * clears the calling thread's pending HIP error (hipGetLastError) before it
+ * launches, so an error left by the caller's earlier HIP calls is dropped, not
+ * reported as this call's.  Work is
  * enqueued on `stream` (a hipStream_t; NULL is the default stream) and runs
  * asynchronously; results are visible after the stream is synchronised.  Values
  * are not inspected: NaN or Inf inputs propagate into y as IEEE arithmetic does.

@@ -131,11 +131,18 @@ _lib = None
 
 
 def load_library():
-    """Load libssm.so from the package directory (raises if it was not built)."""
+    """Load libssm.so from the package directory (raises if it was not built).
+
+    torch is imported first: its HIP runtime must be the one libssm.so binds to.  Loaded
+    before torch, libssm.so would bring in the system's libamdhip64.so.7 and torch its
+    own copy afterwards, two runtimes in one process, and launches on torch's streams
+    would then fail."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m selective_state_space_79_amd.build`")
+        import torch  # noqa: F401  (binds libamdhip64 before libssm.so needs it)
+
         lib = ctypes.CDLL(LIB_PATH)
         vp = ctypes.c_void_p
         lib.ssm_selective_scan_fwd.argtypes = [vp] * 9 + [ctypes.POINTER(SsmDims), vp]

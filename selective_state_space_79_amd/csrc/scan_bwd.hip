@@ -2010,6 +2010,7 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
         p.rEin = at(pl.off_rein);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // drop an error left by the caller's earlier HIP calls: only this call's launches are reported
     const bool scalar = dims->nheads > 0;
     hipError_t e;
     if (dims->io_dtype == SSM_BF16)

@@ -1443,6 +1443,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // drop an error left by the caller's earlier HIP calls: only this call's launches are reported
     hipError_t e;
     if (with_ckpt)
         e = dims->io_dtype == SSM_BF16 ? dispatch_ckpt<uint16_t>(p, pl, vec, s) : dispatch_ckpt<float>(p, pl, vec, s);
@@ -1566,6 +1567,7 @@ int step_impl(const void* u, const void* delta, const float* A, const void* B, c
     if (cdiv(dims->batch * dims->dim * 16, 256) > 0x7fffffff) return SSM_ERR_DIMS;
     const bool scalar = dims->nheads > 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // drop an error left by the caller's earlier HIP calls: only this call's launches are reported
     hipError_t e;
     if (dims->io_dtype == SSM_BF16)
         e = scalar ? launch_step<uint16_t, true>(p, vec4, s) : launch_step<uint16_t, false>(p, vec4, s);

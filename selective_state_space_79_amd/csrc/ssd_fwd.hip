@@ -896,6 +896,7 @@ extern "C" SSM_API int ssm_ssd_fwd(const void* u, const void* delta, const float
     bool vec = L % 8 == 0;
     for (const void* q : {u, B, C, z, static_cast<const void*>(y)}) vec = vec && !misaligned(q, 16);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // drop an error left by the caller's earlier HIP calls: only this call's launches are reported
     if (N == 128) return vec ? ssd_launch<128, true>(p, pl, s) : ssd_launch<128, false>(p, pl, s);
     return vec ? ssd_launch<64, true>(p, pl, s) : ssd_launch<64, false>(p, pl, s);
 }
