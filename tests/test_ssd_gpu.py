@@ -163,19 +163,22 @@ def test_repeatable_bitwise():
     assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
 
 
-def test_full_workload_sampled_heads():
+def test_full_workload_all_heads():
     """The scalar-decay large-state workload (batch 2, L 8192, 64 heads x 64, N 128) in
-    the launch configuration the benchmark times; every output of four heads (first,
-    last and two inside) is checked against the oracle, and the whole output for
-    finiteness."""
-    announce("ssd full workload")
+    the launch configuration the benchmark times; every output and every final-state
+    entry of all 64 heads is checked against the oracle (run 16 heads at a time)."""
+    announce("ssd full workload, all heads")
     x = make_ssd_workload()
     y, h = run_gpu(x)
     assert np.isfinite(y).all() and np.isfinite(h).all()
-    heads = [0, 17, 40, x.nheads - 1]
-    yref, href = run_oracle(x, heads=heads)
-    ch = np.concatenate([np.arange(k * 64, (k + 1) * 64) for k in heads])
-    check(y[:, ch], h[:, ch], yref, href, "workload 5 per-head dt")
+    ey = eh = 0.0
+    for h0 in range(0, x.nheads, 16):
+        heads = list(range(h0, min(h0 + 16, x.nheads)))
+        yref, href = run_oracle(x, heads=heads)
+        ch = slice(heads[0] * x.headdim, (heads[-1] + 1) * x.headdim)
+        ey, eh = max(ey, rel_err(y[:, ch], yref)), max(eh, rel_err(h[:, ch], href))
+    print(f"workload 5 per-head dt, all {y.size} outputs: err y={ey:.3e} h={eh:.3e}", flush=True)
+    assert ey <= TOL and ey <= TIGHT and eh <= STATE_TOL
 
 
 def test_worked_example_through_ssd_abi():
