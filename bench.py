@@ -34,8 +34,59 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # minimal VALU operations per state update of the diagonal-A method:
 # dt*A (mul), exp2, (dt*u)*B (mul), a*h + b (fma), C*h + y (fma)
 OPS_PER_UPDATE = 5
+# scalar decay (one rate per head): the decay is one exp2 per (b,t,d), shared by the
+# state entries; per update x*B (mul), a*h + b (fma), C*h + y (fma)
+OPS_PER_UPDATE_SCALAR = 3
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_79_amd", "csrc", "scan_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_mamba13b_hbm_traffic.json")
+VALU_FILE = os.path.join(ROOT, "profiles", "scan_fwd_mamba13b_valu_issue.json")
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+
+# Untimed warm-up runs for at least this long, whatever --warmup asks for: the GPU clock
+# ramps up over the first milliseconds of work, and a handful of 0.3 ms calls would
+# otherwise time the ramp.  The number of warm-up calls actually run is reported.
+MIN_WARMUP_S = 0.25
+
+
+def time_calls(call, steps: int, warmup: int, stream, min_warmup_s: float | None = None):
+    """Warm up with at least `warmup` calls and at least `min_warmup_s` seconds, then
+    time exactly `steps` calls, each bracketed by HIP events recorded on `stream` (the
+    stream the kernels are launched on), the whole loop also by the wall clock, with a
+    device synchronisation on both sides.  call(i) launches call number i (i lets the
+    caller rotate input sets).  Returns per-call statistics in milliseconds."""
+    import statistics
+    import torch
+
+    if min_warmup_s is None:
+        min_warmup_s = MIN_WARMUP_S
+    n = 0
+    t0 = time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < min_warmup_s:
+        call(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()   # keep the host within a few calls of the device
+    torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        call(i)
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total = ev[0].elapsed_time(ev[-1])
+    srt = sorted(per)
+    return {"ms_events": total / steps, "ms_wall": wall * 1e3 / steps, "ms_per_step": max(total / steps, wall * 1e3 / steps),
+            "ms_median": statistics.median(per), "ms_min": srt[0], "ms_max": srt[-1],
+            "ms_p90": srt[min(len(srt) - 1, int(0.9 * len(srt)))], "warmup_calls_run": n,
+            "warmup_s": round(warm_s, 3)}
+
 
 
 def algorithmic_bytes(x) -> int:
@@ -46,6 +97,116 @@ def algorithmic_bytes(x) -> int:
     bc = 2 * esz * x.batch * x.N * x.L
     params = 4 * (x.A.size + 2 * x.dim)
     return per_elem + bc + params
+
+
+# Inputs of a workload smaller than this are rotated over several resident copies, so
+# that the 256 MB Infinity Cache cannot serve a call from the previous call's data.
+ROTATE_BYTES = 512 << 20
+
+
+def scan_workload_bench(x, dev, steps: int, warmup: int, stream, extra_sets=None):
+    """Time ssm_selective_scan_fwd over the workload x (device tensors `dev`; further
+    input sets `extra_sets` are rotated call by call).  One call = the whole forward
+    pass of the workload, every kernel it launches.  Returns its record: plan, timing
+    statistics, updates/s and both rooflines of the call (algorithmic bytes against the
+    HBM peak; fp32 VALU lane operations against the VALU peak)."""
+    import torch
+    import selective_state_space_79_amd as ssm
+
+    sets = [dev] + list(extra_sets or [])
+    dims = ssm.dims_for(dev["u"], dev["B"], dev["A"])
+    plan = ssm.ssm_selective_scan_plan(dims).as_dict()
+    ws = None
+    if plan["workspace_bytes"]:
+        ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
+        dims.workspace, dims.workspace_bytes = ws.data_ptr(), plan["workspace_bytes"]
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    ys = [torch.empty_like(d["u"]) for d in sets]
+    argsets = [(p(d["u"]), p(d["delta"]), p(d["A"]), p(d["B"]), p(d["C"]), p(d["D"]), p(d["z"]), p(d["dt_bias"]),
+                p(y), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)) for d, y in zip(sets, ys)]
+    fn = ssm.load_library().ssm_selective_scan_fwd
+
+    def call(i):
+        st = fn(*argsets[i % len(argsets)])
+        if st != 0:
+            raise ssm.SsmError(st, "ssm_selective_scan_fwd")
+
+    t = time_calls(call, steps, warmup, stream)
+    ms = t["ms_events"]            # average call duration, HIP events on the launch stream
+    nbytes = algorithmic_bytes(x)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    scalar = x.nheads > 0
+    ops = OPS_PER_UPDATE_SCALAR if scalar else OPS_PER_UPDATE
+    tops = ops * x.updates / (ms * 1e-3) / 1e12
+    ceiling = ops / (ops + (0 if scalar else 1))   # the exp2 is half rate (diagonal A only)
+    alu = {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TFLOP/s",
+           "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": None,
+           "note": (f"FLOP = one fp32 VALU lane operation; {ops} per state update ("
+                    + ("x*B mul, a*h+b fma, C*h+y fma; the decay's exp2 is per (b,t,d)" if scalar else
+                       "dt*A mul, exp2, x*B mul, a*h+b fma, C*h+y fma")
+                    + "); peak = 256 CU x 64 lanes x 2.4 GHz, packed fp32 not used"
+                    + ("" if scalar else "; v_exp_f32 issues at half rate, so 6 issue slots carry these 5 "
+                       "operations and frac cannot exceed 5/6 = 0.833")),
+           "frac_ceiling": round(ceiling, 4)}
+    hbm = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes_per_launch": nbytes}
+    rec = {"workload": f"{x.batch}x{x.L}x{x.dim}, N {x.N}, {x.io} I/O" + (f", {x.nheads} heads scalar decay"
+                                                                       if scalar else ", diagonal A"),
+           "plan": plan, "timing": t, "ms_per_call": round(t["ms_per_step"], 5),
+           "updates_per_s": x.updates / (t["ms_per_step"] * 1e-3), "gbs": round(gbs, 1),
+           "input_sets_rotated": len(sets), "hbm": hbm, "alu": alu,
+           "roofline": alu if alu["frac"] >= hbm["frac"] else hbm}
+    if plan["nchunks"] == 1 and not scalar:
+        vi = measured_valu_issue(x, ms)
+        if vi:
+            rec["valu_issue"] = vi
+    return rec
+
+
+def other_workloads_bench(indices, steps: int, warmup: int, stream):
+    """scan_workload_bench on the other named workloads, one at a time (inputs freed
+    in between); a workload smaller than ROTATE_BYTES is rotated over copies drawn from
+    further seeds."""
+    import torch
+    from selective_state_space_79_amd.inputs import WORKLOADS, make_workload, to_device
+
+    out = {}
+    for idx in indices:
+        x = make_workload(idx)
+        dev = to_device(x, "cuda:0")
+        nsets = 1
+        if algorithmic_bytes(x) < ROTATE_BYTES and x.updates > 1e6:
+            nsets = -(-ROTATE_BYTES // algorithmic_bytes(x))
+        extra = [to_device(make_workload(idx, seed=1000 + 17 * k + idx), "cuda:0") for k in range(1, nsets)]
+        r = scan_workload_bench(x, dev, steps, warmup, stream, extra_sets=extra)
+        r["seed"] = idx
+        out[WORKLOADS[idx]["name"]] = r
+        del dev, extra, x
+        torch.cuda.empty_cache()
+    return out
+
+
+def linear_in_L_bench(steps: int, warmup: int, stream, Ls=(1024, 2048, 4096, 8192)):
+    """Call time of the 1.3B-layer shape (batch 4, dim 4096, N 16, bf16) at several
+    sequence lengths, the same plan (one piece, 256 workgroups) at each: the scan's
+    work is linear in L, so the time should be too."""
+    import numpy as np
+    from selective_state_space_79_amd.inputs import ScanInputs, make_inputs, to_device
+
+    big = make_inputs(4, max(Ls), 4096, 16, seed=77, io="bf16")
+    rows = []
+    for L in Ls:
+        cut = lambda a: np.ascontiguousarray(a[..., :L])
+        x = ScanInputs(big.batch, L, big.dim, big.N, 0, "bf16", cut(big.u), cut(big.delta), cut(big.z), cut(big.B),
+                       cut(big.C), big.A, big.D, big.dt_bias)
+        r = scan_workload_bench(x, to_device(x, "cuda:0"), steps, warmup, stream)
+        rows.append({"L": L, "ms_median": round(r["timing"]["ms_median"], 5), "ms_mean": round(r["timing"]["ms_events"], 5),
+                     "updates_per_s": r["updates_per_s"], "workgroups": r["plan"]["workgroups"]})
+    base = rows[0]
+    for r in rows:
+        r["time_ratio_to_first"] = round(r["ms_median"] / base["ms_median"], 3)
+        r["L_ratio_to_first"] = r["L"] / base["L"]
+    return rows
 
 
 def kernel_hash() -> str:
@@ -64,6 +225,35 @@ def measured_traffic():
     if rec.get("kernel_source_sha256_16") != kernel_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def measured_valu_issue(x, ms):
+    """VALU issue occupancy of the forward kernel from the committed rocprofv3 counters
+    (SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32 per dispatch), if they were taken on the
+    current kernel source and this workload's shape; else None.  A wave64 VALU
+    instruction holds a SIMD16 for 4 cycles, a transcendental one for 8, so the issue
+    cycles are 4 x (VALU + TRANS); the fraction is over 1024 SIMDs x 2.4 GHz x the call
+    time measured here."""
+    try:
+        with open(VALU_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    if rec.get("shape") != [x.batch, x.L, x.dim, x.N]:
+        return None
+    v, tr = rec["SQ_INSTS_VALU"], rec["SQ_INSTS_VALU_TRANS_F32"]
+    cycles = 4 * (v + tr)
+    avail = SIMDS * CLOCK_HZ * ms * 1e-3
+    # the method's own floor: 6 issue slots per state update (5 operations, exp2 at half
+    # rate), wave64 instructions
+    walk = 4 * 6 * x.updates / 64
+    return {"valu_instructions_per_call": v, "trans_instructions_per_call": tr, "issue_cycles_per_call": cycles,
+            "issue_frac": round(cycles / avail, 4), "walk_floor_issue_frac": round(walk / avail, 4),
+            "issue_cycles_over_walk_floor": round(cycles / walk, 3),
+            "note": "issue_frac = 4*(VALU+TRANS) cycles / (1024 SIMDs x 2.4 GHz x call time); walk floor = 6 slots "
+                    "per state update; counters from " + os.path.relpath(VALU_FILE, ROOT)}
 
 
 def cpu_baseline(x, rows_batches: int, repeats: int = 3):
@@ -86,28 +276,47 @@ def cpu_baseline(x, rows_batches: int, repeats: int = 3):
         times.append(time.perf_counter() - t0)
     dt = statistics.median(times)
     updates = nb * x.L * x.dim * x.N
+    # one thread, on the first 256 channels of batch row 0 (full L)
+    nd = min(256, x.dim)
+    one = [np.ascontiguousarray(a[0:1, 0:nd], dtype=np.float64) for a in (x.u, x.delta, x.z)]
+    t1 = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.selective_scan_fwd(one[0], one[1], A[:nd], args[2][0:1], args[3][0:1], x.D[:nd], one[2],
+                                  x.dt_bias[:nd], nthreads=1)
+        t1.append(time.perf_counter() - t0)
+    dt1 = statistics.median(t1)
+    up1 = x.L * nd * x.N
     return {"value": updates / dt, "unit": "state updates/s", "cores": threads, "kind": "oracle",
             "sample": f"batch rows 0..{nb - 1} of {x.batch} (all {x.dim} channels, full L={x.L}, N={x.N}); "
                       f"{updates:.3e} updates, median of {repeats} runs {dt:.2f} s wall on {threads} OpenMP "
-                      f"threads (about {dt * threads * repeats:.0f} s of CPU time in all), fp64"}
+                      f"threads (about {dt * threads * repeats:.0f} s of CPU time in all), fp64",
+            "single_thread": {"value": up1 / dt1, "unit": "state updates/s", "cores": 1,
+                              "sample": f"batch row 0, channels 0..{nd - 1}, full L={x.L}, N={x.N}: {up1:.3e} "
+                                        f"updates, median of {repeats} runs {dt1:.2f} s, fp64"}}
 
 
+# the counter passes time only the headline workload, with no warm-up floor (every
+# dispatch is serialised and sampled under --pmc)
+_ONLY = "--steps 3 --warmup 1 --min-warmup-s 0 --no-cpu-baseline --no-backward --no-decode --no-ssd --no-workloads --no-linear"
 PROFILE_COMMANDS = {
     "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/stats -o scan -- python3 bench.py",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/fetch -o scan -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward --no-decode --no-ssd",
-    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/write -o scan -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-backward --no-decode --no-ssd",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/fetch -o scan -- python3 bench.py " + _ONLY,
+    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/write -o scan -- python3 bench.py " + _ONLY,
+    "valu": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS SQ_INSTS_SALU SQ_BUSY_CYCLES "
+            "--kernel-trace --output-format csv -d {d}/valu -o scan -- python3 bench.py " + _ONLY,
     "conv_stats": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/convstats -o conv -- "
-                  "python3 bench.py --steps 200 --warmup 50 --no-cpu-baseline --no-backward --no-decode --no-ssd --fused-conv",
+                  "python3 bench.py --steps 200 --warmup 50 --no-cpu-baseline --no-backward --no-decode --no-ssd "
+                  "--no-workloads --no-linear --fused-conv",
     "copyfetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/copyfetch -o copy -- "
                  "python3 bench.py --calibrate-copy",
     "copywrite": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/copywrite -o copy -- "
                  "python3 bench.py --calibrate-copy",
 }
 COPY_BYTES = 2 << 30
-# output directory the profile commands write to (relative to the repository root)
-PROFILE_DIR = "rocprof_out"
+# output directory the profile commands write to (relative to the repository root); raw
+# rocprofv3 output stays out of the repository's tracked files
+PROFILE_DIR = "gpurun_out/rocprof"
 
 
 def calibrate_copy():
@@ -123,100 +332,192 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes_each_way": COPY_BYTES, "launches": 4}))
 
 
-def summarize_profiles(d):
-    """Write profiles/scan_fwd_mamba13b_*.{md,json} from the rocprofv3 CSV outputs
-    of PROFILE_COMMANDS run under directory d."""
+def _grid(row) -> int:
+    """Work-items of a dispatch from a rocprofv3 CSV row (Grid_Size, or its x/y/z)."""
+    if row.get("Grid_Size"):
+        return int(float(row["Grid_Size"]))
+    g = 1
+    for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"):
+        if row.get(k):
+            g *= int(float(row[k]))
+    return g
+
+
+def _trace_rows(path):
+    """Per (kernel, grid) dispatch statistics from a rocprofv3 kernel_trace.csv, in ns:
+    calls, average, median, min, max, ordered by total time."""
     import csv
     import statistics
 
-    def counter(sub, prefix, kernel):
-        path = os.path.join(d, sub, f"{prefix}_counter_collection.csv")
-        return [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]]
+    by = {}
+    for r in csv.DictReader(open(path)):
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        by.setdefault((r["Kernel_Name"], _grid(r)), []).append(ns)
+    rows = [{"name": k[0], "grid": k[1], "calls": len(v), "avg": statistics.fmean(v), "median": statistics.median(v),
+             "min": min(v), "max": max(v), "total": sum(v)} for k, v in by.items()]
+    return sorted(rows, key=lambda r: -r["total"])
+
+
+def _trace_table(rows, width=110):
+    md = ["| kernel | grid (work-items) | calls | average ns | median ns | min ns | max ns |",
+          "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| `{r['name'][:width]}` | {r['grid']} | {r['calls']} | {r['avg']:.0f} | {r['median']:.0f} | "
+                  f"{r['min']} | {r['max']} |")
+    return md
+
+
+def _find(d, sub, suffix):
+    """The rocprofv3 output file ending in `suffix` under d/sub (it may sit in a
+    per-host/per-process subdirectory)."""
+    for root, _, files in os.walk(os.path.join(d, sub)):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    return None
+
+
+HEADLINE_GRID = 256 * 512   # the 1.3B layer's forward: 256 workgroups of 8 waves
+
+
+def summarize_profiles(d):
+    """Write the profiles/ summaries from the rocprofv3 CSV outputs of PROFILE_COMMANDS
+    run under directory d (each pass that is present)."""
+    import csv
+    import statistics
+
+    def counters(sub, kernel, grid=None):
+        """{counter name: [value per dispatch]} of the dispatches of `kernel` (and grid)."""
+        path = _find(d, sub, "counter_collection.csv")
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"] and (grid is None or _grid(r) == grid):
+                out.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return out
 
     from selective_state_space_79_amd.inputs import make_workload
     x = make_workload(3)
-    alg = algorithmic_bytes(x)
-    esz = 2
-    alg_read = 3 * esz * x.batch * x.L * x.dim + 2 * esz * x.batch * x.N * x.L + 4 * (x.A.size + 2 * x.dim)
-    alg_write = esz * x.batch * x.L * x.dim
-    fetch = counter("fetch", "scan", "scan_fwd_kernel")
-    write = counter("write", "scan", "scan_fwd_kernel")
-    cfetch = [v for v in counter("copyfetch", "copy", "") if v > 1e5]
-    cwrite = [v for v in counter("copywrite", "copy", "") if v > 1e5]
-    kib = COPY_BYTES / 1024
-    ffac = kib / statistics.median(cfetch)
-    wfac = kib / statistics.median(cwrite)
-    rd = statistics.median(fetch) * 1024 * ffac
-    wr = statistics.median(write) * 1024 * wfac
-    rec = {"kernel": "scan_fwd_kernel<bf16, 4 states/lane, diagonal A, full, 16-byte rows, 4 waves>",
-           "workload": "mamba-1.3b-layer (4, 4096, 4096, 16) bf16", "kernel_source_sha256_16": kernel_hash(),
-           "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
-           "copy_fetch_kib": cfetch, "copy_write_kib": cwrite, "copy_bytes_each_way": COPY_BYTES,
-           "fetch_scale": ffac, "write_scale": wfac, "hbm_read_bytes_per_launch": rd,
-           "hbm_write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
-           "algorithmic_read_bytes": alg_read, "algorithmic_write_bytes": alg_write, "algorithmic_bytes": alg,
-           "commands": [PROFILE_COMMANDS[k].format(d=PROFILE_DIR) for k in ("fetch", "write", "copyfetch", "copywrite")]}
+    head = "scan_fwd_kernel<unsigned short, 4, false, 0, true, 4, false, false>"
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
-    stats_path = os.path.join(d, "stats", "scan_kernel_stats.csv")
-    rows = list(csv.DictReader(open(stats_path)))
-    md = ["# scan_fwd_kernel, mamba-1.3b-layer workload (4 x 4096 x 4096, N=16, bf16): rocprofv3 summaries", "",
-          f"Kernel source sha256[:16]: `{kernel_hash()}`", "",
-          "## Kernel time (`--kernel-trace --stats`)", "",
-          "Command (from the repository root on the GPU box):", "",
-          "    " + PROFILE_COMMANDS["stats"].format(d=PROFILE_DIR), "",
-          "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
-    for r in rows:
-        md.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
-    md += ["", "## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, one run each)", "",
-           "Commands:", ""] + ["    " + c for c in rec["commands"]] + [
-           "", "Calibration: a plain 2 GiB device copy (`bench.py --calibrate-copy`) reads "
-           f"{statistics.median(cfetch):.0f} KiB of FETCH_SIZE and {statistics.median(cwrite):.0f} KiB of WRITE_SIZE per "
-           f"launch for {kib:.0f} KiB moved each way: scale factors {ffac:.4f} (fetch) and {wfac:.4f} (write).", "",
-           "| per launch | counter (KiB, median) | scaled bytes | algorithmic bytes | ratio |", "|---|---|---|---|---|",
-           f"| read | {statistics.median(fetch):.0f} | {rd:.4g} | {alg_read:.4g} | {rd / alg_read:.3f} |",
-           f"| write | {statistics.median(write):.0f} | {wr:.4g} | {alg_write:.4g} | {wr / alg_write:.3f} |",
-           f"| total | | {rd + wr:.4g} | {alg:.4g} | {(rd + wr) / alg:.3f} |", ""]
-    with open(os.path.join(ROOT, "profiles", "scan_fwd_mamba13b.md"), "w") as f:
-        f.write("\n".join(md))
-    print(json.dumps({"traffic_bytes_per_launch": rd + wr, "ratio_to_algorithmic": (rd + wr) / alg}))
-    conv_stats = os.path.join(d, "convstats", "conv_kernel_stats.csv")
-    if os.path.exists(conv_stats):
-        rows = list(csv.DictReader(open(conv_stats)))
-        md = ["# Fused convolution front end + scan, mamba-1.3b-layer workload (4 x 4096 x 4096, N=16, bf16, "
-              "width-4 SiLU convolution): rocprofv3 summary", "",
+    cmd = lambda k: PROFILE_COMMANDS[k].format(d=PROFILE_DIR)
+
+    # kernel time, split by grid: the bench times several workloads with the same kernel
+    stats_trace = _find(d, "stats", "kernel_trace.csv")
+    if stats_trace:
+        rows = _trace_rows(stats_trace)
+        hr = [r for r in rows if head in r["name"] and r["grid"] == HEADLINE_GRID]
+        md = ["# scan_fwd_kernel, mamba-1.3b-layer workload (4 x 4096 x 4096, N=16, bf16): rocprofv3 kernel times", "",
               f"Kernel source sha256[:16]: `{kernel_hash()}`", "",
-              "The run times the plain scan first (`--steps` calls) and then the fused front end (100 calls of "
-              "`ssm_selective_scan_fwd_conv`, then the fused decode step); both scans launch the same kernel, so "
-              "its calls here are the two kinds together.", "",
-              "Command (from the repository root on the GPU box):", "",
-              "    " + PROFILE_COMMANDS["conv_stats"].format(d=PROFILE_DIR), "",
-              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
-        for r in rows:
-            md.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
-        with open(os.path.join(ROOT, "profiles", "scan_fwd_conv_mamba13b.md"), "w") as f:
+              "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+              "    " + cmd("stats"), "",
+              "The default bench times several workloads; per-dispatch times from the kernel trace are grouped by "
+              "kernel and grid size, so the headline forward (256 workgroups x 512 work-items = "
+              f"{HEADLINE_GRID} work-items) has a row of its own.", ""]
+        if hr:
+            r = hr[0]
+            md += [f"**Headline forward:** {r['calls']} dispatches, average {r['avg'] / 1e3:.1f} µs, median "
+                   f"{r['median'] / 1e3:.1f} µs, min {r['min'] / 1e3:.1f} µs (warm-up dispatches included).", ""]
+        md += _trace_table(rows)
+        with open(os.path.join(ROOT, "profiles", "scan_fwd_mamba13b.md"), "w") as f:
             f.write("\n".join(md) + "\n")
-    scalar = re.compile(r"scan_fwd_kernel<[^,]+, \d+, true")
-    rows = [r for r in csv.DictReader(open(stats_path))
-            if "ssd_" in r["Name"] or scalar.search(r["Name"]) or "scan_carry_kernel" in r["Name"]]
-    if any("ssd_" in r["Name"] for r in rows):
-        src = os.path.join(ROOT, "selective_state_space_79_amd", "csrc", "ssd_fwd.hip")
-        with open(src, "rb") as f:
-            ssd_hash = hashlib.sha256(f.read()).hexdigest()[:16]
-        md = ["# ssd_state_kernel + ssd_out_kernel, scalar-decay large-state workload with one step size per head "
-              "(batch 2, L 8192, 64 heads x 64, N 128, bf16): rocprofv3 summary", "",
-              f"Kernel source (`csrc/ssd_fwd.hip`) sha256[:16]: `{ssd_hash}`", "",
-              "From the same `--kernel-trace --stats` run of the default bench as `scan_fwd_mamba13b.md`; one "
-              "`ssm_ssd_fwd` call launches `ssd_state_kernel` (end states of all segments but the last) and then "
-              "`ssd_out_kernel`.  The scalar-decay rows of `scan_fwd_kernel` are the per-channel scan timed on the "
-              "same inputs for comparison.", "",
-              "Command (from the repository root on the GPU box):", "",
-              "    " + PROFILE_COMMANDS["stats"].format(d=PROFILE_DIR), "",
-              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
-        for r in rows:
-            md.append(f"| `{r['Name'][:120]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
-        with open(os.path.join(ROOT, "profiles", "ssd_fwd_scalar_decay_head_dt.md"), "w") as f:
+        ssd = [r for r in rows if "ssd_" in r["name"]]
+        if ssd:
+            src = os.path.join(ROOT, "selective_state_space_79_amd", "csrc", "ssd_fwd.hip")
+            with open(src, "rb") as f:
+                ssd_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+            scal = [r for r in rows if re.search(r"scan_fwd_kernel<[^,]+, \d+, true", r["name"])
+                    or "scan_piece_states_kernel<128, false>" in r["name"] or "scan_carry_kernel" in r["name"]]
+            md = ["# ssd_state_kernel + ssd_out_kernel, scalar-decay large-state workload with one step size per "
+                  "head (batch 2, L 8192, 64 heads x 64, N 128, bf16): rocprofv3 kernel times", "",
+                  f"Kernel source (`csrc/ssd_fwd.hip`) sha256[:16]: `{ssd_hash}`", "",
+                  "From the same `--kernel-trace --stats` run of the default bench as `scan_fwd_mamba13b.md`; one "
+                  "`ssm_ssd_fwd` call launches `ssd_gram_kernel`, `ssd_state_kernel` and `ssd_out_kernel`.  The "
+                  "scalar-decay rows of the per-channel scan (same shapes) are listed below them.", "",
+                  "Command (from the repository root on the GPU box):", "", "    " + cmd("stats"), ""]
+            md += _trace_table(ssd + scal, 120)
+            with open(os.path.join(ROOT, "profiles", "ssd_fwd_scalar_decay_head_dt.md"), "w") as f:
+                f.write("\n".join(md) + "\n")
+
+    # HBM traffic of the headline forward
+    if _find(d, "fetch", "counter_collection.csv") and _find(d, "copyfetch", "counter_collection.csv"):
+        alg = algorithmic_bytes(x)
+        esz = 2
+        alg_read = 3 * esz * x.batch * x.L * x.dim + 2 * esz * x.batch * x.N * x.L + 4 * (x.A.size + 2 * x.dim)
+        alg_write = esz * x.batch * x.L * x.dim
+        fetch = counters("fetch", head, HEADLINE_GRID)["FETCH_SIZE"]
+        write = counters("write", head, HEADLINE_GRID)["WRITE_SIZE"]
+        cfetch = [v for v in counters("copyfetch", "")["FETCH_SIZE"] if v > 1e5]
+        cwrite = [v for v in counters("copywrite", "")["WRITE_SIZE"] if v > 1e5]
+        kib = COPY_BYTES / 1024
+        ffac = kib / statistics.median(cfetch)
+        wfac = kib / statistics.median(cwrite)
+        rd = statistics.median(fetch) * 1024 * ffac
+        wr = statistics.median(write) * 1024 * wfac
+        rec = {"kernel": "scan_fwd_kernel<bf16, 4 states/lane, diagonal A, full, 16-byte rows, 4 waves>",
+               "workload": "mamba-1.3b-layer (4, 4096, 4096, 16) bf16", "kernel_source_sha256_16": kernel_hash(),
+               "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
+               "copy_fetch_kib": cfetch, "copy_write_kib": cwrite, "copy_bytes_each_way": COPY_BYTES,
+               "fetch_scale": ffac, "write_scale": wfac, "hbm_read_bytes_per_launch": rd,
+               "hbm_write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
+               "algorithmic_read_bytes": alg_read, "algorithmic_write_bytes": alg_write, "algorithmic_bytes": alg,
+               "commands": [cmd(k) for k in ("fetch", "write", "copyfetch", "copywrite")]}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        md = ["# scan_fwd_kernel, mamba-1.3b-layer workload: HBM traffic per launch (rocprofv3 counters)", "",
+              f"Kernel source sha256[:16]: `{kernel_hash()}`", "",
+              "`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, one run each; commands (repository root, GPU box):", ""]
+        md += ["    " + c for c in rec["commands"]]
+        md += ["", "Calibration: a plain 2 GiB device copy (`bench.py --calibrate-copy`) reads "
+               f"{statistics.median(cfetch):.0f} KiB of FETCH_SIZE and {statistics.median(cwrite):.0f} KiB of "
+               f"WRITE_SIZE per launch for {kib:.0f} KiB moved each way: scale factors {ffac:.4f} (fetch) and "
+               f"{wfac:.4f} (write).", "",
+               "| per launch | counter (KiB, median) | scaled bytes | algorithmic bytes | ratio |", "|---|---|---|---|---|",
+               f"| read | {statistics.median(fetch):.0f} | {rd:.4g} | {alg_read:.4g} | {rd / alg_read:.3f} |",
+               f"| write | {statistics.median(write):.0f} | {wr:.4g} | {alg_write:.4g} | {wr / alg_write:.3f} |",
+               f"| total | | {rd + wr:.4g} | {alg:.4g} | {(rd + wr) / alg:.3f} |", ""]
+        with open(os.path.join(ROOT, "profiles", "scan_fwd_mamba13b_traffic.md"), "w") as f:
+            f.write("\n".join(md))
+        print(json.dumps({"traffic_bytes_per_launch": rd + wr, "ratio_to_algorithmic": (rd + wr) / alg}))
+
+    # VALU issue of the headline forward
+    if _find(d, "valu", "counter_collection.csv"):
+        c = counters("valu", head, HEADLINE_GRID)
+        med = {k: statistics.median(v) for k, v in c.items()}
+        trace = _find(d, "valu", "kernel_trace.csv")
+        durs = [r for r in _trace_rows(trace) if head in r["name"] and r["grid"] == HEADLINE_GRID] if trace else []
+        rec = {"kernel": head, "shape": [x.batch, x.L, x.dim, x.N], "kernel_source_sha256_16": kernel_hash(),
+               "dispatches": len(c.get("SQ_INSTS_VALU", [])), "command": cmd("valu"), **med}
+        with open(VALU_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        cyc = 4 * (med["SQ_INSTS_VALU"] + med["SQ_INSTS_VALU_TRANS_F32"])
+        walk = 4 * 6 * x.updates / 64
+        md = ["# VALU issue of the forward, mamba-1.3b-layer workload (4 x 4096 x 4096, N 16, bf16 I/O)", "",
+              f"Kernel source sha256[:16]: `{kernel_hash()}`", "",
+              "Command (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+              "    " + cmd("valu"), "",
+              "Counters are totals per dispatch over all waves (median over the dispatches). A wave64 VALU "
+              "instruction holds a SIMD16 for 4 cycles and a transcendental one (`SQ_INSTS_VALU_TRANS_F32`, also "
+              "counted in `SQ_INSTS_VALU`) for 8, so the issue cycles are 4 x (VALU + TRANS), over 1024 SIMDs.", "",
+              "| counter | per dispatch |", "|---|---|"]
+        md += [f"| {k} | {v:.4g} |" for k, v in sorted(med.items())]
+        md += ["", f"Issue cycles per call: {cyc:.4g}; the method's walk alone (6 slots per state update) needs "
+               f"{walk:.4g}, so the kernel issues {cyc / walk:.3f}x its walk floor.",
+               f"At 2.4 GHz over 1024 SIMDs that is {cyc / (SIMDS * CLOCK_HZ) * 1e6:.1f} µs of issue per call."]
+        if durs:
+            md.append(f"Dispatch time in this (profiled) run: median {durs[0]['median'] / 1e3:.1f} µs.")
+        with open(os.path.join(ROOT, "profiles", "scan_fwd_mamba13b_valu_issue.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
+
+    conv_trace = _find(d, "convstats", "kernel_trace.csv")
+    if conv_trace:
+        md = ["# Fused convolution front end + scan, mamba-1.3b-layer workload (4 x 4096 x 4096, N=16, bf16, "
+              "width-4 SiLU convolution): rocprofv3 kernel times", "",
+              f"Kernel source sha256[:16]: `{kernel_hash()}`", "",
+              "The run times the plain scan first and then the fused front end (`ssm_selective_scan_fwd_conv`, "
+              "then the fused decode step); the fused scan is its own instantiation (template flag).", "",
+              "Command (from the repository root on the GPU box):", "", "    " + cmd("conv_stats"), ""]
+        md += _trace_table(_trace_rows(conv_trace))
+        with open(os.path.join(ROOT, "profiles", "scan_fwd_conv_mamba13b.md"), "w") as f:
             f.write("\n".join(md) + "\n")
 
 
@@ -241,16 +542,14 @@ def decode_step_bench(batch: int, steps: int = 200, warmup: int = 50):
     args = (p(col["u"]), p(col["delta"]), p(dev["A"]), p(col["B"]), p(col["C"]), p(dev["D"]), p(col["z"]),
             p(dev["dt_bias"]), p(h), p(y), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream))
     fn = ssm.load_library().ssm_selective_scan_step
-    for _ in range(warmup):
-        assert fn(*args) == 0
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        fn(*args)
-    e1.record(stream)
-    e1.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+
+    def call(i):
+        st = fn(*args)
+        if st != 0:
+            raise ssm.SsmError(st, "ssm_selective_scan_step")
+
+    t = time_calls(call, steps, warmup, stream)
+    us = t["ms_events"] * 1e3
     # algorithmic bytes: state read + written, A once, u/delta/z read and y written,
     # B and C per sequence, D and dt_bias once
     nbytes = 8 * batch * dim * N + 4 * dim * N + 8 * batch * dim + 4 * batch * N + 8 * dim
@@ -258,7 +557,8 @@ def decode_step_bench(batch: int, steps: int = 200, warmup: int = 50):
     return {"workload": f"mamba-1.3b-layer decode step, {batch} sequences (dim {dim}, N {N}, bf16 I/O, fp32 state)",
             "us_per_step": round(us, 3), "tokens_per_s": round(batch / (us * 1e-6), 1),
             "updates_per_s": batch * dim * N / (us * 1e-6), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+            "us_median": round(t["ms_median"] * 1e3, 3), "us_min": round(t["ms_min"] * 1e3, 3)}
 
 
 def fused_conv_bench(x, dev, width: int = 4, steps: int = 100, warmup: int = 30):
@@ -282,18 +582,11 @@ def fused_conv_bench(x, dev, width: int = 4, steps: int = 100, warmup: int = 30)
     fn = ssm.load_library().ssm_selective_scan_fwd_conv
 
     def timed(call, n, nw):
-        for _ in range(nw):
+        def c(i):
             st = call()
             if st != 0:
                 raise ssm.SsmError(st, "fused conv")
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            call()
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1) / n
+        return time_calls(c, n, nw, stream)["ms_events"]
 
     ms = timed(lambda: fn(*args), steps, warmup)
     nbytes = algorithmic_bytes(x) + 4 * x.dim * (width + 1)
@@ -368,18 +661,14 @@ def backward_bench(x, dev, steps: int = 40, warmup: int = 15):
             p(dev["dt_bias"]), None, p(dy), None, ctypes.byref(grads), ctypes.byref(dims),
             ctypes.c_void_p(stream.cuda_stream))
     fn = ssm.load_library().ssm_selective_scan_bwd
-    for _ in range(warmup):
+
+    def call(i):
         st = fn(*args)
         if st != 0:
             raise ssm.SsmError(st, "ssm_selective_scan_bwd")
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        fn(*args)
-    e1.record(stream)
-    e1.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    tb = time_calls(call, steps, warmup, stream)
+    ms = tb["ms_events"]
     esz = 2 if x.io == "bf16" else 4
     # u, delta, z, dy read and du, ddelta, dz written per element; B, C read and dB, dC
     # (float32) written per (b, t, n); A, D, dt_bias read and dA, dD, ddt_bias written
@@ -391,7 +680,8 @@ def backward_bench(x, dev, steps: int = 40, warmup: int = 15):
            "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
                         "unit": "TFLOP/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
                         "note": f"{BWD_OPS_PER_UPDATE} fp32 VALU lane operations per state update"},
-           "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+           "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "ms_median": round(tb["ms_median"], 4), "ms_min": round(tb["ms_min"], 4)}
 
     # training with saved checkpoints: the forward keeps the state every 16 steps and
     # the backward starts from them instead of recomputing them
@@ -405,18 +695,11 @@ def backward_bench(x, dev, steps: int = 40, warmup: int = 15):
         lib = ssm.load_library()
 
         def timed(fn, a, name):
-            for _ in range(warmup):
+            def c(i):
                 st = fn(*a)
                 if st != 0:
                     raise ssm.SsmError(st, name)
-            torch.cuda.synchronize()
-            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0.record(stream)
-            for _ in range(steps):
-                fn(*a)
-            t1.record(stream)
-            t1.synchronize()
-            return t0.elapsed_time(t1) / steps
+            return time_calls(c, steps, warmup, stream)["ms_events"]
 
         f_ms = timed(lib.ssm_selective_scan_fwd_ckpt, fargs, "ssm_selective_scan_fwd_ckpt")
         b_ms = timed(lib.ssm_selective_scan_bwd_ckpt, bargs, "ssm_selective_scan_bwd_ckpt")
@@ -453,21 +736,16 @@ def ssd_bench(steps: int = 100, warmup: int = 30):
             p(y), None, ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream))
     fn = ssm.load_library().ssm_ssd_fwd
 
-    def timed(call, n, w):
-        for _ in range(w):
+    def timed(call, n, w, full=False):
+        def c(i):
             st = call()
             if st != 0:
                 raise ssm.SsmError(st, "bench call")
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            call()
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1) / n
+        t = time_calls(c, n, w, stream)
+        return t if full else t["ms_events"]
 
-    ms = timed(lambda: fn(*args), steps, warmup)
+    tss = timed(lambda: fn(*args), steps, warmup, full=True)
+    ms = tss["ms_events"]
     # the per-channel scan on the same inputs
     sc = to_device(x.per_channel(), "cuda:0")
     ys = torch.empty_like(sc["u"])
@@ -498,7 +776,8 @@ def ssd_bench(steps: int = 100, warmup: int = 30):
     tflops = 2 * chunks * (mac_chunk + mac_state) / (ms * 1e-3) / 1e12
     return {"workload": f"{SSD_WORKLOADS[5]['name']}: batch {x.batch}, L {x.L}, {x.nheads} heads x {x.headdim}, "
                         f"N {x.N}, bf16 I/O, one step size per head",
-            "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3), "plan": plan,
+            "ms_per_call": round(ms, 4), "ms_median": round(tss["ms_median"], 4), "ms_min": round(tss["ms_min"], 4),
+            "updates_per_s": x.updates / (ms * 1e-3), "plan": plan,
             "hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes},
             "mfma": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -510,6 +789,7 @@ def ssd_bench(steps: int = 100, warmup: int = 30):
 
 
 def main():
+    global MIN_WARMUP_S
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -524,6 +804,11 @@ def main():
                     help="also time the fused convolution front end (same scan kernel, so off by default: "
                          "its launches would mix into the scan kernel's profile)")
     ap.add_argument("--cpu-batches", type=int, default=4, help="batch rows in the oracle's timing sample")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other named workloads (tiny, 130M layer, long sequence, scalar decay N=128)")
+    ap.add_argument("--no-linear", action="store_true", help="skip the linear-in-L check")
+    ap.add_argument("--min-warmup-s", type=float, default=MIN_WARMUP_S,
+                    help="least wall time of untimed warm-up before each timed loop (seconds)")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 2 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs in DIR")
     args = ap.parse_args()
@@ -533,6 +818,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    MIN_WARMUP_S = args.min_warmup_s
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -557,58 +843,17 @@ def main():
     gen_s = time.perf_counter() - t_gen
 
     stream = torch.cuda.current_stream()
-    y = torch.empty_like(dev["u"])
-    dims = ssm.dims_for(dev["u"], dev["B"], dev["A"])
-    plan = ssm.ssm_selective_scan_plan(dims).as_dict()
-    ws = None
-    if plan["workspace_bytes"]:
-        ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
-        dims.workspace, dims.workspace_bytes = ws.data_ptr(), plan["workspace_bytes"]
-    p = lambda t: ctypes.c_void_p(t.data_ptr())
-    call_args = (p(dev["u"]), p(dev["delta"]), p(dev["A"]), p(dev["B"]), p(dev["C"]), p(dev["D"]), p(dev["z"]),
-                 p(dev["dt_bias"]), p(y), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream))
-    fn = lib.ssm_selective_scan_fwd
-
-    def step():
-        st = fn(*call_args)
-        if st != 0:
-            raise ssm.SsmError(st, "ssm_selective_scan_fwd")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    # barrier + synchronize on both sides (one process: the barrier is trivial)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    ev1.synchronize()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_events = ev0.elapsed_time(ev1) / args.steps
-    ms_wall = wall * 1e3 / args.steps
-    ms_per_step = max(ms_events, ms_wall)
-
+    rec_main = scan_workload_bench(x, dev, args.steps, args.warmup, stream)
+    t = rec_main["timing"]
+    ms_per_step = t["ms_per_step"]
     updates = x.updates
     value = updates / (ms_per_step * 1e-3)
-    nbytes = algorithmic_bytes(x)
-    # the dominant kernel: with one piece per sequence a step is one launch of it
-    kernel_ms = ms_events
-    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
-    tops = OPS_PER_UPDATE * updates / (kernel_ms * 1e-3) / 1e12
+    plan = rec_main["plan"]
     traffic = measured_traffic() if (args.workload == 3 and plan["nchunks"] == 1) else None
-    alu = {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TFLOP/s",
-           "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
-           "note": "FLOP = one fp32 VALU lane operation; 5 per state update (mul, exp2, mul, fma, fma); peak = "
-                   "256 CU x 64 lanes x 2.4 GHz, packed fp32 not used"}
-    hbm = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-           "algorithmic_bytes_per_launch": nbytes}
-    roofline = alu if alu["frac"] >= hbm["frac"] else hbm
+    rec_main["roofline"]["traffic"] = traffic
+    rec_main["hbm"]["traffic"] = traffic
+    t.update({"input_gen_s": round(gen_s, 2), "kernel_source_sha256_16": kernel_hash(),
+              "device": torch.cuda.get_device_name(0)})
 
     rec = {
         "metric": METRIC,
@@ -626,13 +871,14 @@ def main():
         "config": {"workload": w["name"], "batch": x.batch, "seqlen": x.L, "dim": x.dim, "dstate": x.N,
                    "nheads": x.nheads, "io_dtype": x.io, "state_dtype": "f32", "seed": args.workload,
                    "plan": plan},
-        "hbm_gbs": round(gbs, 1),
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": roofline,
-        "hbm": hbm,
-        "timing": {"ms_events": ms_events, "ms_wall": ms_wall, "input_gen_s": round(gen_s, 2),
-                   "kernel_source_sha256_16": kernel_hash(), "device": torch.cuda.get_device_name(0)},
+        "hbm_gbs": rec_main["hbm"]["achieved"],
+        "hbm_frac": rec_main["hbm"]["frac"],
+        "roofline": rec_main["roofline"],
+        "hbm": rec_main["hbm"],
+        "timing": t,
     }
+    if rec_main.get("valu_issue"):
+        rec["valu_issue"] = rec_main["valu_issue"]
     if args.workload == 3 and not args.no_decode:
         rec["decode_step"] = [decode_step_bench(64), decode_step_bench(256)]
     if args.fused_conv:
@@ -640,9 +886,14 @@ def main():
     if not args.no_backward:
         rec["backward"] = backward_bench(x, dev)
     if not args.no_ssd:
-        del dev, y
+        del dev
         torch.cuda.empty_cache()
         rec["ssd"] = ssd_bench()
+    if not args.no_linear:
+        rec["linear_in_L"] = linear_in_L_bench(args.steps, args.warmup, stream)
+    if not args.no_workloads:
+        others = [i for i in (1, 2, 3, 4, 5) if i != args.workload]
+        rec["workloads"] = other_workloads_bench(others, args.steps, args.warmup, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_batches)
     print(json.dumps(rec), flush=True)

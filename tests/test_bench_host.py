@@ -44,3 +44,35 @@ def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch)
     other = "0" * 16 if bench.kernel_hash() != "0" * 16 else "1" * 16
     path.write_text(json.dumps({"kernel_source_sha256_16": other, "hbm_bytes_per_launch": 5.5e8}))
     assert bench.measured_traffic() is None
+
+
+def test_kernel_trace_rows_split_by_grid(tmp_path):
+    """The profile summary groups dispatches by kernel and grid size, so the headline
+    forward's row is not mixed with another workload's calls of the same kernel."""
+    path = tmp_path / "scan_kernel_trace.csv"
+    rows = ["Kernel_Name,Grid_Size_X,Grid_Size_Y,Grid_Size_Z,Start_Timestamp,End_Timestamp"]
+    for i in range(3):
+        rows.append(f"k<a>,{bench.HEADLINE_GRID},1,1,{1000 * i},{1000 * i + 300}")
+    rows.append("k<a>,98304,1,1,5000,5150")
+    path.write_text("\n".join(rows) + "\n")
+    got = {(r["name"], r["grid"]): r for r in bench._trace_rows(str(path))}
+    head = got[("k<a>", bench.HEADLINE_GRID)]
+    assert head["calls"] == 3 and head["avg"] == 300 and head["min"] == 300
+    assert got[("k<a>", 98304)]["calls"] == 1 and got[("k<a>", 98304)]["avg"] == 150
+
+
+def test_valu_issue_needs_the_profiled_source_and_shape(tmp_path, monkeypatch):
+    path = tmp_path / "valu.json"
+    monkeypatch.setattr(bench, "VALU_FILE", str(path))
+    x = SimpleNamespace(batch=4, L=4096, dim=4096, N=16, updates=4 * 4096 * 4096 * 16)
+    assert bench.measured_valu_issue(x, 0.3) is None
+    rec = {"kernel_source_sha256_16": bench.kernel_hash(), "shape": [4, 4096, 4096, 16],
+           "SQ_INSTS_VALU": 1.2e8, "SQ_INSTS_VALU_TRANS_F32": 2.1e7}
+    path.write_text(json.dumps(rec))
+    vi = bench.measured_valu_issue(x, 0.3)
+    assert abs(vi["issue_frac"] - 4 * 1.41e8 / (1024 * 2.4e9 * 0.3e-3)) < 1e-3
+    # the walk floor: 6 issue slots per state update, wave64 instructions of 4 cycles
+    assert abs(vi["walk_floor_issue_frac"] - 4 * 6 * x.updates / 64 / (1024 * 2.4e9 * 0.3e-3)) < 1e-3
+    rec["shape"] = [8, 2048, 1536, 16]
+    path.write_text(json.dumps(rec))
+    assert bench.measured_valu_issue(x, 0.3) is None
