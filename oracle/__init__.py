@@ -61,8 +61,6 @@ def _load():
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
-        lib.oracle_selective_recurrence.argtypes = [i64, dp, dp, dp, dp, dp]
-        lib.oracle_selective_recurrence.restype = ctypes.c_int
         lib.oracle_selective_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 9 + [ctypes.c_int]
         lib.oracle_selective_scan_fwd.restype = ctypes.c_int
         lib.oracle_selective_scan_state.argtypes = [i64, i64, i64, i64] + [dp] * 11 + [ctypes.c_int]
@@ -105,19 +103,6 @@ def sigmoid(x: float) -> float:
 
 def max_threads() -> int:
     return _load().oracle_max_threads()
-
-
-def selective_recurrence(value, retain, write, read) -> np.ndarray:
-    """Scalar retain/write/read recurrence of the qubittool page's runnable example."""
-    v, r, w, d = (_f64(x).reshape(-1) for x in (value, retain, write, read))
-    n = v.shape[0]
-    if not (r.shape[0] == w.shape[0] == d.shape[0] == n):
-        raise ValueError("all four step fields need the same length")
-    out = np.zeros(max(n, 1), dtype=np.float64)
-    code = _load().oracle_selective_recurrence(n, _ptr(v), _ptr(r), _ptr(w), _ptr(d), _ptr(out))
-    if code != OK:
-        raise OracleError(code, "selective_recurrence")
-    return out[:n]
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, nthreads: int = 0) -> np.ndarray:

@@ -19,8 +19,9 @@
  *   [CB]  cnblogs.com "Mamba3 技术浅析"
  *
  * Parity pins: every function below is pinned by tests that do not reuse this
- * code (tests/test_oracle_pins.py): the worked scalar example printed on [QT],
- * the LTI convolution identity, the semiseparable sum of [CB] §2.2.2, the A = 0
+ * code (tests/test_oracle_pins.py): the worked scalar example printed on [QT]
+ * (its retain/write/read steps expressed as a one-channel, one-state scan), the
+ * LTI convolution identity, the semiseparable sum of [CB] §2.2.2, the A = 0
  * prefix sum, the constant-input geometric series and structural invariants.  The
  * gradients are pinned by tests/test_oracle_bwd_pins.py: central finite differences
  * of the (pinned) forward, hand-derived closed forms for a single step, the adjoint
@@ -63,31 +64,6 @@ static int all_finite(const double* p, int64_t n)
     for (int64_t i = 0; i < n; ++i)
         if (!isfinite(p[i])) return 0;
     return 1;
-}
-
-/*
- * The scalar retain / write / read recurrence of [QT] "一个可运行的标量模型":
- *   state_0 = 0,  state_i = retain_i * state_{i-1} + write_i * value_i,
- *   out_i   = read_i * state_i          (read after the update).
- * Inputs are checked before any state is formed, as on that page: an empty
- * sequence, any non-finite field, or a retain factor outside [0, 1] is refused.
- */
-int oracle_selective_recurrence(int64_t n, const double* value, const double* retain,
-                                const double* write, const double* read, double* out)
-{
-    if (n <= 0) return OR_ERR_EMPTY;
-    if (!value || !retain || !write || !read || !out) return OR_ERR_NULL;
-    for (int64_t i = 0; i < n; ++i) {
-        if (!isfinite(value[i]) || !isfinite(retain[i]) || !isfinite(write[i]) || !isfinite(read[i]))
-            return OR_ERR_NONFINITE;
-        if (retain[i] < 0.0 || retain[i] > 1.0) return OR_ERR_RETAIN;
-    }
-    double state = 0.0;
-    for (int64_t i = 0; i < n; ++i) {
-        state = retain[i] * state + write[i] * value[i];
-        out[i] = read[i] * state;
-    }
-    return OR_OK;
 }
 
 /*

@@ -48,51 +48,69 @@ def silu_ref(x):
 
 # ---------------------------------------------------------------- worked example
 
+def _as_scan_inputs(value, retain, write, read):
+    """The page's retain/write/read steps as a one-channel, one-state scan.
+
+    With A = -1 the retain factor exp(dt*A) equals retain when dt = -ln(retain); the
+    raw step input is the inverse softplus of that dt, log(expm1(dt)).  The write term
+    dt*B*u equals write*value when u = value and B = write/dt.  C = read reads the
+    state after the update; D and the gate are absent."""
+    value, retain, write, read = (np.asarray(a, dtype=np.float64) for a in (value, retain, write, read))
+    dt = -np.log(retain)
+    delta_raw = np.array([math.log(math.expm1(v)) for v in dt])
+    L = value.shape[0]
+    return dict(u=value.reshape(1, 1, L), delta=delta_raw.reshape(1, 1, L), A=np.array([[-1.0]]),
+                B=(write / dt).reshape(1, 1, L), C=read.reshape(1, 1, L))
+
+
 def test_scalar_example_matches_printed_output():
+    """The three steps of the page's runnable scalar model, through the oracle's scan:
+    the outputs it prints, to the two decimals printed and to fp64 rounding."""
     steps, _, expect = _golden()
-    out = oracle.selective_recurrence(steps[:, 0], steps[:, 1], steps[:, 2], steps[:, 3])
+    y, h_last = oracle.selective_scan_state(**_as_scan_inputs(*steps.T))
+    out = y.reshape(-1)
     printed = expect["expect_outputs_2dp"]
     assert ["%.2f" % v for v in out] == printed
     np.testing.assert_allclose(out, [float(v) for v in printed], rtol=0, atol=1e-12)
+    # the second step writes nothing, so its large value never reaches the state:
+    # the state only decays, 2.00 -> 0.95 * 2.00
+    assert out[1] == pytest.approx(0.95 * out[0], rel=1e-14)
+    np.testing.assert_allclose(h_last.reshape(-1), [out[-1]], rtol=0, atol=1e-12)
 
 
 def test_scalar_example_rejects_invalid_retention():
+    """A retain factor of 1.2 (outside [0, 1]) is refused.  In the scan, retain =
+    exp(dt*A) with dt = softplus(.) > 0, so retain > 1 is exactly A > 0: with the raw
+    step input 0 (dt = ln 2), A = ln(1.2)/ln 2 gives retain 1.2."""
     _, invalid, expect = _golden()
     assert expect["expect_invalid_retention_rejected"] == ["true"]
+    value, retain, write, read = invalid
+    assert retain > 1.0
+    dt = math.log(2.0)
+    A = math.log(retain) / dt
+    assert math.exp(dt * A) == pytest.approx(retain, rel=1e-15)
     with pytest.raises(oracle.OracleError) as e:
-        oracle.selective_recurrence(*[invalid[i:i + 1] for i in range(4)])
+        oracle.selective_scan_fwd(u=[[[value]]], delta=[[[0.0]]], A=[[A]], B=[[[write / dt]]], C=[[[read]]])
     assert e.value.code == oracle.ERR_RETAIN
+    # the same step with the retain factor inside [0, 1] is accepted
+    oracle.selective_scan_fwd(u=[[[value]]], delta=[[[0.0]]], A=[[-A]], B=[[[write / dt]]], C=[[[read]]])
 
 
 def test_scalar_example_other_refusals():
+    """The page's model refuses an empty sequence and a non-finite field before it
+    forms any state; so does the scan oracle."""
     with pytest.raises(oracle.OracleError) as e:
-        oracle.selective_recurrence([], [], [], [])
+        oracle.selective_scan_fwd(np.zeros((1, 1, 0)), np.zeros((1, 1, 0)), [[-1.0]], np.zeros((1, 1, 0)),
+                                  np.zeros((1, 1, 0)))
     assert e.value.code == oracle.ERR_EMPTY
-    with pytest.raises(oracle.OracleError) as e:
-        oracle.selective_recurrence([1.0, np.nan], [0.5, 0.5], [1, 1], [1, 1])
-    assert e.value.code == oracle.ERR_NONFINITE
-    with pytest.raises(oracle.OracleError) as e:
-        oracle.selective_recurrence([1.0], [-0.01], [1], [1])
-    assert e.value.code == oracle.ERR_RETAIN
-
-
-def test_scalar_example_through_full_scan():
-    """The same three steps expressed as a one-channel, one-state scan.
-
-    With A = -1 the retain factor exp(dt*A) equals retain when dt = -ln(retain);
-    the raw step input is the inverse softplus of that dt, log(expm1(dt)).  The
-    write term dt*B*u equals write*value when u = value and B = write/dt.  C = 1
-    reads the state, D and the gate are absent.
-    """
-    steps, _, expect = _golden()
-    value, retain, write, read = steps.T
-    dt = -np.log(retain)
-    delta_raw = np.array([math.log(math.expm1(v)) for v in dt])
-    Bv = write / dt
-    y = oracle.selective_scan_fwd(u=value.reshape(1, 1, 3), delta=delta_raw.reshape(1, 1, 3),
-                                  A=np.array([[-1.0]]), B=Bv.reshape(1, 1, 3), C=read.reshape(1, 1, 3))
-    printed = [float(v) for v in expect["expect_outputs_2dp"]]
-    np.testing.assert_allclose(y.reshape(-1), printed, rtol=0, atol=1e-12)
+    steps, _, _ = _golden()
+    for field in range(4):
+        bad = steps.T.copy()
+        bad[field, 1] = np.nan
+        args = _as_scan_inputs(*bad)
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.selective_scan_fwd(**args)
+        assert e.value.code == oracle.ERR_NONFINITE, field
 
 
 # ---------------------------------------------------------------- elementwise functions
