@@ -44,10 +44,10 @@
  *
  * Errors: every status except SSM_ERR_HIP is returned synchronously before
  * anything is enqueued, so a refused call has no effect on the device.
- * SSM_ERR_HIP reports an error of this call's own launches only: an entry point
- * clears the calling thread's pending HIP error (hipGetLastError) before it
- * launches, so an error left by the caller's earlier HIP calls is dropped, not
- * reported as this call's.  Work is
+ * SSM_ERR_HIP reports a failure of this call's own kernel launches only (each
+ * launch's return value is checked).  A HIP error that the caller's earlier HIP
+ * calls left pending is neither reported as this call's nor read nor cleared: the
+ * caller still gets it from hipGetLastError.  Work is
  * enqueued on `stream` (a hipStream_t; NULL is the default stream) and runs
  * asynchronously; results are visible after the stream is synchronised.  Values
  * are not inspected: NaN or Inf inputs propagate into y as IEEE arithmetic does.
@@ -75,7 +75,7 @@ typedef enum ssm_status {
     SSM_ERR_ALIGN = -5,     /* an array is not aligned to its element size */
     SSM_ERR_WORKSPACE = -6, /* workspace missing, too small or not 256-byte aligned */
     SSM_ERR_HIP = -7,       /* the HIP runtime reported an error when enqueuing */
-    SSM_ERR_ALIAS = -8      /* y overlaps one of the inputs */
+    SSM_ERR_ALIAS = -8      /* an output or the workspace overlaps an input or another output */
 } ssm_status;
 
 typedef enum ssm_dtype {
@@ -104,7 +104,8 @@ typedef struct ssm_dims {
                                 same result up to rounding). */
     int32_t reserved;        /* must be 0 */
     void* workspace;         /* device memory for the carries between pieces of one
-                                sequence; may be NULL when the required size is 0 */
+                                sequence; may be NULL when the required size is 0; it
+                                may overlap no input and no output (SSM_ERR_ALIAS) */
     size_t workspace_bytes;  /* size of workspace in bytes */
 } ssm_dims;
 

@@ -1789,15 +1789,15 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, bo
         }
         p.piece_base = 0;
         if (!ext_ck && !mfma_fwd)
-            hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kFwdAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
+            launch_kernel((scan_bwd_kernel<IO, SPL, G, SCALAR, kFwdAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
         p.piece_base = 1;
         if (!mfma_rev)
-            hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kRevAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
+            launch_kernel((scan_bwd_kernel<IO, SPL, G, SCALAR, kRevAgg, VEC>), grid1, block, pl.lds_fwd, s, p);
         p.piece_base = 0;
         const int64_t total = groups * p.np * kLanes;
         const dim3 gridc(unsigned(cdiv(total, 256)));
-        if (!ext_ck) hipLaunchKernelGGL(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 0);
-        hipLaunchKernelGGL(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 1);
+        if (!ext_ck) launch_kernel(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 0);
+        launch_kernel(bwd_carry_kernel, gridc, dim3(256), 0, s, p, total, 1);
     }
     p.piece_base = 0;
     const dim3 grid(unsigned(groups * pl.nch));
@@ -1806,43 +1806,43 @@ hipError_t bwd_launch(BwdParams p, const BwdPlan& pl, bool vec_g, bool vec_c, bo
     } else if constexpr (SPL == wsc::NP / G && G == 8) {
         const dim3 blk_c(static_cast<unsigned>(wsc::Shape::kThreads), 1, 1);
         if (vec_c)
-            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true, 4, 4, 16>), grid, blk_c, wsc::Shape::kLdsBytes, s, p);
+            launch_kernel((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true, 4, 4, 16>), grid, blk_c, wsc::Shape::kLdsBytes, s, p);
         else
-            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, false, 4, 4, 16>), grid, blk_c, wsc::Shape::kLdsBytes, s, p);
+            launch_kernel((scan_bwd_ckpt_ws_kernel<IO, SCALAR, false, 4, 4, 16>), grid, blk_c, wsc::Shape::kLdsBytes, s, p);
     } else if constexpr (SPL == 16 && G == 8 && SCALAR) {
         const dim3 blk_c(static_cast<unsigned>(wscw::Shape::kThreads), 1, 1);
         if (vec_c)
-            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true, 16, 8, 8>), grid, blk_c, wscw::Shape::kLdsBytes, s, p);
+            launch_kernel((scan_bwd_ckpt_ws_kernel<IO, SCALAR, true, 16, 8, 8>), grid, blk_c, wscw::Shape::kLdsBytes, s, p);
         else
-            hipLaunchKernelGGL((scan_bwd_ckpt_ws_kernel<IO, SCALAR, false, 16, 8, 8>), grid, blk_c, wscw::Shape::kLdsBytes, s, p);
+            launch_kernel((scan_bwd_ckpt_ws_kernel<IO, SCALAR, false, 16, 8, 8>), grid, blk_c, wscw::Shape::kLdsBytes, s, p);
     } else {
-        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt, VEC>), grid, block, pl.lds_fwd, s, p);
+        launch_kernel((scan_bwd_kernel<IO, SPL, G, SCALAR, kCkpt, VEC>), grid, block, pl.lds_fwd, s, p);
     }
     if constexpr (SPL == wsg::NP / G && G == 8) {
         const dim3 blk_ws(static_cast<unsigned>(wsg::Shape::kThreads), 1, 1);
         if (vec_g)
-            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, true, 4, 4, 16>), grid, blk_ws, pl.lds_grad, s, p);
+            launch_kernel((scan_bwd_grad_ws_kernel<IO, SCALAR, true, 4, 4, 16>), grid, blk_ws, pl.lds_grad, s, p);
         else
-            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, false, 4, 4, 16>), grid, blk_ws, pl.lds_grad, s, p);
+            launch_kernel((scan_bwd_grad_ws_kernel<IO, SCALAR, false, 4, 4, 16>), grid, blk_ws, pl.lds_grad, s, p);
     } else if constexpr (SPL == 16 && G == 8 && SCALAR) {
         const dim3 blk_ws(static_cast<unsigned>(wsw::Shape::kThreads), 1, 1);
         if (vec_g)
-            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, true, 16, 8, 8>), grid, blk_ws, pl.lds_grad, s, p);
+            launch_kernel((scan_bwd_grad_ws_kernel<IO, SCALAR, true, 16, 8, 8>), grid, blk_ws, pl.lds_grad, s, p);
         else
-            hipLaunchKernelGGL((scan_bwd_grad_ws_kernel<IO, SCALAR, false, 16, 8, 8>), grid, blk_ws, pl.lds_grad, s, p);
+            launch_kernel((scan_bwd_grad_ws_kernel<IO, SCALAR, false, 16, 8, 8>), grid, blk_ws, pl.lds_grad, s, p);
     } else {
-        hipLaunchKernelGGL((scan_bwd_kernel<IO, SPL, G, SCALAR, kGrad, VEC>), grid, block, pl.lds_grad, s, p);
+        launch_kernel((scan_bwd_kernel<IO, SPL, G, SCALAR, kGrad, VEC>), grid, block, pl.lds_grad, s, p);
     }
     const int64_t nbc = int64_t(p.batch) * 2 * p.N * p.L;
-    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned(cdiv(nbc, 256))), dim3(256), 0, s, p, dB, dC, nbc);
+    launch_kernel(bwd_reduce_bc_kernel, dim3(unsigned(cdiv(nbc, 256))), dim3(256), 0, s, p, dB, dC, nbc);
     const int64_t npar = p.dim * p.N;
-    hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3(unsigned(cdiv(npar, 256))), dim3(256), 0, s, p,
+    launch_kernel(bwd_reduce_param_kernel, dim3(unsigned(cdiv(npar, 256))), dim3(256), 0, s, p,
                        SCALAR ? nullptr : dA, dD, dbias, npar);
     if (SCALAR) {
         const int64_t nheads = p.dim / p.head_dim;
-        hipLaunchKernelGGL(bwd_reduce_heads_kernel, dim3(unsigned(nheads)), dim3(256), 0, s, p, dA);
+        launch_kernel(bwd_reduce_heads_kernel, dim3(unsigned(nheads)), dim3(256), 0, s, p, dA);
     }
-    return hipGetLastError();
+    return ssm_detail::launch_error;
 }
 
 // The (entries per lane, waves) pairs the planner produces: 1..4 entries with 4 waves
@@ -2010,7 +2010,7 @@ int bwd_impl(const void* u, const void* delta, const float* A, const void* B, co
         p.rEin = at(pl.off_rein);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();   // drop an error left by the caller's earlier HIP calls: only this call's launches are reported
+    ssm_detail::launch_error = hipSuccess;   // this call's launch failures only (the caller's pending HIP error is left alone)
     const bool scalar = dims->nheads > 0;
     hipError_t e;
     if (dims->io_dtype == SSM_BF16)

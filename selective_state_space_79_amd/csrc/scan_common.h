@@ -8,7 +8,34 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+
 #include "ssm.h"
+
+// ------------------------------------------------------------------ kernel launches
+// Every kernel is launched through launch_kernel(), which calls hipLaunchKernel and
+// keeps the first failure of the calling thread's current entry point in
+// ssm_detail::launch_error.  An entry point resets it before its first launch and
+// reports it after its last, so SSM_ERR_HIP is exactly this call's launch failures;
+// the thread's pending HIP error (hipGetLastError), which the caller's earlier HIP
+// calls may have left, is never read, reported or cleared by the library.
+namespace ssm_detail {
+inline thread_local hipError_t launch_error = hipSuccess;
+}  // namespace ssm_detail
+
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                          Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> held(static_cast<KArgs>(args)...);
+    const hipError_t e = std::apply(
+        [&](auto&... a) {
+            void* ptrs[] = {static_cast<void*>(&a)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream);
+        },
+        held);
+    if (e != hipSuccess && ssm_detail::launch_error == hipSuccess) ssm_detail::launch_error = e;
+}
 
 namespace {
 

@@ -1070,20 +1070,20 @@ hipError_t launch_step(const StepParams& p, bool vec4, hipStream_t s) {
     const int64_t rows = p.batch * p.dim;
     const dim3 block(256);
     if (!vec4) {
-        hipLaunchKernelGGL((scan_step_kernel<IO, SCALAR>), dim3(unsigned(cdiv(rows, 256))), block, 0, s, p);
-        return hipGetLastError();
+        launch_kernel((scan_step_kernel<IO, SCALAR>), dim3(unsigned(cdiv(rows, 256))), block, 0, s, p);
+        return ssm_detail::launch_error;
     }
     const int R = step_lanes(p.N);
     constexpr int ROWS = 1;   // measured: 4 rows per lane (a quarter of the waves) was slower
     const dim3 grid(unsigned(cdiv(rows * R, 256 * ROWS)));
     switch (R) {
-        case 1: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 1, ROWS>), grid, block, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 2, ROWS>), grid, block, 0, s, p); break;
-        case 4: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 4, ROWS>), grid, block, 0, s, p); break;
-        case 8: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 8, ROWS>), grid, block, 0, s, p); break;
-        default: hipLaunchKernelGGL((scan_step_rows_kernel<IO, SCALAR, 16, ROWS>), grid, block, 0, s, p); break;
+        case 1: launch_kernel((scan_step_rows_kernel<IO, SCALAR, 1, ROWS>), grid, block, 0, s, p); break;
+        case 2: launch_kernel((scan_step_rows_kernel<IO, SCALAR, 2, ROWS>), grid, block, 0, s, p); break;
+        case 4: launch_kernel((scan_step_rows_kernel<IO, SCALAR, 4, ROWS>), grid, block, 0, s, p); break;
+        case 8: launch_kernel((scan_step_rows_kernel<IO, SCALAR, 8, ROWS>), grid, block, 0, s, p); break;
+        default: launch_kernel((scan_step_rows_kernel<IO, SCALAR, 16, ROWS>), grid, block, 0, s, p); break;
     }
-    return hipGetLastError();
+    return ssm_detail::launch_error;
 }
 
 // ------------------------------------------------------------------ host side: planning
@@ -1212,14 +1212,14 @@ hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
             }
         }
         if (!done)
-            hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kAggregate, VEC, G, false, CONV>), grid1, block, lds_agg,
+            launch_kernel((scan_fwd_kernel<IO, SPL, SCALAR, kAggregate, VEC, G, false, CONV>), grid1, block, lds_agg,
                                stream, p);
         const int64_t total = groups * p.np * kLanes;
-        hipLaunchKernelGGL(scan_carry_kernel, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, p, total);
+        launch_kernel(scan_carry_kernel, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, p, total);
     }
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, G, CK, CONV>), dim3(unsigned(pl.blocks)), block,
+    launch_kernel((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, G, CK, CONV>), dim3(unsigned(pl.blocks)), block,
                        lds_full, stream, p);
-    return hipGetLastError();
+    return ssm_detail::launch_error;
 }
 
 // One instantiation per (states per lane, waves per workgroup) pair the planner can
@@ -1291,7 +1291,7 @@ const char* ssm_status_string(int status) {
         case SSM_ERR_ALIGN: return "an array is not aligned to its element size";
         case SSM_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case SSM_ERR_HIP: return "the HIP runtime reported an error";
-        case SSM_ERR_ALIAS: return "y overlaps an input array";
+        case SSM_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";
         default: return "unknown status";
     }
 }
@@ -1382,9 +1382,15 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
         if (!dims->workspace || dims->workspace_bytes < pl.ws_bytes ||
             (reinterpret_cast<uintptr_t>(dims->workspace) % 256) != 0)
             return SSM_ERR_WORKSPACE;
-        if (overlaps(dims->workspace, pl.ws_bytes, y, nel) || overlaps(dims->workspace, pl.ws_bytes, h0, nh) ||
-            overlaps(dims->workspace, pl.ws_bytes, h_last, nh) || overlaps(dims->workspace, pl.ws_bytes, u_out, nel))
-            return SSM_ERR_ALIAS;
+        // the carry passes write the workspace before the full pass reads the inputs, so
+        // it may overlap no input and no output
+        const size_t nw = conv ? size_t(dims->dim) * conv->width * 4 : 0;
+        const size_t ns = conv ? size_t(dims->batch) * dims->dim * (conv->width - 1) * esz : 0;
+        const void* all[] = {u,  delta, z,      B,     C,     A,  D, dt_bias, h0, y, h_last, u_out,
+                             conv ? conv->weight : nullptr, conv ? conv->bias : nullptr, conv_state};
+        const size_t all_sz[] = {nel, nel, nel, nbc, nbc, na, nd, nd, nh, nel, nh, nel, nw, nd, ns};
+        for (int k = 0; k < 15; ++k)
+            if (overlaps(dims->workspace, pl.ws_bytes, all[k], all_sz[k])) return SSM_ERR_ALIAS;
     }
 
     if (with_ckpt) {
@@ -1443,7 +1449,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();   // drop an error left by the caller's earlier HIP calls: only this call's launches are reported
+    ssm_detail::launch_error = hipSuccess;   // this call's launch failures only (the caller's pending HIP error is left alone)
     hipError_t e;
     if (with_ckpt)
         e = dims->io_dtype == SSM_BF16 ? dispatch_ckpt<uint16_t>(p, pl, vec, s) : dispatch_ckpt<float>(p, pl, vec, s);
@@ -1489,6 +1495,7 @@ int ssm_selective_scan_fwd_ckpt(const void* u, const void* delta, const float* A
     return fwd_impl(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, dims, stream, nullptr, nullptr, nullptr, true,
                     ckpt);
 }
+
 
 }  // extern "C"
 
@@ -1567,7 +1574,7 @@ int step_impl(const void* u, const void* delta, const float* A, const void* B, c
     if (cdiv(dims->batch * dims->dim * 16, 256) > 0x7fffffff) return SSM_ERR_DIMS;
     const bool scalar = dims->nheads > 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();   // drop an error left by the caller's earlier HIP calls: only this call's launches are reported
+    ssm_detail::launch_error = hipSuccess;   // this call's launch failures only (the caller's pending HIP error is left alone)
     hipError_t e;
     if (dims->io_dtype == SSM_BF16)
         e = scalar ? launch_step<uint16_t, true>(p, vec4, s) : launch_step<uint16_t, false>(p, vec4, s);
@@ -1603,9 +1610,9 @@ bool launch_piece_states(const PieceStatesArgs& a, bool reverse, int64_t npieces
 #define SSM_PIECE_CASE(N_)                                                                              \
     case N_:                                                                                            \
         if (reverse)                                                                                    \
-            hipLaunchKernelGGL((scan_piece_states_kernel<N_, true>), grid, block, 0, s, a);             \
+            launch_kernel((scan_piece_states_kernel<N_, true>), grid, block, 0, s, a);             \
         else                                                                                            \
-            hipLaunchKernelGGL((scan_piece_states_kernel<N_, false>), grid, block, 0, s, a);            \
+            launch_kernel((scan_piece_states_kernel<N_, false>), grid, block, 0, s, a);            \
         return true;
     switch (a.nstate) {
         SSM_PIECE_CASE(32)

@@ -798,18 +798,18 @@ int ssd_plan(const ssm_ssd_dims* d, SsdPlan* pl) {
 
 template <int N, bool VEC>
 int ssd_launch(const SsdParams& p, const SsdPlan& pl, hipStream_t s) {
-    hipLaunchKernelGGL((ssd_gram_kernel<N, VEC>), dim3(unsigned(pl.bh_total / p.nheads * pl.nchunks)), dim3(kThreads),
+    launch_kernel((ssd_gram_kernel<N, VEC>), dim3(unsigned(pl.bh_total / p.nheads * pl.nchunks)), dim3(kThreads),
                        size_t(2 * N * kRow * 2), s, p);
     if (pl.nseg > 1) {
-        hipLaunchKernelGGL((ssd_state_kernel<N, VEC>), dim3(unsigned((pl.nseg - 1) * pl.bh_total)), dim3(kThreads),
+        launch_kernel((ssd_state_kernel<N, VEC>), dim3(unsigned((pl.nseg - 1) * pl.bh_total)), dim3(kThreads),
                            StateLds<N>::bytes, s, p);
     }
     const dim3 grid(unsigned(pl.nseg * pl.bh_total));
     if (p.z)
-        hipLaunchKernelGGL((ssd_out_kernel<N, VEC, true>), grid, dim3(kThreads), OutLds<N>::bytes, s, p);
+        launch_kernel((ssd_out_kernel<N, VEC, true>), grid, dim3(kThreads), OutLds<N>::bytes, s, p);
     else
-        hipLaunchKernelGGL((ssd_out_kernel<N, VEC, false>), grid, dim3(kThreads), OutLds<N>::bytes, s, p);
-    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+        launch_kernel((ssd_out_kernel<N, VEC, false>), grid, dim3(kThreads), OutLds<N>::bytes, s, p);
+    return ssm_detail::launch_error == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 }  // namespace
@@ -896,7 +896,7 @@ extern "C" SSM_API int ssm_ssd_fwd(const void* u, const void* delta, const float
     bool vec = L % 8 == 0;
     for (const void* q : {u, B, C, z, static_cast<const void*>(y)}) vec = vec && !misaligned(q, 16);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();   // drop an error left by the caller's earlier HIP calls: only this call's launches are reported
+    ssm_detail::launch_error = hipSuccess;   // this call's launch failures only (the caller's pending HIP error is left alone)
     if (N == 128) return vec ? ssd_launch<128, true>(p, pl, s) : ssd_launch<128, false>(p, pl, s);
     return vec ? ssd_launch<64, true>(p, pl, s) : ssd_launch<64, false>(p, pl, s);
 }

@@ -457,3 +457,17 @@ def test_ssd_workspace_sizes():
     assert _ssd_call(d, u=FAKE + 0x800000 + 4096) == ssm.SSM_ERR_ALIAS
     assert _ssd_call(d, y=FAKE + 0x800000 + 256) == ssm.SSM_ERR_ALIAS
     assert _ssd_call(d, h_last=FAKE + 0x800000) == ssm.SSM_ERR_ALIAS
+
+
+def test_workspace_overlapping_an_input_is_refused():
+    """The carry passes write the workspace before the full pass reads the inputs, so a
+    workspace over any input (or output) is refused before anything is enqueued."""
+    dims = small_dims(seqlen=4096, dstate=16, io_dtype=ssm.SSM_BF16, nchunks=4)
+    need = ssm.ssm_selective_scan_workspace_bytes(dims)
+    for where in (FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000):
+        dims.workspace, dims.workspace_bytes = where, need        # over u, delta, A, B, C, y
+        assert _call(dims) == ssm.SSM_ERR_ALIAS, hex(where)
+    dims.workspace = FAKE + 0x600000                               # over D
+    assert _call(dims, D=FAKE + 0x600000 + 256) == ssm.SSM_ERR_ALIAS
+    assert _call(dims, z=FAKE + 0x600000 - 64) == ssm.SSM_ERR_ALIAS
+    assert _call(dims, bias=FAKE + 0x600000) == ssm.SSM_ERR_ALIAS
