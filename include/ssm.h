@@ -75,7 +75,9 @@ typedef enum ssm_status {
     SSM_ERR_ALIGN = -5,     /* an array is not aligned to its element size */
     SSM_ERR_WORKSPACE = -6, /* workspace missing, too small or not 256-byte aligned */
     SSM_ERR_HIP = -7,       /* the HIP runtime reported an error when enqueuing */
-    SSM_ERR_ALIAS = -8      /* an output or the workspace overlaps an input or another output */
+    SSM_ERR_ALIAS = -8,     /* an output or the workspace overlaps an input or another output */
+    SSM_ERR_DEVICE = -9,    /* ssm_selective_scan_fwd_noalloc: the stream is not the current device's */
+    SSM_ERR_SCRATCH = -10   /* ssm_selective_scan_fwd_noalloc: the call needs more scratch than it holds */
 } ssm_status;
 
 typedef enum ssm_dtype {
@@ -277,6 +279,33 @@ SSM_API int ssm_selective_scan_bwd_ckpt(const void* u, const void* delta, const 
                                         const void* C, const float* D, const void* z, const float* dt_bias,
                                         const float* h0, const void* dy, const float* dh_last, const float* ckpt,
                                         const ssm_grads* grads, const ssm_dims* dims, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * The forward pass for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as ssm_selective_scan_fwd_state, except that the carries between the pieces
+ * of a sequence live in a scratch array inside the library instead of a caller
+ * workspace (dims->workspace and dims->workspace_bytes are ignored).  The call
+ * itself allocates nothing and calls no allocating routine.
+ *
+ * The scratch is a fixed SSM_NOALLOC_SCRATCH_BYTES per device, held from the moment
+ * the library is loaded on that device until the process ends.  A call whose pieces
+ * need more (ssm_selective_scan_workspace_bytes(dims) > SSM_NOALLOC_SCRATCH_BYTES)
+ * is refused with SSM_ERR_SCRATCH before anything is enqueued.  Nothing in the
+ * scratch needs to start at zero: every call writes each carry before it reads it.
+ * Every call on a device shares that device's scratch, so calls that may overlap in
+ * time on one device (on different streams, or from different threads) race and
+ * must be serialised by the caller.  The stream must belong to the current device
+ * (else SSM_ERR_DEVICE); the scratch's device address is looked up once per device
+ * on its first call that needs pieces.  y and h_last are bitwise those of
+ * ssm_selective_scan_fwd_state with a workspace.  Other rules as
+ * ssm_selective_scan_fwd_state. */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+SSM_API size_t ssm_selective_scan_noalloc_scratch_bytes(void);
+SSM_API int ssm_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                                           const void* C, const float* D, const void* z, const float* dt_bias,
+                                           const float* h0, void* y, float* h_last, const ssm_dims* dims,
+                                           void* stream);
 
 /* Static English text for a status value. */
 SSM_API const char* ssm_status_string(int status);

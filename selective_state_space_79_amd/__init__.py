@@ -29,6 +29,8 @@ SSM_ERR_ALIGN = -5
 SSM_ERR_WORKSPACE = -6
 SSM_ERR_HIP = -7
 SSM_ERR_ALIAS = -8
+SSM_ERR_DEVICE = -9
+SSM_ERR_SCRATCH = -10
 SSM_F32 = 0
 SSM_BF16 = 1
 SSM_MAX_DSTATE = 256
@@ -39,7 +41,8 @@ EXPORTED = ("ssm_selective_scan_fwd", "ssm_selective_scan_fwd_state", "ssm_selec
             "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd_plan",
             "ssm_selective_scan_fwd_conv", "ssm_selective_scan_step_conv", "ssm_ssd_fwd",
             "ssm_ssd_fwd_workspace_bytes", "ssm_ssd_fwd_plan", "ssm_selective_scan_ckpt_bytes",
-            "ssm_selective_scan_fwd_ckpt", "ssm_selective_scan_bwd_ckpt")
+            "ssm_selective_scan_fwd_ckpt", "ssm_selective_scan_bwd_ckpt", "ssm_selective_scan_fwd_noalloc",
+            "ssm_selective_scan_noalloc_scratch_bytes")
 SSM_MAX_DSTATE_BWD = 128
 
 
@@ -177,6 +180,10 @@ def load_library():
         lib.ssm_selective_scan_fwd_ckpt.restype = ctypes.c_int
         lib.ssm_selective_scan_bwd_ckpt.argtypes = [vp] * 12 + [ctypes.POINTER(SsmGrads), ctypes.POINTER(SsmDims), vp]
         lib.ssm_selective_scan_bwd_ckpt.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd_noalloc.argtypes = [vp] * 11 + [ctypes.POINTER(SsmDims), vp]
+        lib.ssm_selective_scan_fwd_noalloc.restype = ctypes.c_int
+        lib.ssm_selective_scan_noalloc_scratch_bytes.argtypes = []
+        lib.ssm_selective_scan_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.ssm_status_string.argtypes = [ctypes.c_int]
         lib.ssm_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -248,6 +255,24 @@ def ssm_selective_scan_fwd_state(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last
     return int(load_library().ssm_selective_scan_fwd_state(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y),
         _ptr(h_last), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
+def ssm_selective_scan_fwd_noalloc(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, dims: SsmDims,
+                                   stream=None) -> int:
+    """C entry point that allocates nothing: ssm_selective_scan_fwd_state with the
+    carries between pieces in the library's own per-device scratch (dims' workspace
+    fields are ignored)."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device)
+    return int(load_library().ssm_selective_scan_fwd_noalloc(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y),
+        _ptr(h_last), ctypes.byref(dims), ctypes.c_void_p(stream.cuda_stream)))
+
+
+def ssm_selective_scan_noalloc_scratch_bytes() -> int:
+    return int(load_library().ssm_selective_scan_noalloc_scratch_bytes())
 
 
 def ssm_selective_scan_ckpt_bytes(dims: SsmDims) -> int:

@@ -37,6 +37,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "ssm.h"
@@ -1292,6 +1293,8 @@ const char* ssm_status_string(int status) {
         case SSM_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case SSM_ERR_HIP: return "the HIP runtime reported an error";
         case SSM_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";
+        case SSM_ERR_DEVICE: return "the stream belongs to a device other than the current one";
+        case SSM_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }
@@ -1496,6 +1499,71 @@ int ssm_selective_scan_fwd_ckpt(const void* u, const void* delta, const float* A
                     ckpt);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------------ the entry point that allocates nothing
+// For callers that cannot allocate device memory (code under graph capture, tight
+// serving loops): the carries between the pieces of a sequence live in this
+// file-scope array instead of a caller workspace.  Each device holds its own copy,
+// from the moment the library's code object is loaded until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SSM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of `scratch` on the current device, which must be the device of
+// `stream` (a NULL stream is the current device's).
+int scratch_address(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSM_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return SSM_ERR_HIP;
+        if (int(sdev) != dev) return SSM_ERR_DEVICE;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return SSM_ERR_HIP;
+    *out = g_scratch_ptr[dev];
+    return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_selective_scan_noalloc_scratch_bytes(void) { return SSM_NOALLOC_SCRATCH_BYTES; }
+
+int ssm_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                   const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
+                                   float* h_last, const ssm_dims* dims, void* stream) {
+    if (!dims) return SSM_ERR_NULL;
+    Plan pl;
+    const int st = make_plan(dims, &pl);
+    if (st != SSM_OK) return st;
+    if (pl.ws_bytes > SSM_NOALLOC_SCRATCH_BYTES) return SSM_ERR_SCRATCH;
+    ssm_dims d = *dims;   // the caller's workspace fields are ignored
+    d.workspace = nullptr;
+    d.workspace_bytes = 0;
+    if (pl.ws_bytes > 0) {
+        void* ptr = nullptr;
+        const int sst = scratch_address(static_cast<hipStream_t>(stream), &ptr);
+        if (sst != SSM_OK) return sst;
+        d.workspace = ptr;
+        d.workspace_bytes = SSM_NOALLOC_SCRATCH_BYTES;
+    }
+    return fwd_impl(u, delta, A, B, C, D, z, dt_bias, h0, y, h_last, &d, stream, nullptr, nullptr, nullptr);
+}
 
 }  // extern "C"
 

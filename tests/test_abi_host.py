@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(-8, 1):
+    for st in range(-10, 1):
         s = ssm.ssm_status_string(st)
         assert isinstance(s, str) and s and s != "unknown status"
     assert ssm.ssm_status_string(-99) == "unknown status"
@@ -471,3 +471,26 @@ def test_workspace_overlapping_an_input_is_refused():
     assert _call(dims, D=FAKE + 0x600000 + 256) == ssm.SSM_ERR_ALIAS
     assert _call(dims, z=FAKE + 0x600000 - 64) == ssm.SSM_ERR_ALIAS
     assert _call(dims, bias=FAKE + 0x600000) == ssm.SSM_ERR_ALIAS
+
+
+def test_noalloc_entry_refuses_before_touching_the_device():
+    """The entry point that allocates nothing refuses, before any HIP call, a call whose
+    pieces need more than its fixed scratch, and the usual invalid dims."""
+    lib = ssm.load_library()
+    assert ssm.ssm_selective_scan_noalloc_scratch_bytes() == 64 << 20
+    vp = lambda a: None if a is None else ctypes.c_void_p(a)
+
+    def call(dims, u=FAKE):
+        return lib.ssm_selective_scan_fwd_noalloc(vp(u), vp(FAKE + 0x100000), vp(FAKE + 0x200000),
+                                                  vp(FAKE + 0x300000), vp(FAKE + 0x400000), None, None, None, None,
+                                                  vp(FAKE + 0x500000), None,
+                                                  ctypes.byref(dims) if dims is not None else None, None)
+
+    assert call(None) == ssm.SSM_ERR_NULL
+    assert call(small_dims(seqlen=0)) == ssm.SSM_ERR_EMPTY
+    # 1024 groups of 64 channels x 16 pieces x 16 states: 1024*16*64*4*(2*16+1) bytes of carries
+    big = ssm.make_dims(16, 512, 4096, 16, nchunks=16)
+    need = ssm.ssm_selective_scan_workspace_bytes(big)
+    assert need > ssm.ssm_selective_scan_noalloc_scratch_bytes()
+    assert call(big) == ssm.SSM_ERR_SCRATCH
+    assert "scratch" in ssm.ssm_status_string(ssm.SSM_ERR_SCRATCH)
