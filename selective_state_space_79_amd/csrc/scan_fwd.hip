@@ -88,19 +88,39 @@ constexpr int kCkptSteps = 16;   // steps between state checkpoints
 enum Mode { kFull = 0, kAggregate = 1 };
 constexpr int kMaxConv = 4;   // widest fused convolution: its history fits one 4-element halo
 
-// LDS layout of one tile buffer (floats); rows of 64 channels are padded to kRow or
-// kRowY entries so that the staging writes and epilogue reads, whose lanes span 4
-// time steps of 16 channels, fall in distinct banks:
+// LDS layout of one tile buffer (floats):
 //   sDX [T][kRow] float2  per (step, channel): (dt2, dt2*u), or (exp(dt*a_h), dt2*u) in
-//                         scalar-decay full mode
+//                         scalar-decay full mode; rows padded to kRow so that the
+//                         staging writes, whose lanes span several steps of a few
+//                         channels, fall in distinct banks
 //   sBC [G][T][2*SPL]     per (wave, step): B*ln2 of the wave's SPL state entries, then C
-//   sY  [G][T][kRowY]     per (wave, step, channel): partial read-out      } full
-//   sSk [T][kRowY]        per (step, channel): skip term D*u               } mode
-//   sGt [T][kRowY]        per (step, channel): gate SiLU(z), or 1 without z } only
+// then, in full mode, the partial read-outs, in one of two layouts:
+//   * four walkers of at most 4 entries (two waves per SIMD: yswizzled):
+//     sY [T][G][64]       per (step, wave, channel).  Channel c of step t sits in column
+//                         c ^ ysw(t), a permutation of the 64 columns per step, so that
+//                         the walkers' row writes and the finishing lanes' reads (several
+//                         steps of a few channels) each touch 64 distinct banks, and every
+//                         row is 256 bytes, so a finishing thread's reads take immediate
+//                         offsets from one address.  The skip terms D*u and gates SiLU(z)
+//                         stay in the staging thread's registers until it finishes the
+//                         same elements.
+//   * otherwise, rows padded to kRowY for distinct banks:
+//     sY  [G][T][kRowY]   per (wave, step, channel): partial read-out
+//     sSk [T][kRowY]      per (step, channel): skip term D*u
+//     sGt [T][kRowY]      per (step, channel): gate SiLU(z), or 1 without z
 constexpr int kRow = kLanes + 1;
 constexpr int kRowY = kLanes + 2;
+__host__ __device__ constexpr bool yswizzled(int G, int spl) { return G == 4 && spl <= 4; }
 inline size_t lds_floats(int T, int G, int np, bool full) {
-    return size_t(T) * kRow * 2 + 2 * size_t(T) * np + (full ? size_t(G + 2) * T * kRowY : 0);
+    const size_t out = yswizzled(G, np / G) ? size_t(G) * T * kLanes : size_t(G + 2) * T * kRowY;
+    return size_t(T) * kRow * 2 + 2 * size_t(T) * np + (full ? out : 0);
+}
+
+// Column swizzle of the swizzled sY: steps t of one 16-byte vector (VW steps) share a
+// value, and the TV vectors of a tile take distinct multiples of 64 / TV.
+template <int T, int VW>
+__host__ __device__ constexpr int ysw(int t) {
+    return ((t / VW) % (T / VW)) * (kLanes / (T / VW));
 }
 
 template <int SPL> struct BCVec { float v[2 * SPL]; };
@@ -124,6 +144,25 @@ __device__ inline BCVec<SPL> read_bc(const float* __restrict__ q) {
     }
     return r;
 }
+
+// Raw buffer windows.  A workgroup addresses each array through a window: a
+// workgroup-uniform base, the first byte of the rows it reads (the block's 64 channel
+// rows, or the batch row's dstate rows of B or C), and their size in bytes, below 2^31
+// (the host takes this path only then), both in scalar registers.  A tile's accesses
+// take the window advanced to the tile's first step and a 32-bit lane offset fixed for
+// the whole piece; an access at or past the window's end -- every lane offset kOob --
+// reads zeros or is dropped.  Word 3 of the descriptor selects 32-bit data, untyped.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((ext_vector_type(4))) unsigned int bvec4;
+constexpr uint32_t kOob = 0x80000000u;
+struct Window {
+    const char* base;
+    uint32_t bytes;
+    // the window from `off` bytes on (off < bytes)
+    __device__ Rsrc at(uint32_t off) const {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0, int(bytes - off), 0x00020000);
+    }
+};
 
 // Kernel shape, by the number G of waves that walk (4, 8 or 16):
 //   G <= 8: 4 more "helper" waves stage tile k+1 and finish tile k-1 while the G
@@ -169,22 +208,32 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     constexpr bool kFullMode = (MODE == kFull);
     constexpr int BCW = 2 * SPL;                   // floats per (wave, step) in sBC
     constexpr int NBC = G * T * BCW;               // sBC values per tile
-    // B/C staging, two ways.  Small tiles: one sBC value per thread and pass, a
-    // wave's 64 lanes covering 64/BCW steps x BCW slots (64 distinct LDS banks per
-    // write).  Large tiles (more than 8 values per thread): 16-byte row vectors of B
-    // and C, each thread writing its vector's values down one sBC column.
+    // B/C staging, two ways.  Small tiles: single values, the first half of the staging
+    // threads taking B's and the second half C's (wave-uniform, so each load's buffer
+    // window stays in scalar registers).  Large tiles (more than 8 values per thread):
+    // 16-byte row vectors of B and C, each thread writing its vector's values down one
+    // sBC column.
     constexpr int KBC = (NBC + NS - 1) / NS;       // values per staging thread
     constexpr bool kVecBC = KBC > 8;
     constexpr int NBV = 2 * NP_ * TV;              // B and C row vectors per tile
     constexpr int KBV = kVecBC ? (NBV + NS - 1) / NS : 0;   // of them per staging thread
-    constexpr int KBE = kVecBC ? 0 : KBC;
+    constexpr int NBH = NBC / 2;                   // sBC values of one matrix per tile
+    constexpr int KBE = kVecBC ? 0 : (VEC ? (NBH + NS / 2 - 1) / (NS / 2) : KBC);
     constexpr int QB = SPL <= 4 ? 4 : (SPL == 8 ? 2 : 1);   // steps whose LDS operands are read together
     constexpr int NP = NP_;                        // padded state count
     constexpr float kLn2f = kLn2;
-    constexpr int BUF = T * kRow * 2 + NBC + (kFullMode ? (G + 2) * T * kRowY : 0);   // floats per buffer
+    // Two LDS layouts of the read-out (see lds_floats).  With four walkers of at most
+    // 4 entries and four helpers (two waves per SIMD, the N <= 16 shapes) the partial
+    // read-outs sit in swizzled 64-float rows and the skip terms and gates stay in the
+    // helper's registers; otherwise padded rows and LDS for all three.
+    constexpr bool kSGReg = yswizzled(G, SPL);
+    constexpr int BUF = T * kRow * 2 + NBC + (kFullMode ? (kSGReg ? G * T * kLanes : (G + 2) * T * kRowY) : 0);   // floats per buffer
+    constexpr int kEsz = int(sizeof(IO));
     static_assert(T % 8 == 0, "time tile must hold whole vectors and step groups");
     static_assert(!CK || (MODE == kFull && NP_ == 16 && T % kCkptSteps == 0 && kCkptSteps % QB == 0),
                   "checkpoints: full mode, 16 padded entries, whole checkpoint intervals per tile");
+    static_assert(!kVecBC || (NP * TV) % kLanes == 0, "B/C row vectors: whole waves per matrix");
+    static_assert(NS % (2 * kLanes) == 0, "B/C single values: whole waves per matrix");
 
     extern __shared__ float smem[];
     const int tid = threadIdx.x;
@@ -213,6 +262,20 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     const IO* __restrict__ gC = static_cast<const IO*>(p.Cm);
     IO* __restrict__ gy = static_cast<IO*>(p.y);
 
+    // ---- buffer windows (rows of 16-byte vectors): the block's channel rows of u, delta,
+    //      z and y, and the batch row's N rows of B and C
+    const int64_t xoff = (int64_t(b) * p.dim + c0) * p.L * kEsz;
+    const int64_t xrows = p.dim - c0 < kLanes ? p.dim - c0 : kLanes;
+    const uint32_t xbytes = VEC ? uint32_t(xrows * p.L * kEsz) : 0u;
+    const int64_t bcoff = int64_t(b) * p.N * p.L * kEsz;
+    const uint32_t bcbytes = VEC ? uint32_t(p.N * p.L * kEsz) : 0u;
+    const Window win_u{reinterpret_cast<const char*>(p.u) + xoff, xbytes};
+    const Window win_dl{reinterpret_cast<const char*>(p.delta) + xoff, xbytes};
+    const Window win_z{reinterpret_cast<const char*>(has_z ? p.z : p.u) + xoff, xbytes};
+    const Window win_y{reinterpret_cast<const char*>(p.y) + xoff, xbytes};
+    const Window win_B{reinterpret_cast<const char*>(p.Bm) + bcoff, bcbytes};
+    const Window win_C{reinterpret_cast<const char*>(kFullMode ? p.Cm : p.Bm) + bcoff, bcbytes};
+
     // ---- walk constants: this lane's channel and its SPL decay rates
     const int64_t dch = c0 + lane;
     const bool lane_ok = walker && dch < p.dim;
@@ -235,6 +298,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     bool sv_on[KX], sv_ok[KX];
     float sv_bias[KX], sv_skip[KX], sv_ah[KX];
     int64_t sv_row[KX];
+    uint32_t sv_voff[KX];   // byte offset of the vector in the block's window (kOob: none)
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
         const int v = stid + k * NS;
@@ -248,6 +312,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
         sv_ah[k] = 0.0f;
         if constexpr (SCALAR) sv_ah[k] = sv_ok[k] ? p.A[d / p.head_dim] : 0.0f;
         sv_row[k] = (int64_t(b) * p.dim + (sv_ok[k] ? d : 0)) * p.L;
+        sv_voff[k] = sv_ok[k] ? uint32_t((int64_t(sv_ch[k]) * p.L + sv_tv[k] * VW) * kEsz) : kOob;
     }
     // ---- fused convolution: tap j of a vector's halo-extended window multiplies
     //      x[t - 3 + j] (taps before the first weight are 0)
@@ -271,6 +336,7 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     const IO* bc_row[KBV > 0 ? KBV : 1];
     int bc_dst[KBV > 0 ? KBV : 1], bc_tv[KBV > 0 ? KBV : 1];
     bool bc_on[KBV > 0 ? KBV : 1], bc_ok[KBV > 0 ? KBV : 1], bc_isC[KBV > 0 ? KBV : 1];
+    uint32_t bc_voff[KBV > 0 ? KBV : 1];
 #pragma unroll
     for (int k = 0; k < KBV; ++k) {
         const int v = stid + k * NS;
@@ -283,21 +349,40 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
         bc_ok[k] = bc_on[k] && n < p.N && (kFullMode || !isC);
         bc_row[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bc_ok[k] ? n : 0)) * p.L;
         bc_dst[k] = (n / SPL) * T * BCW + (n % SPL) + (isC ? SPL : 0);
+        bc_voff[k] = bc_ok[k] ? uint32_t((int64_t(n) * p.L + bc_tv[k] * VW) * kEsz) : kOob;
     }
 
+    // single B/C values.  With buffer loads (VEC) staging threads stid < NS/2 take B's and
+    // the others C's (value i of a matrix is entry n = (i / (T*SPL)) * SPL + i % SPL at
+    // step (i / SPL) % T), so that each wave reads one matrix through one window; with
+    // element loads, value idx = stid + k*NS of the tile's sBC, B or C by its slot.
     const IO* bce_ptr[KBE > 0 ? KBE : 1];
     int bce_t[KBE > 0 ? KBE : 1];
     bool bce_on[KBE > 0 ? KBE : 1];
+    uint32_t bce_voff[KBE > 0 ? KBE : 1];
+    int bce_dst[VEC && KBE > 0 ? KBE : 1];
+    const bool bce_isC = VEC && stid >= NS / 2;
+    const int bce_i0 = bce_isC ? stid - NS / 2 : stid;
 #pragma unroll
     for (int k = 0; k < KBE; ++k) {
-        const int idx = stid + k * NS;
-        const int wn = idx / (T * BCW), rem = idx % (T * BCW);
-        const int t = rem / BCW, slot = rem % BCW;
-        const int64_t n = int64_t(wn) * SPL + (slot % SPL);
-        const bool isC = slot >= SPL;
-        bce_on[k] = stager && idx >= 0 && idx < NBC && n < p.N && (kFullMode || !isC);
-        bce_t[k] = t;
-        bce_ptr[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bce_on[k] ? n : 0)) * p.L + t;
+        if constexpr (VEC) {
+            const int i = bce_i0 + k * (NS / 2);
+            const int wn = i / (T * SPL), j = i % SPL, t = (i / SPL) % T;
+            const int64_t n = int64_t(wn) * SPL + j;
+            bce_on[k] = stager && i < NBH && n < p.N && (kFullMode || !bce_isC);
+            bce_t[k] = t;
+            bce_dst[k] = (wn * T + t) * BCW + j + (bce_isC ? SPL : 0);
+            bce_voff[k] = bce_on[k] ? uint32_t((n * p.L + t) * kEsz) : kOob;
+        } else {
+            const int idx = stid + k * NS;
+            const int wn = idx / (T * BCW), rem = idx % (T * BCW);
+            const int t = rem / BCW, slot = rem % BCW;
+            const int64_t n = int64_t(wn) * SPL + (slot % SPL);
+            const bool isC = slot >= SPL;
+            bce_on[k] = stager && idx >= 0 && idx < NBC && n < p.N && (kFullMode || !isC);
+            bce_t[k] = t;
+            bce_ptr[k] = (isC ? gC : gB) + (int64_t(b) * p.N + (bce_on[k] ? n : 0)) * p.L + t;
+        }
     }
 
     // ---- starting state of this piece
@@ -327,19 +412,75 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
     Vec<IO> nu[KX], ndl[KX], nz[KX], nbc[KBV > 0 ? KBV : 1];
     IO nbce[KBE > 0 ? KBE : 1];
     IO nhalo[KX][kMaxConv];   // fused convolution: x[t-4 .. t-1] before each vector
+    // the skip term D*u and the gate SiLU(z) of the elements a thread stages, kept until
+    // it finishes them: slot (tile index & 1) with helper waves, slot 0 without
+    float skr[kSGReg && kSpec ? 2 : 1][KX][VW], gtr[kSGReg && kSpec ? 2 : 1][KX][VW];
 
-    // ---- global -> registers for the tile starting at t0 (staging threads)
-    auto issue_loads = [&](int64_t t0) {
+    // ---- global -> registers for the tile starting at t0 (staging threads).  With
+    //      16-byte rows (VEC) every load goes through a buffer window advanced to the
+    //      tile (scalar arithmetic only) at a fixed lane offset: no address arithmetic
+    //      and no bounds checks in the vector unit; reads past the array return zeros,
+    //      and values past the piece's end are masked where they are staged.
+    auto issue_loads = [&](int64_t t0) __attribute__((always_inline)) {
+        if constexpr (VEC) {
+            const uint32_t toff = uint32_t(t0) * kEsz;
+            const Rsrc ru = win_u.at(toff), rd = win_dl.at(toff), rz = win_z.at(toff);
 #pragma unroll
-        for (int k = 0; k < KX; ++k) {
-            if (sv_on[k]) {
-                const int64_t t = t0 + sv_tv[k] * VW;
-                nu[k] = load_vec<IO, VEC>(gu + sv_row[k], t, tend, sv_ok[k]);
-                ndl[k] = load_vec<IO, VEC>(gdl + sv_row[k], t, tend, sv_ok[k]);
-                if (has_z) nz[k] = load_vec<IO, VEC>(gz + sv_row[k], t, tend, sv_ok[k]);
-                if (conv) {
+            for (int k = 0; k < KX; ++k) {
+                if (NVX % NS == 0 || sv_on[k]) {
+                    nu[k] = __builtin_bit_cast(Vec<IO>, __builtin_amdgcn_raw_buffer_load_b128(ru, sv_voff[k], 0, 0));
+                    ndl[k] = __builtin_bit_cast(Vec<IO>, __builtin_amdgcn_raw_buffer_load_b128(rd, sv_voff[k], 0, 0));
+                    if (has_z)
+                        nz[k] = __builtin_bit_cast(Vec<IO>, __builtin_amdgcn_raw_buffer_load_b128(rz, sv_voff[k], 0, 0));
+                }
+            }
+            if constexpr (KBV > 0) {
+                const Rsrc rb = win_B.at(toff), rc = win_C.at(toff);
+#pragma unroll
+                for (int k = 0; k < KBV; ++k) {
+                    // B or C is the same for a whole wave (whole waves per matrix)
+                    const bool isC = __builtin_amdgcn_readfirstlane(int(bc_isC[k])) != 0;
+                    nbc[k] = __builtin_bit_cast(
+                        Vec<IO>, __builtin_amdgcn_raw_buffer_load_b128(isC ? rc : rb, bc_voff[k], 0, 0));
+                }
+            }
+            if constexpr (KBE > 0) {
+                // B or C is the same for a whole wave: read the choice from the first lane so
+                // that the window stays in scalar registers
+                const bool isC = __builtin_amdgcn_readfirstlane(int(bce_isC)) != 0;
+                const Rsrc rbc = isC ? win_C.at(toff) : win_B.at(toff);
+#pragma unroll
+                for (int k = 0; k < KBE; ++k) {
+                    if constexpr (sizeof(IO) == 2)
+                        nbce[k] = __builtin_bit_cast(IO, __builtin_amdgcn_raw_buffer_load_b16(rbc, bce_voff[k], 0, 0));
+                    else
+                        nbce[k] = __builtin_bit_cast(IO, __builtin_amdgcn_raw_buffer_load_b32(rbc, bce_voff[k], 0, 0));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KX; ++k) {
+                if (sv_on[k]) {
+                    const int64_t t = t0 + sv_tv[k] * VW;
+                    nu[k] = load_vec<IO, VEC>(gu + sv_row[k], t, tend, sv_ok[k]);
+                    ndl[k] = load_vec<IO, VEC>(gdl + sv_row[k], t, tend, sv_ok[k]);
+                    if (has_z) nz[k] = load_vec<IO, VEC>(gz + sv_row[k], t, tend, sv_ok[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < KBV; ++k)
+                if (bc_on[k]) nbc[k] = load_vec<IO, VEC>(bc_row[k], t0 + bc_tv[k] * VW, tend, bc_ok[k]);
+#pragma unroll
+            for (int k = 0; k < KBE; ++k)
+                nbce[k] = (bce_on[k] && t0 + bce_t[k] < tend) ? bce_ptr[k][t0] : IO(0);
+        }
+        if constexpr (conv) {
+#pragma unroll
+            for (int k = 0; k < KX; ++k) {
+                if (sv_on[k]) {
                     // the 4 inputs before the vector (t is a multiple of the vector width,
                     // so t >= 4 unless t == 0, whose history stage takes from conv_state)
+                    const int64_t t = t0 + sv_tv[k] * VW;
                     const IO* src = gu + sv_row[k] + (t >= kMaxConv ? t - kMaxConv : 0);
                     if constexpr (VEC) {
                         using R = typename std::conditional<sizeof(IO) == 2, uint2, uint4>::type;
@@ -352,21 +493,15 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
                 }
             }
         }
-#pragma unroll
-        for (int k = 0; k < KBV; ++k)
-            if (bc_on[k]) nbc[k] = load_vec<IO, VEC>(bc_row[k], t0 + bc_tv[k] * VW, tend, bc_ok[k]);
-#pragma unroll
-        for (int k = 0; k < KBE; ++k)
-            nbce[k] = (bce_on[k] && t0 + bce_t[k] < tend) ? bce_ptr[k][t0] : IO(0);
     };
 
     // ---- registers -> LDS buffer `buf` for the tile starting at t0 (staging threads):
-    //      per element (dt2, dt2*u) or (exp(dt*a_h), dt2*u); B*ln2 and C
-    auto stage = [&](float* buf, int64_t t0) {
+    //      per element (dt2, dt2*u) or (exp(dt*a_h), dt2*u); B*ln2 and C; the skip term
+    //      and gate into register slot SL
+    auto stage = [&](float* buf, int64_t t0, auto slot) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot)::value;
         float2* sDX = reinterpret_cast<float2*>(buf);
         float* sBC = buf + T * kRow * 2;
-        float* sSk = sBC + NBC + G * T * kRowY;
-        float* sGt = sSk + T * kRowY;
         const bool full_tile = t0 + T <= tend;
         float uval[KX][VW];   // the scan's input u of each vector element
 #pragma unroll
@@ -405,22 +540,32 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
                 }
             }
         }
-        auto elem = [&](int k, int e, bool in) {
-            const float uu = uval[k][e];
+        // element e of vector k: `in` = inside the piece and the channels; outside, the
+        // step is an identity step (dt2 = 0, x = 0) whatever the loaded values were
+        auto elem = [&](int k, int e, bool in) __attribute__((always_inline)) {
+            // (element loads already read zeros outside; buffer loads read what is there)
+            const float uu = (!VEC || in) ? uval[k][e] : 0.0f;
             const float dt2 = in ? softplus_log2(IOT<IO>::to_f32(ndl[k].e[e]) + sv_bias[k]) : 0.0f;
             float first = dt2;
             if constexpr (SCALAR && kFullMode) first = __builtin_amdgcn_exp2f(dt2 * sv_ah[k]);
             const int tl = sv_tv[k] * VW + e;
             sDX[tl * kRow + sv_ch[k]] = make_float2(first, dt2 * uu);
             if constexpr (kFullMode) {
-                sSk[tl * kRowY + sv_ch[k]] = sv_skip[k] * uu;
-                const float g = silu_f32(IOT<IO>::to_f32(nz[k].e[e]));
-                sGt[tl * kRowY + sv_ch[k]] = has_z ? g : 1.0f;
+                const float sk = sv_skip[k] * uu;
+                const float gt = has_z ? silu_f32(IOT<IO>::to_f32(nz[k].e[e])) : 1.0f;
+                if constexpr (kSGReg) {
+                    skr[SL][k][e] = sk;
+                    gtr[SL][k][e] = gt;
+                } else {
+                    float* sSk = buf + T * kRow * 2 + NBC + G * T * kRowY;
+                    sSk[tl * kRowY + sv_ch[k]] = sk;
+                    sSk[(T + tl) * kRowY + sv_ch[k]] = gt;
+                }
             }
         };
 #pragma unroll
         for (int k = 0; k < KX; ++k) {
-            if (sv_on[k]) {
+            if (NVX % NS == 0 || sv_on[k]) {
                 if (full_tile && sv_ok[k]) {
 #pragma unroll
                     for (int e = 0; e < VW; ++e) elem(k, e, true);
@@ -431,29 +576,51 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
                 }
             }
         }
+        // steps of this tile inside the piece (a workgroup-uniform count)
+        const int tin = full_tile ? T : int(tend - t0);
 #pragma unroll
         for (int k = 0; k < KBV; ++k) {
             if (bc_on[k]) {
                 const float sc = bc_isC[k] ? 1.0f : kLn2f;
                 float* dst = sBC + bc_dst[k] + bc_tv[k] * VW * BCW;
+                if (!VEC || full_tile) {
 #pragma unroll
-                for (int e = 0; e < VW; ++e) dst[e * BCW] = IOT<IO>::to_f32(nbc[k].e[e]) * sc;
+                    for (int e = 0; e < VW; ++e) dst[e * BCW] = IOT<IO>::to_f32(nbc[k].e[e]) * sc;
+                } else {
+                    const int lim = tin - bc_tv[k] * VW;
+#pragma unroll
+                    for (int e = 0; e < VW; ++e) dst[e * BCW] = e < lim ? IOT<IO>::to_f32(nbc[k].e[e]) * sc : 0.0f;
+                }
             }
         }
 #pragma unroll
         for (int k = 0; k < KBE; ++k) {
-            const int idx = stid + k * NS;
-            if (stager && (NBC % NS == 0 || idx < NBC))
-                sBC[idx] = IOT<IO>::to_f32(nbce[k]) * ((idx % BCW) < SPL ? kLn2f : 1.0f);
+            if constexpr (VEC) {
+                if (stager && (NBH % (NS / 2) == 0 || bce_i0 + k * (NS / 2) < NBH)) {
+                    const float v = IOT<IO>::to_f32(nbce[k]) * (bce_isC ? 1.0f : kLn2f);
+                    if (full_tile)
+                        sBC[bce_dst[k]] = v;
+                    else
+                        sBC[bce_dst[k]] = bce_t[k] < tin ? v : 0.0f;
+                }
+            } else {
+                const int idx = stid + k * NS;
+                if (stager && (NBC % NS == 0 || idx < NBC))
+                    sBC[idx] = IOT<IO>::to_f32(nbce[k]) * ((idx % BCW) < SPL ? kLn2f : 1.0f);
+            }
         }
     };
 
     // ---- walk one tile from LDS buffer `buf` (walking waves): SPL state entries per
     //      lane, sequential in t; the LDS operands of QB steps are read up front
-    auto walk = [&](float* buf, int64_t t0) {
+    // this lane's sY column for each vector of steps of a tile (see ysw)
+    int ycol[kSGReg ? TV : 1];
+#pragma unroll
+    for (int j = 0; j < (kSGReg ? TV : 1); ++j) ycol[j] = lane ^ ysw<T, VW>(j * VW);
+    auto walk = [&](float* buf, int64_t t0) __attribute__((always_inline)) {
         const float2* dxp = reinterpret_cast<const float2*>(buf) + lane;
         const float* bcp = buf + T * kRow * 2 + w * T * BCW;
-        float* yo = buf + T * kRow * 2 + NBC + w * T * kRowY + lane;
+        float* yo = buf + T * kRow * 2 + NBC + (kSGReg ? w * kLanes : w * T * kRowY + lane);
 #pragma unroll
         for (int t = 0; t < T; t += QB) {
             if constexpr (CK) {
@@ -490,87 +657,166 @@ __global__ void __launch_bounds__((Shape<G, SPL>::NW * kLanes)) scan_fwd_kernel(
                     h[j] = fmaf(a, h[j], dx[q].y * bc[q].v[j]);
                     if constexpr (kFullMode) yp = fmaf(bc[q].v[SPL + j], h[j], yp);
                 }
-                if constexpr (kFullMode) yo[(t + q) * kRowY] = yp;
+                if constexpr (kFullMode) {
+                    if constexpr (kSGReg)
+                        yo[(t + q) * G * kLanes + ycol[(t + q) / VW]] = yp;
+                    else
+                        yo[(t + q) * kRowY] = yp;
+                }
             }
         }
     };
 
     // ---- finish the tile starting at t0 from LDS buffer `buf` (staging threads): sum
-    //      the G partial read-outs in wave order, skip, gate, round, store
+    //      the G partial read-outs in wave order, skip and gate from register slot SL,
+    //      round, store.
     // With bf16 rows and 32-step tiles a tile covers half of each row's 128-byte
     // cache line; the even tile's output is held and stored together with the odd
     // tile's, so both halves of a line reach the L2 back to back and are written to
     // HBM as one full line.
     constexpr bool kPairStores = VEC && (T * int(sizeof(IO)) == 64);
     Vec<IO> held[KX];
-    auto finish = [&](const float* buf, int64_t t0, int kt) {
+    // vector k of this thread's row in the tile starting at tile_t0 (a workgroup-uniform
+    // step, so that the window stays in scalar registers)
+    auto store = [&](int k, int64_t tile_t0, const Vec<IO>& v, bool full_tile) __attribute__((always_inline)) {
+        if constexpr (VEC) {
+            if (full_tile) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(bvec4, v), win_y.at(uint32_t(tile_t0) * kEsz),
+                                                       sv_voff[k], 0, 0);
+                return;
+            }
+        }
+        store_vec<IO, VEC>(gy + sv_row[k], tile_t0 + sv_tv[k] * VW, tend, sv_ok[k], v);
+    };
+    auto finish = [&](const float* buf, int64_t t0, int kt, auto slot) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot)::value;
         if constexpr (kFullMode) {
             const float* sY = buf + T * kRow * 2 + NBC;
-            const float* sSk = sY + G * T * kRowY;
-            const float* sGt = sSk + T * kRowY;
+            const bool full_tile = t0 + T <= tend;
 #pragma unroll
             for (int k = 0; k < KX; ++k) {
-                if (sv_on[k]) {
-                    const int off = (sv_tv[k] * VW) * kRowY + sv_ch[k];
+                if (NVX % NS == 0 || sv_on[k]) {
+                    // steps tv*VW .. +VW-1 of channel ch, summed over the walkers in order
                     float acc[VW];
+                    if constexpr (kSGReg) {
+                        // column ch ^ ysw, rows (t, w)
+                        const float* src = sY + sv_tv[k] * VW * G * kLanes + (sv_ch[k] ^ ysw<T, VW>(sv_tv[k] * VW));
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) acc[e] = sY[off + e * kRowY];
+                        for (int e = 0; e < VW; ++e) acc[e] = src[e * G * kLanes];
 #pragma unroll
-                    for (int ww = 1; ww < G; ++ww)
+                        for (int ww = 1; ww < G; ++ww)
 #pragma unroll
-                        for (int e = 0; e < VW; ++e) acc[e] += sY[off + (ww * T + e) * kRowY];
+                            for (int e = 0; e < VW; ++e) acc[e] += src[(e * G + ww) * kLanes];
+                    } else {
+                        const int off = (sv_tv[k] * VW) * kRowY + sv_ch[k];
+#pragma unroll
+                        for (int e = 0; e < VW; ++e) acc[e] = sY[off + e * kRowY];
+#pragma unroll
+                        for (int ww = 1; ww < G; ++ww)
+#pragma unroll
+                            for (int e = 0; e < VW; ++e) acc[e] += sY[off + (ww * T + e) * kRowY];
+                    }
                     Vec<IO> out;
 #pragma unroll
-                    for (int e = 0; e < VW; ++e)
-                        out.e[e] = IOT<IO>::from_f32((acc[e] + sSk[off + e * kRowY]) * sGt[off + e * kRowY]);
+                    for (int e = 0; e < VW; ++e) {
+                        float sk, gt;
+                        if constexpr (kSGReg) {
+                            sk = skr[SL][k][e];
+                            gt = gtr[SL][k][e];
+                        } else {
+                            const float* sSk = sY + G * T * kRowY;
+                            const int off = (sv_tv[k] * VW + e) * kRowY + sv_ch[k];
+                            sk = sSk[off];
+                            gt = sSk[T * kRowY + off];
+                        }
+                        out.e[e] = IOT<IO>::from_f32((acc[e] + sk) * gt);
+                    }
                     if constexpr (kPairStores) {
                         if ((kt & 1) == 0 && kt + 1 < ntiles) {
                             held[k] = out;            // stored with the next tile's vector
                             continue;
                         }
-                        if (kt & 1) store_vec<IO, VEC>(gy + sv_row[k], t0 - T + sv_tv[k] * VW, tend, sv_ok[k], held[k]);
+                        if (kt & 1) store(k, t0 - T, held[k], true);
                     }
-                    store_vec<IO, VEC>(gy + sv_row[k], t0 + sv_tv[k] * VW, tend, sv_ok[k], out);
+                    store(k, t0, out, full_tile);
                 }
             }
         }
     };
 
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     if constexpr (kSpec) {
         // walkers walk tile kt from buffer kt&1 while the helpers finish tile kt-1
-        // (buffer (kt-1)&1) and then stage tile kt+1 into that same buffer
+        // (buffer (kt-1)&1) and then stage tile kt+1 into that same buffer; tile k's
+        // skip terms and gates are in register slot k&1, so the loop takes two tiles
+        // per turn and every slot index is a compile-time constant
         if (stager) {
             issue_loads(tbeg);
-            stage(smem, tbeg);
+            stage(smem, tbeg, I0{});
             if (ntiles > 1) issue_loads(tbeg + T);
         }
         __syncthreads();
-        for (int kt = 0; kt < ntiles; ++kt) {
-            float* cur = smem + (kt & 1) * BUF;
-            float* oth = smem + ((kt + 1) & 1) * BUF;
+        auto period = [&](int kt, auto par) __attribute__((always_inline)) {
+            constexpr int P = decltype(par)::value;
+            using Other = std::integral_constant<int, 1 - P>;
+            float* cur = smem + P * BUF;
+            float* oth = smem + (1 - P) * BUF;
             const int64_t t0 = tbeg + int64_t(kt) * T;
             if (walker) {
                 walk(cur, t0);
             } else {
-                if (kt >= 1) finish(oth, t0 - T, kt - 1);
+                if (kt >= 1) finish(oth, t0 - T, kt - 1, Other{});
                 if (kt + 1 < ntiles) {
-                    stage(oth, t0 + T);
+                    stage(oth, t0 + T, Other{});
                     if (kt + 2 < ntiles) issue_loads(t0 + 2 * T);
                 }
             }
             __syncthreads();
+        };
+        if constexpr (kSGReg) {
+            for (int kt = 0; kt < ntiles; kt += 2) {
+                period(kt, I0{});
+                if (kt + 1 < ntiles) period(kt + 1, I1{});
+            }
+            if (stager) {
+                const int kl = ntiles - 1;
+                const int64_t tl = tbeg + int64_t(kl) * T;
+                if (kl & 1)
+                    finish(smem + BUF, tl, kl, I1{});
+                else
+                    finish(smem, tl, kl, I0{});
+            }
+        } else {
+            // skip terms and gates in LDS: one tile per turn (a two-tile body would hold
+            // both tiles' walk in registers at three waves per SIMD)
+            for (int kt = 0; kt < ntiles; ++kt) {
+                float* cur = smem + (kt & 1) * BUF;
+                float* oth = smem + ((kt + 1) & 1) * BUF;
+                const int64_t t0 = tbeg + int64_t(kt) * T;
+                if (walker) {
+                    walk(cur, t0);
+                } else {
+                    if (kt >= 1) finish(oth, t0 - T, kt - 1, I0{});
+                    if (kt + 1 < ntiles) {
+                        stage(oth, t0 + T, I0{});
+                        if (kt + 2 < ntiles) issue_loads(t0 + 2 * T);
+                    }
+                }
+                __syncthreads();
+            }
+            if (stager) finish(smem + ((ntiles - 1) & 1) * BUF, tbeg + int64_t(ntiles - 1) * T, ntiles - 1, I0{});
         }
-        if (stager) finish(smem + ((ntiles - 1) & 1) * BUF, tbeg + int64_t(ntiles - 1) * T, ntiles - 1);
     } else {
         issue_loads(tbeg);
         for (int kt = 0; kt < ntiles; ++kt) {
             const int64_t t0 = tbeg + int64_t(kt) * T;
-            stage(smem, t0);
+            stage(smem, t0, I0{});
             if (kt + 1 < ntiles) issue_loads(t0 + T);   // prefetch the next tile
             __syncthreads();
             walk(smem, t0);
             __syncthreads();
-            finish(smem, t0, kt);
+            finish(smem, t0, kt, I0{});
         }
     }
 
@@ -1411,7 +1657,11 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     // row length that is a whole number of vectors
     const size_t vw = 16 / esz;
     auto a16 = [](const void* q) { return !q || (reinterpret_cast<uintptr_t>(q) % 16) == 0; };
-    const bool vec = (dims->seqlen % int64_t(vw)) == 0 && a16(u) && a16(delta) && a16(z) && a16(B) && a16(C) && a16(y);
+    // (the kernels' buffer windows also need a block's 64 rows and a batch row's dstate
+    // rows to span less than 2^31 bytes)
+    const int64_t rows_bytes = (dims->dstate > kLanes ? dims->dstate : kLanes) * dims->seqlen * int64_t(esz);
+    const bool vec = (dims->seqlen % int64_t(vw)) == 0 && a16(u) && a16(delta) && a16(z) && a16(B) && a16(C) &&
+                     a16(y) && rows_bytes < (int64_t(1) << 31);
 
     Params p;
     p.u = u;
