@@ -51,10 +51,14 @@ MIN_WARMUP_S = 0.25
 
 def time_calls(call, steps: int, warmup: int, stream, min_warmup_s: float | None = None):
     """Warm up with at least `warmup` calls and at least `min_warmup_s` seconds, then
-    time exactly `steps` calls, each bracketed by HIP events recorded on `stream` (the
-    stream the kernels are launched on), the whole loop also by the wall clock, with a
-    device synchronisation on both sides.  call(i) launches call number i (i lets the
-    caller rotate input sets).  Returns per-call statistics in milliseconds."""
+    time exactly `steps` calls bracketed by two HIP events recorded on `stream` (the
+    stream the kernels are launched on) and by the wall clock, with a device
+    synchronisation on both sides: the mean per call (`ms_events`, `ms_wall`,
+    `ms_per_step` = the larger).  Then the same number of calls again, each bracketed by
+    its own pair of events, for the distribution (median, min, max, p90); an event
+    between two launches costs short kernels a few microseconds, so the mean is taken
+    from the first loop only.  call(i) launches call number i (i lets the caller rotate
+    input sets).  Returns the statistics in milliseconds."""
     import statistics
     import torch
 
@@ -69,24 +73,28 @@ def time_calls(call, steps: int, warmup: int, stream, min_warmup_s: float | None
             torch.cuda.synchronize()   # keep the host within a few calls of the device
     torch.cuda.synchronize()
     warm_s = time.perf_counter() - t0
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev[0].record(stream)
+    e0.record(stream)
     for i in range(steps):
         call(i)
-        ev[i + 1].record(stream)
-    ev[-1].synchronize()
+    e1.record(stream)
+    e1.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    total = ev[0].elapsed_time(ev[-1])
-    srt = sorted(per)
+    total = e0.elapsed_time(e1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record(stream)
+        call(i)
+        ev[2 * i + 1].record(stream)
+    ev[-1].synchronize()
+    per = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
     return {"ms_events": total / steps, "ms_wall": wall * 1e3 / steps, "ms_per_step": max(total / steps, wall * 1e3 / steps),
-            "ms_median": statistics.median(per), "ms_min": srt[0], "ms_max": srt[-1],
-            "ms_p90": srt[min(len(srt) - 1, int(0.9 * len(srt)))], "warmup_calls_run": n,
+            "ms_median": statistics.median(per), "ms_min": per[0], "ms_max": per[-1],
+            "ms_p90": per[min(len(per) - 1, int(0.9 * len(per)))], "warmup_calls_run": n,
             "warmup_s": round(warm_s, 3)}
-
 
 
 def algorithmic_bytes(x) -> int:
@@ -187,13 +195,14 @@ def other_workloads_bench(indices, steps: int, warmup: int, stream):
 
 
 def linear_in_L_bench(steps: int, warmup: int, stream, Ls=(1024, 2048, 4096, 8192)):
-    """Call time of the 1.3B-layer shape (batch 4, dim 4096, N 16, bf16) at several
-    sequence lengths, the same plan (one piece, 256 workgroups) at each: the scan's
-    work is linear in L, so the time should be too."""
+    """Call time of a 1.3B-layer-like shape (batch 5, dim 4096, N 16, bf16) at several
+    sequence lengths, the same plan (one piece, 320 workgroups) at each: the scan's
+    work is linear in L, so the time should be too.  (Batch 5 rather than 4 gives these
+    launches a grid of their own, so a profile tells them apart from the headline's.)"""
     import numpy as np
     from selective_state_space_79_amd.inputs import ScanInputs, make_inputs, to_device
 
-    big = make_inputs(4, max(Ls), 4096, 16, seed=77, io="bf16")
+    big = make_inputs(5, max(Ls), 4096, 16, seed=77, io="bf16")
     rows = []
     for L in Ls:
         cut = lambda a: np.ascontiguousarray(a[..., :L])
@@ -304,7 +313,8 @@ PROFILE_COMMANDS = {
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {d}/fetch -o scan -- python3 bench.py " + _ONLY,
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/write -o scan -- python3 bench.py " + _ONLY,
     "valu": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS SQ_INSTS_SALU SQ_BUSY_CYCLES "
-            "--kernel-trace --output-format csv -d {d}/valu -o scan -- python3 bench.py " + _ONLY,
+            "--kernel-trace --output-format csv -d {d}/valu -o scan -- python3 bench.py --steps 3 --warmup 1 "
+            "--min-warmup-s 0 --no-cpu-baseline --no-decode --no-ssd --no-workloads --no-linear",
     "conv_stats": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/convstats -o conv -- "
                   "python3 bench.py --steps 200 --warmup 50 --no-cpu-baseline --no-backward --no-decode --no-ssd "
                   "--no-workloads --no-linear --fused-conv",
@@ -505,6 +515,21 @@ def summarize_profiles(d):
                f"At 2.4 GHz over 1024 SIMDs that is {cyc / (SIMDS * CLOCK_HZ) * 1e6:.1f} µs of issue per call."]
         if durs:
             md.append(f"Dispatch time in this (profiled) run: median {durs[0]['median'] / 1e3:.1f} µs.")
+        # every kernel of the run (the forward, and the backward's passes, timed in the same run)
+        allc = {}
+        for r in csv.DictReader(open(_find(d, "valu", "counter_collection.csv"))):
+            allc.setdefault((r["Kernel_Name"], _grid(r)), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        md += ["", "All kernels of the run (medians per dispatch; issue = 4 x (VALU + TRANS) cycles at 2.4 GHz over "
+               "1024 SIMDs):", "", "| kernel | grid | dispatches | SQ_INSTS_VALU | TRANS_F32 | SQ_INSTS_LDS | issue µs |",
+               "|---|---|---|---|---|---|---|"]
+        for (name, grid), cs in sorted(allc.items(), key=lambda kv: -statistics.median(kv[1].get("SQ_INSTS_VALU", [0]))):
+            v = statistics.median(cs.get("SQ_INSTS_VALU", [0]))
+            t = statistics.median(cs.get("SQ_INSTS_VALU_TRANS_F32", [0]))
+            if v < 1e6:
+                continue
+            md.append(f"| `{name[:100]}` | {grid} | {len(cs.get('SQ_INSTS_VALU', []))} | {v:.4g} | {t:.4g} | "
+                      f"{statistics.median(cs.get('SQ_INSTS_LDS', [0])):.4g} | {4 * (v + t) / (SIMDS * CLOCK_HZ) * 1e6:.1f} |")
         with open(os.path.join(ROOT, "profiles", "scan_fwd_mamba13b_valu_issue.md"), "w") as f:
             f.write("\n".join(md) + "\n")
 
