@@ -659,6 +659,11 @@ def to_device_cols(xd):
 # e = a*g: mul; a*h_prev: mul; g*(a*h_prev): mul; dA, sum A*.., sum g*B: 3 fma;
 # ds*h and g*x for dC, dB: 2 mul) and the sums of dB and dC over channels (2 add)
 BWD_OPS_PER_UPDATE = 16
+# with a scalar decay per head the decay is one exp2 per (b,t,d), shared by the state
+# entries: the recompute (x*B mul, state fma, read-out fma for the gate's derivative),
+# the reverse step (g fma, e = a*g mul, sums of g*a*h_prev and g*B: 2 fma; ds*h and g*x
+# for dC, dB: 2 mul) and the channel sums of dB, dC (2 add)
+BWD_OPS_PER_UPDATE_SCALAR = 11
 
 
 def backward_bench(x, dev, steps: int = 40, warmup: int = 15):
@@ -699,12 +704,14 @@ def backward_bench(x, dev, steps: int = 40, warmup: int = 15):
     # (float32) written per (b, t, n); A, D, dt_bias read and dA, dD, ddt_bias written
     nbytes = (7 * esz * x.batch * x.L * x.dim + (2 * esz + 8) * x.batch * x.N * x.L
               + 8 * (x.A.size + 2 * x.dim))
-    tops = BWD_OPS_PER_UPDATE * x.updates / (ms * 1e-3) / 1e12
-    rec = {"workload": f"{x.batch}x{x.L}x{x.dim}, N {x.N}, {x.io} I/O: gradients of every input",
+    ops = BWD_OPS_PER_UPDATE_SCALAR if x.nheads else BWD_OPS_PER_UPDATE
+    tops = ops * x.updates / (ms * 1e-3) / 1e12
+    rec = {"workload": f"{x.batch}x{x.L}x{x.dim}, N {x.N}, {x.io} I/O" + (f", {x.nheads} heads scalar decay" if x.nheads else "")
+                       + ": gradients of every input",
            "ms_per_call": round(ms, 4), "updates_per_s": x.updates / (ms * 1e-3), "plan": plan,
            "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
                         "unit": "TFLOP/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
-                        "note": f"{BWD_OPS_PER_UPDATE} fp32 VALU lane operations per state update"},
+                        "note": f"{ops} fp32 VALU lane operations per state update"},
            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "ms_median": round(tb["ms_median"], 4), "ms_min": round(tb["ms_min"], 4)}
 
@@ -910,6 +917,14 @@ def main():
         rec["fused_conv"] = fused_conv_bench(x, dev)
     if not args.no_backward:
         rec["backward"] = backward_bench(x, dev)
+        if args.workload != 5:
+            # the scalar-decay N = 128 shapes (workload 5, per-channel step sizes)
+            from selective_state_space_79_amd.inputs import make_workload as _mw
+            x5 = _mw(5)
+            d5 = to_device(x5, "cuda:0")
+            rec["backward_scalar_decay_n128"] = backward_bench(x5, d5, steps=10, warmup=3)
+            del d5, x5
+            torch.cuda.empty_cache()
     if not args.no_ssd:
         del dev
         torch.cuda.empty_cache()
