@@ -297,7 +297,8 @@ SSM_API int ssm_selective_scan_bwd_ckpt(const void* u, const void* delta, const 
  * time on one device (on different streams, or from different threads) race and
  * must be serialised by the caller.  The stream must belong to the current device
  * (else SSM_ERR_DEVICE); the scratch's device address is looked up once per device
- * on its first call that needs pieces.  y and h_last are bitwise those of
+ * on its first call that needs pieces (device ordinals 0 .. 63; a call that needs the
+ * scratch on a higher ordinal returns SSM_ERR_HIP).  y and h_last are bitwise those of
  * ssm_selective_scan_fwd_state with a workspace.  Other rules as
  * ssm_selective_scan_fwd_state. */
 #define SSM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
