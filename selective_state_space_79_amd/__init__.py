@@ -115,7 +115,7 @@ class SsmSsdPlan(ctypes.Structure):
         ("nsegments", ctypes.c_int32),
         ("chunks_per_segment", ctypes.c_int32),
         ("chunk_len", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("state_pieces", ctypes.c_int32),
         ("nchunks", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
     ]

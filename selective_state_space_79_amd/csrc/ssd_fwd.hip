@@ -23,10 +23,11 @@
 // Products accumulate in fp32.
 //
 // Work split: ssd_gram_kernel forms C^T B of every chunk once for all heads.  A sequence
-// is cut into segments of whole chunks.  ssd_state_kernel computes each segment's end
-// state from a zero start (and its total decay);
-// ssd_out_kernel composes the states of the segments before its own with h0, then
-// walks its chunks in order, producing y and carrying the state in registers.  In
+// is cut into segments of whole chunks, and each segment before the last into pieces.
+// ssd_state_kernel computes each such piece's end state from a zero start (and its
+// total decay); ssd_out_kernel composes the states of the pieces before its segment
+// with h0, then walks its chunks in order, producing y and carrying the state in
+// registers.  In
 // both, wave w of a workgroup owns the head's channels 16w .. 16w+15: their state
 // columns (all N rows), the chunk's state contribution to them, and their outputs.
 // The masked decay matrix of a chunk is shared by all channels: its 10 lower-
@@ -56,26 +57,32 @@ constexpr int kThreads = kWaves * kLanes;
 constexpr int kRow = kQ + 8;            // LDS row (bf16): 144 bytes, 36 dwords
 static_assert(kQ == kLanes, "one step per lane in the step-size prefix");
 
-// LDS, in bf16 units: B[n][s], C[n][t], u[p][s], and the masked decay matrix
-// M[t][s] as high and low bf16 parts; then the fp32 step arrays.
+// fp32 step arrays of a chunk (offsets in floats): cum (log2 units), dt, the state
+// weights exp(cum_last - cum_s) dt_s, the read-out decays exp(cum_t), and cum_last.
+// The kernels keep two such sets, chunk c using set c % 2, so that one wave can fill the
+// next chunk's set while the others still read the current one.
+constexpr int kFCum = 0, kFDt = kQ, kFW = 2 * kQ, kFE = 3 * kQ, kFTot = 4 * kQ;
+constexpr int kFSet = 4 * kQ + 4;       // floats per set (16-byte multiple)
+
+// LDS, in bf16 units: B[n][s], C[n][t], u[p][s], z[p][t] (the gate input; a wave's
+// outputs y[p][t] replace its rows of it once read), and the masked decay matrix
+// M[t][s] as high and low bf16 parts; then the two sets of step arrays.
 template <int N> struct OutLds {
     static constexpr int Bn = 0;
     static constexpr int Cn = Bn + N * kRow;
     static constexpr int U = Cn + N * kRow;
-    static constexpr int Mhi = U + kP * kRow;
+    static constexpr int Z = U + kP * kRow;
+    static constexpr int Mhi = Z + kP * kRow;
     static constexpr int Mlo = Mhi + kQ * kRow;
     static constexpr int F = Mlo + kQ * kRow;
-    static constexpr size_t bytes = size_t(F) * 2 + (4 * kQ + 4) * sizeof(float);
+    static constexpr size_t bytes = size_t(F) * 2 + 2 * kFSet * sizeof(float);
 };
 template <int N> struct StateLds {
     static constexpr int Bn = 0;
     static constexpr int U = Bn + N * kRow;
     static constexpr int F = U + kP * kRow;
-    static constexpr size_t bytes = size_t(F) * 2 + (4 * kQ + 4) * sizeof(float);
+    static constexpr size_t bytes = size_t(F) * 2 + 2 * kFSet * sizeof(float);
 };
-// fp32 step arrays (offsets in floats): cum (log2 units), dt, the state weights
-// exp(cum_last - cum_s) dt_s, the read-out decays exp(cum_t), and cum_last.
-constexpr int kFCum = 0, kFDt = kQ, kFW = 2 * kQ, kFE = 3 * kQ, kFTot = 4 * kQ;
 
 struct SsdParams {
     const uint16_t* u;
@@ -90,10 +97,11 @@ struct SsdParams {
     uint16_t* y;
     float* h_last;
     float* gram;             // (batch, nchunks, 10 tiles, 64 lanes, 4) fp32: C^T B per chunk
-    float* seg_state;        // (nseg-1, batch*nheads) blocks of P*N fp32, in lane order
-    float* seg_decay;        // (nseg-1, batch*nheads) fp32, log2 units
+    float* seg_state;        // ((nseg-1) * pps, batch*nheads) blocks of P*N fp32, in lane order
+    float* seg_decay;        // ((nseg-1) * pps, batch*nheads) fp32, log2 units
     int64_t L, nheads, bh_total;
     int nseg, cps, nchunks;
+    int pps, cpp;            // state pieces per segment before the last, chunks per piece
 };
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also orders global memory,
@@ -435,6 +443,16 @@ __device__ inline int tile_t(int ti) { return (ti >= 1) + (ti >= 3) + (ti >= 6);
 __device__ inline int tile_s(int ti) { const int tb = tile_t(ti); return ti - tb * (tb + 1) / 2; }
 constexpr int kTiles = 10;
 
+// Tile k (0..2) of wave w in the output pass: w, w + 4, then w + 6 for waves 2 and 3
+// (tiles 8 and 9).  Waves 0 and 1 instead write the two tiles above the diagonal that
+// the 32-step contraction blocks include (t block 0 x s block 1, t block 2 x s block 3:
+// all zeros, as every s > t there), so that all waves take the same branch-free path.
+// out_tile names the C^T B tile the wave reads (for waves 0 and 1 at k = 2 it is read
+// unused); out_tb / out_sb the tile of M it writes.
+__device__ inline int out_tile(int w, int k) { return k < 2 ? w + 4 * k : w + 6; }
+__device__ inline int out_tb(int w, int k) { return k < 2 || w >= 2 ? tile_t(out_tile(w, k)) : 2 * w; }
+__device__ inline int out_sb(int w, int k) { return k < 2 || w >= 2 ? tile_s(out_tile(w, k)) : 2 * w + 1; }
+
 // G[t][s] = sum_n C[n][t] B[n][s] does not depend on the head, so it is formed once per
 // (batch row, chunk) and stored as GT tiles in the register layout the output pass uses:
 // tile ti of chunk c of batch row b at ((b * nchunks + c) * 10 + ti) * 64 + lane, four
@@ -475,11 +493,13 @@ template <int N, bool VEC>
 __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
     using Lay = StateLds<N>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    float* sf = reinterpret_cast<float*>(lds + Lay::F);
+    float* const sf0 = reinterpret_cast<float*>(lds + Lay::F);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int nsm = p.nseg - 1;
-    const int seg = int(blockIdx.x % unsigned(nsm));
-    const int64_t bh = blockIdx.x / unsigned(nsm);
+    // piece pc of a segment before the last: chunks j * cpp .. of segment seg
+    const int npc = (p.nseg - 1) * p.pps;
+    const int pc = int(blockIdx.x % unsigned(npc));
+    const int64_t bh = blockIdx.x / unsigned(npc);
+    const int seg = pc / p.pps, j = pc % p.pps;
     const int64_t b = bh / p.nheads, h = bh % p.nheads;
     const float a = p.A[h];
     const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
@@ -488,10 +508,10 @@ __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb) H[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float dsum = 0.0f;
-    const int c0 = seg * p.cps, c1 = c0 + p.cps;
+    const int c0 = seg * p.cps + j * p.cpp, c1 = min(c0 + p.cpp, (seg + 1) * p.cps);
     // Every chunk of a segment before the last lies wholly inside the sequence (the last
-    // segment holds the last chunk), so no chunk here needs masking, and the next chunk
-    // (the following segment's first after this segment's last) is always in bounds.
+    // segment holds the last chunk), so no chunk here needs masking, and the chunk after
+    // a piece (at most the following segment's first) is always in bounds.
     // Loads are issued in one order throughout -- u and the step input (from HBM)
     // first, then B -- and each after the last use of the registers it refills.
     Chunk<N, false> nx;
@@ -501,19 +521,23 @@ __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
     __builtin_amdgcn_sched_barrier(0);   // keep the loads in the loop's order
     load_chunk<N, false, VEC, 1>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
     load_chunk<N, false, VEC, 2>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    // Wave 0 stages each chunk's step arrays a chunk ahead, at the end of the one before
+    // (whose step input it has by then), so no wave waits for them between barriers.
+    if (w == 0) stage_steps(nx.draw, true, a, bias, sf0 + (c0 & 1) * kFSet, l);
     for (int c = c0; c < c1; ++c) {
         const int64_t t0 = int64_t(c) * kQ;
+        const float* sf = sf0 + (c & 1) * kFSet;
         lds_barrier();
         store_chunk<N, false>(nx, lds, Lay::Bn, 0, Lay::U, tid, true);
-        if (w == 0) stage_steps(nx.draw, true, a, bias, sf, l);
         load_chunk<N, false, VEC, 3>(nx, src, p, b, bh, t0 + kQ, tid);
         lds_barrier();
         load_chunk<N, false, VEC, 1>(nx, src, p, b, bh, t0 + kQ, tid);
         load_chunk<N, false, VEC, 2>(nx, src, p, b, bh, t0 + kQ, tid);
         dsum += sf[kFTot];
         chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
+        if (w == 0) stage_steps(nx.draw, true, a, bias, sf0 + ((c + 1) & 1) * kFSet, l);
     }
-    const int64_t k = int64_t(seg) * p.bh_total + bh;
+    const int64_t k = int64_t(pc) * p.bh_total + bh;
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb)
         *reinterpret_cast<f32x4*>(p.seg_state + seg_index<N>(k, nb, w, l)) = H[nb];
@@ -528,7 +552,7 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
     constexpr int NK = N / 32;    // 32-wide blocks of the state index
     constexpr int NB = N / 16;    // state tiles per wave
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    float* sf = reinterpret_cast<float*>(lds + Lay::F);
+    float* const sf0 = reinterpret_cast<float*>(lds + Lay::F);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
     const int seg = int(blockIdx.x % unsigned(p.nseg));
     const int64_t bh = blockIdx.x / unsigned(p.nseg);
@@ -542,73 +566,103 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
     const Rsrc rz = make_rsrc(GATE ? zb : p.u, 2 * kP * p.L);
     const Rsrc ry = make_rsrc(yb, 2 * kP * p.L);
     const uint32_t prow = uint32_t(pc) * uint32_t(p.L);
-    const uint32_t lane_off = 2u * (prow + 4u * uint32_t(lg));   // bytes: channel pc, step 4 lg
-
-    // state entering the segment: h0 carried through the segments before it
-    f32x4 H[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.h0) {
-            const float* hr = p.h0 + (bh * kP + pc) * N + nrow(nb >> 1, lg, nb & 1, 0);
-            v = f32x4{hr[0], hr[2], hr[4], hr[6]};
-        }
-        for (int j = 0; j < seg; ++j) {
-            const int64_t k = int64_t(j) * p.bh_total + bh;
-            const float dec = __builtin_amdgcn_exp2f(p.seg_decay[k]);
-            v = dec * v + *reinterpret_cast<const f32x4*>(p.seg_state + seg_index<N>(k, nb, w, l));
-        }
-        H[nb] = v;
-    }
-    // the tiles of M above the diagonal that the 32-step contraction blocks include
-    // (t block 0 x s block 1, t block 2 x s block 3) stay zero
-    for (int i = tid; i < 2 * 16 * 16; i += kThreads) {
-        const int blk = i >> 8, r = (i >> 4) & 15, col = i & 15;
-        const int off = (32 * blk + r) * kRow + 32 * blk + 16 + col;
-        lds[Lay::Mhi + off] = 0;
-        lds[Lay::Mlo + off] = 0;
-    }
+    // y leaves in 16-byte pieces of the wave's rows, 8 lanes per 128-byte run of a row:
+    // lane l takes row 16 w + l / 8 (and the row 8 below it), steps 8 (l % 8) .. + 7
+    const int yrow = 16 * w + (l >> 3);
+    const uint32_t y_off = 2u * (uint32_t(yrow) * uint32_t(p.L) + 8u * uint32_t(l & 7));
+    const uint32_t y_8rows = 16u * uint32_t(p.L);
 
     const int c0 = seg * p.cps, c1 = min(c0 + p.cps, p.nchunks);
     Chunk<N, true> nx;
     ChunkSrc<N, true> src;
     init_src<N, true>(src, p, b, bh, tid);
-    // this wave's tiles of C^T B (tiles w, w + 4, w + 8 < 10); a wave without a third
-    // tile reads the next tile (or zeros past the end) unused
+    // this wave's tiles of C^T B: tiles w and w + 4, and tile w + 6 for waves 2 and 3
+    // (wave 0 also stages the step arrays); waves 0 and 1 read their third tile unused
     const Rsrc rg = make_rsrc(p.gram + b * p.nchunks * (kTiles * 256), int64_t(p.nchunks) * kTiles * 1024);
     u32x4 gn[3];
     auto load_g = [&](int c) {
 #pragma unroll
         for (int k = 0; k < 3; ++k)
-            gn[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, uint32_t(((w + 4 * k) * 64 + l) * 16), c * kTiles * 1024, 0);
+            gn[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, uint32_t((out_tile(w, k) * 64 + l) * 16),
+                                                          c * kTiles * 1024, 0);
     };
-    // gate inputs of the lane's outputs, steps 16 tb + 4 lg .. +3 of channel pc.  A step
-    // past L reads other data or zeros; its output is not stored.
-    u32x2 zn[4];
+    // The chunk's gate inputs: 16-byte pieces of the head's z rows, taken and staged in
+    // LDS like u's (full 128-byte runs of a row per 8 lanes, where reading each lane's
+    // own outputs' steps directly would touch 16 rows in 32-byte pieces per access).
+    constexpr int kZ = Chunk<N, true>::kU;
+    u32x4 zc[kZ];
     auto load_z = [&](int64_t t0) {
         if constexpr (GATE) {
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                if constexpr (VEC)
-                    zn[tb] = __builtin_amdgcn_raw_buffer_load_b64(rz, lane_off + 32u * tb, int(2 * t0), 0);
-                else
-                    zn[tb] = ld4<false>(zb + prow, t0 + 16 * tb + 4 * lg, p.L);
+            for (int q = 0; q < kZ; ++q) {
+                if constexpr (VEC) {
+                    zc[q] = __builtin_amdgcn_raw_buffer_load_b128(rz, src.off_u[q], int(2 * t0), 0);
+                } else {
+                    const int i = tid + q * kThreads;
+                    zc[q] = ld8<false>(zb + int64_t(piece_row(i)) * p.L, t0 + (i & 7) * 8, p.L);
+                }
             }
         }
     };
-    // The first chunk's inputs, in the order the chunk loop issues the next chunk's (u
-    // and the step input -- read from HBM, so first --, then the C^T B tiles, B, C and
-    // the gate inputs): loads complete in order, and with the same order before the loop
-    // as inside it the compiler can wait for exactly the loads each use needs.
+    // (nx.ok, from the same chunk's u loads, marks the pieces past L: stored as zeros)
+    auto store_z = [&](bool full_chunk) {
+        if constexpr (GATE) {
+            const bool ok = full_chunk || nx.ok;
+#pragma unroll
+            for (int q = 0; q < kZ; ++q) {
+                const int i = tid + q * kThreads;
+                u32x4* dst = reinterpret_cast<u32x4*>(lds + Lay::Z + piece_row(i) * kRow + (i & 7) * 8);
+                *dst = ok ? zc[q] : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    // The first chunk's inputs, in the order the chunk loop issues the next chunk's (u,
+    // z and the step input -- read from HBM, so first --, then the C^T B tiles, B and
+    // C): loads complete in order, and with the same order before the loop as inside it
+    // the compiler can wait for exactly the loads each use needs.
     load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    load_z(int64_t(c0) * kQ);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads in the loop's order
     load_g(c0);
     __builtin_amdgcn_sched_barrier(0);
     load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
     __builtin_amdgcn_sched_barrier(0);
     load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
-    __builtin_amdgcn_sched_barrier(0);
-    load_z(int64_t(c0) * kQ);
+    // The state entering the segment: h0 carried through the state pieces before it, read
+    // while the first chunk's loads are in flight, three pieces' reads at a time (the
+    // fold is serial, the reads are not).
+    f32x4 H[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        H[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.h0) {
+            const float* hr = p.h0 + (bh * kP + pc) * N + nrow(nb >> 1, lg, nb & 1, 0);
+            H[nb] = f32x4{hr[0], hr[2], hr[4], hr[6]};
+        }
+    }
+    const int npieces = seg * p.pps;
+    for (int j0 = 0; j0 < npieces; j0 += 3) {
+        f32x4 st[3][NB];
+        float dg[3];
+#pragma unroll
+        for (int g = 0; g < 3; ++g) {
+            const int64_t k = int64_t(min(j0 + g, npieces - 1)) * p.bh_total + bh;   // past the end: read unused
+            dg[g] = p.seg_decay[k];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                st[g][nb] = *reinterpret_cast<const f32x4*>(p.seg_state + seg_index<N>(k, nb, w, l));
+        }
+#pragma unroll
+        for (int g = 0; g < 3; ++g) {
+            const bool in = j0 + g < npieces;
+            const float dec = in ? __builtin_amdgcn_exp2f(dg[g]) : 1.0f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) H[nb] = dec * H[nb] + (in ? st[g][nb] : f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        }
+    }
+    // Wave 0 stages each chunk's step arrays a chunk ahead, at the end of the one before
+    // (whose step input it has by then), so no wave waits for them between barriers.
+    if (w == 0) stage_steps(nx.draw, int64_t(c0) * kQ + l < p.L, a, bias, sf0 + (c0 & 1) * kFSet, l);
     // One chunk.  FULL: the chunk lies wholly inside the sequence, so every global
     // access takes one straight path (with a per-element tail path the compiler would
     // drain all outstanding loads and stores at the top of every chunk); the sequence's
@@ -616,10 +670,12 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
     auto chunk = [&](const int c, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int64_t t0 = int64_t(c) * kQ;
+        const float* sf = sf0 + (c & 1) * kFSet;
         lds_barrier();
         store_chunk<N, true>(nx, lds, Lay::Bn, Lay::Cn, Lay::U, tid, FULL);
-        if (w == 0) stage_steps(nx.draw, FULL || t0 + l < p.L, a, bias, sf, l);
+        store_z(FULL);
         load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, t0 + kQ, tid);
+        load_z(t0 + kQ);
         // The next chunk's inputs are loaded over this chunk's phases, each after the
         // last use of the registers it replaces, so no copies (and no early waits) are
         // needed between iterations.  After the segment's last chunk they are the next
@@ -631,18 +687,20 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
         // GT[s][t] = sum_n B[n][s] C[n][t]; result row 4 lg + r is step s, column lr step t
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            const int ti = w + 4 * k;
-            if (ti < kTiles) {
-                const int tb = tile_t(ti), sb = tile_s(ti);
+            {
+                const int tb = out_tb(w, k), sb = out_sb(w, k);
                 const f32x4 g = __builtin_bit_cast(f32x4, gn[k]);
                 const int t = 16 * tb + lr;
+                // the lane's four steps s = 16 sb + 4 lg + r are adjacent: one read each
                 const float cum_t = sf[kFCum + t];
+                const f32x4 cum_s = *reinterpret_cast<const f32x4*>(sf + kFCum + 16 * sb + 4 * lg);
+                const f32x4 dt_s = *reinterpret_cast<const f32x4*>(sf + kFDt + 16 * sb + 4 * lg);
                 float m[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = 16 * sb + 4 * lg + r;
-                    const float e = __builtin_amdgcn_exp2f(cum_t - sf[kFCum + s]) * sf[kFDt + s];
-                    m[r] = s <= t ? g[r] * e : 0.0f;
+                    const float e = __builtin_amdgcn_exp2f(cum_t - cum_s[r]) * dt_s[r];
+                    m[r] = s <= t ? g[r] * e : 0.0f;   // a select: inf or NaN above the diagonal is dropped
                 }
                 uint32_t mh[2], ml[2];
                 split<4>(m, mh, ml);
@@ -705,6 +763,8 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             const int tq = 16 * tb + 4 * lg;
             const f32x4 e4 = *reinterpret_cast<const f32x4*>(sf + kFE + tq);
             const u32x2 uu = *reinterpret_cast<const u32x2*>(lds + Lay::U + pc * kRow + tq);
+            u32x2 zz = {0u, 0u};
+            if constexpr (GATE) zz = *reinterpret_cast<const u32x2*>(lds + Lay::Z + pc * kRow + tq);
             uint32_t o[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -714,17 +774,25 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
                     const int r = 2 * q + e;
                     float x = fmaf(e4[r], yo[tb][r], yd[tb][r]);
                     x = fmaf(Dp, bf_half(uu[q], e), x);
-                    if constexpr (GATE) x *= silu_f32(bf_half(zn[tb][q], e));
+                    if constexpr (GATE) x *= silu_f32(bf_half(zz[q], e));
                     v[e] = x;
                 }
                 o[q] = pack_bf16(v[0], v[1]);
             }
-            if constexpr (full)
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{o[0], o[1]}, ry, lane_off + 32u * tb, int(2 * t0), 0);
+            if constexpr (full)   // in place of the gate inputs just read (this lane's own)
+                *reinterpret_cast<u32x2*>(lds + Lay::Z + pc * kRow + tq) = u32x2{o[0], o[1]};
             else
                 st4<false>(yb + prow, t0 + tq, p.L, u32x2{o[0], o[1]});
         }
-        load_z(t0 + kQ);
+        if constexpr (full) {
+            // the wave's 16 rows of y, written by its own lanes just above (a wave's LDS
+            // accesses take effect in order), leave in whole 128-byte runs
+            const u32x4 y0 = *reinterpret_cast<const u32x4*>(lds + Lay::Z + yrow * kRow + 8 * (l & 7));
+            const u32x4 y1 = *reinterpret_cast<const u32x4*>(lds + Lay::Z + (yrow + 8) * kRow + 8 * (l & 7));
+            __builtin_amdgcn_raw_buffer_store_b128(y0, ry, y_off, int(2 * t0), 0);
+            __builtin_amdgcn_raw_buffer_store_b128(y1, ry, y_off + y_8rows, int(2 * t0), 0);
+        }
+        if (w == 0) stage_steps(nx.draw, t0 + kQ + l < p.L, a, bias, sf0 + ((c + 1) & 1) * kFSet, l);
     };
     const int c_full = std::min<int64_t>(c1, p.L / kQ);   // chunks wholly inside L
     int c = c0;
@@ -743,7 +811,7 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
 
 // ------------------------------------------------------------------ host side
 struct SsdPlan {
-    int nseg, cps, nchunks;
+    int nseg, cps, nchunks, pps, cpp;
     int64_t bh_total;
     size_t ws_bytes, state_floats, gram_bytes;
 };
@@ -784,15 +852,26 @@ int ssd_plan(const ssm_ssd_dims* d, SsdPlan* pl) {
     nseg = std::min<int64_t>(std::max<int64_t>(nseg, 1), nchunks);
     const int64_t cps = cdiv(nchunks, nseg);
     nseg = cdiv(nchunks, cps);
-    if (nseg * bh > int64_t(INT32_MAX)) return SSM_ERR_DIMS;
+    // The end states of the segments before the last are computed in pieces of cpp
+    // chunks, pps per segment, enough for about three of the state pass's workgroups per
+    // CU (its time is that of the most loaded CU: at N = 128, 384 segment-long
+    // workgroups take 51 us, 896 half as long 44 us).
+    int64_t pps = 1;
+    if (nseg > 1) pps = std::max<int64_t>(1, std::min<int64_t>({cdiv(768, (nseg - 1) * bh), 4, cps}));
+    const int64_t cpp = cdiv(cps, pps);
+    pps = cdiv(cps, cpp);
+    if (nseg * bh > int64_t(INT32_MAX) || (nseg - 1) * pps * bh > int64_t(INT32_MAX)) return SSM_ERR_DIMS;
     pl->nseg = int(nseg);
     pl->cps = int(cps);
+    pl->pps = int(pps);
+    pl->cpp = int(cpp);
     pl->nchunks = int(nchunks);
     pl->bh_total = bh;
-    pl->state_floats = size_t(nseg - 1) * size_t(bh) * size_t(kP) * size_t(d->dstate);  // P*N per head
+    pl->state_floats = size_t(nseg - 1) * size_t(pps) * size_t(bh) * size_t(kP) * size_t(d->dstate);  // P*N per head
     pl->gram_bytes = round256(size_t(d->batch) * size_t(nchunks) * kTiles * 1024);
     pl->ws_bytes = pl->gram_bytes +
-                   (nseg > 1 ? round256(pl->state_floats * 4) + round256(size_t(nseg - 1) * size_t(bh) * 4) : 0);
+                   (nseg > 1 ? round256(pl->state_floats * 4) + round256(size_t(nseg - 1) * size_t(pps) * size_t(bh) * 4)
+                             : 0);
     return SSM_OK;
 }
 
@@ -801,7 +880,7 @@ int ssd_launch(const SsdParams& p, const SsdPlan& pl, hipStream_t s) {
     launch_kernel((ssd_gram_kernel<N, VEC>), dim3(unsigned(pl.bh_total / p.nheads * pl.nchunks)), dim3(kThreads),
                        size_t(2 * N * kRow * 2), s, p);
     if (pl.nseg > 1) {
-        launch_kernel((ssd_state_kernel<N, VEC>), dim3(unsigned((pl.nseg - 1) * pl.bh_total)), dim3(kThreads),
+        launch_kernel((ssd_state_kernel<N, VEC>), dim3(unsigned((pl.nseg - 1) * pl.pps * pl.bh_total)), dim3(kThreads),
                            StateLds<N>::bytes, s, p);
     }
     const dim3 grid(unsigned(pl.nseg * pl.bh_total));
@@ -822,7 +901,7 @@ extern "C" SSM_API int ssm_ssd_fwd_plan(const ssm_ssd_dims* dims, ssm_ssd_plan* 
     plan->nsegments = pl.nseg;
     plan->chunks_per_segment = pl.cps;
     plan->chunk_len = kQ;
-    plan->reserved = 0;
+    plan->state_pieces = pl.pps;
     plan->nchunks = pl.nchunks;
     plan->workspace_bytes = pl.ws_bytes;
     return SSM_OK;
@@ -891,6 +970,8 @@ extern "C" SSM_API int ssm_ssd_fwd(const void* u, const void* delta, const float
     p.bh_total = pl.bh_total;
     p.nseg = pl.nseg;
     p.cps = pl.cps;
+    p.pps = pl.pps;
+    p.cpp = pl.cpp;
     p.nchunks = pl.nchunks;
 
     bool vec = L % 8 == 0;

@@ -426,7 +426,16 @@ def test_ssd_workspace_sizes():
         nchunks = (L + 63) // 64
         assert pl.nchunks == nchunks and pl.chunk_len == 64
         assert pl.nsegments == -(-nchunks // pl.chunks_per_segment)
+        # the segments before the last are cut into state pieces of whole chunks: about
+        # three of the end-state pass's workgroups per CU (768 in all), at most 4 per segment
         sub = pl.nsegments - 1
+        pps = 1
+        if sub:
+            pps = max(1, min(-(-768 // (sub * batch * H)), 4, pl.chunks_per_segment))
+            cpp = -(-pl.chunks_per_segment // pps)
+            pps = -(-pl.chunks_per_segment // cpp)
+        assert pl.state_pieces == pps
+        sub *= pps
         size = gram(batch, L) + (r(sub * batch * H * 64 * N * 4) + r(sub * batch * H * 4) if sub else 0)
         assert pl.workspace_bytes == size
         assert ssm.ssm_ssd_fwd_workspace_bytes(_ssd_dims(batch=batch, seqlen=L, nheads=H, dstate=N, nsegments=nseg)) == size
@@ -435,7 +444,7 @@ def test_ssd_workspace_sizes():
     assert expect(1, 64, 2, 64, 1).nsegments == 1
     assert expect(1, 64, 2, 64, 4).nsegments == 1                 # one chunk: one piece
     pl = expect(2, 8192, 64, 128, 4)
-    assert (pl.nsegments, pl.chunks_per_segment) == (4, 32)
+    assert (pl.nsegments, pl.chunks_per_segment, pl.state_pieces) == (4, 32, 2)   # 3 x 2 x 128 = 768
     # pieces are whole chunks: 10 chunks in 4 pieces of 3 chunks leave 4 pieces
     pl = expect(1, 640, 1, 64, 4)
     assert (pl.nsegments, pl.chunks_per_segment) == (4, 3)
