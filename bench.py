@@ -322,6 +322,11 @@ PROFILE_COMMANDS = {
                  "python3 bench.py --calibrate-copy",
     "copywrite": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/copywrite -o copy -- "
                  "python3 bench.py --calibrate-copy",
+    "ssd_counters": "rocprofv3 --kernel-include-regex ssd_ --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
+                    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+                    "GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d {d}/ssdctr -o scan -- python3 bench.py "
+                    "--steps 3 --warmup 1 --min-warmup-s 0 --no-cpu-baseline --no-backward --no-decode --no-workloads "
+                    "--no-linear",
 }
 COPY_BYTES = 2 << 30
 # output directory the profile commands write to (relative to the repository root); raw
@@ -447,6 +452,43 @@ def summarize_profiles(d):
             md += _trace_table(ssd + scal, 120)
             with open(os.path.join(ROOT, "profiles", "ssd_fwd_scalar_decay_head_dt.md"), "w") as f:
                 f.write("\n".join(md) + "\n")
+
+    # occupancy and matrix-core use of the duality pass's kernels
+    if _find(d, "ssdctr", "counter_collection.csv"):
+        src = os.path.join(ROOT, "selective_state_space_79_amd", "csrc", "ssd_fwd.hip")
+        with open(src, "rb") as f:
+            ssd_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+        md = ["# ssd_gram_kernel, ssd_state_kernel, ssd_out_kernel: occupancy and matrix-core counters, scalar-decay "
+              "large-state workload with one step size per head (batch 2, L 8192, 64 heads x 64, N 128, bf16)", "",
+              f"Kernel source (`csrc/ssd_fwd.hip`) sha256[:16]: `{ssd_hash}`", "",
+              "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+              "    " + cmd("ssd_counters"), "",
+              "Medians per dispatch.  `GRBM_GUI_ACTIVE` is summed over the 8 XCDs, so the dispatch's cycles are a "
+              "eighth of it; `SQ_WAVE_CYCLES` counts resident wave-cycles in units of 4 cycles; "
+              "`SQ_VALU_MFMA_BUSY_CYCLES` sums the 1024 SIMDs' matrix-core busy cycles.  Derived: mean resident "
+              "waves per SIMD = 4 x SQ_WAVE_CYCLES / (1024 x cycles); matrix-core busy = "
+              "SQ_VALU_MFMA_BUSY_CYCLES / (1024 x cycles); LDS bank-conflict cycles per CU-cycle = "
+              "SQ_LDS_BANK_CONFLICT / (256 x cycles).  Dispatch times under counter collection run longer than "
+              "in `ssd_fwd_scalar_decay_head_dt.md`.", ""]
+        names = [("ssd_gram_kernel", "C^T B per chunk"), ("ssd_state_kernel", "end states of the pieces"),
+                 ("ssd_out_kernel", "outputs")]
+        cols = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+                "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
+        md += ["| kernel | " + " | ".join(cols) + " | cycles | waves/SIMD | MFMA busy | LDS conflict / CU-cycle |",
+               "|---|" + "---|" * (len(cols) + 4)]
+        for kname, what in names:
+            c = counters("ssdctr", kname + "<128")
+            if not c:
+                continue
+            med = {k: statistics.median(v) for k, v in c.items()}
+            cyc = med.get("GRBM_GUI_ACTIVE", 0.0) / 8
+            occ = 4 * med.get("SQ_WAVE_CYCLES", 0.0) / (1024 * cyc) if cyc else 0.0
+            mfma = med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * cyc) if cyc else 0.0
+            lds = med.get("SQ_LDS_BANK_CONFLICT", 0.0) / (256 * cyc) if cyc else 0.0
+            md.append(f"| `{kname}` ({what}) | " + " | ".join(f"{med.get(k, 0.0):.4g}" for k in cols) +
+                      f" | {cyc:.4g} | {occ:.2f} | {mfma:.3f} | {lds:.3f} |")
+        with open(os.path.join(ROOT, "profiles", "ssd_fwd_counters.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
 
     # HBM traffic of the headline forward
     if _find(d, "fetch", "counter_collection.csv") and _find(d, "copyfetch", "counter_collection.csv"):
