@@ -616,10 +616,36 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             }
         }
     };
-    // The first chunk's inputs, in the order the chunk loop issues the next chunk's (u,
-    // z and the step input -- read from HBM, so first --, then the C^T B tiles, B and
-    // C): loads complete in order, and with the same order before the loop as inside it
-    // the compiler can wait for exactly the loads each use needs.
+    // B and C of chunk cc, from the registers into LDS (pieces past L as zeros).  They
+    // go in once the chunk before has read its own B and C (its third barrier), a chunk
+    // ahead of their use, so that the top of a chunk stores only u and z.
+    auto store_bc = [&](int cc) {
+        using Ch = Chunk<N, true>;
+        const int64_t tc = int64_t(cc) * kQ;
+        const bool ok = tc + kQ <= p.L || tc + 8 * (tid & 7) < p.L;
+#pragma unroll
+        for (int q = 0; q < Ch::kBC; ++q) {
+            const int i = tid + q * kThreads;
+            const int arr = i / (N * (kQ / 8)), k = i % (N * (kQ / 8));
+            u32x4* dst = reinterpret_cast<u32x4*>(lds + (arr ? Lay::Cn : Lay::Bn) + piece_row(k) * kRow + (k & 7) * 8);
+            *dst = ok ? nx.bc[q] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_u = [&](bool full_chunk) {
+        using Ch = Chunk<N, true>;
+        const bool ok = full_chunk || nx.ok;
+#pragma unroll
+        for (int q = 0; q < Ch::kU; ++q) {
+            const int i = tid + q * kThreads;
+            u32x4* dst = reinterpret_cast<u32x4*>(lds + Lay::U + piece_row(i) * kRow + (i & 7) * 8);
+            *dst = ok ? nx.u[q] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    // The first chunk's inputs, in the order the chunk loop issues them (u, z and the
+    // step input -- read from HBM, so first --, then the C^T B tiles; B and C, stored
+    // here, then the next chunk's): loads complete in order, and with the same order
+    // before the loop as inside it the compiler can wait for exactly the loads each use
+    // needs.
     load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
     load_z(int64_t(c0) * kQ);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads in the loop's order
@@ -628,6 +654,9 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
     load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
     __builtin_amdgcn_sched_barrier(0);
     load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+    store_bc(c0);
+    load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0 + 1) * kQ, tid);
+    load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0 + 1) * kQ, tid);
     // The state entering the segment: h0 carried through the state pieces before it, read
     // while the first chunk's loads are in flight, three pieces' reads at a time (the
     // fold is serial, the reads are not).
@@ -672,15 +701,16 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
         const int64_t t0 = int64_t(c) * kQ;
         const float* sf = sf0 + (c & 1) * kFSet;
         lds_barrier();
-        store_chunk<N, true>(nx, lds, Lay::Bn, Lay::Cn, Lay::U, tid, FULL);
+        store_u(FULL);
         store_z(FULL);
         load_chunk<N, true, VEC, 3>(nx, src, p, b, bh, t0 + kQ, tid);
         load_z(t0 + kQ);
-        // The next chunk's inputs are loaded over this chunk's phases, each after the
+        // The next chunks' inputs are loaded over this chunk's phases, each after the
         // last use of the registers it replaces, so no copies (and no early waits) are
-        // needed between iterations.  After the segment's last chunk they are the next
-        // segment's or past the end: read but unused (buffer reads past a block return
-        // zeros; flat reads past L are not made).
+        // needed between iterations: u, z, the step input and C^T B of the next chunk,
+        // B and C of the one after (B and C are a chunk ahead in LDS).  Past the
+        // segment's last chunk they are the next segment's or past the end: read but
+        // unused (buffer reads past a block return zeros; flat reads past L are not made).
         lds_barrier();
 
         // masked decay tiles: M[t][s] = GT[s][t] exp2(cum_t - cum_s) dt_s for s <= t,
@@ -711,7 +741,6 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
         }
 
         load_g(c + 1);
-        load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, t0 + kQ, tid);
 
         // read-out of the chunk's starting state: yo[tb][t][p] = sum_n C[n][t] H[n][p]
         f32x4 yo[4];
@@ -736,9 +765,11 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             }
         }
 
-        load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, t0 + kQ, tid);
         chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
-        lds_barrier();   // M complete
+        lds_barrier();   // M complete; this chunk's B and C read
+        store_bc(c + 1);
+        load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, t0 + 2 * kQ, tid);
+        load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, t0 + 2 * kQ, tid);
 
         // within the chunk: yd[tb][t][p] = sum_{s} M[t][s] u[s][p] over the 32-step
         // blocks that reach the diagonal of t block tb
