@@ -322,6 +322,11 @@ PROFILE_COMMANDS = {
                  "python3 bench.py --calibrate-copy",
     "copywrite": "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {d}/copywrite -o copy -- "
                  "python3 bench.py --calibrate-copy",
+    "bwd_counters": "rocprofv3 --kernel-include-regex scan_bwd_ --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
+                    "SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_SALU "
+                    "GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d {d}/bwdctr -o scan -- python3 bench.py "
+                    "--steps 3 --warmup 1 --min-warmup-s 0 --no-cpu-baseline --no-decode --no-ssd --no-workloads "
+                    "--no-linear",
     "ssd_counters": "rocprofv3 --kernel-include-regex ssd_ --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
                     "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
                     "GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d {d}/ssdctr -o scan -- python3 bench.py "
@@ -488,6 +493,43 @@ def summarize_profiles(d):
             md.append(f"| `{kname}` ({what}) | " + " | ".join(f"{med.get(k, 0.0):.4g}" for k in cols) +
                       f" | {cyc:.4g} | {occ:.2f} | {mfma:.3f} | {lds:.3f} |")
         with open(os.path.join(ROOT, "profiles", "ssd_fwd_counters.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
+
+    # instruction issue of the backward's role-split passes
+    if _find(d, "bwdctr", "counter_collection.csv"):
+        src = os.path.join(ROOT, "selective_state_space_79_amd", "csrc", "scan_bwd.hip")
+        with open(src, "rb") as f:
+            bwd_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+        md = ["# scan_bwd_ckpt_ws_kernel, scan_bwd_grad_ws_kernel: instruction-issue counters of the backward, "
+              "mamba-1.3b-layer (4 x 4096 x 4096, N 16) and scalar-decay large-state (2 x 8192 x 4096, N 128) "
+              "workloads, bf16", "",
+              f"Kernel source (`csrc/scan_bwd.hip`) sha256[:16]: `{bwd_hash}`", "",
+              "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+              "    " + cmd("bwd_counters"), "",
+              "Medians per dispatch.  `GRBM_GUI_ACTIVE` is summed over the 8 XCDs, so the dispatch's cycles are an "
+              "eighth of it.  A wave64 VALU instruction holds a SIMD16 for 4 cycles and a transcendental one for 8, "
+              "so VALU issue = 4 x (SQ_INSTS_VALU + SQ_INSTS_VALU_TRANS_F32) / (1024 x cycles), the fraction of the "
+              "1024 SIMDs' cycles spent issuing VALU work.  State updates per dispatch: 1.074e9 (N 16), 8.59e9 "
+              "(N 128).", ""]
+        cols = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32",
+                "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"]
+        md += ["| kernel | " + " | ".join(cols) + " | cycles | VALU issue | VALU per update |",
+               "|---|" + "---|" * (len(cols) + 3)]
+        shapes = [("scan_bwd_ckpt_ws_kernel<unsigned short, false, true, 4, 4, 16>", "checkpoints, N 16", 1.074e9),
+                  ("scan_bwd_grad_ws_kernel<unsigned short, false, true, 4, 4, 16>", "gradients, N 16", 1.074e9),
+                  ("scan_bwd_ckpt_ws_kernel<unsigned short, true, true, 16, 8, 8>", "checkpoints, N 128", 8.59e9),
+                  ("scan_bwd_grad_ws_kernel<unsigned short, true, true, 16, 8, 8>", "gradients, N 128", 8.59e9)]
+        for kname, what, upd in shapes:
+            c = counters("bwdctr", kname)
+            if not c:
+                continue
+            med = {k: statistics.median(v) for k, v in c.items()}
+            cyc = med.get("GRBM_GUI_ACTIVE", 0.0) / 8
+            issue = 4 * (med.get("SQ_INSTS_VALU", 0.0) + med.get("SQ_INSTS_VALU_TRANS_F32", 0.0)) / (1024 * cyc) if cyc else 0.0
+            per = 64 * med.get("SQ_INSTS_VALU", 0.0) / upd
+            md.append(f"| `{kname.split('<')[0]}` ({what}) | " + " | ".join(f"{med.get(k, 0.0):.4g}" for k in cols) +
+                      f" | {cyc:.4g} | {issue:.3f} | {per:.1f} |")
+        with open(os.path.join(ROOT, "profiles", "scan_bwd_counters.md"), "w") as f:
             f.write("\n".join(md) + "\n")
 
     # HBM traffic of the headline forward
