@@ -463,7 +463,7 @@ def summarize_profiles(d):
         src = os.path.join(ROOT, "selective_state_space_79_amd", "csrc", "ssd_fwd.hip")
         with open(src, "rb") as f:
             ssd_hash = hashlib.sha256(f.read()).hexdigest()[:16]
-        md = ["# ssd_gram_kernel, ssd_state_kernel, ssd_out_kernel: occupancy and matrix-core counters, scalar-decay "
+        md = ["# ssd_gram_kernel, ssd_state_(dma_)kernel, ssd_out_kernel: occupancy and matrix-core counters, scalar-decay "
               "large-state workload with one step size per head (batch 2, L 8192, 64 heads x 64, N 128, bf16)", "",
               f"Kernel source (`csrc/ssd_fwd.hip`) sha256[:16]: `{ssd_hash}`", "",
               "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
@@ -475,8 +475,9 @@ def summarize_profiles(d):
               "SQ_VALU_MFMA_BUSY_CYCLES / (1024 x cycles); LDS bank-conflict cycles per CU-cycle = "
               "SQ_LDS_BANK_CONFLICT / (256 x cycles).  Dispatch times under counter collection run longer than "
               "in `ssd_fwd_scalar_decay_head_dt.md`.", ""]
-        names = [("ssd_gram_kernel", "C^T B per chunk"), ("ssd_state_kernel", "end states of the pieces"),
-                 ("ssd_out_kernel", "outputs")]
+        names = [("ssd_gram_kernel", "C^T B per chunk"),
+                 ("ssd_state_dma_kernel", "end states of the pieces, 16-byte rows straight to LDS"),
+                 ("ssd_state_kernel", "end states of the pieces"), ("ssd_out_kernel", "outputs")]
         cols = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
                 "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
         md += ["| kernel | " + " | ".join(cols) + " | cycles | waves/SIMD | MFMA busy | LDS conflict / CU-cycle |",

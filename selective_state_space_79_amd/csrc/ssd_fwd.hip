@@ -24,8 +24,8 @@
 //
 // Work split: ssd_gram_kernel forms C^T B of every chunk once for all heads.  A sequence
 // is cut into segments of whole chunks, and each segment before the last into pieces.
-// ssd_state_kernel computes each such piece's end state from a zero start (and its
-// total decay); ssd_out_kernel composes the states of the pieces before its segment
+// ssd_state_kernel (ssd_state_dma_kernel with 16-byte rows) computes each such piece's
+// end state from a zero start (and its total decay); ssd_out_kernel composes the states of the pieces before its segment
 // with h0, then walks its chunks in order, producing y and carrying the state in
 // registers.  In
 // both, wave w of a workgroup owns the head's channels 16w .. 16w+15: their state
@@ -81,6 +81,24 @@ template <int N> struct StateLds {
     static constexpr int Bn = 0;
     static constexpr int U = Bn + N * kRow;
     static constexpr int F = U + kP * kRow;
+    static constexpr size_t bytes = size_t(F) * 2 + 2 * kFSet * sizeof(float);
+};
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds + 16 l
+// (lds wave-uniform), counted like any other vector-memory load.  (A plain device
+// function: the builtin inside a kernel template left that template without a host
+// stub.)
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// The end-state pass with 16-byte rows (VEC): B and u go straight from global memory to
+// LDS, double-buffered: two buffers of B [N][64] and u [64][64] in 128-byte rows with
+// swizzled pieces (swz_off), then the two step-array sets.
+template <int N> struct StateDmaLds {
+    static constexpr int Bn = 0;
+    static constexpr int U = N * 64;
+    static constexpr int Buf = (N + kP) * 64;    // bf16 per buffer
+    static constexpr int F = 2 * Buf;
     static constexpr size_t bytes = size_t(F) * 2 + 2 * kFSet * sizeof(float);
 };
 
@@ -404,16 +422,25 @@ __device__ inline void stage_steps(uint32_t draw, bool valid, float a, float bia
 //
 // The chunk's contribution: H <- exp2(cum_last) H + B[n][s] X[s][p], X[s][p] = w_s u[s][p],
 // contracted over the chunk's 64 steps in two 32-step blocks.
-template <int N>
+// Element offset of (row r, column c) in a [row][64] bf16 array of exactly 128-byte rows
+// whose 16-byte pieces are stored at position (piece ^ ((r >> 1) & 7)) of their row:
+// rows written whole by direct global-to-LDS loads, 16 bytes per lane (no padding is
+// possible there), and read 16 bytes per lane by 16 lanes at 16 rows whose residues mod
+// 16 are all distinct (the state update's operand reads) -- the XOR puts those 16 reads
+// on distinct bank quads, as the padded 144-byte rows do for the other layout.
+__device__ constexpr int swz_off(int r, int c) { return r * 64 + (((c >> 3) ^ ((r >> 1) & 7)) << 3) + (c & 7); }
+
+template <int N, bool SWZ = false>
 __device__ inline void chunk_state(f32x4 (&H)[N / 16], const uint16_t* sBn, const uint16_t* sU, const float* sf,
                                    int w, int lr, int lg) {
+    auto at = [](int r, int c) { return SWZ ? swz_off(r, c) : r * kRow + c; };
     const float dec = __builtin_amdgcn_exp2f(sf[kFTot]);
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb) H[nb] *= dec;
 #pragma unroll
     for (int kb = 0; kb < kQ / 32; ++kb) {
         const int s0 = 32 * kb + 8 * lg;
-        const u32x4 uv = *reinterpret_cast<const u32x4*>(sU + (16 * w + lr) * kRow + s0);
+        const u32x4 uv = *reinterpret_cast<const u32x4*>(sU + at(16 * w + lr, s0));
         float xv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) xv[j] = sf[kFW + s0 + j] * bf_half(uv[j >> 1], j & 1);
@@ -422,7 +449,7 @@ __device__ inline void chunk_state(f32x4 (&H)[N / 16], const uint16_t* sBn, cons
         const bf16x8 xo_h = as_bf16x8(xh), xo_l = as_bf16x8(xl);
 #pragma unroll
         for (int nb = 0; nb < N / 16; ++nb) {
-            const bf16x8 bo = lds16(sBn + nrow(nb >> 1, lr >> 2, nb & 1, lr & 3) * kRow + s0);
+            const bf16x8 bo = lds16(sBn + at(nrow(nb >> 1, lr >> 2, nb & 1, lr & 3), s0));
             H[nb] = mfma(bo, xo_h, H[nb]);
             H[nb] = mfma(bo, xo_l, H[nb]);
         }
@@ -536,6 +563,85 @@ __global__ void __launch_bounds__(kThreads) ssd_state_kernel(SsdParams p) {
         dsum += sf[kFTot];
         chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
         if (w == 0) stage_steps(nx.draw, true, a, bias, sf0 + ((c + 1) & 1) * kFSet, l);
+    }
+    const int64_t k = int64_t(pc) * p.bh_total + bh;
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb)
+        *reinterpret_cast<f32x4*>(p.seg_state + seg_index<N>(k, nb, w, l)) = H[nb];
+    if (tid == 0) p.seg_decay[k] = dsum;
+}
+
+// The same pass with 16-byte rows: B and u of chunk c + 1 go straight from global memory
+// into the other LDS buffer (buffer_load ... lds, 16 bytes per lane, each wave 8 whole
+// rows per load) while chunk c is computed, so a chunk needs one barrier and no
+// register staging.  A load's lane l lands at byte 16 l of the wave's 1 KB block (a
+// 16-byte slot per lane); the lane loads the row's piece that belongs in that slot.
+template <int N>
+__global__ void __launch_bounds__(kThreads) ssd_state_dma_kernel(SsdParams p) {
+    using Lay = StateDmaLds<N>;
+    constexpr int QB = N / 32;                     // 1 KB blocks of B per wave (N rows / 8 / 4 waves)
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    float* const sf0 = reinterpret_cast<float*>(lds + Lay::F);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int npc = (p.nseg - 1) * p.pps;
+    const int pc = int(blockIdx.x % unsigned(npc));
+    const int64_t bh = blockIdx.x / unsigned(npc);
+    const int seg = pc / p.pps, j = pc % p.pps;
+    const int64_t b = bh / p.nheads, h = bh % p.nheads;
+    const float a = p.A[h];
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+
+    f32x4 H[N / 16];
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) H[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float dsum = 0.0f;
+    const int c0 = seg * p.cps + j * p.cpp, c1 = min(c0 + p.cpp, (seg + 1) * p.cps);
+    // (every chunk of a segment before the last lies wholly inside the sequence)
+    const uint32_t L32 = uint32_t(p.L);
+    const Rsrc rb = make_rsrc(p.B + b * N * p.L, 2 * N * p.L);
+    const Rsrc ru = make_rsrc(p.u + bh * kP * p.L, 2 * kP * p.L);
+    const Rsrc rd = make_rsrc(p.delta + bh * p.L, 2 * p.L);
+    // B block q of wave w: rows 8 (QB w + q) .. + 7; u block q: rows 8 (2 w + q) .. + 7
+    uint32_t voff_b[QB], voff_u[2];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        const int r = 8 * (QB * w + q) + (l >> 3);
+        voff_b[q] = 2u * (uint32_t(r) * L32 + 8u * uint32_t((l & 7) ^ ((r >> 1) & 7)));
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = 8 * (2 * w + q) + (l >> 3);
+        voff_u[q] = 2u * (uint32_t(r) * L32 + 8u * uint32_t((l & 7) ^ ((r >> 1) & 7)));
+    }
+    auto issue = [&](int cc, int buf) {
+        const uint32_t so = uint32_t(2 * int64_t(cc) * kQ);
+        uint16_t* base = lds + buf * Lay::Buf;
+#pragma unroll
+        for (int q = 0; q < QB; ++q) load_lds16(rb, base + Lay::Bn + (QB * w + q) * 512, voff_b[q], so);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) load_lds16(ru, base + Lay::U + (2 * w + q) * 512, voff_u[q], so);
+    };
+    auto load_draw = [&](int cc) {
+        return __builtin_amdgcn_raw_buffer_load_b16(rd, 2u * uint32_t(l), int(2 * int64_t(cc) * kQ), 0);
+    };
+    uint32_t draw = load_draw(c0);
+    issue(c0, 0);
+    if (w == 0) stage_steps(draw, true, a, bias, sf0, l);
+    for (int c = c0; c < c1; ++c) {
+        const int par = (c - c0) & 1;
+        const float* sf = sf0 + par * kFSet;
+        // this wave's direct loads of the chunk have landed; after the barrier every
+        // wave's have, and every wave is done with the other buffer and step-array set
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        // the step input goes first: waiting for it below does not wait for the loads
+        if (c + 1 < c1) {
+            draw = load_draw(c + 1);
+            issue(c + 1, par ^ 1);
+        }
+        dsum += sf[kFTot];
+        chunk_state<N, true>(H, lds + par * Lay::Buf + Lay::Bn, lds + par * Lay::Buf + Lay::U, sf, w, lr, lg);
+        if (w == 0 && c + 1 < c1) stage_steps(draw, true, a, bias, sf0 + (par ^ 1) * kFSet, l);
     }
     const int64_t k = int64_t(pc) * p.bh_total + bh;
 #pragma unroll
@@ -911,8 +1017,11 @@ int ssd_launch(const SsdParams& p, const SsdPlan& pl, hipStream_t s) {
     launch_kernel((ssd_gram_kernel<N, VEC>), dim3(unsigned(pl.bh_total / p.nheads * pl.nchunks)), dim3(kThreads),
                        size_t(2 * N * kRow * 2), s, p);
     if (pl.nseg > 1) {
-        launch_kernel((ssd_state_kernel<N, VEC>), dim3(unsigned((pl.nseg - 1) * pl.pps * pl.bh_total)), dim3(kThreads),
-                           StateLds<N>::bytes, s, p);
+        const dim3 sgrid(unsigned((pl.nseg - 1) * pl.pps * pl.bh_total));
+        if constexpr (VEC)
+            launch_kernel((ssd_state_dma_kernel<N>), sgrid, dim3(kThreads), StateDmaLds<N>::bytes, s, p);
+        else
+            launch_kernel((ssd_state_kernel<N, VEC>), sgrid, dim3(kThreads), StateLds<N>::bytes, s, p);
     }
     const dim3 grid(unsigned(pl.nseg * pl.bh_total));
     if (p.z)
