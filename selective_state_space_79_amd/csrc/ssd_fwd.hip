@@ -67,10 +67,12 @@ constexpr int kFSet = 4 * kQ + 4;       // floats per set (16-byte multiple)
 // LDS, in bf16 units: B[n][s], C[n][t], u[p][s], z[p][t] (the gate input; a wave's
 // outputs y[p][t] replace its rows of it once read), and the masked decay matrix
 // M[t][s] as high and low bf16 parts; then the two sets of step arrays.
-template <int N> struct OutLds {
+// With 16-byte rows (DMA) B and C arrive straight from global memory and sit in 128-byte
+// rows with swizzled pieces instead (swz_off for B, swz_c_off for C).
+template <int N, bool DMA = false> struct OutLds {
     static constexpr int Bn = 0;
-    static constexpr int Cn = Bn + N * kRow;
-    static constexpr int U = Cn + N * kRow;
+    static constexpr int Cn = Bn + N * (DMA ? 64 : kRow);
+    static constexpr int U = Cn + N * (DMA ? 64 : kRow);
     static constexpr int Z = U + kP * kRow;
     static constexpr int Mhi = Z + kP * kRow;
     static constexpr int Mlo = Mhi + kQ * kRow;
@@ -170,12 +172,20 @@ __device__ inline bf16x8 lds16(const uint16_t* q) {
 // column col0 + 4a of a [row][col] array, lane 16g + i therefore gets the four rows'
 // entries at column col0 + i: an operand whose column is the lane and whose
 // contraction index is the row.
+// Element offset of (row r, column c) in a [row][64] bf16 array of 128-byte rows whose
+// 16-byte pieces sit at position piece ^ (2 ((r >> 1) mod 4)): for the transposed reads
+// below, the four rows 2 apart that one lane group reads then take pieces in distinct
+// pairs of positions, so the group's 8-byte reads cover distinct banks.
+__device__ constexpr int swz_c_off(int r, int c) {
+    return r * 64 + (((c >> 3) ^ (2 * ((r >> 1) & 3))) << 3) + (c & 7);
+}
+
+template <bool SWZ = false>
 __device__ inline bf16x8 lds_tr(const uint16_t* base, int kb, int col0, int lane) {
     const int g = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(base + nrow(kb, g, 0, j) * kRow + col0 + 4 * a));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(base + nrow(kb, g, 1, j) * kRow + col0 + 4 * a));
+    auto at = [](int r, int c) { return SWZ ? swz_c_off(r, c) : r * kRow + c; };
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + at(nrow(kb, g, 0, j), col0 + 4 * a)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + at(nrow(kb, g, 1, j), col0 + 4 * a)));
     typedef __attribute__((ext_vector_type(8))) short s16x8;
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
@@ -430,17 +440,18 @@ __device__ inline void stage_steps(uint32_t draw, bool valid, float a, float bia
 // on distinct bank quads, as the padded 144-byte rows do for the other layout.
 __device__ constexpr int swz_off(int r, int c) { return r * 64 + (((c >> 3) ^ ((r >> 1) & 7)) << 3) + (c & 7); }
 
-template <int N, bool SWZ = false>
+template <int N, bool SWZB = false, bool SWZU = false>
 __device__ inline void chunk_state(f32x4 (&H)[N / 16], const uint16_t* sBn, const uint16_t* sU, const float* sf,
                                    int w, int lr, int lg) {
-    auto at = [](int r, int c) { return SWZ ? swz_off(r, c) : r * kRow + c; };
+    auto atb = [](int r, int c) { return SWZB ? swz_off(r, c) : r * kRow + c; };
+    auto atu = [](int r, int c) { return SWZU ? swz_off(r, c) : r * kRow + c; };
     const float dec = __builtin_amdgcn_exp2f(sf[kFTot]);
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb) H[nb] *= dec;
 #pragma unroll
     for (int kb = 0; kb < kQ / 32; ++kb) {
         const int s0 = 32 * kb + 8 * lg;
-        const u32x4 uv = *reinterpret_cast<const u32x4*>(sU + at(16 * w + lr, s0));
+        const u32x4 uv = *reinterpret_cast<const u32x4*>(sU + atu(16 * w + lr, s0));
         float xv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) xv[j] = sf[kFW + s0 + j] * bf_half(uv[j >> 1], j & 1);
@@ -449,7 +460,7 @@ __device__ inline void chunk_state(f32x4 (&H)[N / 16], const uint16_t* sBn, cons
         const bf16x8 xo_h = as_bf16x8(xh), xo_l = as_bf16x8(xl);
 #pragma unroll
         for (int nb = 0; nb < N / 16; ++nb) {
-            const bf16x8 bo = lds16(sBn + at(nrow(nb >> 1, lr >> 2, nb & 1, lr & 3), s0));
+            const bf16x8 bo = lds16(sBn + atb(nrow(nb >> 1, lr >> 2, nb & 1, lr & 3), s0));
             H[nb] = mfma(bo, xo_h, H[nb]);
             H[nb] = mfma(bo, xo_l, H[nb]);
         }
@@ -640,7 +651,7 @@ __global__ void __launch_bounds__(kThreads) ssd_state_dma_kernel(SsdParams p) {
             issue(c + 1, par ^ 1);
         }
         dsum += sf[kFTot];
-        chunk_state<N, true>(H, lds + par * Lay::Buf + Lay::Bn, lds + par * Lay::Buf + Lay::U, sf, w, lr, lg);
+        chunk_state<N, true, true>(H, lds + par * Lay::Buf + Lay::Bn, lds + par * Lay::Buf + Lay::U, sf, w, lr, lg);
         if (w == 0 && c + 1 < c1) stage_steps(draw, true, a, bias, sf0 + (par ^ 1) * kFSet, l);
     }
     const int64_t k = int64_t(pc) * p.bh_total + bh;
@@ -654,7 +665,8 @@ __global__ void __launch_bounds__(kThreads) ssd_state_dma_kernel(SsdParams p) {
 
 template <int N, bool VEC, bool GATE>
 __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
-    using Lay = OutLds<N>;
+    constexpr bool DMA = VEC;     // B and C straight from global memory into LDS
+    using Lay = OutLds<N, DMA>;
     constexpr int NK = N / 32;    // 32-wide blocks of the state index
     constexpr int NB = N / 16;    // state tiles per wave
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -722,6 +734,50 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             }
         }
     };
+    // With 16-byte rows, B and C of chunk cc go straight into LDS: load q of wave w covers
+    // rows 8 (QB w + q) .. + 7 of B (and of C), lane l row + l / 8 and the 16-byte slot
+    // l % 8 of it, which holds the row's piece (l % 8) ^ swizzle.  In the sequence's
+    // ragged last chunk a piece past L (16-byte rows: a piece lies wholly inside L or
+    // past it) would read the next row's first steps; its offset is moved past the
+    // descriptor's range instead, where the load writes zeros.
+    constexpr int QB = N / 32;
+    uint32_t voff_b[DMA ? QB : 1], voff_c[DMA ? QB : 1];
+    if constexpr (DMA) {
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+            const int r = 8 * (QB * w + q) + (l >> 3);
+            voff_b[q] = 2u * (uint32_t(r) * uint32_t(p.L) + 8u * uint32_t((l & 7) ^ ((r >> 1) & 7)));
+            voff_c[q] = 2u * (uint32_t(r) * uint32_t(p.L) + 8u * uint32_t((l & 7) ^ (2 * ((r >> 1) & 3))));
+        }
+    }
+    auto issue_bc = [&](int cc) {
+        if constexpr (DMA) {
+            const uint32_t so = uint32_t(2 * int64_t(cc) * kQ);
+            const int64_t rem = p.L - int64_t(cc) * kQ;   // the chunk's steps inside L
+            uint32_t vb[QB], vc[QB];
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                vb[q] = voff_b[q];
+                vc[q] = voff_c[q];
+            }
+            if (rem < kQ) {
+                // the chunk's offset is below 2^31, so its sum with 2^31 neither wraps nor
+                // lands inside the range (at most 2^31 - 1 bytes)
+                constexpr uint32_t kPast = 0x80000000u;
+#pragma unroll
+                for (int q = 0; q < QB; ++q) {
+                    const int r = 8 * (QB * w + q) + (l >> 3);
+                    if (8 * ((l & 7) ^ ((r >> 1) & 7)) >= rem) vb[q] = kPast;
+                    if (8 * ((l & 7) ^ (2 * ((r >> 1) & 3))) >= rem) vc[q] = kPast;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                load_lds16(src.rb, lds + Lay::Bn + (QB * w + q) * 512, vb[q], so);
+                load_lds16(src.rc, lds + Lay::Cn + (QB * w + q) * 512, vc[q], so);
+            }
+        }
+    };
     // B and C of chunk cc, from the registers into LDS (pieces past L as zeros).  They
     // go in once the chunk before has read its own B and C (its third barrier), a chunk
     // ahead of their use, so that the top of a chunk stores only u and z.
@@ -757,12 +813,16 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
     __builtin_amdgcn_sched_barrier(0);   // keep the loads in the loop's order
     load_g(c0);
     __builtin_amdgcn_sched_barrier(0);
-    load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
-    __builtin_amdgcn_sched_barrier(0);
-    load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
-    store_bc(c0);
-    load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0 + 1) * kQ, tid);
-    load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0 + 1) * kQ, tid);
+    if constexpr (DMA) {
+        issue_bc(c0);
+    } else {
+        load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0) * kQ, tid);
+        store_bc(c0);
+        load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, int64_t(c0 + 1) * kQ, tid);
+        load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, int64_t(c0 + 1) * kQ, tid);
+    }
     // The state entering the segment: h0 carried through the state pieces before it, read
     // while the first chunk's loads are in flight, three pieces' reads at a time (the
     // fold is serial, the reads are not).
@@ -806,6 +866,8 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int64_t t0 = int64_t(c) * kQ;
         const float* sf = sf0 + (c & 1) * kFSet;
+        // this wave's B and C loads for the chunk have landed (see issue_bc)
+        if constexpr (DMA) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
         lds_barrier();
         store_u(FULL);
         store_z(FULL);
@@ -865,17 +927,25 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
             const bf16x8 ho_h = as_bf16x8(hh), ho_l = as_bf16x8(hl);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const bf16x8 co = lds_tr(lds + Lay::Cn, kb, 16 * tb, l);
+                const bf16x8 co = lds_tr<DMA>(lds + Lay::Cn, kb, 16 * tb, l);
                 yo[tb] = mfma(co, ho_h, yo[tb]);
                 yo[tb] = mfma(co, ho_l, yo[tb]);
             }
         }
 
-        chunk_state<N>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
+        chunk_state<N, DMA, false>(H, lds + Lay::Bn, lds + Lay::U, sf, w, lr, lg);
         lds_barrier();   // M complete; this chunk's B and C read
-        store_bc(c + 1);
-        load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, t0 + 2 * kQ, tid);
-        load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, t0 + 2 * kQ, tid);
+        if constexpr (DMA) {
+            issue_bc(c + 1);
+            // the only vector-memory operations after these loads in a chunk are its two
+            // 16-byte y stores per lane: the top of the next chunk waits for the loads
+            // with vmcnt(2) (vector memory completes in issue order)
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            store_bc(c + 1);
+            load_chunk<N, true, VEC, 1>(nx, src, p, b, bh, t0 + 2 * kQ, tid);
+            load_chunk<N, true, VEC, 2>(nx, src, p, b, bh, t0 + 2 * kQ, tid);
+        }
 
         // within the chunk: yd[tb][t][p] = sum_{s} M[t][s] u[s][p] over the 32-step
         // blocks that reach the diagonal of t block tb
@@ -931,6 +1001,8 @@ __global__ void __launch_bounds__(kThreads) ssd_out_kernel(SsdParams p) {
         }
         if (w == 0) stage_steps(nx.draw, t0 + kQ + l < p.L, a, bias, sf0 + ((c + 1) & 1) * kFSet, l);
     };
+    // the first chunk's B and C (the loop's own wait counts only the chunks' loads)
+    if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int c_full = std::min<int64_t>(c1, p.L / kQ);   // chunks wholly inside L
     int c = c0;
     for (; c < c_full; ++c) chunk(c, std::true_type{});
