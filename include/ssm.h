@@ -312,7 +312,12 @@ SSM_API int ssm_selective_scan_fwd_noalloc(const void* u, const void* delta, con
 SSM_API const char* ssm_status_string(int status);
 
 /* How a call would be run: pieces per sequence, states per lane, lanes' waves per
- * workgroup, time tile and workgroup count.  Returns an ssm_status value; fills
+ * workgroup, time tile and workgroup count of the lane walk, and which form runs the
+ * full pass: form 0 is the lane walk; form 1 (a scalar decay with bf16 rows of 64 or
+ * 128 states and the library's choice of states per lane) is the chunked form, whose
+ * state reads and updates are matrix-core products over 16-step chunks, used when the
+ * call's rows also allow 16-byte loads (else the walk runs with the same pieces);
+ * lds_bytes is that of the form's full pass.  Returns an ssm_status value; fills
  * *plan only on SSM_OK.  Pure host function, never touches the device. */
 typedef struct ssm_plan {
     int32_t nchunks;
@@ -323,6 +328,8 @@ typedef struct ssm_plan {
     int64_t workgroups;
     size_t workspace_bytes;
     size_t lds_bytes;
+    int32_t form;
+    int32_t reserved;
 } ssm_plan;
 SSM_API int ssm_selective_scan_plan(const ssm_dims* dims, ssm_plan* plan);
 

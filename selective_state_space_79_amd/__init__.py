@@ -74,6 +74,8 @@ class SsmPlan(ctypes.Structure):
         ("workgroups", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
         ("lds_bytes", ctypes.c_size_t),
+        ("form", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     def as_dict(self):

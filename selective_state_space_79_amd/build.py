@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", name) for name in ("scan_fwd.hip", "scan_bwd.hip", "ssd_fwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("scan_fwd.hip", "scan_bwd.hip", "ssd_fwd.hip", "scan_chunked.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
 

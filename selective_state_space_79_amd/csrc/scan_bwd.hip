@@ -1895,6 +1895,8 @@ int ssm_selective_scan_bwd_plan(const ssm_dims* dims, ssm_plan* plan) {
     plan->workgroups = pl.groups * pl.nch;
     plan->workspace_bytes = pl.ws_bytes;
     plan->lds_bytes = pl.lds_grad;
+    plan->form = 0;
+    plan->reserved = 0;
     return SSM_OK;
 }
 

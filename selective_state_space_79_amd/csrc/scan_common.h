@@ -212,3 +212,31 @@ struct PieceStatesArgs {
 // from piece_base; returns false (launching nothing) when nstate is not supported.
 bool launch_piece_states(const PieceStatesArgs& a, bool reverse, int64_t npieces, hipStream_t s);
 }  // namespace ssm_detail
+
+// The full pass in chunked form for a scalar decay per head with a step size per channel
+// (scan_chunked.hip): bf16 rows that allow 16-byte loads, 64 or 128 states.  One
+// workgroup per (batch row, 64-channel block, piece); every piece starts from Hin
+// ([groups][nchunks][nstate][64], the piece carries) when nchunks > 1, else from h0 or
+// zero; the last piece writes h_last when given.
+namespace ssm_detail {
+struct ChunkedArgs {
+    const void* u;
+    const void* delta;
+    const void* z;        // nullable
+    const void* B;
+    const void* C;
+    const float* A;       // (nheads,)
+    const float* D;       // nullable
+    const float* bias;    // nullable
+    void* y;
+    const float* h0;      // nullable
+    float* h_last;        // nullable
+    const float* Hin;     // piece starting states when nchunks > 1
+    int64_t L, dim, nstate, head_dim, chunk_len;
+    int32_t nchunks, nblk_d, batch;
+};
+bool chunked_supported(int64_t nstate);
+size_t chunked_lds_bytes(int64_t nstate);
+// Launches the full pass; returns false (launching nothing) when nstate is not supported.
+bool launch_chunked(const ChunkedArgs& a, hipStream_t s);
+}  // namespace ssm_detail

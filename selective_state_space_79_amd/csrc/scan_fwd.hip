@@ -1346,6 +1346,7 @@ struct Plan {
     size_t ws_bytes;
     size_t lds_bytes;
     bool scalar;
+    int form;           // 0: lane walk; 1: chunked form on the matrix cores (scan_chunked.hip)
 };
 
 
@@ -1373,8 +1374,26 @@ int make_plan(const ssm_dims* d, Plan* pl) {
     pl->nblk_d = cdiv(d->dim, kLanes);
     const int64_t groups = d->batch * pl->nblk_d;
     const int64_t tiles = cdiv(d->seqlen, pl->T);
+    // A scalar decay with bf16 rows of 64 or 128 states and the library's choice of
+    // states per lane runs its full pass in the chunked form (when, at the call, the rows
+    // also allow 16-byte loads; else the walk runs with the same pieces).
+    const int64_t rows_bytes = (N > kLanes ? N : kLanes) * d->seqlen * 2;
+    pl->form = (pl->scalar && d->io_dtype == SSM_BF16 && ssm_detail::chunked_supported(N) &&
+                d->states_per_lane == 0 && d->seqlen % 8 == 0 && pl->T == 16 && rows_bytes < (int64_t(1) << 31))
+                   ? 1 : 0;
     int64_t nch = d->nchunks;
-    if (nch == 0) {
+    if (nch == 0 && pl->form == 1) {
+        // The chunked pass holds 3 workgroups per CU (160 VGPRs: three waves per SIMD);
+        // its pieces' carries come from the matrix-core aggregate, so aim for one full
+        // round of 3 x 256 workgroups, at least 8 tiles per piece.
+        const int64_t slots = 3 * 256;
+        const int64_t max_pieces = tiles / 8 > 1 ? tiles / 8 : 1;
+        nch = cdiv(slots, groups);
+        const int64_t cap = max_pieces < SSM_MAX_CHUNKS ? max_pieces : SSM_MAX_CHUNKS;
+        nch = round_friendly_pieces(groups, nch, cap, slots);
+        if (nch > cap) nch = cap;
+        if (nch < 1) nch = 1;
+    } else if (nch == 0) {
         // One wave per SIMD (256 CUs x 4 SIMDs) is the floor below which the sequence is
         // cut into pieces; pieces cost a second pass over all but the last, so cut
         // only when the machine would otherwise be at most half busy.
@@ -1415,7 +1434,7 @@ int make_plan(const ssm_dims* d, Plan* pl) {
         size_t bytes = per * np * 2 + per;   // H, Hin, S
         pl->ws_bytes = (bytes + 255) & ~size_t(255);
     }
-    pl->lds_bytes = lds_floats_g(pl->G, spl, true) * sizeof(float);
+    pl->lds_bytes = pl->form == 1 ? ssm_detail::chunked_lds_bytes(N) : lds_floats_g(pl->G, spl, true) * sizeof(float);
     return SSM_OK;
 }
 
@@ -1463,6 +1482,32 @@ hipError_t launch_all(const Params& p, const Plan& pl, hipStream_t stream) {
                                stream, p);
         const int64_t total = groups * p.np * kLanes;
         launch_kernel(scan_carry_kernel, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, p, total);
+    }
+    if constexpr (SCALAR && VEC && !CONV && !CK && std::is_same<IO, uint16_t>::value) {
+        if (pl.form == 1) {
+            ssm_detail::ChunkedArgs a;
+            a.u = p.u;
+            a.delta = p.delta;
+            a.z = p.z;
+            a.B = p.Bm;
+            a.C = p.Cm;
+            a.A = p.A;
+            a.D = p.Dskip;
+            a.bias = p.bias;
+            a.y = p.y;
+            a.h0 = p.h0;
+            a.h_last = p.h_last;
+            a.Hin = p.ws_Hin;
+            a.L = p.L;
+            a.dim = p.dim;
+            a.nstate = p.N;
+            a.head_dim = p.head_dim;
+            a.chunk_len = p.chunk_len;
+            a.nchunks = p.nchunks;
+            a.nblk_d = p.nblk_d;
+            a.batch = p.batch;
+            if (ssm_detail::launch_chunked(a, stream)) return ssm_detail::launch_error;
+        }
     }
     launch_kernel((scan_fwd_kernel<IO, SPL, SCALAR, kFull, VEC, G, CK, CONV>), dim3(unsigned(pl.blocks)), block,
                        lds_full, stream, p);
@@ -1558,6 +1603,8 @@ int ssm_selective_scan_plan(const ssm_dims* dims, ssm_plan* plan) {
     plan->workgroups = pl.blocks;
     plan->workspace_bytes = pl.ws_bytes;
     plan->lds_bytes = pl.lds_bytes;
+    plan->form = pl.form;
+    plan->reserved = 0;
     return SSM_OK;
 }
 

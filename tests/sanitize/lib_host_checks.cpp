@@ -94,10 +94,14 @@ static void forward_sweep() {
                             CHECK(n == (pl.nchunks > 1 ? 3u : 1u), "launches %zu for %d pieces", n, pl.nchunks);
                             if (n >= 1) {
                                 CHECK(stub_launch_grid(n - 1) == unsigned(pl.workgroups), "grid %u", stub_launch_grid(n - 1));
-                                CHECK(stub_launch_lds(n - 1) == pl.lds_bytes, "lds %zu vs %zu", stub_launch_lds(n - 1),
-                                      pl.lds_bytes);
-                                CHECK(strstr(stub_launch_name(n - 1), "scan_fwd_kernel") != nullptr, "%s",
-                                      stub_launch_name(n - 1));
+                                // the chunked form's full pass (form 1; the sweep's pointers allow
+                                // 16-byte loads) holds its LDS statically, the lane walk asks for it
+                                const bool chunked = pl.form == 1;
+                                CHECK(stub_launch_lds(n - 1) == (chunked ? 0 : pl.lds_bytes), "lds %zu vs %zu",
+                                      stub_launch_lds(n - 1), pl.lds_bytes);
+                                CHECK(strstr(stub_launch_name(n - 1), chunked ? "scan_chunked_kernel" : "scan_fwd_kernel") !=
+                                          nullptr,
+                                      "%s", stub_launch_name(n - 1));
                             }
                             ++calls;
                             // the no-allocation entry point: same launches, no workspace

@@ -112,11 +112,27 @@ def test_plans_of_the_five_workloads(index):
         assert plan["nchunks"] > 1 and plan["workspace_bytes"] > 0     # too few channels to fill the GPU
     if index == 3:
         assert plan["nchunks"] == 1 and plan["workspace_bytes"] == 0
+    assert plan["form"] == (1 if index == 5 else 0)
     if index == 5:
-        # 128 channel blocks would leave half of the 256 CUs idle; with the first pass on
-        # the matrix cores (scalar decay, bf16, 128 states) pieces are cheap and the plan
-        # aims at two workgroups per CU
-        assert plan["nchunks"] == 4
+        # scalar decay, bf16, 128 states: the chunked form (three 4-wave workgroups per
+        # CU), whose pieces' carries come from the matrix-core aggregate, so the plan
+        # fills one round of 768 workgroups: 128 channel blocks x 6 pieces
+        assert plan["nchunks"] == 6 and plan["workgroups"] == 768
+
+
+def test_chunked_form_only_where_it_applies():
+    """Form 1 needs a scalar decay, bf16 rows, 64 or 128 states, the library's choice of
+    states per lane and L % 8 == 0; everything else keeps the lane walk."""
+    form = lambda *a, **k: ssm.ssm_selective_scan_plan(ssm.make_dims(*a, **k)).form
+    assert form(1, 256, 128, 128, nheads=2) == 1
+    assert form(1, 256, 128, 64, nheads=2) == 1
+    assert form(1, 256, 128, 32, nheads=2) == 0                        # 32 states
+    assert form(1, 256, 128, 128, nheads=0) == 0                       # diagonal A
+    assert form(1, 256, 128, 128, nheads=2, io_dtype=ssm.SSM_F32) == 0
+    assert form(1, 252, 128, 128, nheads=2) == 0                       # L % 8 != 0
+    assert form(1, 256, 128, 128, nheads=2, states_per_lane=16) == 0   # forced walk layout
+    assert form(1, 256, 128, 128, nheads=2, nchunks=3) == 1            # forced pieces keep it
+    assert ssm.ssm_selective_scan_bwd_plan(ssm.make_dims(1, 256, 128, 128, nheads=2)).form == 0
 
 
 @pytest.mark.parametrize("shape, fwd_pieces, bwd_pieces", [

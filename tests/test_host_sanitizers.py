@@ -1,7 +1,7 @@
 """The library's host code and the oracle under AddressSanitizer and
 UndefinedBehaviorSanitizer, on the CPU.
 
-* The three HIP sources are compiled for the host only (no device code) with ASan and
+* The HIP sources are compiled for the host only (no device code) with ASan and
   UBSan and linked with tests/sanitize/hip_stub.cpp in place of the HIP runtime: the
   checks in tests/sanitize/lib_host_checks.cpp sweep the planners over shapes, call
   every entry point (nothing reaches a device; the stub checks and records each
@@ -39,7 +39,7 @@ def test_library_host_code_under_sanitizers(tmp_path):
     for flag in SAN:
         host += ["-Xarch_host", flag]
     objs, procs = [], []
-    for name in ("scan_fwd", "scan_bwd", "ssd_fwd"):
+    for name in ("scan_fwd", "scan_bwd", "ssd_fwd", "scan_chunked"):
         obj = str(tmp_path / f"{name}.o")
         objs.append(obj)
         procs.append(subprocess.Popen([HIPCC, *host, "-c", "-o", obj, os.path.join(CSRC, f"{name}.hip")],
