@@ -38,9 +38,12 @@ OPS_PER_UPDATE = 5
 # state entries; per update x*B (mul), a*h + b (fma), C*h + y (fma)
 OPS_PER_UPDATE_SCALAR = 3
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_79_amd", "csrc", "scan_fwd.hip")
+CHUNKED_SRC = os.path.join(ROOT, "selective_state_space_79_amd", "csrc", "scan_chunked.hip")
+CHUNKED_FILE = os.path.join(ROOT, "profiles", "scan_chunked_scalar_decay_counters.json")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_mamba13b_hbm_traffic.json")
 VALU_FILE = os.path.join(ROOT, "profiles", "scan_fwd_mamba13b_valu_issue.json")
 SIMDS = 256 * 4
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 CLOCK_HZ = 2.4e9
 
 # Untimed warm-up runs for at least this long, whatever --warmup asks for: the GPU clock
@@ -164,6 +167,24 @@ def scan_workload_bench(x, dev, steps: int, warmup: int, stream, extra_sets=None
            "updates_per_s": x.updates / (t["ms_per_step"] * 1e-3), "gbs": round(gbs, 1),
            "input_sets_rotated": len(sets), "hbm": hbm, "alu": alu,
            "roofline": alu if alu["frac"] >= hbm["frac"] else hbm}
+    if plan.get("form") == 1:
+        # the chunked form does not walk the recurrence (3 operations per state update):
+        # its contractions over the state are matrix products, so it is measured against
+        # the matrix-core and HBM roofs, and its VALU issue comes from the counters
+        del rec["alu"]
+        mf = chunked_mfma_flops(x, plan)
+        tf = mf / (ms * 1e-3) / 1e12
+        mfma = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "flops_per_call": mf,
+                "note": "bf16 matrix work the chunked form issues (fp32 operands split in two bf16 parts count "
+                        "twice): C^T B per 16-step chunk in each of a workgroup's 4 waves, the state read and the "
+                        "state update per chunk, and the piece aggregate of all pieces but the last"}
+        rec["form"] = "chunked: state read, state update and C^T B on the matrix cores per 16-step chunk"
+        rec["mfma"] = mfma
+        rec["roofline"] = mfma if mfma["frac"] >= hbm["frac"] else hbm
+        vi = measured_chunked_issue(x, ms)
+        if vi:
+            rec["valu_issue"] = vi
     if plan["nchunks"] == 1 and not scalar:
         vi = measured_valu_issue(x, ms)
         if vi:
@@ -265,6 +286,46 @@ def measured_valu_issue(x, ms):
                     "per state update; counters from " + os.path.relpath(VALU_FILE, ROOT)}
 
 
+def chunked_hash() -> str:
+    with open(CHUNKED_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def chunked_mfma_flops(x, plan) -> float:
+    """bf16 matrix flops one call of the chunked form issues (split operands twice):
+    per 64-channel block and 16-step chunk, C^T B (16 x 16, depth N) in each of the 4
+    waves, the state read (16 x 64, depth N, two parts) and the state update (N x 64,
+    depth 16, two parts); the matrix-core piece aggregate adds N x 64 depth-1 products
+    in two parts per step of every piece but the last."""
+    import math
+
+    blocks = x.batch * math.ceil(x.dim / 64)
+    chunks = math.ceil(x.L / 16)
+    per = 4 * 2 * 16 * 16 * x.N + 2 * 2 * 16 * 64 * x.N + 2 * 2 * x.N * 64 * 16
+    agg_steps = min(x.L, (plan["nchunks"] - 1) * plan["chunk_len"])
+    return float(blocks * chunks * per + blocks * agg_steps * 2 * 2 * x.N * 64)
+
+
+def measured_chunked_issue(x, ms):
+    """VALU issue of the chunked form's kernels (piece aggregate, carry, chunked pass)
+    from the committed rocprofv3 counters, if they were taken on the current source and
+    this shape; else None."""
+    try:
+        with open(CHUNKED_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != chunked_hash() or rec.get("shape") != [x.batch, x.L, x.dim, x.N]:
+        return None
+    v, tr = rec["SQ_INSTS_VALU"], rec["SQ_INSTS_VALU_TRANS_F32"]
+    cycles = 4 * (v + tr)
+    avail = SIMDS * CLOCK_HZ * ms * 1e-3
+    return {"valu_instructions_per_call": v, "trans_instructions_per_call": tr, "issue_cycles_per_call": cycles,
+            "issue_frac": round(cycles / avail, 4),
+            "note": "issue_frac = 4*(VALU+TRANS) cycles of the call's kernels / (1024 SIMDs x 2.4 GHz x call time); "
+                    "counters from " + os.path.relpath(CHUNKED_FILE, ROOT)}
+
+
 def cpu_baseline(x, rows_batches: int, repeats: int = 3):
     """Time the fp64 oracle on the first ``rows_batches`` batch rows (all channels,
     the full sequence) of the same inputs, with all host threads OpenMP offers;
@@ -327,6 +388,11 @@ PROFILE_COMMANDS = {
                     "GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d {d}/bwdctr -o scan -- python3 bench.py "
                     "--steps 3 --warmup 1 --min-warmup-s 0 --no-cpu-baseline --no-decode --no-ssd --no-workloads "
                     "--no-linear",
+    "chunked_counters": "rocprofv3 --kernel-include-regex 'scan_chunked|scan_piece_states|scan_carry' --pmc SQ_WAVES "
+                        "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
+                        "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS GRBM_GUI_ACTIVE --kernel-trace --output-format csv "
+                        "-d {d}/chkctr -o scan -- python3 bench.py --steps 3 --warmup 1 --min-warmup-s 0 "
+                        "--no-cpu-baseline --no-backward --no-decode --no-ssd --no-linear --only-workloads 5",
     "ssd_counters": "rocprofv3 --kernel-include-regex ssd_ --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
                     "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
                     "GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d {d}/ssdctr -o scan -- python3 bench.py "
@@ -457,6 +523,55 @@ def summarize_profiles(d):
             md += _trace_table(ssd + scal, 120)
             with open(os.path.join(ROOT, "profiles", "ssd_fwd_scalar_decay_head_dt.md"), "w") as f:
                 f.write("\n".join(md) + "\n")
+
+    # the chunked form of the scalar-decay scan (workload 5): kernel times from the stats
+    # pass, occupancy and issue counters from their own pass
+    chk_rows = [r for r in _trace_rows(stats_trace) if "scan_chunked_kernel" in r["name"]
+                or ("scan_piece_states_kernel<128, false>" in r["name"]) or "scan_carry_kernel" in r["name"]] \
+        if stats_trace else []
+    ctr_path = _find(d, "chkctr", "counter_collection.csv")
+    if chk_rows or ctr_path:
+        x5 = make_workload(5)
+        md = ["# Chunked form of the scalar-decay scan, per-channel step sizes (workload 5: batch 2, L 8192, dim "
+              "4096 in 64 heads, N 128, bf16): rocprofv3 kernel times and counters", "",
+              f"Kernel source (`csrc/scan_chunked.hip`) sha256[:16]: `{chunked_hash()}`", "",
+              "One call launches `scan_piece_states_kernel<128, false>` (the end states of all pieces but the last, "
+              "on the matrix cores), `scan_carry_kernel` (the pieces' starting states) and "
+              "`scan_chunked_kernel<128>` (the full pass).", ""]
+        if chk_rows:
+            md += ["Kernel times, from the default bench's stats pass (all kernels of these names; the per-head "
+                   "duality pass of `ssd_fwd_scalar_decay_head_dt.md` launches other kernels):", "",
+                   "    " + cmd("stats"), ""]
+            md += _trace_table(chk_rows, 100)
+            md.append("")
+        if ctr_path:
+            c = {}
+            for r in csv.DictReader(open(ctr_path)):
+                c.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            md += ["Counters (medians per dispatch), command:", "", "    " + cmd("chunked_counters"), "",
+                   "`GRBM_GUI_ACTIVE` is summed over the 8 XCDs (cycles = a eighth of it); `SQ_WAVE_CYCLES` counts "
+                   "resident wave-cycles in units of 4 cycles; issue = 4 x (VALU + TRANS) SIMD-cycles over 1024 SIMDs.",
+                   "", "| kernel | waves | cycles | waves/SIMD | VALU | TRANS | issue frac | MFMA busy | LDS instr |",
+                   "|---|---|---|---|---|---|---|---|---|"]
+            tot = {"SQ_INSTS_VALU": 0.0, "SQ_INSTS_VALU_TRANS_F32": 0.0}
+            for name, cs in sorted(c.items(), key=lambda kv: -statistics.median(kv[1].get("SQ_INSTS_VALU", [0]))):
+                med = {k: statistics.median(v) for k, v in cs.items()}
+                cyc = med.get("GRBM_GUI_ACTIVE", 0) / 8
+                if cyc <= 0:
+                    continue
+                for k in tot:
+                    tot[k] += med.get(k, 0)
+                iss = 4 * (med.get("SQ_INSTS_VALU", 0) + med.get("SQ_INSTS_VALU_TRANS_F32", 0)) / (SIMDS * cyc)
+                md.append(f"| `{name[:90]}` | {med.get('SQ_WAVES', 0):.0f} | {cyc:.4g} | "
+                          f"{4 * med.get('SQ_WAVE_CYCLES', 0) / (SIMDS * cyc):.2f} | {med.get('SQ_INSTS_VALU', 0):.4g} | "
+                          f"{med.get('SQ_INSTS_VALU_TRANS_F32', 0):.4g} | {iss:.3f} | "
+                          f"{med.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / (SIMDS * cyc):.3f} | {med.get('SQ_INSTS_LDS', 0):.4g} |")
+            rec = {"kernels": sorted(c), "shape": [x5.batch, x5.L, x5.dim, x5.N],
+                   "kernel_source_sha256_16": chunked_hash(), "command": cmd("chunked_counters"), **tot}
+            with open(CHUNKED_FILE, "w") as f:
+                json.dump(rec, f, indent=1)
+        with open(os.path.join(ROOT, "profiles", "scan_chunked_scalar_decay.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
 
     # occupancy and matrix-core use of the duality pass's kernels
     if _find(d, "ssdctr", "counter_collection.csv"):
@@ -827,7 +942,6 @@ def backward_bench(x, dev, steps: int = 40, warmup: int = 15):
     return rec
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def ssd_bench(steps: int = 100, warmup: int = 30):
@@ -924,6 +1038,8 @@ def main():
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other named workloads (tiny, 130M layer, long sequence, scalar decay N=128)")
     ap.add_argument("--no-linear", action="store_true", help="skip the linear-in-L check")
+    ap.add_argument("--only-workloads", default="", help="comma-separated indices of the other workloads to time "
+                    "(default: all but the headline)")
     ap.add_argument("--min-warmup-s", type=float, default=MIN_WARMUP_S,
                     help="least wall time of untimed warm-up before each timed loop (seconds)")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 2 GiB device copy (counter calibration)")
@@ -1018,6 +1134,8 @@ def main():
         rec["linear_in_L"] = linear_in_L_bench(args.steps, args.warmup, stream)
     if not args.no_workloads:
         others = [i for i in (1, 2, 3, 4, 5) if i != args.workload]
+        if args.only_workloads:
+            others = [i for i in others if str(i) in args.only_workloads.split(",")]
         rec["workloads"] = other_workloads_bench(others, args.steps, args.warmup, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_batches)

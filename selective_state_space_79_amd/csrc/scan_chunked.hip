@@ -175,31 +175,28 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
     const Rsrc rC = make_rsrc(static_cast<const uint16_t*>(p.C) + bcoff, N * rowbytes);
     const uint32_t lane_off = uint32_t(chl) * uint32_t(rowbytes) + 8u * uint32_t(g);
 
-    // B/C staging: piece v = tid + 256 k of the chunk is matrix v / (2N) (B, then C),
-    // row (v % 2N) / 2, steps 8 (v % 2) .. +7
-    uint32_t bc_goff[VPT];
-    int bc_loff[VPT], bc_h[VPT];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int v = tid + kThreads * k;
-        const int n = (v % (2 * N)) >> 1, h = v & 1;
-        bc_goff[k] = uint32_t(n) * uint32_t(rowbytes) + 16u * uint32_t(h);
-        bc_loff[k] = (v / (2 * N)) * MAT + n * kQ + 8 * (h ^ ((n >> 3) & 1));
-        bc_h[k] = h;
-    }
-    // the matrix of piece k: for N = 128 piece 0 is B and piece 1 is C for every thread;
-    // for N = 64 waves 0-1 load B and waves 2-3 C (wave-uniform either way)
-    auto bc_rsrc = [&](int k) { return ((tid + kThreads * k) / (2 * N)) == 0 ? rB : rC; };
+    // B/C staging, one 16-byte piece (8 steps of a row) per thread and matrix: for
+    // N = 128 every thread loads row tid / 2 of B and of C; for N = 64 waves 0-1 load B
+    // and waves 2-3 C (the descriptor is chosen per wave, never per lane)
+    const int bc_n = (N == 128 ? tid : (tid & 127)) >> 1, bc_h = tid & 1;
+    const uint32_t bc_goff = uint32_t(bc_n) * uint32_t(rowbytes) + 16u * uint32_t(bc_h);
+    const int bc_loff = bc_n * kQ + 8 * (bc_h ^ ((bc_n >> 3) & 1));
     auto load_bc = [&](u32x4 (&v)[VPT], int64_t t0) {
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const bool in = t0 + 8 * bc_h[k] < p.L;
-            v[k] = __builtin_amdgcn_raw_buffer_load_b128(bc_rsrc(k), in ? bc_goff[k] + uint32_t(2 * t0) : kPast, 0, 0);
+        const uint32_t off = (t0 + 8 * bc_h < p.L) ? bc_goff + uint32_t(2 * t0) : kPast;
+        if constexpr (N == 128) {
+            v[0] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+            v[1] = __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 0);
+        } else {
+            v[0] = __builtin_amdgcn_raw_buffer_load_b128(wv < 2 ? rB : rC, off, 0, 0);
         }
     };
     auto store_bc = [&](const u32x4 (&v)[VPT], int buf) {
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) *reinterpret_cast<u32x4*>(&sBC[buf][bc_loff[k]]) = v[k];
+        if constexpr (N == 128) {
+            *reinterpret_cast<u32x4*>(&sBC[buf][bc_loff]) = v[0];
+            *reinterpret_cast<u32x4*>(&sBC[buf][MAT + bc_loff]) = v[1];
+        } else {
+            *reinterpret_cast<u32x4*>(&sBC[buf][(wv < 2 ? 0 : MAT) + bc_loff]) = v[0];
+        }
     };
     auto elem_off = [&](int64_t t0) {
         return (dok && t0 + 4 * g < tend) ? lane_off + uint32_t(2 * t0) : kPast;
@@ -223,6 +220,8 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
             for (int r = 0; r < 4; ++r) H[jt][r] = h0[16 * jt + 4 * g + r];
     }
 
+    float sc = 1.0f;   // the true state is sc * H (sc per channel)
+
     // ---- chunk 0's inputs
     u32x4 bcv[VPT];
     load_bc(bcv, tbeg);
@@ -233,33 +232,31 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
     store_bc(bcv, 0);
     lds_barrier();
 
+    // Every prefetch register is reloaded right after its last use (no copies between
+    // loop-carried registers, whose waits would drain the outstanding stores too).  The
+    // loads after a piece's last chunk read zeros or the next piece's data, unused.
     for (int q = 0; q < nq; ++q) {
         const int64_t t0 = tbeg + int64_t(q) * kQ;
         const uint16_t* sb = sBC[q & 1];
-        const bool more = q + 1 < nq;
-        // the next chunk's loads, in flight during this chunk
-        u32x2 drn = dr, uun = uu, zzn = zz;
         const uint32_t eoffn = elem_off(t0 + kQ);
-        if (more) {
-            load_bc(bcv, t0 + kQ);
-            drn = __builtin_amdgcn_raw_buffer_load_b64(rd, eoffn, 0, 0);
-            uun = __builtin_amdgcn_raw_buffer_load_b64(ru, eoffn, 0, 0);
-            zzn = __builtin_amdgcn_raw_buffer_load_b64(rz, eoffn, 0, 0);
-        }
+        load_bc(bcv, t0 + kQ);
 
         // ---- elementwise: steps 4g..4g+3 of channel chl (steps past the piece are
         // identity steps: dt2 = 0, x = 0)
         const bool valid = dok && t0 + 4 * g < tend;
         const float draw[4] = {bf_lo(dr[0]), bf_hi(dr[0]), bf_lo(dr[1]), bf_hi(dr[1])};
         const float uv[4] = {bf_lo(uu[0]), bf_hi(uu[0]), bf_lo(uu[1]), bf_hi(uu[1])};
-        float dt2[4], xs[4], al[4], pre[4];
+        float dt2[4], xs[4], al[4], pre[4], skip[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             dt2[i] = valid ? softplus_log2(draw[i] + bias) : 0.0f;
             xs[i] = valid ? dt2[i] * uv[i] : 0.0f;        // x / ln2
             al[i] = __builtin_amdgcn_exp2f(a * dt2[i]);
             pre[i] = (i == 0) ? dt2[0] : pre[i - 1] + dt2[i];
+            skip[i] = Dd * uv[i];
         }
+        dr = __builtin_amdgcn_raw_buffer_load_b64(rd, eoffn, 0, 0);
+        uu = __builtin_amdgcn_raw_buffer_load_b64(ru, eoffn, 0, 0);
         sw[kTot + 4 * c + g] = pre[3];
         *reinterpret_cast<f32x4*>(&sw[kAl + c * kRs + 4 * g]) = f32x4{al[0], al[1], al[2], al[3]};
         *reinterpret_cast<f32x4*>(&sw[kXs + c * kRs + 4 * g]) = f32x4{xs[0], xs[1], xs[2], xs[3]};
@@ -267,16 +264,16 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
         const f32x4 tot = *reinterpret_cast<const f32x4*>(&sw[kTot + 4 * c]);
         const float excl = g == 0 ? 0.0f : g == 1 ? tot[0] : g == 2 ? tot[0] + tot[1] : tot[0] + tot[1] + tot[2];
         const float cumq = (tot[0] + tot[1]) + (tot[2] + tot[3]);
-        // read-out decays E(t,-1) = 2^(a cum_t); state weights ln2 2^(a (cumq - cum_s)) x_s / ln2
-        float ev[4], wx[4];
+        // The state is held scaled: the true state is sc * H, so a chunk's decay changes
+        // sc (one multiply) instead of every entry of H.  The read-out decays
+        // sc * E(t,-1) = sc 2^(a cum_t) are a running product of the steps' decays from
+        // one exponential.
         constexpr float kLog2Ln2 = -0.5287663729448977f;   // log2(ln 2)
+        float ev[4], wx[4];
+        ev[0] = sc * __builtin_amdgcn_exp2f(a * (excl + pre[0]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float cum = excl + pre[i];
-            ev[i] = __builtin_amdgcn_exp2f(a * cum);
-            wx[i] = __builtin_amdgcn_exp2f(fmaf(a, cumq - cum, kLog2Ln2)) * xs[i];
-        }
-        const float decay = __builtin_amdgcn_exp2f(a * cumq);
+        for (int i = 1; i < 4; ++i) ev[i] = ev[i - 1] * al[i];
+        float scn = sc * __builtin_amdgcn_exp2f(a * cumq);
 
         // ---- matrix cores: G = C^T B, the state read C^T H, the state update
         bf16x8 ct[NKB];
@@ -296,6 +293,22 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
             rd4 = mfma(ct[kb], __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), rd4);
         }
         {
+            // the state update of the scaled state: when some lane's new scale would fall
+            // below 2^-60 the wave first folds the scales into H (scale 1), so that 1 / scale
+            // stays finite; the weights ln2 2^(a (cumq - cum_s)) (x_s / ln2) / scale are a
+            // running product of the steps' decays from one exponential
+            if (__builtin_amdgcn_ballot_w64(scn < 0x1p-60f) != 0) {
+#pragma unroll
+                for (int jt = 0; jt < NT; ++jt) H[jt] *= scn;
+                scn = 1.0f;
+            }
+            float rw = __builtin_amdgcn_exp2f(fmaf(a, cumq - (excl + pre[3]), kLog2Ln2)) * __builtin_amdgcn_rcpf(scn);
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                wx[i] = rw * xs[i];
+                if (i > 0) rw *= al[i];
+            }
+            sc = scn;
             uint32_t whi[2], wlo[2];
             split2(wx[0], wx[1], whi[0], wlo[0]);
             split2(wx[2], wx[3], whi[1], wlo[1]);
@@ -304,7 +317,7 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
             for (int jt = 0; jt < NT; ++jt) {
                 const int n = 16 * jt + c;
                 const u32x2 bw = *reinterpret_cast<const u32x2*>(sb + bc_off(n, g));
-                H[jt] = mfma(__builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[0], bw[1]}), xop, H[jt] * decay);
+                H[jt] = mfma(__builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[0], bw[1]}), xop, H[jt]);
             }
         }
         // G (times ln2) into the wave's [t][s] array: rows 4g..4g+3 of column c
@@ -312,36 +325,31 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
         for (int r = 0; r < 4; ++r) sw[kG + (4 * g + r) * kRs + c] = gm[r] * kLn2;
         __builtin_amdgcn_wave_barrier();
 
-        // ---- in-chunk part, per channel in Horner form
-        float alc[16], xsc[16];
+        // ---- in-chunk part, per channel in Horner form: output k of the lane (step
+        // t_k = horner_t(k, g), k = 0..3) takes acc <- acc * al_s + G[t_k][s] x_s over
+        // s = 0..t_k.  The steps go in blocks of 4 (the block's decays and values read
+        // once, as 16-byte vectors); block m feeds the outputs k >= m, and only the
+        // last block of output k has steps past t_k in some lanes.
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        int tk[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const f32x4 va = *reinterpret_cast<const f32x4*>(&sw[kAl + c * kRs + 4 * k]);
-            const f32x4 vx = *reinterpret_cast<const f32x4*>(&sw[kXs + c * kRs + 4 * k]);
+        for (int k = 0; k < 4; ++k) tk[k] = horner_t(k, g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                alc[4 * k + e] = va[e];
-                xsc[4 * k + e] = vx[e];
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 va = *reinterpret_cast<const f32x4*>(&sw[kAl + c * kRs + 4 * m]);
+            const f32x4 vx = *reinterpret_cast<const f32x4*>(&sw[kXs + c * kRs + 4 * m]);
+#pragma unroll
+            for (int k = m; k < 4; ++k) {
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(&sw[kG + tk[k] * kRs + 4 * m]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float nv = fmaf(acc[k], va[e], gv[e] * vx[e]);
+                    acc[k] = (m < k || 4 * m + e <= tk[k]) ? nv : acc[k];   // steps 0..4k are <= t_k in every lane
+                }
             }
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int t = horner_t(k, g);
-            float grow[16];
-#pragma unroll
-            for (int m = 0; m <= k; ++m) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&sw[kG + t * kRs + 4 * m]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) grow[4 * m + e] = v[e];
-            }
-            float acc = 0.0f;
-#pragma unroll
-            for (int s = 0; s <= 4 * k + 3; ++s) {
-                const float nv = fmaf(acc, alc[s], grow[s] * xsc[s]);
-                acc = (s <= 4 * k || s <= t) ? nv : acc;   // steps 0..4k are <= t in every lane
-            }
-            sw[kI + c * kRs + t] = acc;
-        }
+        for (int k = 0; k < 4; ++k) sw[kI + c * kRs + tk[k]] = acc[k];
         __builtin_amdgcn_wave_barrier();
         const f32x4 intra = *reinterpret_cast<const f32x4*>(&sw[kI + c * kRs + 4 * g]);
 
@@ -350,16 +358,14 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
         const float zv[4] = {bf_lo(zz[0]), bf_hi(zz[0]), bf_lo(zz[1]), bf_hi(zz[1])};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float pre_gate = fmaf(ev[i], rd4[i], intra[i]) + Dd * uv[i];
+            const float pre_gate = fmaf(ev[i], rd4[i], intra[i]) + skip[i];
             yv[i] = has_z ? pre_gate * silu_f32(zv[i]) : pre_gate;
         }
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])}, ry, eoff, 0, 0);
-
-        if (more) store_bc(bcv, (q + 1) & 1);
-        dr = drn;
-        uu = uun;
-        zz = zzn;
+        zz = __builtin_amdgcn_raw_buffer_load_b64(rz, eoffn, 0, 0);
         eoff = eoffn;
+
+        store_bc(bcv, (q + 1) & 1);
         lds_barrier();
     }
 
@@ -368,7 +374,7 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) hl[16 * jt + 4 * g + r] = H[jt][r];
+            for (int r = 0; r < 4; ++r) hl[16 * jt + 4 * g + r] = sc * H[jt][r];
     }
 }
 

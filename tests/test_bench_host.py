@@ -76,3 +76,27 @@ def test_valu_issue_needs_the_profiled_source_and_shape(tmp_path, monkeypatch):
     rec["shape"] = [8, 2048, 1536, 16]
     path.write_text(json.dumps(rec))
     assert bench.measured_valu_issue(x, 0.3) is None
+
+
+def test_chunked_form_counts(tmp_path, monkeypatch):
+    """Matrix work of the chunked form on the scalar-decay N = 128 workload (128 channel
+    blocks x 512 chunks of 16 steps; pieces of 1376 steps, the aggregate over five), and
+    its VALU issue reported only for the profiled source and shape."""
+    x = SimpleNamespace(batch=2, L=8192, dim=4096, N=128)
+    plan = {"nchunks": 6, "chunk_len": 1376}
+    gram = 2 * 16 * 16 * 128                 # C^T B, in each of the 4 waves
+    read = 2 * 16 * 64 * 128                 # state read, one part
+    update = 2 * 128 * 64 * 16               # state update, one part
+    agg = 2 * 128 * 64                       # aggregate, per step and part
+    assert bench.chunked_mfma_flops(x, plan) == 128 * 512 * (4 * gram + 2 * read + 2 * update) + 128 * 5 * 1376 * 2 * agg
+    path = tmp_path / "chk.json"
+    monkeypatch.setattr(bench, "CHUNKED_FILE", str(path))
+    assert bench.measured_chunked_issue(x, 0.4) is None
+    rec = {"kernel_source_sha256_16": bench.chunked_hash(), "shape": [2, 8192, 4096, 128],
+           "SQ_INSTS_VALU": 1.3e8, "SQ_INSTS_VALU_TRANS_F32": 8e6}
+    path.write_text(json.dumps(rec))
+    vi = bench.measured_chunked_issue(x, 0.4)
+    assert abs(vi["issue_frac"] - 4 * 1.38e8 / (1024 * 2.4e9 * 0.4e-3)) < 1e-3
+    rec["kernel_source_sha256_16"] = "0" * 16 if bench.chunked_hash() != "0" * 16 else "1" * 16
+    path.write_text(json.dumps(rec))
+    assert bench.measured_chunked_issue(x, 0.4) is None
