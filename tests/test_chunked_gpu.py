@@ -123,3 +123,15 @@ def test_chunked_form_carried_state_in_slices():
     ey, eh = rel_err(ycat, yref), rel_err(h.cpu().numpy(), href)
     print(f"slices: err y={ey:.3e} h={eh:.3e}", flush=True)
     assert ey <= TOL["bf16"] and eh <= 1e-4
+
+
+def test_chunked_form_is_bitwise_deterministic():
+    """Two calls on the same inputs (the library's plan, in pieces) give the same bits:
+    every sum has a fixed order (matrix products, per-wave exchanges, no atomics)."""
+    announce("chunked form determinism (2, 4096, 256, 128) 4 heads")
+    x = make_inputs(2, 4096, 256, 128, seed=723, io="bf16", nheads=4)
+    dev = to_device(x)
+    assert plan_of(2, 4096, 256, 128, 4)["form"] == 1
+    y1 = run_gpu(x, dev=dev)
+    y2 = run_gpu(x, dev=dev)
+    np.testing.assert_array_equal(y1, y2)
