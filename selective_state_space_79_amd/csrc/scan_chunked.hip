@@ -15,11 +15,14 @@
 // sum of cnblogs.com "Mamba3 技术浅析" §2.2.2).  The state read C^T H, the state update
 // B (E x) and the chunk's Gram matrix G = C^T B are dense products on
 // v_mfma_f32_16x16x32_bf16.  The decays E(t,s) differ per channel, so the masked
-// in-chunk part sum_{s<=t} G[t,s] E(t,s) x_s is not one product for all channels; it
-// is evaluated per channel on the vector ALUs in Horner form,
+// in-chunk part sum_{s<=t} G[t,s] E(t,s) x_s has no decay matrix shared by the
+// channels.  Since E(t,s) = E(Q-1,s) / E(Q-1,t), it is the masked G times the state
+// update's weighted inputs E(Q-1,s) x_s (one more product), each output then divided
+// by E(Q-1,t) -- when the chunk's decay stays above 2^-80, so that the division is
+// safe; a wave where it does not evaluates the part per channel in Horner form,
 //   acc <- acc * al_s + G[t,s] x_s   for s = 0..t,
-// two operations per (t, s) pair.  With kQ = 16 that is 8.5 pairs per output, against
-// the N = 128 state updates per output of the lane walk.
+// two operations per (t, s) pair (8.5 pairs per output with kQ = 16, against the
+// N = 128 state updates per output of the lane walk).
 //
 // Precision: G multiplies bf16 inputs exactly (fp32 accumulation).  The state and the
 // weighted inputs E x are fp32 quantities, split into a high and a low bf16 part
@@ -258,8 +261,6 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
         dr = __builtin_amdgcn_raw_buffer_load_b64(rd, eoffn, 0, 0);
         uu = __builtin_amdgcn_raw_buffer_load_b64(ru, eoffn, 0, 0);
         sw[kTot + 4 * c + g] = pre[3];
-        *reinterpret_cast<f32x4*>(&sw[kAl + c * kRs + 4 * g]) = f32x4{al[0], al[1], al[2], al[3]};
-        *reinterpret_cast<f32x4*>(&sw[kXs + c * kRs + 4 * g]) = f32x4{xs[0], xs[1], xs[2], xs[3]};
         __builtin_amdgcn_wave_barrier();
         const f32x4 tot = *reinterpret_cast<const f32x4*>(&sw[kTot + 4 * c]);
         const float excl = g == 0 ? 0.0f : g == 1 ? tot[0] : g == 2 ? tot[0] + tot[1] : tot[0] + tot[1] + tot[2];
@@ -273,7 +274,16 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
         ev[0] = sc * __builtin_amdgcn_exp2f(a * (excl + pre[0]));
 #pragma unroll
         for (int i = 1; i < 4; ++i) ev[i] = ev[i - 1] * al[i];
-        float scn = sc * __builtin_amdgcn_exp2f(a * cumq);
+        const float dec = __builtin_amdgcn_exp2f(a * cumq);
+        float scn = sc * dec;
+        // The in-chunk part as a matrix product (fast) needs the chunk's decay to stay
+        // above 2^-80 in every lane of the wave; otherwise the wave sums it per channel in
+        // Horner form, from the steps' decays and values in its LDS area.
+        const bool fast = __builtin_amdgcn_ballot_w64(dec < 0x1p-80f) == 0;
+        if (!fast) {
+            *reinterpret_cast<f32x4*>(&sw[kAl + c * kRs + 4 * g]) = f32x4{al[0], al[1], al[2], al[3]};
+            *reinterpret_cast<f32x4*>(&sw[kXs + c * kRs + 4 * g]) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+        }
 
         // ---- matrix cores: G = C^T B, the state read C^T H, the state update
         bf16x8 ct[NKB];
@@ -292,6 +302,8 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
             rd4 = mfma(ct[kb], __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}), rd4);
             rd4 = mfma(ct[kb], __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), rd4);
         }
+        bf16x8 xop;
+        float rwv[4];
         {
             // the state update of the scaled state: when some lane's new scale would fall
             // below 2^-60 the wave first folds the scales into H (scale 1), so that 1 / scale
@@ -305,6 +317,7 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
             float rw = __builtin_amdgcn_exp2f(fmaf(a, cumq - (excl + pre[3]), kLog2Ln2)) * __builtin_amdgcn_rcpf(scn);
 #pragma unroll
             for (int i = 3; i >= 0; --i) {
+                rwv[i] = rw;
                 wx[i] = rw * xs[i];
                 if (i > 0) rw *= al[i];
             }
@@ -312,7 +325,7 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
             uint32_t whi[2], wlo[2];
             split2(wx[0], wx[1], whi[0], wlo[0]);
             split2(wx[2], wx[3], whi[1], wlo[1]);
-            const bf16x8 xop = __builtin_bit_cast(bf16x8, u32x4{whi[0], whi[1], wlo[0], wlo[1]});
+            xop = __builtin_bit_cast(bf16x8, u32x4{whi[0], whi[1], wlo[0], wlo[1]});
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) {
                 const int n = 16 * jt + c;
@@ -325,33 +338,55 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
         for (int r = 0; r < 4; ++r) sw[kG + (4 * g + r) * kRs + c] = gm[r] * kLn2;
         __builtin_amdgcn_wave_barrier();
 
-        // ---- in-chunk part, per channel in Horner form: output k of the lane (step
-        // t_k = horner_t(k, g), k = 0..3) takes acc <- acc * al_s + G[t_k][s] x_s over
-        // s = 0..t_k.  The steps go in blocks of 4 (the block's decays and values read
-        // once, as 16-byte vectors); block m feeds the outputs k >= m, and only the
-        // last block of output k has steps past t_k in some lanes.
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        int tk[4];
+        // ---- in-chunk part sum_{s<=t} G[t,s] E(t,s) x_s
+        f32x4 intra;
+        if (fast) {
+            // E(t,s) = E(15,s) / E(15,t): the state update's weighted inputs
+            // wx_s = E(15,s) x_s / sc (its B operand, already split) times the masked G,
+            // one matrix product, then each output divided by its own E(15,t) / sc factor
+            // (1 / rw_t, ln2 included: the array holds G times ln2).  Lane l supplies
+            // row t = l % 16 of G at the slots of steps 4(l/16)..+3, both parts.
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(&sw[kG + c * kRs + 4 * g]);
+            float gmk[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) tk[k] = horner_t(k, g);
+            for (int e = 0; e < 4; ++e) gmk[e] = (4 * g + e <= c) ? gv[e] : 0.0f;
+            uint32_t ghi[2], glo[2];
+            split2(gmk[0], gmk[1], ghi[0], glo[0]);
+            split2(gmk[2], gmk[3], ghi[1], glo[1]);
+            f32x4 ia = mfma(__builtin_bit_cast(bf16x8, u32x4{ghi[0], ghi[1], ghi[0], ghi[1]}), xop,
+                            f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            ia = mfma(__builtin_bit_cast(bf16x8, u32x4{glo[0], glo[1], glo[0], glo[1]}), xop, ia);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f32x4 va = *reinterpret_cast<const f32x4*>(&sw[kAl + c * kRs + 4 * m]);
-            const f32x4 vx = *reinterpret_cast<const f32x4*>(&sw[kXs + c * kRs + 4 * m]);
+            for (int i = 0; i < 4; ++i) intra[i] = ia[i] * __builtin_amdgcn_rcpf(rwv[i]);
+        } else {
+            // ---- in-chunk part, per channel in Horner form: output k of the lane (step
+            // t_k = horner_t(k, g), k = 0..3) takes acc <- acc * al_s + G[t_k][s] x_s over
+            // s = 0..t_k.  The steps go in blocks of 4 (the block's decays and values read
+            // once, as 16-byte vectors); block m feeds the outputs k >= m, and only the
+            // last block of output k has steps past t_k in some lanes.
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            int tk[4];
 #pragma unroll
-            for (int k = m; k < 4; ++k) {
-                const f32x4 gv = *reinterpret_cast<const f32x4*>(&sw[kG + tk[k] * kRs + 4 * m]);
+            for (int k = 0; k < 4; ++k) tk[k] = horner_t(k, g);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float nv = fmaf(acc[k], va[e], gv[e] * vx[e]);
-                    acc[k] = (m < k || 4 * m + e <= tk[k]) ? nv : acc[k];   // steps 0..4k are <= t_k in every lane
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 va = *reinterpret_cast<const f32x4*>(&sw[kAl + c * kRs + 4 * m]);
+                const f32x4 vx = *reinterpret_cast<const f32x4*>(&sw[kXs + c * kRs + 4 * m]);
+#pragma unroll
+                for (int k = m; k < 4; ++k) {
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&sw[kG + tk[k] * kRs + 4 * m]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float nv = fmaf(acc[k], va[e], gv[e] * vx[e]);
+                        acc[k] = (m < k || 4 * m + e <= tk[k]) ? nv : acc[k];   // steps 0..4k are <= t_k in every lane
+                    }
                 }
             }
-        }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) sw[kI + c * kRs + tk[k]] = acc[k];
-        __builtin_amdgcn_wave_barrier();
-        const f32x4 intra = *reinterpret_cast<const f32x4*>(&sw[kI + c * kRs + 4 * g]);
+            for (int k = 0; k < 4; ++k) sw[kI + c * kRs + tk[k]] = acc[k];
+            __builtin_amdgcn_wave_barrier();
+            intra = *reinterpret_cast<const f32x4*>(&sw[kI + c * kRs + 4 * g]);
+        }
 
         // ---- outputs of steps 4g..4g+3: (in-chunk + decayed read + D u) * SiLU(z)
         float yv[4];
