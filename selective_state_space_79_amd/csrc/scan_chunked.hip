@@ -33,9 +33,11 @@
 // four waves.  Wave w owns channels 16w .. 16w+15: their state columns (all N rows, in
 // the MFMA result layout), and lane l the channel 16w + l % 16 at steps 4(l/16)..+3 of
 // each chunk, for everything elementwise.  B and C of a chunk are staged once in LDS
-// for the four waves (double-buffered, one barrier per chunk); everything else is
-// exchanged within a wave.  The pieces' starting states come from the piece carries
-// (scan_piece_states_kernel and scan_carry_kernel in scan_fwd.hip).
+// for the four waves (double-buffered, one barrier per chunk).  delta, u and z come in
+// groups of 4 chunks -- each row's whole 128-byte line of 64 steps at once, straight
+// into a per-wave LDS area -- so that a line is fetched once instead of once per chunk;
+// everything else is exchanged within a wave.  The pieces' starting states come from
+// the piece carries (scan_piece_states_kernel and scan_carry_kernel in scan_fwd.hip).
 #include "scan_common.h"
 
 namespace {
@@ -59,19 +61,35 @@ constexpr int kRs = 20;                     // row stride (floats) of the per-wa
                                             // 16-lane row accesses of 16 bytes cover all banks
 constexpr uint32_t kPast = 0x80000000u;     // a buffer offset past every window
 
-// Per-wave LDS (floats): the 4 group sums of dt2 of each channel, then, per channel,
-// the decays al_s and the values x_s / ln2 of the chunk's steps, the chunk's Gram
-// matrix G[t][s] (times ln2), and the in-chunk outputs of each channel.
+// Per-wave LDS (floats): the 4 group sums of dt2 of each channel and the chunk's Gram
+// matrix G[t][s] (times ln2).
 constexpr int kTot = 0;                     // [16 ch][4]
-constexpr int kAl = kTot + 64;              // [16 ch][kRs]
-constexpr int kXs = kAl + 16 * kRs;         // [16 ch][kRs]
-constexpr int kG = kXs + 16 * kRs;          // [16 t][kRs]
-constexpr int kI = kG + 16 * kRs;           // [16 ch][kRs]
-constexpr int kWaveFloats = kI + 16 * kRs;
+constexpr int kG = kTot + 64;               // [16 t][kRs]
+constexpr int kWaveFloats = kG + 16 * kRs;
+
+// Per-wave staging of the wave's 16 channel rows of delta, u and z for a group of 4
+// chunks (64 steps: one whole 128-byte line per row), loaded straight into LDS.
+constexpr int kGroup = 4 * kQ;              // steps per group
+constexpr int kStage = 16 * kGroup;         // bf16 per array and wave
+enum { kSD = 0, kSU = 1, kSZ = 2 };
 
 template <int N> constexpr size_t lds_bytes() {
-    return size_t(2) * 2 * N * kQ * sizeof(uint16_t) + size_t(kWaves) * kWaveFloats * sizeof(float);
+    return size_t(2) * 2 * N * kQ * sizeof(uint16_t) + size_t(kWaves) * kWaveFloats * sizeof(float) +
+           size_t(kWaves) * 3 * kStage * sizeof(uint16_t);
 }
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds + 16 l
+// (lds wave-uniform), counted like any other vector-memory load.  (A plain device
+// function: the builtin inside a kernel template leaves the template without a host
+// stub.)
+__device__ inline void load_lds16(Rsrc r, void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Staged row r (0..15) keeps its 16-byte piece p (steps 8p..8p+7 of the group) in slot
+// p ^ ((r >> 1) & 7) of its 128-byte row: the 8-byte reads of a chunk (rows 0..15, one
+// piece each, two lane groups per pass) then touch each bank once.
+__device__ constexpr int stage_slot(int r, int p) { return p ^ ((r >> 1) & 7); }
 
 __device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
@@ -122,11 +140,6 @@ __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF000
 // s_barrier; outstanding global loads (the next chunk's prefetch) are not waited for.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Step of the k-th in-chunk output a lane of group g computes in the Horner part:
-// g, 7 - g, 8 + g, 15 - g, so that every lane evaluates 34 (t, s) pairs.
-__device__ inline int horner_t(int k, int g) {
-    return k == 0 ? g : k == 1 ? 7 - g : k == 2 ? 8 + g : 15 - g;
-}
 }  // namespace chk
 
 template <int N>
@@ -139,6 +152,7 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
     static_assert(N == 64 || N == 128, "64 or 128 states");
     __shared__ __attribute__((aligned(16))) uint16_t sBC[2][2 * MAT];
     __shared__ __attribute__((aligned(16))) float sWave[kWaves * kWaveFloats];
+    __shared__ __attribute__((aligned(16))) uint16_t sStage[kWaves][3][kStage];
 
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -204,6 +218,24 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
     auto elem_off = [&](int64_t t0) {
         return (dok && t0 + 4 * g < tend) ? lane_off + uint32_t(2 * t0) : kPast;
     };
+    // Group loads: instruction h of an array puts rows 8h..8h+7 of the wave; lane l
+    // loads piece (l & 7) ^ ((r >> 1) & 7) of row r = 8h + (l >> 3), so that it lands in
+    // the slot stage_slot() gives.  Rows past dim and steps past L read zeros.
+    uint32_t st_off[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + (lane >> 3);
+        st_off[h] = uint32_t(16 * wv + r) * uint32_t(rowbytes) + 16u * uint32_t(stage_slot(r, lane & 7));
+    }
+    auto stage = [&](int arr, const Rsrc& rs, int64_t tg) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) load_lds16(rs, &sStage[wv][arr][512 * h], st_off[h] + uint32_t(2 * tg));
+    };
+    // this lane's 4 steps (16k + 4g ..) of chunk k of the group in array arr
+    auto staged = [&](int arr, int k) {
+        const int slot = stage_slot(c, 2 * k + (g >> 1));
+        return *reinterpret_cast<const u32x2*>(&sStage[wv][arr][c * kGroup + 8 * slot + 4 * (g & 1)]);
+    };
 
     // ---- starting state: rows n = 16 jt + 4g + r of column chl
     f32x4 H[NT];
@@ -227,22 +259,40 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
 
     // ---- chunk 0's inputs
     u32x4 bcv[VPT];
+    stage(kSD, rd, tbeg);
+    stage(kSU, ru, tbeg);
+    if (has_z) stage(kSZ, rz, tbeg);
     load_bc(bcv, tbeg);
-    uint32_t eoff = elem_off(tbeg);
-    u32x2 dr = __builtin_amdgcn_raw_buffer_load_b64(rd, eoff, 0, 0);
-    u32x2 uu = __builtin_amdgcn_raw_buffer_load_b64(ru, eoff, 0, 0);
-    u32x2 zz = __builtin_amdgcn_raw_buffer_load_b64(rz, eoff, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     store_bc(bcv, 0);
     lds_barrier();
 
-    // Every prefetch register is reloaded right after its last use (no copies between
-    // loop-carried registers, whose waits would drain the outstanding stores too).  The
-    // loads after a piece's last chunk read zeros or the next piece's data, unused.
+    // Loads: B and C one chunk ahead (registers, then LDS); delta, u and z one group of
+    // 4 chunks ahead, straight into the wave's staging area, each issued right after the
+    // group's last read of it (delta and u after the last chunk's elementwise part, z
+    // after its outputs) and waited for at their first read in the next group:
+    // vector memory completes in issue order, and after the delta and u loads at most
+    // the outputs' store, the 2 z loads and this chunk's VPT B/C loads are issued; after
+    // the z loads only the VPT B/C loads.  The loads after a piece's last chunk read
+    // zeros or the next piece's data, unused.
+    uint32_t eoff = elem_off(tbeg);
     for (int q = 0; q < nq; ++q) {
         const int64_t t0 = tbeg + int64_t(q) * kQ;
         const uint16_t* sb = sBC[q & 1];
+        const int k = q & 3;
+        const bool group_end = (k == 3) && (q + 1 < nq);   // the next group's loads go out in this chunk
         const uint32_t eoffn = elem_off(t0 + kQ);
         load_bc(bcv, t0 + kQ);
+        if (k == 0 && q > 0) {
+            // after this group's delta and u loads: the previous chunk's store (counted or
+            // not), its 2 z loads when there is a gate, and the VPT B/C loads just issued
+            if (has_z)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 + VPT) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPT) : "memory");
+        }
+        const u32x2 dr = staged(kSD, k);
+        const u32x2 uu = staged(kSU, k);
 
         // ---- elementwise: steps 4g..4g+3 of channel chl (steps past the piece are
         // identity steps: dt2 = 0, x = 0)
@@ -258,8 +308,6 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
             pre[i] = (i == 0) ? dt2[0] : pre[i - 1] + dt2[i];
             skip[i] = Dd * uv[i];
         }
-        dr = __builtin_amdgcn_raw_buffer_load_b64(rd, eoffn, 0, 0);
-        uu = __builtin_amdgcn_raw_buffer_load_b64(ru, eoffn, 0, 0);
         sw[kTot + 4 * c + g] = pre[3];
         __builtin_amdgcn_wave_barrier();
         const f32x4 tot = *reinterpret_cast<const f32x4*>(&sw[kTot + 4 * c]);
@@ -278,12 +326,16 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
         float scn = sc * dec;
         // The in-chunk part as a matrix product (fast) needs the chunk's decay to stay
         // above 2^-80 in every lane of the wave; otherwise the wave sums it per channel in
-        // Horner form, from the steps' decays and values in its LDS area.
+        // Horner form.
         const bool fast = __builtin_amdgcn_ballot_w64(dec < 0x1p-80f) == 0;
-        if (!fast) {
-            *reinterpret_cast<f32x4*>(&sw[kAl + c * kRs + 4 * g]) = f32x4{al[0], al[1], al[2], al[3]};
-            *reinterpret_cast<f32x4*>(&sw[kXs + c * kRs + 4 * g]) = f32x4{xs[0], xs[1], xs[2], xs[3]};
-        }
+        // the next group's delta and u, once this group's last reads of them are done
+        // (the Horner form reads them again further down)
+        auto stage_du = [&]() {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            stage(kSD, rd, t0 + kQ);
+            stage(kSU, ru, t0 + kQ);
+        };
+        if (group_end && fast) stage_du();
 
         // ---- matrix cores: G = C^T B, the state read C^T H, the state update
         bf16x8 ct[NKB];
@@ -359,37 +411,45 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
 #pragma unroll
             for (int i = 0; i < 4; ++i) intra[i] = ia[i] * __builtin_amdgcn_rcpf(rwv[i]);
         } else {
-            // ---- in-chunk part, per channel in Horner form: output k of the lane (step
-            // t_k = horner_t(k, g), k = 0..3) takes acc <- acc * al_s + G[t_k][s] x_s over
-            // s = 0..t_k.  The steps go in blocks of 4 (the block's decays and values read
-            // once, as 16-byte vectors); block m feeds the outputs k >= m, and only the
-            // last block of output k has steps past t_k in some lanes.
+            // ---- in-chunk part per channel in Horner form, acc <- acc * al_s + G[t][s] x_s
+            // over s = 0..t for the lane's outputs t = 4g + i: every lane recomputes its
+            // channel's step sizes, decays and values from the staged rows, 4 steps at a
+            // time (this wave only, when a chunk's decay falls below 2^-80)
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            int tk[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) tk[k] = horner_t(k, g);
-#pragma unroll
+#pragma unroll 1
             for (int m = 0; m < 4; ++m) {
-                const f32x4 va = *reinterpret_cast<const f32x4*>(&sw[kAl + c * kRs + 4 * m]);
-                const f32x4 vx = *reinterpret_cast<const f32x4*>(&sw[kXs + c * kRs + 4 * m]);
+                const int slot = stage_slot(c, 2 * k + (m >> 1));
+                const u32x2 bd = *reinterpret_cast<const u32x2*>(&sStage[wv][kSD][c * kGroup + 8 * slot + 4 * (m & 1)]);
+                const u32x2 bu = *reinterpret_cast<const u32x2*>(&sStage[wv][kSU][c * kGroup + 8 * slot + 4 * (m & 1)]);
+                const bool vm = dok && t0 + 4 * m < tend;
+                const float bdr[4] = {bf_lo(bd[0]), bf_hi(bd[0]), bf_lo(bd[1]), bf_hi(bd[1])};
+                const float buv[4] = {bf_lo(bu[0]), bf_hi(bu[0]), bf_lo(bu[1]), bf_hi(bu[1])};
+                float alm[4], xsm[4];
 #pragma unroll
-                for (int k = m; k < 4; ++k) {
-                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&sw[kG + tk[k] * kRs + 4 * m]);
+                for (int e = 0; e < 4; ++e) {
+                    const float dt = vm ? softplus_log2(bdr[e] + bias) : 0.0f;
+                    xsm[e] = vm ? dt * buv[e] : 0.0f;
+                    alm[e] = __builtin_amdgcn_exp2f(a * dt);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&sw[kG + (4 * g + i) * kRs + 4 * m]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float nv = fmaf(acc[k], va[e], gv[e] * vx[e]);
-                        acc[k] = (m < k || 4 * m + e <= tk[k]) ? nv : acc[k];   // steps 0..4k are <= t_k in every lane
+                        const float nv = fmaf(acc[i], alm[e], gv[e] * xsm[e]);
+                        acc[i] = (4 * m + e <= 4 * g + i) ? nv : acc[i];
                     }
                 }
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) sw[kI + c * kRs + tk[k]] = acc[k];
-            __builtin_amdgcn_wave_barrier();
-            intra = *reinterpret_cast<const f32x4*>(&sw[kI + c * kRs + 4 * g]);
+            for (int i = 0; i < 4; ++i) intra[i] = acc[i];
+            if (group_end) stage_du();
         }
 
         // ---- outputs of steps 4g..4g+3: (in-chunk + decayed read + D u) * SiLU(z)
         float yv[4];
+        if (k == 0 && q > 0 && has_z) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPT) : "memory");
+        const u32x2 zz = has_z ? staged(kSZ, k) : u32x2{0u, 0u};
         const float zv[4] = {bf_lo(zz[0]), bf_hi(zz[0]), bf_lo(zz[1]), bf_hi(zz[1])};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -397,7 +457,10 @@ __global__ void __launch_bounds__(chk::kThreads) scan_chunked_kernel(ssm_detail:
             yv[i] = has_z ? pre_gate * silu_f32(zv[i]) : pre_gate;
         }
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])}, ry, eoff, 0, 0);
-        zz = __builtin_amdgcn_raw_buffer_load_b64(rz, eoffn, 0, 0);
+        if (group_end && has_z) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this group's z reads are done
+            stage(kSZ, rz, t0 + kQ);
+        }
         eoff = eoffn;
 
         store_bc(bcv, (q + 1) & 1);
