@@ -135,3 +135,32 @@ def test_chunked_form_is_bitwise_deterministic():
     y1 = run_gpu(x, dev=dev)
     y2 = run_gpu(x, dev=dev)
     np.testing.assert_array_equal(y1, y2)
+
+
+def test_form_one_plan_with_unaligned_rows_runs_the_walk():
+    """A plan of form 1 whose rows, at the call, do not allow 16-byte loads (the arrays
+    start 2 bytes past a 16-byte boundary) runs the lane walk with the same pieces; the
+    outputs still match the oracle."""
+    import torch
+    import selective_state_space_79_amd as ssm
+
+    announce("form-1 plan, unaligned rows (1, 520, 128, 128) 2 heads, 3 pieces")
+    x = make_inputs(1, 520, 128, 128, seed=724, io="bf16", nheads=2)
+    assert plan_of(1, 520, 128, 128, 2, 3)["form"] == 1
+    dev = to_device(x)
+
+    def shifted(t):
+        # same values, a buffer that starts one element past the allocation's start
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 != 0
+        return v
+
+    un = {k: (shifted(v) if k in ("u", "delta", "z", "B", "C") else v) for k, v in dev.items()}
+    y = ssm.selective_scan_fwd(un["u"], un["delta"], un["A"], un["B"], un["C"], un["D"], un["z"], un["dt_bias"],
+                               nchunks=3)
+    torch.cuda.synchronize()
+    err = rel_err(y.float().cpu().numpy(), run_oracle(x))
+    print(f"err={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
