@@ -5,7 +5,8 @@ They cover the planner's branches together:
 - state counts across the narrow, role-split and wide paths, padding included;
 - diagonal and scalar decay, f32 and bf16 rows;
 - ragged lengths and channel counts, and lengths that allow or rule out vector loads;
-- forced piece counts, including the pieces whose states the matrix cores form.
+- forced piece counts, including the pieces whose states the matrix cores form;
+- and, drawn separately, shapes that run the chunked form of the scalar-decay scan.
 Bars are the contract's: 1e-4 for f32 rows, 2e-2 for bf16 (and, for the backward's
 float32 reductions, 1e-4 of each tensor's scale; see bwd_cases.py).
 """
@@ -77,3 +78,45 @@ def test_backward_random_shape(case):
     for k, e in errs.items():
         bar = 2e-2 if (io == "bf16" and k in ("du", "ddelta", "dz")) else 1e-4
         assert e <= bar, (k, e)
+
+
+def _draw_chunked(seed: int, count: int, max_elems: int):
+    """Shapes the planner gives the chunked form (plan form 1): scalar decay, bf16 rows,
+    64 or 128 states, L a multiple of 8; heads of 8..128 channels, ragged channel
+    blocks and last chunks, library-chosen or forced piece counts, with or without the
+    skip, gate and bias."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        N = int(rng.choice([64, 128]))
+        nheads = int(rng.integers(1, 7))
+        head_dim = int(rng.choice([8, 13, 40, 64, 128]))
+        dim = nheads * head_dim
+        L = 8 * int(rng.integers(1, 400))
+        batch = int(rng.integers(1, 4))
+        nch = int(rng.choice([0, 0, 2, 3, 7]))
+        flags = tuple(bool(v) for v in rng.integers(0, 2, size=3))
+        if batch * L * dim * N > max_elems:
+            continue
+        cases.append((batch, L, dim, N, nheads, nch) + flags)
+    return cases
+
+
+CHUNKED = _draw_chunked(5152, 12, 8_000_000)
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=lambda c: "b{}L{}d{}N{}h{}ch{}D{:d}z{:d}bias{:d}".format(*c))
+def test_chunked_form_random_shape(case):
+    import selective_state_space_79_amd as ssm
+
+    batch, L, dim, N, nheads, nch, wD, wz, wb = case
+    seed = 5400 + CHUNKED.index(case)
+    plan = ssm.ssm_selective_scan_plan(ssm.make_dims(batch, L, dim, N, nheads=nheads, nchunks=nch)).as_dict()
+    announce(f"chunked random {case} seed={seed} plan {plan['nchunks']} pieces")
+    assert plan["form"] == 1
+    x = make_inputs(batch, L, dim, N, seed=seed, io="bf16", nheads=nheads)
+    y = run_gpu(x, with_D=wD, with_z=wz, with_bias=wb, nchunks=nch)
+    err = rel_err(y, run_oracle(x, with_D=wD, with_z=wz, with_bias=wb))
+    print(f"err={err:.3e}", flush=True)
+    assert np.all(np.isfinite(y))
+    assert err <= TOL["bf16"]
